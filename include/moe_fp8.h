@@ -1,0 +1,172 @@
+/*
+ * moe_fp8.h — C ABI of libmoe_fp8.so: one Mixture-of-Experts FFN layer whose
+ * expert weights are stored as block-FP8 (OCP E4M3FN bytes with one fp32 scale
+ * per square block), computed on one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes, per token t (x_t is one row of x):
+ *   l      = x_t · Wrᵀ (+ b)                      router logits, fp32 accumulate
+ *   S      = the top_k experts by l, ties to the lower expert index,
+ *            in descending-logit order (slot j = 0 .. top_k-1)
+ *   g_j    = exp(l_{S_j}) / Σ_{e∈S} exp(l_e)      softmax renormalised over S
+ *   for each selected expert e (and, if present, the shared expert with weight 1):
+ *     W    = dec(q) · scale[row/B][col/B]         block-FP8 dequantisation
+ *     h    = silu(x_t · Wgᵀ) ⊙ (x_t · Wuᵀ)         SwiGLU, silu(z) = z / (1 + e^-z)
+ *     y_e  = h · Wdᵀ
+ *   out_t  = Σ_j g_j · y_{S_j} (+ y_shared)        fixed order j = 0..k-1, then shared
+ *
+ * Sources. The colizig page ("What this project is trying to prove", "Features",
+ * "Status", "Architecture & how it works") names the pieces: natively block-FP8
+ * (E4M3) expert weights, top-8-of-128 and top-10-of-512 routing with one
+ * always-on shared expert, dequantisation fused into the dot product, per-expert
+ * fan-out, and experts as the bulk of the parameters. The pages do not write
+ * out the routing function, the FFN non-linearity, the block size, the E4M3
+ * variant or the layout; the readings taken here are the ones stated above and
+ * beside each field below (softmax over the logits, renormalised top-k gates,
+ * SwiGLU, OCP E4M3FN with max 448, multiplicative fp32 block scales).
+ *
+ * Conventions for every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *    never frees, keeps or aliases it beyond the call's stream work.
+ *  - The library allocates no memory; scratch lives in the caller's workspace,
+ *    whose size moe_workspace_bytes() reports (256-byte aligned base required).
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *    legacy default stream) and the call returns without host synchronisation.
+ *  - Arguments are validated on the host before anything is launched. A status
+ *    other than MOE_OK from validation means nothing was enqueued. MOE_ERR_HIP
+ *    means a launch failed; work enqueued before it may have run.
+ *  - Results are deterministic: the same inputs give the same bits (no float
+ *    atomics; sums are taken in a fixed order).
+ *  - tokens == 0 is valid and enqueues nothing.
+ *  - There is no CPU fallback: a layer shape without a compiled kernel returns
+ *    MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                            */
+  MOE_ERR_SHAPE = 2,       /* non-positive size, top_k outside [1, experts], block   */
+                           /* not dividing hidden/inter, bad enum value             */
+  MOE_ERR_UNSUPPORTED = 3, /* no kernel instantiated for this (hidden, inter, block, */
+                           /* dtype, path) combination                              */
+  MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_bytes()          */
+                           /* or not 256-byte aligned                               */
+  MOE_ERR_HIP = 5          /* a HIP launch or event call failed                     */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Expert-pass kernel family. AUTO picks the wavefront GEMV family when
+ * tokens <= 16 or x is fp32, and the bf16-MFMA grouped family otherwise.
+ * The forced values exist so both families can be exercised at any size;
+ * MFMA requires bf16 activations. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_MFMA = 2 } moe_path;
+
+typedef struct {
+  int64_t tokens;      /* T: rows of x and out                                    */
+  int32_t hidden;      /* H                                                       */
+  int32_t experts;     /* E: routed experts (1 .. 1024)                           */
+  int32_t inter;       /* I: expert intermediate size                             */
+  int32_t top_k;       /* k: experts selected per token, 1 .. min(E, 16)          */
+  int32_t block;       /* B: square scale-block edge; must divide H and I         */
+  int32_t has_shared;  /* 0 or 1: an always-on shared expert of the same shape    */
+  moe_dtype x_dtype;   /* dtype of x (MOE_F32 or MOE_BF16)                        */
+  moe_dtype out_dtype; /* dtype of out (MOE_F32 or MOE_BF16)                      */
+  moe_path path;       /* expert kernel family                                    */
+} moe_config;
+
+/* One bank of n experts (n = E for the routed bank, 1 for the shared expert).
+ * Row-major, contiguous, expert-major:
+ *   w_gate_up [n][2I][H]     E4M3FN bytes; rows 0..I-1 are the gate projection,
+ *                            rows I..2I-1 the up projection
+ *   w_down    [n][H][I]      E4M3FN bytes
+ *   s_gate_up [n][2I/B][H/B] fp32 scale of each B×B block of w_gate_up
+ *   s_down    [n][H/B][I/B]  fp32 scale of each B×B block of w_down
+ * A weight's value is dec(byte) · scale of its block, dec = OCP E4M3FN
+ * (bias 7, no infinities, 0x7F/0xFF NaN, max finite 448). NaN bytes are not
+ * supported inputs. */
+typedef struct {
+  const uint8_t* w_gate_up;
+  const uint8_t* w_down;
+  const float* s_gate_up;
+  const float* s_down;
+} moe_expert_bank;
+
+/* Optional per-phase HIP events (hipEvent_t passed as void*). Each non-NULL
+ * event is recorded on `stream` at the named phase boundary, so a caller can
+ * time the phases of a call with hipEventElapsedTime. NULL entries are
+ * skipped; pass NULL for the whole struct to record nothing. */
+typedef enum {
+  MOE_EV_START = 0,        /* before the router                            */
+  MOE_EV_ROUTED = 1,       /* after logits + top-k + gates                 */
+  MOE_EV_PERMUTED = 2,     /* after the token→expert permutation           */
+  MOE_EV_GATE_UP = 3,      /* after gate/up + SwiGLU (routed and shared)   */
+  MOE_EV_DOWN = 4,         /* after the down projection                    */
+  MOE_EV_END = 5,          /* after the combine                            */
+  MOE_EV_COUNT = 6
+} moe_phase;
+typedef struct {
+  void* ev[MOE_EV_COUNT];
+} moe_phase_events;
+
+/* Bytes of workspace moe_forward / moe_route / moe_permute need for `cfg`
+ * (0 on an invalid cfg). The same workspace serves all three. */
+size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Whole layer (router, top-k, permutation, SwiGLU experts, combine).
+ *   x           [T][H] of cfg->x_dtype
+ *   router_w    [E][H] fp32
+ *   router_bias [E] fp32 added to the logits (affects selection and gates),
+ *               or NULL for none
+ *   experts     routed bank, n = E (struct itself is read on the host)
+ *   shared      shared bank, n = 1; required iff cfg->has_shared, else ignored
+ *   top_k       must equal cfg->top_k
+ *   out         [T][H] of cfg->out_dtype; written, never read
+ *   workspace   device scratch of at least moe_workspace_bytes(cfg) bytes
+ *   events      optional phase events (see moe_phase_events), or NULL        */
+moe_status moe_forward(const void* x, const float* router_w, const float* router_bias,
+                       const moe_expert_bank* experts, const moe_expert_bank* shared,
+                       int32_t top_k, void* out, const moe_config* cfg,
+                       void* workspace, size_t workspace_bytes,
+                       const moe_phase_events* events, void* stream);
+
+/* Router and selection only (the first two steps of moe_forward).
+ *   topk_idx [T][k] int32 expert ids, descending logit, ties to lower id
+ *   gates    [T][k] fp32 renormalised softmax weights (sum to 1 per token)
+ *   logits   [T][E] fp32 router logits, or NULL to keep them in the workspace */
+moe_status moe_route(const void* x, const float* router_w, const float* router_bias,
+                     int32_t* topk_idx, float* gates, float* logits,
+                     const moe_config* cfg, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Token→expert permutation only (the third step of moe_forward), from a
+ * given topk_idx [T][k]. Slot s = t·k + j is the j-th choice of token t;
+ * when cfg->has_shared, slots T·k + t (t = 0..T-1) are the shared expert's.
+ *   offsets [E+2] int32: rows of routed expert e are offsets[e] .. offsets[e+1]-1;
+ *           the shared group is offsets[E] .. offsets[E+1]-1 (empty without one)
+ *   pair    [P] int32, P = T·k (+T): pair[row] = slot, rows of one expert in
+ *           ascending token order (stable by slot index)
+ *   inv     [P] int32: inv[slot] = row                                       */
+moe_status moe_permute(const int32_t* topk_idx, int32_t* offsets, int32_t* pair,
+                       int32_t* inv, const moe_config* cfg, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

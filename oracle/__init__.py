@@ -1,0 +1,20 @@
+"""CPU oracle of the block-FP8 routed MoE layer — test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package. The HIP library and its Python binding never do.
+"""
+from .moe_oracle import (  # noqa: F401
+    TIE_BAND,
+    dequantise,
+    e4m3fn_decode,
+    expert_matrices,
+    gate_weights,
+    moe_layer,
+    permutation,
+    router_logits,
+    select_topk,
+    silu,
+    softmax,
+    swiglu_expert,
+    tie_flags,
+)

@@ -1,0 +1,215 @@
+"""CPU oracle of the block-FP8 routed MoE layer (fp64 NumPy).
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import or run this module. The HIP library
+never calls it and shares no code with it; inputs reach both sides from the
+separate `workloads` generator.
+
+It is plain and slow on purpose: every step is the textbook definition, in
+fp64, one expert at a time, so that it can be checked against the pages by
+eye. Sources, per function below:
+  * colizig page, "What this project is trying to prove" (model table): both
+    model families are natively block-FP8; top-8 of 128 experts with no shared
+    expert, top-10 of 512 experts plus one shared expert.
+  * colizig page, "Features": block-FP8 (E4M3) weights whose dequantisation is
+    fused into the dot products; per-expert evaluation fanned out over workers,
+    bit-identical to the serial path; an independent NumPy reference used as a
+    correctness net for the engine.
+  * colizig page, "Architecture & how it works": experts are the bulk of the
+    parameters; the router is small and always resident.
+  * ferrite page (both languages): the CPU backend is the golden standard that
+    every other backend is validated against.
+The pages never write the layer's formulas down. Readings taken where they are
+silent (each restated at the function that uses it):
+  R1 E4M3 is OCP E4M3FN: bias 7, subnormals, no infinities, 0x7F/0xFF are NaN,
+     max finite 448 (consistent with scales of amax/448).
+  R2 a block scale multiplies: W = dec(q) * scale[row // B, col // B].
+  R3 gate/up are one [2I][H] matrix, gate rows first.
+  R4 routing is softmax over all logits, top-k on the logits with ties to the
+     lower expert index, slot order by descending logit, gates renormalised
+     over the selected experts.
+  R5 a router bias is added to the logits before selection and gating.
+  R6 the expert FFN is SwiGLU: h = silu(x Wg^T) * (x Wu^T), y = h Wd^T.
+  R7 the shared expert is always on with weight 1 and has the routed shape.
+  R8 out_t = sum_j g_j y_{t,j} (+ y_shared,t).
+  R9 a token is tie-flagged when its k-th and (k+1)-th largest logits differ by
+     less than 1e-5 (absolute, on these fp64 logits); its selection is then not
+     unique at the kernel's precision.
+Every function here is pinned by tests/test_oracle_pins.py; no function is
+parity-unpinned.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional
+
+import numpy as np
+
+TIE_BAND = 1e-5
+
+
+# --------------------------------------------------------------------------
+# block-FP8 weights (R1, R2, R3)
+# --------------------------------------------------------------------------
+def e4m3fn_decode(codes) -> np.ndarray:
+    """Value of each OCP E4M3FN byte, by the closed form (R1):
+    sign s = b >> 7, exponent e = (b >> 3) & 15, mantissa m = b & 7;
+    e == 0: (-1)^s * m * 2^-9 (subnormal); e == 15 and m == 7: NaN;
+    otherwise (-1)^s * 2^(e - 7) * (1 + m / 8)."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = b >> 7
+    e = (b >> 3) & 15
+    m = b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
+    val = np.where(s == 1, -mag, mag)
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return val.astype(np.float64)
+
+
+def dequantise(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
+    """W[r, c] = dec(codes[r, c]) * scales[r // block, c // block] (R2), fp64."""
+    w = e4m3fn_decode(codes)
+    if np.isnan(w).any():
+        raise ValueError("E4M3 NaN code in a weight matrix")
+    s = np.asarray(scales, dtype=np.float64)
+    s_full = np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+    assert s_full.shape == w.shape, (s_full.shape, w.shape)
+    return w * s_full
+
+
+def expert_matrices(expert: dict, inter: int, block: int):
+    """(Wg [I][H], Wu [I][H], Wd [H][I]) in fp64 from one expert's bytes and
+    scales (R3: the first I rows of w_gate_up are the gate projection)."""
+    wgu = dequantise(expert["w_gate_up"], expert["s_gate_up"], block)
+    wd = dequantise(expert["w_down"], expert["s_down"], block)
+    return wgu[:inter], wgu[inter:], wd
+
+
+# --------------------------------------------------------------------------
+# router and selection (R4, R5, R9)
+# --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, router_w: np.ndarray,
+                  router_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """l[t, e] = sum_h x[t, h] Wr[e, h] (+ b[e]) in fp64 (R5)."""
+    l = np.asarray(x, np.float64) @ np.asarray(router_w, np.float64).T
+    if router_bias is not None:
+        l = l + np.asarray(router_bias, np.float64)[None, :]
+    return l
+
+
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """Per token, the k experts with the largest logits (R4): a full stable
+    sort of the experts by descending logit, so equal logits keep ascending
+    expert order; the first k are slots j = 0..k-1."""
+    T, E = logits.shape
+    assert 1 <= k <= E
+    idx = np.empty((T, k), np.int64)
+    for t in range(T):
+        order = np.argsort(-logits[t], kind="stable")
+        idx[t] = order[:k]
+    return idx
+
+
+def softmax(v: np.ndarray) -> np.ndarray:
+    """Max-subtracted softmax of a 1-D fp64 vector."""
+    z = np.exp(v - v.max())
+    return z / z.sum()
+
+
+def gate_weights(logits: np.ndarray, topk_idx: np.ndarray) -> np.ndarray:
+    """g[t, j] = p[t, idx[t, j]] / sum_j' p[t, idx[t, j']] with p the softmax
+    over all E logits of token t (R4)."""
+    T, k = topk_idx.shape
+    g = np.empty((T, k), np.float64)
+    for t in range(T):
+        p = softmax(logits[t])
+        sel = p[topk_idx[t]]
+        g[t] = sel / sel.sum()
+    return g
+
+
+def tie_flags(logits: np.ndarray, k: int, band: float = TIE_BAND) -> np.ndarray:
+    """True for tokens whose k-th and (k+1)-th largest logits differ by less
+    than `band` (R9). With k == E nothing can be swapped and no token is
+    flagged."""
+    T, E = logits.shape
+    if k >= E:
+        return np.zeros(T, bool)
+    srt = -np.sort(-logits, axis=1)
+    return (srt[:, k - 1] - srt[:, k]) < band
+
+
+# --------------------------------------------------------------------------
+# token -> expert permutation
+# --------------------------------------------------------------------------
+def permutation(topk_idx: np.ndarray, experts: int, shared: bool):
+    """Group the slots s = t*k + j by expert: rows of expert e are its slots in
+    ascending slot (hence token) order; the shared expert, if present, is group
+    E holding slots T*k + t for t = 0..T-1. Returns (offsets [E+2], pair [P],
+    inv [P]) with pair[row] = slot and inv[slot] = row."""
+    T, k = topk_idx.shape
+    flat = topk_idx.reshape(-1)
+    order = np.argsort(flat, kind="stable")  # ascending expert, ties by slot
+    counts = np.bincount(flat, minlength=experts)
+    offsets = np.zeros(experts + 2, np.int64)
+    offsets[1:experts + 1] = np.cumsum(counts)
+    pair = list(order)
+    if shared:
+        pair += [T * k + t for t in range(T)]
+    offsets[experts + 1] = len(pair)
+    pair = np.asarray(pair, np.int64)
+    inv = np.empty_like(pair)
+    inv[pair] = np.arange(len(pair))
+    return offsets, pair, inv
+
+
+# --------------------------------------------------------------------------
+# expert FFN and combine (R6, R7, R8)
+# --------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z)), fp64."""
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """y = (silu(xs Wg^T) * (xs Wu^T)) Wd^T for rows xs [n][H] (R6)."""
+    a = xs @ wg.T
+    u = xs @ wu.T
+    return (silu(a) * u) @ wd.T
+
+
+def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndarray],
+              expert: Callable[[int], dict], top_k: int, inter: int, block: int,
+              shared: Optional[dict] = None, routing: Optional[np.ndarray] = None,
+              tokens: Optional[np.ndarray] = None):
+    """The whole layer in fp64.
+
+    expert(e) returns expert e's block-FP8 dict (w_gate_up, s_gate_up, w_down,
+    s_down); only experts some token selects are fetched. `routing` [T][k]
+    overrides the selection (used to re-run the oracle with another valid set
+    for a tie-flagged token); gates are then taken over those experts. With
+    `tokens` given, only those rows of the output are computed (the logits of
+    every token are still formed, since they are cheap).
+
+    Returns dict(out [T'][H], logits [T][E], topk_idx [T][k], gates [T][k],
+    ties [T]) where T' = len(tokens) or T.
+    """
+    x = np.asarray(x, np.float64)
+    logits = router_logits(x, router_w, router_bias)
+    idx = select_topk(logits, top_k) if routing is None else np.asarray(routing, np.int64)
+    gates = gate_weights(logits, idx)
+    rows = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
+    out = np.zeros((len(rows), x.shape[1]), np.float64)
+    sub_idx = idx[rows]
+    for e in np.unique(sub_idx):
+        wg, wu, wd = expert_matrices(expert(int(e)), inter, block)
+        who, slot = np.nonzero(sub_idx == e)
+        y = swiglu_expert(x[rows[who]], wg, wu, wd)
+        # each (token, slot) pair appears once; in fp64 the order of the k
+        # terms of a token is immaterial at the tolerances this oracle serves
+        for r, (i, j) in enumerate(zip(who, slot)):
+            out[i] += gates[rows[i], j] * y[r]
+    if shared is not None:
+        wg, wu, wd = expert_matrices(shared, inter, block)
+        out += swiglu_expert(x[rows], wg, wu, wd)
+    return {"out": out, "logits": logits, "topk_idx": idx, "gates": gates,
+            "ties": tie_flags(logits, top_k)}

@@ -1,0 +1,322 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each pin checks the oracle against something independent of its own code:
+a library routine (torch's float8_e4m3fn conversion, torch's silu and matmul),
+a published table (tests/golden/e4m3fn_anchors.txt, OCP OFP8), brute force
+over all subsets, a scalar pure-Python evaluation of the definitions, or a
+closed-form special case (one expert; all experts with equal gates). The
+mutation test at the end plants plausible mistakes in copies of the oracle and
+requires every one of them to fail at least one pin.
+"""
+import importlib.util
+import itertools
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as ORACLE
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ORACLE_SRC = os.path.join(os.path.dirname(HERE), "oracle", "moe_oracle.py")
+
+
+# ---------------------------------------------------------------- helpers ---
+def lib_decode(codes):
+    """E4M3FN bytes -> fp64 through torch's own float8_e4m3fn conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def lib_dequant(codes, scales, block):
+    """Library dequantisation: torch fp8 decode times a Kronecker-expanded scale grid."""
+    w = torch.from_numpy(lib_decode(codes))
+    s = torch.from_numpy(np.asarray(scales, np.float64))
+    return (w * torch.kron(s, torch.ones(block, block, dtype=torch.float64))).numpy()
+
+
+def random_codes(rng, shape):
+    """Random E4M3FN bytes excluding the two NaN codes."""
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E
+    return c
+
+
+def random_expert(rng, H, I, B, scale_lo=0.001, scale_hi=0.01):
+    return {
+        "w_gate_up": random_codes(rng, (2 * I, H)),
+        "s_gate_up": rng.uniform(scale_lo, scale_hi, (2 * I // B, H // B)).astype(np.float32),
+        "w_down": random_codes(rng, (H, I)),
+        "s_down": rng.uniform(scale_lo, scale_hi, (H // B, I // B)).astype(np.float32),
+    }
+
+
+def torch_swiglu(x, expert, I, B):
+    """Dense SwiGLU expert through torch library routines."""
+    wgu = torch.from_numpy(lib_dequant(expert["w_gate_up"], expert["s_gate_up"], B))
+    wd = torch.from_numpy(lib_dequant(expert["w_down"], expert["s_down"], B))
+    xt = torch.from_numpy(np.asarray(x, np.float64))
+    a = xt @ wgu[:I].T
+    u = xt @ wgu[I:].T
+    return (torch.nn.functional.silu(a) * u @ wd.T).numpy()
+
+
+# ------------------------------------------------------------------- pins ---
+def pin_decode_matches_library(O):
+    codes = np.arange(256, dtype=np.uint8)
+    ours, lib = O.e4m3fn_decode(codes), lib_decode(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(lib)) and np.isnan(ours).sum() == 2
+    fin = ~np.isnan(ours)
+    assert np.array_equal(ours[fin], lib[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(lib[fin]))
+
+
+def pin_decode_anchors(O):
+    path = os.path.join(HERE, "golden", "e4m3fn_anchors.txt")
+    n = 0
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code, val = line.split()
+        got = float(O.e4m3fn_decode(np.array([int(code, 16)], np.uint8))[0])
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            want = float(val)
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+        n += 1
+    assert n >= 10
+
+
+def pin_dequant_bruteforce(O):
+    rng = np.random.default_rng(1)
+    B = 2
+    codes = random_codes(rng, (6 * B, 4 * B))  # non-square block grid (6 x 4)
+    scales = rng.uniform(0.5, 3.0, (6, 4)).astype(np.float32)
+    ours = O.dequantise(codes, scales, B)
+    dec = lib_decode(codes)
+    for r in range(codes.shape[0]):
+        for c in range(codes.shape[1]):
+            assert ours[r, c] == dec[r, c] * float(scales[r // B, c // B])
+    assert np.array_equal(ours, lib_dequant(codes, scales, B))
+
+
+def brute_topk(l, k):
+    """Max-sum k-subset, lexicographically lowest among ties, in slot order."""
+    E = len(l)
+    best, best_sum = None, -math.inf
+    for sub in itertools.combinations(range(E), k):  # lexicographic order
+        s = sum(l[e] for e in sub)
+        if s > best_sum:
+            best, best_sum = sub, s
+    return sorted(best, key=lambda e: (-l[e], e))
+
+
+def pin_topk_bruteforce(O):
+    rng = np.random.default_rng(2)
+    for trial in range(300):
+        E = int(rng.integers(2, 9))
+        k = int(rng.integers(1, E + 1))
+        # few distinct integer values: many exact ties, exactly summable
+        l = rng.integers(-3, 4, size=(1, E)).astype(np.float64)
+        got = list(O.select_topk(l, k)[0])
+        assert got == brute_topk(list(l[0]), k), (l, k, got)
+
+
+def pin_gates(O):
+    rng = np.random.default_rng(3)
+    for trial in range(100):
+        E = int(rng.integers(2, 40))
+        k = int(rng.integers(1, E + 1))
+        l = rng.normal(0, 3, (2, E))
+        if trial % 3 == 0:
+            l = np.round(l)  # ties
+        idx = O.select_topk(l, k)
+        g = O.gate_weights(l, idx)
+        assert np.allclose(g.sum(axis=1), 1.0, atol=1e-12, rtol=0)
+        for t in range(2):
+            sel = np.array([l[t, e] for e in idx[t]])
+            restricted = [math.exp(v - sel.max()) for v in sel]
+            tot = math.fsum(restricted)
+            assert np.allclose(g[t], [v / tot for v in restricted], atol=1e-12, rtol=0)
+            # non-increasing in slot order, since slots follow descending logits
+            assert all(g[t, j] >= g[t, j + 1] for j in range(k - 1))
+        # a common shift of the logits changes nothing
+        assert np.allclose(O.gate_weights(l + 7.25, idx), g, atol=1e-12, rtol=0)
+
+
+def pin_permutation(O):
+    rng = np.random.default_rng(4)
+    for trial in range(50):
+        T, E = int(rng.integers(1, 30)), int(rng.integers(1, 12))
+        k = int(rng.integers(1, E + 1))
+        shared = bool(trial % 2)
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        off, pair, inv = O.permutation(idx, E, shared)
+        flat = idx.reshape(-1)
+        want = sorted(range(T * k), key=lambda s: (flat[s], s // k))
+        if shared:
+            want += [T * k + t for t in range(T)]
+        assert list(pair) == want
+        counts = np.bincount(flat, minlength=E)
+        assert off[0] == 0 and all(off[e + 1] - off[e] == counts[e] for e in range(E))
+        assert off[E] == T * k and off[E + 1] == T * k + (T if shared else 0)
+        assert np.array_equal(inv[pair], np.arange(len(pair)))
+        for e in range(E):
+            assert all(flat[s] == e for s in pair[off[e]:off[e + 1]])
+
+
+def pin_single_expert_is_dense(O):
+    rng = np.random.default_rng(5)
+    H, I, B = 12, 8, 4  # H != I, non-square scale grids
+    ex = random_expert(rng, H, I, B, 0.05, 0.5)
+    x = rng.normal(0, 1, (5, H))
+    wr = rng.normal(0, 1, (1, H))
+    res = O.moe_layer(x, wr, None, lambda e: ex, top_k=1, inter=I, block=B)
+    assert np.allclose(res["gates"], 1.0, atol=0, rtol=0)
+    assert np.allclose(res["out"], torch_swiglu(x, ex, I, B), rtol=1e-12, atol=1e-12)
+
+
+def pin_all_experts_equal_gates_is_dense_mean(O):
+    rng = np.random.default_rng(6)
+    H, I, B, E = 8, 4, 4, 5
+    bank = [random_expert(rng, H, I, B, 0.05, 0.5) for _ in range(E)]
+    shared = random_expert(rng, H, I, B, 0.05, 0.5)
+    x = rng.normal(0, 1, (3, H))
+    wr = np.zeros((E, H))
+    res = O.moe_layer(x, wr, np.zeros(E), lambda e: bank[e], top_k=E, inter=I, block=B,
+                      shared=shared)
+    assert np.allclose(res["gates"], 1.0 / E, atol=1e-15, rtol=0)
+    assert [list(r) for r in res["topk_idx"]] == [list(range(E))] * 3
+    dense = sum(torch_swiglu(x, bank[e], I, B) for e in range(E)) / E
+    dense = dense + torch_swiglu(x, shared, I, B)
+    assert np.allclose(res["out"], dense, rtol=1e-12, atol=1e-12)
+
+
+def scalar_layer(x, wr, bias, bank, shared, k, I, B):
+    """The layer's definitions evaluated with Python scalars and loops."""
+    T, H = len(x), len(x[0])
+    E = len(wr)
+
+    def weights(ex):
+        dgu, dd = lib_decode(ex["w_gate_up"]), lib_decode(ex["w_down"])
+        sgu, sd = ex["s_gate_up"], ex["s_down"]
+        wgu = [[float(dgu[r][c]) * float(sgu[r // B][c // B]) for c in range(H)]
+               for r in range(2 * I)]
+        wdn = [[float(dd[r][c]) * float(sd[r // B][c // B]) for c in range(I)] for r in range(H)]
+        return wgu, wdn
+
+    def ffn(xt, w):
+        wgu, wdn = w
+        h = []
+        for i in range(I):
+            a = math.fsum(wgu[i][c] * xt[c] for c in range(H))
+            u = math.fsum(wgu[I + i][c] * xt[c] for c in range(H))
+            h.append(a / (1.0 + math.exp(-a)) * u)
+        return [math.fsum(wdn[n][i] * h[i] for i in range(I)) for n in range(H)]
+
+    cache = {}
+    out = []
+    for t in range(T):
+        xt = [float(v) for v in x[t]]
+        l = [math.fsum(xt[c] * float(wr[e][c]) for c in range(H))
+             + (float(bias[e]) if bias is not None else 0.0) for e in range(E)]
+        sel = brute_topk(l, k)
+        m = max(l[e] for e in sel)
+        den = math.fsum(math.exp(l[e] - m) for e in sel)
+        o = [0.0] * H
+        for e in sel:
+            if e not in cache:
+                cache[e] = weights(bank[e])
+            y = ffn(xt, cache[e])
+            g = math.exp(l[e] - m) / den
+            o = [o[n] + g * y[n] for n in range(H)]
+        if shared is not None:
+            y = ffn(xt, weights(shared))
+            o = [o[n] + y[n] for n in range(H)]
+        out.append(o)
+    return np.array(out)
+
+
+def pin_whole_layer_scalar(O):
+    import workloads as W
+    for name, bias, shared in (("c0", None, False), ("c0", "zipf", True)):
+        shape = W.CONFIGS[name]
+        if bias:
+            shape = shape.with_(bias=("zipf", 1.1, 0.5), shared=True)
+        d = W.gen_layer(shape)
+        bank = [W.bank_expert(d["bank"], e) for e in range(shape.experts)]
+        sh = W.bank_expert(d["shared"], 0) if shared else None
+        res = O.moe_layer(d["x"], d["router_w"], d["router_bias"], lambda e: bank[e],
+                          top_k=shape.top_k, inter=shape.inter, block=shape.block, shared=sh)
+        want = scalar_layer(d["x"], d["router_w"], d["router_bias"], bank, sh,
+                            shape.top_k, shape.inter, shape.block)
+        scale = np.sqrt(np.mean(want ** 2))
+        assert np.max(np.abs(res["out"] - want)) <= 1e-12 * scale, name
+
+
+def pin_tie_flags(O):
+    l = np.array([[3.0, 2.0, 2.0 - 5e-6, 0.0],
+                  [3.0, 2.0, 2.0 - 2e-5, 0.0],
+                  [3.0, 3.0, 3.0, 3.0],
+                  [4.0, 3.0, 3.0 - 1.5e-5, 0.0]])
+    assert list(O.tie_flags(l, 2)) == [True, False, True, False]
+    assert not O.tie_flags(l, 4).any()
+
+
+PINS = [pin_decode_matches_library, pin_decode_anchors, pin_dequant_bruteforce,
+        pin_topk_bruteforce, pin_gates, pin_permutation, pin_single_expert_is_dense,
+        pin_all_experts_equal_gates_is_dense_mean, pin_whole_layer_scalar, pin_tie_flags]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(ORACLE)
+
+
+# ------------------------------------------------------------- mutations ---
+# Plausible mistakes, each planted in a fresh copy of the oracle's source.
+MUTATIONS = {
+    "exponent_bias_8": ("(e - 7).astype", "(e - 8).astype"),
+    "subnormal_scale": ("m * 2.0 ** -9", "m * 2.0 ** -10"),
+    "sign_dropped": ("np.where(s == 1, -mag, mag)", "mag"),
+    "gate_up_swapped": ("return wgu[:inter], wgu[inter:], wd", "return wgu[inter:], wgu[:inter], wd"),
+    "scale_grid_transposed": ("s_full = np.repeat(np.repeat(s, block, axis=0), block, axis=1)",
+                              "s_full = np.repeat(np.repeat(s.T, block, axis=0), block, axis=1)"),
+    "bias_dropped": ("l = l + np.asarray(router_bias, np.float64)[None, :]", "l = l"),
+    "ties_to_higher_index": ('order = np.argsort(-logits[t], kind="stable")',
+                             'order = (len(logits[t]) - 1 - np.argsort(-logits[t][::-1], kind="stable"))'),
+    "gates_not_renormalised": ("g[t] = sel / sel.sum()", "g[t] = sel"),
+    "silu_sign": ("return z / (1.0 + np.exp(-z))", "return z / (1.0 + np.exp(z))"),
+    "down_not_transposed": ("return (silu(a) * u) @ wd.T", "return (silu(a) * u) @ wd.T[::-1]"),
+    "shared_dropped": ("out += swiglu_expert(x[rows], wg, wu, wd)", "pass"),
+    "permutation_ties_by_descending_slot": ('order = np.argsort(flat, kind="stable")',
+                                            "order = np.lexsort((-np.arange(flat.size), flat))"),
+    "tie_band_relative": ("return (srt[:, k - 1] - srt[:, k]) < band",
+                          "return (srt[:, k - 1] - srt[:, k]) < band * np.abs(srt[:, k - 1])"),
+}
+
+
+def load_mutant(name, old, new):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, f"mutation {name}: anchor text not found exactly once"
+    spec = importlib.util.spec_from_loader(f"oracle_mutant_{name}", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_fails_a_pin(name):
+    mod = load_mutant(name, *MUTATIONS[name])
+    failed = []
+    for pin in PINS:
+        try:
+            pin(mod)
+        except Exception:  # AssertionError, shape errors, ...
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name!r} passed every pin"
