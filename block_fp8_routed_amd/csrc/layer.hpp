@@ -1,0 +1,69 @@
+// layer.hpp — host-side description of one layer call, shared by the C ABI
+// (moe_api.hip) and the kernel launchers. Internal to libmoe_fp8.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_fp8.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;  // permute keeps per-wave expert counters in LDS
+constexpr int kMaxTopK = 16;       // top-k keeps the selection in registers
+constexpr int kGemvMaxTokens = 16; // AUTO path: wavefront GEMV up to this many tokens
+constexpr int kMfmaBM = 64;        // rows (tokens) of one grouped-MFMA tile
+constexpr size_t kAlign = 256;
+
+struct Dims {
+  int64_t T;     // tokens
+  int H, E, I;   // hidden, routed experts, intermediate
+  int k, B, S;   // top-k, block edge, shared expert count (0/1)
+  int64_t P;     // rows of the permuted problem: T*k + S*T
+  bool x_bf16, out_bf16;
+  bool mfma;     // expert family: grouped bf16 MFMA (true) or wavefront GEMV
+};
+
+// Carved workspace. Every region is kAlign-aligned.
+struct Work {
+  float* logits;     // [T][E]
+  int32_t* topk;     // [T][k]
+  float* gates;      // [T][k]
+  int32_t* offsets;  // [E+2]
+  int32_t* meta;     // [16]: meta[0] = active groups, meta[1] = MFMA tiles
+  int32_t* active;   // [E+1] ids of non-empty groups (shared group = E)
+  int32_t* pair;     // [P] row -> slot
+  int32_t* inv;      // [P] slot -> row
+  int32_t* tiles;    // [max_tiles][2] (group, first row) of each MFMA row tile
+  void* h;           // [P][I] fp32 (GEMV family) or bf16 (MFMA family)
+  float* y;          // [P][H] fp32
+};
+
+inline int64_t max_mfma_tiles(const Dims& d) {
+  return d.P / kMfmaBM + d.E + d.S + 1;
+}
+
+// Sum of region sizes; carve() lays them out in this order.
+size_t workspace_bytes(const Dims& d);
+Work carve(const Dims& d, void* base);
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----------
+hipError_t launch_router(const Dims& d, const void* x, const float* wr, const float* bias,
+                         float* logits, hipStream_t s);
+hipError_t launch_topk(const Dims& d, const float* logits, int32_t* topk, float* gates,
+                       hipStream_t s);
+hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
+                          hipStream_t s);
+// expert passes; returns hipErrorInvalidValue if no instantiation matches
+hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_bank& routed,
+                               const moe_expert_bank* shared, const Work& w, hipStream_t s,
+                               hipEvent_t after_gate_up);
+hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_bank& routed,
+                               const moe_expert_bank* shared, const Work& w, hipStream_t s,
+                               hipEvent_t after_gate_up);
+bool has_gemv_instance(const Dims& d);
+bool has_mfma_instance(const Dims& d);
+hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,219 @@
+// moe_api.hip — the C ABI of libmoe_fp8.so (declared in include/moe_fp8.h):
+// argument validation, workspace layout and the launch sequence of one layer.
+//
+// Nothing here allocates, synchronises the host or keeps state between calls.
+// Every check runs on the host before the first launch, following the colizig
+// page's rule (Status / Contributing) that an unsupported or invalid request
+// returns an error instead of a plausible-looking wrong number.
+#include <algorithm>
+
+#include "layer.hpp"
+
+namespace moe {
+
+static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Region sizes in carve order.
+static void region_sizes(const Dims& d, size_t* sz) {
+  sz[0] = (size_t)d.T * d.E * 4;          // logits
+  sz[1] = (size_t)d.T * d.k * 4;          // topk
+  sz[2] = (size_t)d.T * d.k * 4;          // gates
+  sz[3] = (size_t)(d.E + 2) * 4;          // offsets
+  sz[4] = 16 * 4;                         // meta
+  sz[5] = (size_t)(d.E + 1) * 4;          // active
+  sz[6] = (size_t)d.P * 4;                // pair
+  sz[7] = (size_t)d.P * 4;                // inv
+  sz[8] = (size_t)max_mfma_tiles(d) * 8;  // tiles
+  sz[9] = (size_t)d.P * d.I * 4;          // h (fp32 bound; MFMA family uses half)
+  sz[10] = (size_t)d.P * d.H * 4;         // y
+}
+
+size_t workspace_bytes(const Dims& d) {
+  size_t sz[11], b = 0;
+  region_sizes(d, sz);
+  for (size_t v : sz) b += al(v);
+  return b;
+}
+
+Work carve(const Dims& d, void* base) {
+  size_t sz[11];
+  region_sizes(d, sz);
+  char* p = static_cast<char*>(base);
+  void* r[11];
+  for (int i = 0; i < 11; ++i) {
+    r[i] = p;
+    p += al(sz[i]);
+  }
+  Work w;
+  w.logits = static_cast<float*>(r[0]);
+  w.topk = static_cast<int32_t*>(r[1]);
+  w.gates = static_cast<float*>(r[2]);
+  w.offsets = static_cast<int32_t*>(r[3]);
+  w.meta = static_cast<int32_t*>(r[4]);
+  w.active = static_cast<int32_t*>(r[5]);
+  w.pair = static_cast<int32_t*>(r[6]);
+  w.inv = static_cast<int32_t*>(r[7]);
+  w.tiles = static_cast<int32_t*>(r[8]);
+  w.h = r[9];
+  w.y = static_cast<float*>(r[10]);
+  return w;
+}
+
+// Shape checks shared by every entry point (no HIP call).
+static moe_status basic_dims(const moe_config* c, Dims* d) {
+  if (!c) return MOE_ERR_NULL;
+  if (c->tokens < 0 || c->hidden <= 0 || c->experts <= 0 || c->inter <= 0 || c->top_k <= 0 ||
+      c->block <= 0)
+    return MOE_ERR_SHAPE;
+  if (c->top_k > c->experts) return MOE_ERR_SHAPE;
+  if (c->hidden % c->block != 0 || c->inter % c->block != 0) return MOE_ERR_SHAPE;
+  if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_SHAPE;
+  if ((c->x_dtype != MOE_F32 && c->x_dtype != MOE_BF16) ||
+      (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16))
+    return MOE_ERR_SHAPE;
+  if (c->path != MOE_PATH_AUTO && c->path != MOE_PATH_GEMV && c->path != MOE_PATH_MFMA)
+    return MOE_ERR_SHAPE;
+  if (c->experts > kMaxExperts || c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (c->hidden % 16 != 0 || c->inter % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t P = c->tokens * (int64_t)(c->top_k + c->has_shared);
+  if (P >= ((int64_t)1 << 31) || c->tokens * (int64_t)c->experts >= ((int64_t)1 << 40))
+    return MOE_ERR_UNSUPPORTED;
+  d->T = c->tokens;
+  d->H = c->hidden;
+  d->E = c->experts;
+  d->I = c->inter;
+  d->k = c->top_k;
+  d->B = c->block;
+  d->S = c->has_shared;
+  d->P = P;
+  d->x_bf16 = c->x_dtype == MOE_BF16;
+  d->out_bf16 = c->out_dtype == MOE_BF16;
+  d->mfma = c->path == MOE_PATH_MFMA ||
+            (c->path == MOE_PATH_AUTO && d->x_bf16 && c->tokens > kGemvMaxTokens);
+  return MOE_OK;
+}
+
+static moe_status expert_family_ok(const Dims& d) {
+  if (d.mfma) {
+    if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
+    return has_mfma_instance(d) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+  }
+  return has_gemv_instance(d) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+static bool bank_ok(const moe_expert_bank* b) {
+  return b && b->w_gate_up && b->w_down && b->s_gate_up && b->s_down;
+}
+
+static moe_status check_workspace(const Dims& d, void* ws, size_t bytes) {
+  if (!ws) return MOE_ERR_NULL;
+  if (bytes < workspace_bytes(d) || reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+static bool rec(const moe_phase_events* ev, moe_phase p, hipStream_t s) {
+  if (!ev || !ev->ev[p]) return true;
+  return hipEventRecord(static_cast<hipEvent_t>(ev->ev[p]), s) == hipSuccess;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+  Dims d;
+  if (basic_dims(cfg, &d) != MOE_OK) return 0;
+  return workspace_bytes(d);
+}
+
+moe_status moe_forward(const void* x, const float* router_w, const float* router_bias,
+                       const moe_expert_bank* experts, const moe_expert_bank* shared,
+                       int32_t top_k, void* out, const moe_config* cfg, void* workspace,
+                       size_t workspace_bytes_, const moe_phase_events* events, void* stream) {
+  Dims d;
+  moe_status st = basic_dims(cfg, &d);
+  if (st != MOE_OK) return st;
+  if (top_k != cfg->top_k) return MOE_ERR_SHAPE;
+  if (!x || !router_w || !out || !bank_ok(experts)) return MOE_ERR_NULL;
+  if (d.S && !bank_ok(shared)) return MOE_ERR_NULL;
+  st = expert_family_ok(d);
+  if (st != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  st = check_workspace(d, workspace, workspace_bytes_);
+  if (st != MOE_OK) return st;
+
+  const Work w = carve(d, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev_gate_up =
+      events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr;
+  if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, router_bias, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_topk(d, w.logits, w.topk, w.gates, s) != hipSuccess) return MOE_ERR_HIP;
+  if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
+  if (launch_permute(d, w.topk, w, d.mfma ? kMfmaBM : 0, s) != hipSuccess) return MOE_ERR_HIP;
+  if (!rec(events, MOE_EV_PERMUTED, s)) return MOE_ERR_HIP;
+  const moe_expert_bank* sh = d.S ? shared : nullptr;
+  const hipError_t e = d.mfma ? launch_experts_mfma(d, x, *experts, sh, w, s, ev_gate_up)
+                              : launch_experts_gemv(d, x, *experts, sh, w, s, ev_gate_up);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (!rec(events, MOE_EV_DOWN, s)) return MOE_ERR_HIP;
+  if (launch_combine(d, w, out, s) != hipSuccess) return MOE_ERR_HIP;
+  if (!rec(events, MOE_EV_END, s)) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_route(const void* x, const float* router_w, const float* router_bias,
+                     int32_t* topk_idx, float* gates, float* logits, const moe_config* cfg,
+                     void* workspace, size_t workspace_bytes_, void* stream) {
+  Dims d;
+  moe_status st = basic_dims(cfg, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !router_w || !topk_idx || !gates) return MOE_ERR_NULL;
+  if (d.T == 0) return MOE_OK;
+  st = check_workspace(d, workspace, workspace_bytes_);
+  if (st != MOE_OK) return st;
+  const Work w = carve(d, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* l = logits ? logits : w.logits;
+  if (launch_router(d, x, router_w, router_bias, l, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_topk(d, l, topk_idx, gates, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_permute(const int32_t* topk_idx, int32_t* offsets, int32_t* pair, int32_t* inv,
+                       const moe_config* cfg, void* workspace, size_t workspace_bytes_,
+                       void* stream) {
+  Dims d;
+  moe_status st = basic_dims(cfg, &d);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !offsets || !pair || !inv) return MOE_ERR_NULL;
+  if (d.T == 0) return MOE_OK;
+  st = check_workspace(d, workspace, workspace_bytes_);
+  if (st != MOE_OK) return st;
+  Work w = carve(d, workspace);
+  w.offsets = offsets;
+  w.pair = pair;
+  w.inv = inv;
+  if (launch_permute(d, topk_idx, w, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid shape or argument";
+    case MOE_ERR_UNSUPPORTED: return "no kernel for this shape, dtype or path";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t moe_version(void) { return 100; }
+
+}  // extern "C"

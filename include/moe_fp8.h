@@ -159,6 +159,16 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t* offsets, int32_t* pair,
                        int32_t* inv, const moe_config* cfg, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Expand one block-FP8 matrix to fp32 on the device:
+ *   out[r][c] = dec(w[r][c]) * scales[r / block][c / block]
+ * with the same in-register E4M3FN decode the expert kernels use (colizig page,
+ * "Features": block-FP8 E4M3 weights). w [rows][cols] uint8, scales
+ * [rows/block][cols/block] fp32, out [rows][cols] fp32, all device memory.
+ * block must divide rows and cols (else MOE_ERR_SHAPE); cols must be a
+ * multiple of 16 (else MOE_ERR_UNSUPPORTED); rows == 0 enqueues nothing. */
+moe_status moe_dequant_e4m3(const uint8_t* w, const float* scales, int64_t rows, int32_t cols,
+                            int32_t block, float* out, void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

@@ -1,0 +1,148 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+include/moe_fp8.h declares, and rejects invalid calls with the documented
+status before any HIP call is made (the pointers passed here are never
+dereferenced, because validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_fp8_routed_amd as moe
+from block_fp8_routed_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before use
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(_lib.EXPORTS) <= set(names), names
+    assert {"moe_forward", "moe_route", "moe_permute", "moe_workspace_bytes"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libmoe_fp8.so does not export {name}"
+
+
+def test_status_strings_and_version():
+    for st in range(6):
+        s = moe.status_string(st)
+        assert isinstance(s, str) and s
+    assert moe.status_string(99) == "unknown status"
+    assert moe.version() >= 100
+
+
+def cfg(**kw):
+    base = dict(tokens=4, hidden=64, experts=8, inter=32, top_k=2, block=32, has_shared=False,
+                x_dtype=_lib.torch.float32, out_dtype=_lib.torch.float32, path="auto")
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+def bank(null=False):
+    b = _lib.MoeExpertBank()
+    if not null:
+        b.w_gate_up = b.w_down = b.s_gate_up = b.s_down = 0x2000
+    return b
+
+
+def forward(c, x=FAKE, wr=FAKE, bias=None, b=None, sh=None, top_k=None, out=FAKE, ws=FAKE,
+            ws_bytes=None, cfgp=True):
+    lib = moe.load()
+    b = bank() if b is None else b
+    top_k = c.top_k if top_k is None else top_k
+    ws_bytes = moe.workspace_bytes(c) if ws_bytes is None else ws_bytes
+    return lib.moe_forward(x, wr, bias, ctypes.byref(b), ctypes.byref(sh) if sh else None, top_k,
+                           out, ctypes.byref(c) if cfgp else None, ws, ws_bytes, None, None)
+
+
+def test_workspace_bytes():
+    c = cfg()
+    n = moe.workspace_bytes(c)
+    assert n > 0 and n % 256 == 0
+    big = cfg(tokens=4096, hidden=4096, experts=512, inter=1024, top_k=10, block=128,
+              has_shared=True)
+    P = 4096 * 11
+    assert moe.workspace_bytes(big) >= P * 4096 * 4 + P * 1024 * 4
+    assert moe.workspace_bytes(cfg(top_k=9)) == 0  # invalid config
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=9), _lib.MOE_ERR_SHAPE),
+    (dict(top_k=0), _lib.MOE_ERR_SHAPE),
+    (dict(tokens=-1), _lib.MOE_ERR_SHAPE),
+    (dict(hidden=0), _lib.MOE_ERR_SHAPE),
+    (dict(hidden=48), _lib.MOE_ERR_SHAPE),          # block does not divide hidden
+    (dict(inter=40), _lib.MOE_ERR_SHAPE),           # block does not divide inter
+    (dict(experts=2048, top_k=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(experts=64, top_k=17), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=128, inter=64), _lib.MOE_ERR_UNSUPPORTED),  # no kernel for this shape
+    (dict(path="mfma"), _lib.MOE_ERR_UNSUPPORTED),  # MFMA needs bf16 activations
+])
+def test_forward_rejects_bad_configs(kw, status):
+    assert forward(cfg(**kw)) == status
+
+
+def test_forward_rejects_bad_enums():
+    c = cfg()
+    c.x_dtype = 7
+    assert forward(c) == _lib.MOE_ERR_SHAPE
+    c = cfg()
+    c.path = 5
+    assert forward(c) == _lib.MOE_ERR_SHAPE
+    c = cfg()
+    c.has_shared = 2
+    assert forward(c) == _lib.MOE_ERR_SHAPE
+
+
+def test_forward_rejects_null_pointers():
+    c = cfg()
+    assert forward(c, cfgp=False) == _lib.MOE_ERR_NULL
+    assert forward(c, x=None) == _lib.MOE_ERR_NULL
+    assert forward(c, wr=None) == _lib.MOE_ERR_NULL
+    assert forward(c, out=None) == _lib.MOE_ERR_NULL
+    assert forward(c, b=bank(null=True)) == _lib.MOE_ERR_NULL
+    assert forward(c, ws=None) == _lib.MOE_ERR_NULL
+    cs = cfg(has_shared=True)
+    assert forward(cs) == _lib.MOE_ERR_NULL          # shared bank required
+    assert forward(cs, sh=bank(null=True)) == _lib.MOE_ERR_NULL
+
+
+def test_forward_rejects_top_k_mismatch_and_workspace():
+    c = cfg()
+    assert forward(c, top_k=3) == _lib.MOE_ERR_SHAPE
+    n = moe.workspace_bytes(c)
+    assert forward(c, ws_bytes=n - 1) == _lib.MOE_ERR_WORKSPACE
+    assert forward(c, ws=ctypes.c_void_p(0x1004)) == _lib.MOE_ERR_WORKSPACE  # misaligned
+
+
+def test_zero_tokens_is_a_no_op():
+    assert forward(cfg(tokens=0), ws=None, ws_bytes=0) == _lib.MOE_OK
+
+
+def test_route_and_permute_validation():
+    lib = moe.load()
+    c = cfg()
+    n = moe.workspace_bytes(c)
+    assert lib.moe_route(None, FAKE, None, FAKE, FAKE, None, ctypes.byref(c), FAKE, n,
+                         None) == _lib.MOE_ERR_NULL
+    assert lib.moe_route(FAKE, FAKE, None, FAKE, FAKE, None, ctypes.byref(c), FAKE, n - 1,
+                         None) == _lib.MOE_ERR_WORKSPACE
+    bad = cfg(top_k=9)
+    assert lib.moe_route(FAKE, FAKE, None, FAKE, FAKE, None, ctypes.byref(bad), FAKE, n,
+                         None) == _lib.MOE_ERR_SHAPE
+    assert lib.moe_permute(FAKE, None, FAKE, FAKE, ctypes.byref(c), FAKE, n,
+                           None) == _lib.MOE_ERR_NULL
+    assert lib.moe_permute(FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE, 8,
+                           None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(FAKE, FAKE, FAKE, FAKE, None, FAKE, n, None) == _lib.MOE_ERR_NULL
