@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-FP8 routed MoE layer on one MI355X.
+
+One step = one moe_forward call (router, top-k, permutation, gate/up+SwiGLU,
+down, combine) over one batch of synthetic tokens already resident in HBM.
+Successive steps rotate over R input batches and C device copies of the
+expert bank, so that repeated calls cannot be served from the 256 MB MALL.
+
+Prints one JSON line: MoE-layer tokens/s, plus
+  roofline:     the dominant kernel (gate/up expert pass) timed with HIP events
+                recorded around its launch on the layer's stream during the
+                timed steps; algorithmic bytes = the bytes of the experts the
+                step's routing touches (E4M3 weights + fp32 scales), or
+                algorithmic FLOPs for MFMA-bound workloads;
+  cpu_baseline: the CPU oracle (fp64 NumPy) timed on a bounded sample of the
+                same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--tokens 16]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (the process's own runtime)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)) == 0
+        return ms.value
+
+
+def expert_bytes(shape):
+    return shape.expert_bytes()
+
+
+def cpu_baseline(shape, host, x_batches, seconds):
+    """Time the CPU oracle on successive input batches for about `seconds`."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    bank, shared = host
+    sh = W.bank_expert(shared, 0) if shape.shared else None
+    wr, b = W.gen_router(shape), W.gen_bias(shape)
+    done, t0, i = 0, time.perf_counter(), 0
+    while True:
+        x = x_batches[i % len(x_batches)]
+        oracle.moe_layer(x, wr, b, lambda e: W.bank_expert(bank, e), shape.top_k, shape.inter,
+                         shape.block, shared=sh)
+        done += len(x)
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{i} oracle forwards of {len(x_batches[0])} tokens ({done} tokens, "
+                   f"{el:.1f} s) on the first input batches of the same workload; fp64 NumPy, "
+                   f"BLAS may use {cores} threads, decode and dequantisation single-threaded; "
+                   f"host CPU: {model}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--tokens", type=int, default=None, help="tokens per step (default: config)")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--batches", type=int, default=8, help="distinct input batches rotated")
+    ap.add_argument("--copies", type=int, default=0, help="device copies of the bank (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this layer is built and measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import block_fp8_routed_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    lib = moe.load()
+    hip = Hip()
+    dev = torch.device("cuda:0")
+    shape = W.CONFIGS[args.config]
+    T = args.tokens if args.tokens is not None else shape.tokens
+    H, E, I, B, k = shape.hidden, shape.experts, shape.inter, shape.block, shape.top_k
+    xdt = torch.bfloat16 if shape.x_dtype == "bf16" else torch.float32
+
+    log(f"generating {args.config} bank (E={E}, H={H}, I={I})")
+    t0 = time.perf_counter()
+    bank_h = W.gen_bank(shape)
+    shared_h = W.gen_bank(shape, shared=True) if shape.shared else None
+    log(f"bank generated in {time.perf_counter() - t0:.1f} s")
+    bank_bytes = (E + int(shape.shared)) * expert_bytes(shape)
+    copies = args.copies or max(1, min(8, math.ceil(2.5e9 / bank_bytes)))
+    banks = [moe.Bank.from_numpy(bank_h, dev)]
+    for _ in range(copies - 1):
+        b0 = banks[0]
+        banks.append(moe.Bank(b0.w_gate_up.clone(), b0.s_gate_up.clone(), b0.w_down.clone(),
+                              b0.s_down.clone()))
+    shared = moe.Bank.from_numpy(shared_h, dev) if shape.shared else None
+    router = torch.from_numpy(W.gen_router(shape)).to(dev)
+    bias_h = W.gen_bias(shape)
+    bias = None if bias_h is None else torch.from_numpy(bias_h).to(dev)
+    x_host = [W.gen_x(shape, T, batch=r) for r in range(args.batches)]
+    xs = [torch.from_numpy(x).to(xdt).to(dev) for x in x_host]
+
+    cfg = moe.make_config(T, H, E, I, k, B, shape.shared, xdt, torch.float32, args.path)
+    ws = moe.make_workspace(cfg, dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    mfma = args.path == "mfma" or (args.path == "auto" and xdt == torch.bfloat16 and T > 16)
+
+    # routing of each batch: which experts a step touches (outside the timed region)
+    uniq = []
+    for x in xs:
+        idx, _ = moe.moe_route(x, router, k, I, B, router_bias=bias)
+        uniq.append(len(np.unique(idx.cpu().numpy())) + int(shape.shared))
+    gu_bytes_per_expert = 2 * I * H + 4 * (2 * I // B) * (H // B)
+    all_bytes_per_expert = expert_bytes(shape)
+
+    def call(i, evs=None):
+        r, c = i % len(xs), i % len(banks)
+        st = lib.moe_forward(ctypes.c_void_p(xs[r].data_ptr()), ctypes.c_void_p(router.data_ptr()),
+                             None if bias is None else ctypes.c_void_p(bias.data_ptr()),
+                             ctypes.byref(banks[c].c),
+                             ctypes.byref(shared.c) if shared is not None else None, k,
+                             ctypes.c_void_p(out.data_ptr()), ctypes.byref(cfg),
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                             ctypes.byref(evs) if evs is not None else None, ctypes.c_void_p(sp))
+        if st != 0:
+            raise moe.MoeError(st, "moe_forward")
+
+    # per-step events around the gate/up launch (PERMUTED -> GATE_UP)
+    K, Wm = args.steps, args.warmup
+    ev_pairs = [(hip.event(), hip.event()) for _ in range(K)]
+    ev_structs = []
+    for a, b in ev_pairs:
+        s = moe.MoePhaseEvents()
+        s.ev[moe.MOE_EV_PERMUTED] = a
+        s.ev[moe.MOE_EV_GATE_UP] = b
+        ev_structs.append(s)
+    start, stop = hip.event(), hip.event()
+
+    log(f"warmup {Wm} steps (T={T}, copies={copies}, batches={len(xs)}, path={'mfma' if mfma else 'gemv'})")
+    for i in range(Wm):
+        call(i)
+    torch.cuda.synchronize()
+    log(f"timing {K} steps")
+    hip.record(start, sp)
+    for i in range(K):
+        call(Wm + i, ev_structs[i])
+    hip.record(stop, sp)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed_ms(start, stop)
+    ms = total_ms / K
+    gu_ms = [hip.elapsed_ms(a, b) for a, b in ev_pairs]
+    gu_avg_ms = sum(gu_ms) / K
+    steps_uniq = [uniq[(Wm + i) % len(xs)] for i in range(K)]
+    mean_uniq = sum(steps_uniq) / K
+    gu_bytes = mean_uniq * gu_bytes_per_expert
+    layer_bytes = mean_uniq * all_bytes_per_expert
+
+    # phase breakdown (outside the timed region): all phase events on a few steps
+    phase = {n: [] for n in ("route", "permute", "gate_up", "down", "combine")}
+    for i in range(min(20, K)):
+        evs = [hip.event() for _ in range(moe.MOE_EV_COUNT)]
+        s = moe.MoePhaseEvents()
+        for j, e in enumerate(evs):
+            s.ev[j] = e
+        call(i, s)
+        torch.cuda.synchronize()
+        for j, n in enumerate(phase):
+            phase[n].append(hip.elapsed_ms(evs[j], evs[j + 1]) * 1e3)
+    phases_us = {n: round(sorted(v)[len(v) // 2], 2) for n, v in phase.items()}
+
+    tokens_per_s = T / (ms / 1e3)
+    flops = (T * k + T * int(shape.shared)) * 6 * H * I
+    if mfma:
+        gu_flops = (T * k + T * int(shape.shared)) * 4 * H * I
+        achieved = gu_flops / (gu_avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "kernel": "expert gate/up + SwiGLU (grouped bf16 MFMA)",
+                "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = gu_bytes / (gu_avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "expert gate/up + SwiGLU (wavefront GEMV)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["avg_launch_us"] = round(gu_avg_ms * 1e3, 2)
+    roof["algorithmic_per_launch"] = (round(gu_bytes) if not mfma else
+                                      (T * k + T * int(shape.shared)) * 4 * H * I)
+
+    res = {
+        "metric": "MoE-layer tokens/s; decode HBM GB/s vs peak, prefill MFMA util",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mfma else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.config} {shape.name}: hidden {H}, {E} experts top-{k}"
+                         f"{' + 1 shared' if shape.shared else ''}, inter {I}, E4M3 weights "
+                         f"with {B}x{B} fp32 block scales, {T} tokens per step, "
+                         f"{shape.x_dtype} activations, fp32 output"),
+            "tokens": T, "hidden": H, "experts": E, "top_k": k, "inter": I, "block": B,
+            "shared": shape.shared, "path": "mfma" if mfma else "gemv",
+            "bank_copies": copies, "input_batches": len(xs),
+        },
+        "roofline": roof,
+        "layer": {
+            "unique_experts_per_step": round(mean_uniq, 2),
+            "expert_bytes_per_step": round(layer_bytes),
+            "expert_GBps": round(layer_bytes / (ms / 1e3) / 1e9, 1),
+            "expert_GBps_frac": round(layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "flops_per_step": flops,
+            "mfma_util": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+            "phases_us_median": phases_us,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(shape, (bank_h, shared_h), x_host, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

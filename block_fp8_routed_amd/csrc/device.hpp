@@ -21,6 +21,22 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* o) {
   o[3] = hi.y;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two E4M3FN bytes (bytes 2*HI and 2*HI+1 of a dword) to a bf16 pair. Every
+// E4M3FN value is a bf16 value, and with a unit scale gfx950's
+// v_cvt_scalef32_pk_bf16_fp8 converts exactly.
+template <bool HI>
+__device__ __forceinline__ bf16x2_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
+}
+
+// c + a.lo * b.lo + a.hi * b.hi with bf16 inputs and an fp32 accumulator
+// (v_dot2c_f32_bf16); b is a dword holding two bf16 values.
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // bf16 halves of a dword to fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -32,20 +48,75 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
-// the group ends with the group's sum. The order of additions is fixed, so
-// the result is reproducible.
+// ---- cross-lane reductions (DPP within 16-lane rows, readlane across rows) ----
+// DPP controls: quad_perm [1,0,3,2] (xor 1), [2,3,0,1] (xor 2), row_half_mirror
+// (lane i <-> 7-i in each 8) and row_mirror (i <-> 15-i in each 16). Applied in
+// that order they leave every lane of a 16-lane row holding the row's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xf, 0xf, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of W lanes (W = 1, 2, 4, 8, 16 or 64); every lane
+// of a group ends with the group's sum (for W = 64 the result is uniform).
+// The order of additions is fixed, so results are reproducible.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 64, "group width");
+  if (W >= 2) v += dpp_f<kDppXor1>(v);
+  if (W >= 4) v += dpp_f<kDppXor2>(v);
+  if (W >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (W >= 16) v += dpp_f<kDppMirror>(v);
+  if (W == 64)
+    v = (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
   return v;
+}
+
+// Larger value wins; equal values go to the lower index.
+__device__ __forceinline__ void take_max(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Wave-wide argmax of (v, i); the result is uniform across the wave.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  take_max(v, i, dpp_f<kDppXor1>(v), dpp_i<kDppXor1>(i));
+  take_max(v, i, dpp_f<kDppXor2>(v), dpp_i<kDppXor2>(i));
+  take_max(v, i, dpp_f<kDppHalfMirror>(v), dpp_i<kDppHalfMirror>(i));
+  take_max(v, i, dpp_f<kDppMirror>(v), dpp_i<kDppMirror>(i));
+  float bv = readlane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16)
+    take_max(bv, bi, readlane_f(v, r), __builtin_amdgcn_readlane(i, r));
+  v = bv;
+  i = bi;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // 16-byte global load through the vector memory path.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// 16-byte non-temporal global load, for data read exactly once (expert
+// weights streamed by the decode passes): it does not displace reused lines.
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Lanes of a 64-wide wave laid over rows of K bytes, 16 bytes per lane per
 // load. K >= 1024: the whole wave covers 1024 bytes of one row per load and a

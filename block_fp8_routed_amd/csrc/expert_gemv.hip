@@ -5,20 +5,29 @@
 // streaming the selected experts' E4M3 bytes from HBM once (colizig page,
 // "Benchmarks": decode is memory-bandwidth-bound, not FLOP-bound). Following
 // the "Features" description of fused dequant + dot product, weights are
-// decoded in registers right after their 16-byte coalesced load (gfx950
-// v_cvt_pk_f32_fp8) and multiplied into fp32 partial sums; a block's scale is
-// applied once to the partial sum of its columns, never to single weights.
+// decoded in registers after their 16-byte coalesced load and multiplied into
+// fp32 partial sums; a block's scale is applied once to the partial sum of its
+// columns, never to single weights.
 //
-// Launch shape (both kernels): blockIdx.y indexes the non-empty groups listed
-// by the permutation (extra blocks exit at once); blockIdx.x picks a slab of
-// output rows; each of the 4 wavefronts of a workgroup owns a few rows and
-// reads them whole. Tokens of a group are taken NT at a time; a larger group
-// re-reads its rows (from cache) for each further NT tokens.
+// The work of a pass is cut into slabs: a few whole weight rows of one group
+// (~8 KiB for gate/up, ~6 KiB for down), one slab per wavefront. Measured on
+// MI355X, HBM reads come closest to peak with many short-lived wavefronts that
+// each issue a few KiB of independent 16-byte loads (non-temporal, since the
+// weights are read once) at high occupancy, so the kernels keep register use
+// low (two tokens per pass) and issue every weight load of the slab before
+// anything else.
 //
-//   gate/up: rows i (gate) and I + i (up) in the same wavefront, so SwiGLU
-//            h = silu(a) * u is applied before anything leaves registers;
+//   gate/up: rows i (gate) and I + i (up) in the same slab, so SwiGLU
+//            h = silu(a) * u is applied before anything leaves registers. With
+//            bf16 activations, weights become exact bf16 pairs
+//            (v_cvt_scalef32_pk_bf16_fp8, unit scale) and meet the packed
+//            activations in v_dot2c_f32_bf16; fp32 activations use fp32 FMA.
 //            h is written in fp32, row-major [P][I] in permuted row order.
-//   down:    y[row][n] = sum_i h[row][i] * Wd[n][i], fp32 [P][H].
+//   down:    y[row][n] = sum_i h[row][i] * Wd[n][i], fp32 FMA, fp32 [P][H].
+// Tokens of a group are taken NT at a time; a larger group takes several
+// passes over the weights already held in registers.
+#include <algorithm>
+
 #include "device.hpp"
 #include "layer.hpp"
 
@@ -35,87 +44,72 @@ struct BankPtrs {
   const float* sh_sd;
 };
 
-// Token id of permuted row `row`: routed slots are t*k + j, shared slots T*k + t.
-__device__ __forceinline__ int row_token(const int32_t* pair, int row, int k, int64_t TK) {
-  const int s = pair[row];
-  return s < TK ? s / k : (int)(s - TK);
-}
-
-// 16 activations of token `tok` at column `col`, as fp32.
-template <bool XBF16>
-__device__ __forceinline__ void load_x16(const void* x, int H, int tok, int col, float* o) {
-  if (XBF16) {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + (size_t)tok * H + col;
-    const uint4 a = ld16(p), b = ld16(p + 8);
-    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      o[2 * i] = bf16_lo(u[i]);
-      o[2 * i + 1] = bf16_hi(u[i]);
-    }
-  } else {
-    const float* p = reinterpret_cast<const float*>(x) + (size_t)tok * H + col;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 v = *reinterpret_cast<const float4*>(p + 4 * i);
-      o[4 * i] = v.x;
-      o[4 * i + 1] = v.y;
-      o[4 * i + 2] = v.z;
-      o[4 * i + 3] = v.w;
-    }
-  }
-}
-
-// sum_i dec(w[i]) * xv[i] over 16 E4M3 bytes.
-__device__ __forceinline__ float dot16(const uint4 w, const float* xv) {
-  float d[16];
+__device__ __forceinline__ void dec16(const uint4 w, float* d) {
   e4m3x4_to_f32(w.x, d);
   e4m3x4_to_f32(w.y, d + 4);
   e4m3x4_to_f32(w.z, d + 8);
   e4m3x4_to_f32(w.w, d + 12);
+}
+
+__device__ __forceinline__ float dot16(const float* d, const float* xv) {
   float p = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) p = fmaf(d[i], xv[i], p);
   return p;
 }
 
-template <int H, int I, int B, int NT, int RP, bool XBF16>
-__global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, BankPtrs bk,
-                                                   const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ meta,
-                                                   const int32_t* __restrict__ active,
-                                                   const int32_t* __restrict__ pair, int k,
-                                                   int64_t TK, int E, float* __restrict__ h) {
+// ------------------------------------------------------------- gate/up ---
+template <int H, int I, int RP>
+struct GateUpSlab {
   using M = RowMap<H>;
-  static_assert(I % (RP * M::RPL) == 0, "gate rows must split evenly over wavefronts");
-  if ((int)blockIdx.y >= meta[0]) return;
-  const int g = active[blockIdx.y];
+  uint4 wg[RP][M::CH], wu[RP][M::CH];
+  float sg[RP][M::CH], su[RP][M::CH];
+  int r0, n, i0;
+};
+
+template <int H, int I, int B, int RP>
+__device__ __forceinline__ void gate_up_load(GateUpSlab<H, I, RP>& sl, int s, const BankPtrs& bk,
+                                             const int4* __restrict__ gdesc, int E, int lane) {
+  using M = RowMap<H>;
+  constexpr int SPG = I / (RP * M::RPL);  // slabs per group
+  const int y = s / SPG;
+  const int4 gd = gdesc[y];
+  const int g = gd.x;
   const bool sh = g == E;
   const uint8_t* W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
   const float* Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / B) * (H / B);
-  const int r0 = offsets[g], n = offsets[g + 1] - r0;
-  const int lane = threadIdx.x & 63;
-  const int i0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RP * M::RPL;
-  if (i0 >= I) return;
+  sl.r0 = gd.y;
+  sl.n = gd.z;
+  sl.i0 = (s - y * SPG) * RP * M::RPL;
   const bool act = M::active(lane);
   const int roff = M::row(lane);
-
-  float sg[RP][M::CH], su[RP][M::CH];
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
-    const int i = i0 + r * M::RPL + roff;
+    const int i = sl.i0 + r * M::RPL + roff;
 #pragma unroll
     for (int c = 0; c < M::CH; ++c) {
       const int col = M::col(lane, c);
-      sg[r][c] = act ? Sc[(i / B) * (H / B) + col / B] : 0.f;
-      su[r][c] = act ? Sc[((I + i) / B) * (H / B) + col / B] : 0.f;
+      sl.wg[r][c] = act ? ld16_nt(W + (size_t)i * H + col) : make_uint4(0, 0, 0, 0);
+      sl.wu[r][c] = act ? ld16_nt(W + (size_t)(I + i) * H + col) : make_uint4(0, 0, 0, 0);
+      sl.sg[r][c] = act ? Sc[(i / B) * (H / B) + col / B] : 0.f;
+      sl.su[r][c] = act ? Sc[((I + i) / B) * (H / B) + col / B] : 0.f;
     }
   }
+}
 
-  for (int t0 = 0; t0 < n; t0 += NT) {
+template <int H, int I, int NT, int RP, bool XBF16>
+__device__ __forceinline__ void gate_up_compute(const GateUpSlab<H, I, RP>& sl,
+                                                const void* __restrict__ x,
+                                                const int32_t* __restrict__ rtok,
+                                                float* __restrict__ h, int lane) {
+  using M = RowMap<H>;
+  const bool act = M::active(lane);
+  const int roff = M::row(lane);
+  for (int t0 = 0; t0 < sl.n; t0 += NT) {
+    const int nv = sl.n - t0 < NT ? sl.n - t0 : NT;  // tokens in this pass (uniform)
     int tok[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) tok[t] = (t0 + t < n) ? row_token(pair, r0 + t0 + t, k, TK) : -1;
+    for (int t = 0; t < NT; ++t) tok[t] = t < nv ? rtok[sl.r0 + t0 + t] : 0;
     float ag[RP][NT], au[RP][NT];
 #pragma unroll
     for (int r = 0; r < RP; ++r)
@@ -125,31 +119,83 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
 #pragma unroll
     for (int c = 0; c < M::CH; ++c) {
       const int col = M::col(lane, c);
-      uint4 wg[RP], wu[RP];
+      if (XBF16) {
+        uint32_t xr[NT][8];
 #pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        const int i = i0 + r * M::RPL + roff;
-        if (act) {
-          wg[r] = ld16(W + (size_t)i * H + col);
-          wu[r] = ld16(W + (size_t)(I + i) * H + col);
-        } else {
-          wg[r] = wu[r] = make_uint4(0, 0, 0, 0);
-        }
-      }
+        for (int t = 0; t < NT; ++t) {
+          if (t < nv && act) {
+            const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + (size_t)tok[t] * H + col;
+            const uint4 a = ld16(p), b = ld16(p + 8);
+            xr[t][0] = a.x;
+            xr[t][1] = a.y;
+            xr[t][2] = a.z;
+            xr[t][3] = a.w;
+            xr[t][4] = b.x;
+            xr[t][5] = b.y;
+            xr[t][6] = b.z;
+            xr[t][7] = b.w;
+          } else {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (tok[t] < 0) continue;
-        float xv[16];
-        if (act) {
-          load_x16<XBF16>(x, H, tok[t], col, xv);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) xv[q] = 0.f;
+            for (int q = 0; q < 8; ++q) xr[t][q] = 0u;
+          }
         }
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-          ag[r][t] = fmaf(sg[r][c], dot16(wg[r], xv), ag[r][t]);
-          au[r][t] = fmaf(su[r][c], dot16(wu[r], xv), au[r][t]);
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint4 wq = half ? sl.wu[r][c] : sl.wg[r][c];
+            const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+            bf16x2_t wb[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              wb[2 * q] = e4m3x2_to_bf16x2<false>(wd[q]);
+              wb[2 * q + 1] = e4m3x2_to_bf16x2<true>(wd[q]);
+            }
+            const float sc = half ? sl.su[r][c] : sl.sg[r][c];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              if (t < nv) {
+                float p = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) p = dot2_bf16(wb[j], xr[t][j], p);
+                if (half)
+                  au[r][t] = fmaf(sc, p, au[r][t]);
+                else
+                  ag[r][t] = fmaf(sc, p, ag[r][t]);
+              }
+            }
+          }
+        }
+      } else {
+        float xv[NT][16];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t < nv && act) {
+            const float* p = reinterpret_cast<const float*>(x) + (size_t)tok[t] * H + col;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 v = *reinterpret_cast<const float4*>(p + 4 * q);
+              xv[t][4 * q] = v.x;
+              xv[t][4 * q + 1] = v.y;
+              xv[t][4 * q + 2] = v.z;
+              xv[t][4 * q + 3] = v.w;
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) xv[t][q] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          float d[16];
+          dec16(sl.wg[r][c], d);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if (t < nv) ag[r][t] = fmaf(sl.sg[r][c], dot16(d, xv[t]), ag[r][t]);
+          dec16(sl.wu[r][c], d);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if (t < nv) au[r][t] = fmaf(sl.su[r][c], dot16(d, xv[t]), au[r][t]);
         }
       }
     }
@@ -157,47 +203,80 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
     for (int r = 0; r < RP; ++r) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        if (t >= nv) continue;
         const float a = group_sum<M::RED>(ag[r][t]);
         const float u = group_sum<M::RED>(au[r][t]);
         const int q = r * NT + t;
         const bool writer = M::RED == 64 ? lane == (q & 63) : (lane % M::RED) == (q % M::RED);
-        if (tok[t] >= 0 && writer)
-          h[(size_t)(r0 + t0 + t) * I + i0 + r * M::RPL + roff] = silu(a) * u;
+        if (writer) h[(size_t)(sl.r0 + t0 + t) * I + sl.i0 + r * M::RPL + roff] = silu(a) * u;
       }
     }
   }
 }
 
-template <int H, int I, int B, int NT, int RD>
-__global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int32_t* __restrict__ offsets,
-                                                const int32_t* __restrict__ meta,
-                                                const int32_t* __restrict__ active, int E,
-                                                const float* __restrict__ h,
-                                                float* __restrict__ y) {
+// grid: (slab blocks of 4 slabs, group slots); slots past the last group exit.
+template <int H, int I, int B, int NT, int RP, bool XBF16>
+__global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, BankPtrs bk,
+                                                   const int4* __restrict__ gdesc,
+                                                   const int32_t* __restrict__ rtok, int E,
+                                                   float* __restrict__ h) {
+  using M = RowMap<H>;
+  static_assert(I % (RP * M::RPL) == 0, "gate rows must split evenly into slabs");
+  constexpr int SPG = I / (RP * M::RPL);
+  const int lane = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= SPG || gdesc[blockIdx.y].x < 0) return;
+  GateUpSlab<H, I, RP> a;
+  gate_up_load<H, I, B, RP>(a, (int)blockIdx.y * SPG + blk, bk, gdesc, E, lane);
+  gate_up_compute<H, I, NT, RP, XBF16>(a, x, rtok, h, lane);
+}
+
+// ---------------------------------------------------------------- down ---
+template <int H, int I, int RD>
+struct DownSlab {
   using M = RowMap<I>;
-  static_assert(H % (RD * M::RPL) == 0, "down rows must split evenly over wavefronts");
-  if ((int)blockIdx.y >= meta[0]) return;
-  const int g = active[blockIdx.y];
+  uint4 w[RD][M::CH];
+  float sd[RD][M::CH];
+  int r0, n, n0;
+};
+
+template <int H, int I, int B, int RD>
+__device__ __forceinline__ void down_load(DownSlab<H, I, RD>& sl, int s, const BankPtrs& bk,
+                                          const int4* __restrict__ gdesc, int E, int lane) {
+  using M = RowMap<I>;
+  constexpr int SPG = H / (RD * M::RPL);
+  const int y = s / SPG;
+  const int4 gd = gdesc[y];
+  const int g = gd.x;
   const bool sh = g == E;
   const uint8_t* W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
   const float* Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / B) * (I / B);
-  const int r0 = offsets[g], n = offsets[g + 1] - r0;
-  const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RD * M::RPL;
-  if (n0 >= H) return;
+  sl.r0 = gd.y;
+  sl.n = gd.z;
+  sl.n0 = (s - y * SPG) * RD * M::RPL;
   const bool act = M::active(lane);
   const int roff = M::row(lane);
-
-  float sd[RD][M::CH];
 #pragma unroll
   for (int r = 0; r < RD; ++r) {
-    const int row = n0 + r * M::RPL + roff;
+    const int row = sl.n0 + r * M::RPL + roff;
 #pragma unroll
-    for (int c = 0; c < M::CH; ++c)
-      sd[r][c] = act ? Sc[(row / B) * (I / B) + M::col(lane, c) / B] : 0.f;
+    for (int c = 0; c < M::CH; ++c) {
+      const int col = M::col(lane, c);
+      sl.w[r][c] = act ? ld16_nt(W + (size_t)row * I + col) : make_uint4(0, 0, 0, 0);
+      sl.sd[r][c] = act ? Sc[(row / B) * (I / B) + col / B] : 0.f;
+    }
   }
+}
 
-  for (int t0 = 0; t0 < n; t0 += NT) {
+template <int H, int I, int NT, int RD>
+__device__ __forceinline__ void down_compute(const DownSlab<H, I, RD>& sl,
+                                             const float* __restrict__ h, float* __restrict__ y,
+                                             int lane) {
+  using M = RowMap<I>;
+  const bool act = M::active(lane);
+  const int roff = M::row(lane);
+  for (int t0 = 0; t0 < sl.n; t0 += NT) {
+    const int nv = sl.n - t0 < NT ? sl.n - t0 : NT;  // tokens in this pass (uniform)
     float acc[RD][NT];
 #pragma unroll
     for (int r = 0; r < RD; ++r)
@@ -206,82 +285,101 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int32_t* __r
 #pragma unroll
     for (int c = 0; c < M::CH; ++c) {
       const int col = M::col(lane, c);
-      uint4 wv[RD];
-#pragma unroll
-      for (int r = 0; r < RD; ++r)
-        wv[r] = act ? ld16(W + (size_t)(n0 + r * M::RPL + roff) * I + col)
-                    : make_uint4(0, 0, 0, 0);
+      float hv[NT][16];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (t0 + t >= n) continue;
-        float hv[16];
-        if (act) {
-          const float* p = h + (size_t)(r0 + t0 + t) * I + col;
+        if (t < nv && act) {
+          const float* p = h + (size_t)(sl.r0 + t0 + t) * I + col;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 v = *reinterpret_cast<const float4*>(p + 4 * q);
-            hv[4 * q] = v.x;
-            hv[4 * q + 1] = v.y;
-            hv[4 * q + 2] = v.z;
-            hv[4 * q + 3] = v.w;
+            hv[t][4 * q] = v.x;
+            hv[t][4 * q + 1] = v.y;
+            hv[t][4 * q + 2] = v.z;
+            hv[t][4 * q + 3] = v.w;
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < 16; ++q) hv[q] = 0.f;
+          for (int q = 0; q < 16; ++q) hv[t][q] = 0.f;
         }
+      }
 #pragma unroll
-        for (int r = 0; r < RD; ++r) acc[r][t] = fmaf(sd[r][c], dot16(wv[r], hv), acc[r][t]);
+      for (int r = 0; r < RD; ++r) {
+        float d[16];
+        dec16(sl.w[r][c], d);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t < nv) acc[r][t] = fmaf(sl.sd[r][c], dot16(d, hv[t]), acc[r][t]);
       }
     }
 #pragma unroll
     for (int r = 0; r < RD; ++r) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        if (t >= nv) continue;
         const float v = group_sum<M::RED>(acc[r][t]);
         const int q = r * NT + t;
         const bool writer = M::RED == 64 ? lane == (q & 63) : (lane % M::RED) == (q % M::RED);
-        if (t0 + t < n && writer)
-          y[(size_t)(r0 + t0 + t) * H + n0 + r * M::RPL + roff] = v;
+        if (writer) y[(size_t)(sl.r0 + t0 + t) * H + sl.n0 + r * M::RPL + roff] = v;
       }
     }
   }
 }
 
+template <int H, int I, int B, int NT, int RD>
+__global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __restrict__ gdesc,
+                                                int E, const float* __restrict__ h,
+                                                float* __restrict__ y) {
+  using M = RowMap<I>;
+  static_assert(H % (RD * M::RPL) == 0, "down rows must split evenly into slabs");
+  constexpr int SPG = H / (RD * M::RPL);
+  const int lane = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= SPG || gdesc[blockIdx.y].x < 0) return;
+  DownSlab<H, I, RD> a;
+  down_load<H, I, B, RD>(a, (int)blockIdx.y * SPG + blk, bk, gdesc, E, lane);
+  down_compute<H, I, NT, RD>(a, h, y, lane);
+}
+
 // ---------------------------------------------------------------------------
+// Rows per slab: about `bytes` of weights, never fewer than one wavefront-load.
+template <int K>
+constexpr int rows_for(int bytes) {
+  return RowMap<K>::RPL * RowMap<K>::CH * 1024 >= bytes ? 1 : bytes / (RowMap<K>::CH * 1024);
+}
+
 template <int H, int I, int B, int NT, bool XBF16>
 static void run_gemv(const Dims& d, const void* x, const BankPtrs& bk, const Work& w,
                      hipStream_t s, hipEvent_t after_gate_up) {
   using MG = RowMap<H>;
   using MD = RowMap<I>;
-  // gate rows (and as many up rows) per wavefront-load, and down rows
-  constexpr int RP = I / MG::RPL < 2 ? I / MG::RPL : 2;
-  constexpr int RD = H / MD::RPL < 4 ? H / MD::RPL : 4;
+  // slab sizes: gate/up RP gate rows plus RP up rows (~8 KiB), down RD rows
+  // (~6-8 KiB)
+  constexpr int RP0 = rows_for<H>(4096);
+  constexpr int RP = I / MG::RPL < RP0 ? I / MG::RPL : RP0;
+  constexpr int RD0 = rows_for<I>(8192) > 8 ? 8 : rows_for<I>(8192);
+  constexpr int RD = H / MD::RPL < RD0 ? H / MD::RPL : RD0;
+  constexpr int SPG1 = I / (RP * MG::RPL), SPG2 = H / (RD * MD::RPL);
+  const int4* gdesc = reinterpret_cast<const int4*>(w.gdesc);
   const int groups = (int)std::min<int64_t>(d.E, d.T * d.k) + d.S;
-  const dim3 g1((I / (RP * MG::RPL) + 3) / 4, groups);
-  gemv_gate_up<H, I, B, NT, RP, XBF16><<<g1, 256, 0, s>>>(
-      x, bk, w.offsets, w.meta, w.active, w.pair, d.k, d.T * d.k, d.E,
-      reinterpret_cast<float*>(w.h));
+  gemv_gate_up<H, I, B, NT, RP, XBF16><<<dim3((SPG1 + 3) / 4, groups), 256, 0, s>>>(
+      x, bk, gdesc, w.rtok, d.E, reinterpret_cast<float*>(w.h));
   if (after_gate_up) (void)hipEventRecord(after_gate_up, s);
-  const dim3 g2((H / (RD * MD::RPL) + 3) / 4, groups);
-  gemv_down<H, I, B, NT, RD><<<g2, 256, 0, s>>>(bk, w.offsets, w.meta, w.active, d.E,
-                                                reinterpret_cast<const float*>(w.h), w.y);
+  gemv_down<H, I, B, 1, RD><<<dim3((SPG2 + 3) / 4, groups), 256, 0, s>>>(
+      bk, gdesc, d.E, reinterpret_cast<const float*>(w.h), w.y);
 }
 
 template <int H, int I, int B>
 static void run_gemv_nt(const Dims& d, const void* x, const BankPtrs& bk, const Work& w,
                         hipStream_t s, hipEvent_t ev) {
-  // tokens per pass: enough for the largest possible group up to 8
-  const int64_t most = d.T;
+  // tokens per gate/up pass: up to 2 with bf16 activations, 1 with fp32 ones
+  // (the down pass takes one); larger groups take several passes over the
+  // weights held in registers
   if (d.x_bf16) {
-    if (most <= 1) run_gemv<H, I, B, 1, true>(d, x, bk, w, s, ev);
-    else if (most <= 2) run_gemv<H, I, B, 2, true>(d, x, bk, w, s, ev);
-    else if (most <= 4) run_gemv<H, I, B, 4, true>(d, x, bk, w, s, ev);
-    else run_gemv<H, I, B, 8, true>(d, x, bk, w, s, ev);
+    if (d.T <= 1) run_gemv<H, I, B, 1, true>(d, x, bk, w, s, ev);
+    else run_gemv<H, I, B, 2, true>(d, x, bk, w, s, ev);
   } else {
-    if (most <= 1) run_gemv<H, I, B, 1, false>(d, x, bk, w, s, ev);
-    else if (most <= 2) run_gemv<H, I, B, 2, false>(d, x, bk, w, s, ev);
-    else if (most <= 4) run_gemv<H, I, B, 4, false>(d, x, bk, w, s, ev);
-    else run_gemv<H, I, B, 8, false>(d, x, bk, w, s, ev);
+    run_gemv<H, I, B, 1, false>(d, x, bk, w, s, ev);
   }
 }
 
@@ -304,10 +402,10 @@ hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_ba
   BankPtrs bk{routed.w_gate_up, routed.w_down, routed.s_gate_up, routed.s_down,
               shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
               shared ? shared->s_gate_up : nullptr, shared ? shared->s_down : nullptr};
-#define X(h, i, b)                                              \
-  if (d.H == h && d.I == i && d.B == b) {                       \
-    run_gemv_nt<h, i, b>(d, x, bk, w, s, after_gate_up);        \
-    return hipGetLastError();                                   \
+#define X(h, i, b)                                       \
+  if (d.H == h && d.I == i && d.B == b) {                \
+    run_gemv_nt<h, i, b>(d, x, bk, w, s, after_gate_up); \
+    return hipGetLastError();                            \
   }
   MOE_GEMV_SHAPES(X)
 #undef X

@@ -25,14 +25,26 @@ struct Dims {
   bool mfma;     // expert family: grouped bf16 MFMA (true) or wavefront GEMV
 };
 
+// Router partial logits: decode-sized calls split H into slices of
+// kRouterSlice columns (or one slice of H < kRouterSlice) and the top-k kernel
+// sums the slices in order. 0 = the tiled-GEMM router (one full slice).
+constexpr int kRouterSlice = 512;
+inline int router_slices(const Dims& d) {
+  if (d.T > kGemvMaxTokens) return 0;
+  if (d.H < kRouterSlice) return 1;
+  return d.H % kRouterSlice == 0 ? d.H / kRouterSlice : 0;
+}
+
 // Carved workspace. Every region is kAlign-aligned.
 struct Work {
-  float* logits;     // [T][E]
+  float* logits;     // [slices][T][E] partial router logits (bias not added)
   int32_t* topk;     // [T][k]
   float* gates;      // [T][k]
   int32_t* offsets;  // [E+2]
   int32_t* meta;     // [16]: meta[0] = active groups, meta[1] = MFMA tiles
-  int32_t* active;   // [E+1] ids of non-empty groups (shared group = E)
+  int32_t* gdesc;    // [E+2][4] per non-empty group: (group, first row, rows, 0);
+                     // group = -1 past the last one (shared group = E)
+  int32_t* rtok;     // [P] token of each permuted row
   int32_t* pair;     // [P] row -> slot
   int32_t* inv;      // [P] slot -> row
   int32_t* tiles;    // [max_tiles][2] (group, first row) of each MFMA row tile
@@ -49,12 +61,18 @@ size_t workspace_bytes(const Dims& d);
 Work carve(const Dims& d, void* base);
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
-hipError_t launch_router(const Dims& d, const void* x, const float* wr, const float* bias,
-                         float* logits, hipStream_t s);
-hipError_t launch_topk(const Dims& d, const float* logits, int32_t* topk, float* gates,
-                       hipStream_t s);
+hipError_t launch_router(const Dims& d, const void* x, const float* wr, float* plogits,
+                         hipStream_t s);
+// Sums the router slices, adds the bias, selects and gates; optionally writes
+// the final logits.
+hipError_t launch_topk(const Dims& d, const float* plogits, const float* bias, int32_t* topk,
+                       float* gates, float* logits_out, hipStream_t s);
 hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
                           hipStream_t s);
+// Decode sizes: top-k + gates + permutation in one workgroup.
+bool small_select_permute(const Dims& d);
+hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
+                                       const Work& w, int tile_rows, hipStream_t s);
 // expert passes; returns hipErrorInvalidValue if no instantiation matches
 hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,

@@ -14,33 +14,37 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
+constexpr int kRegions = 12;
+
 static void region_sizes(const Dims& d, size_t* sz) {
-  sz[0] = (size_t)d.T * d.E * 4;          // logits
+  const int ns = router_slices(d) > 0 ? router_slices(d) : 1;
+  sz[0] = (size_t)ns * d.T * d.E * 4;     // partial router logits
   sz[1] = (size_t)d.T * d.k * 4;          // topk
   sz[2] = (size_t)d.T * d.k * 4;          // gates
   sz[3] = (size_t)(d.E + 2) * 4;          // offsets
   sz[4] = 16 * 4;                         // meta
-  sz[5] = (size_t)(d.E + 1) * 4;          // active
-  sz[6] = (size_t)d.P * 4;                // pair
-  sz[7] = (size_t)d.P * 4;                // inv
-  sz[8] = (size_t)max_mfma_tiles(d) * 8;  // tiles
-  sz[9] = (size_t)d.P * d.I * 4;          // h (fp32 bound; MFMA family uses half)
-  sz[10] = (size_t)d.P * d.H * 4;         // y
+  sz[5] = (size_t)(d.E + 2) * 16;         // group descriptors
+  sz[6] = (size_t)d.P * 4;                // rtok
+  sz[7] = (size_t)d.P * 4;                // pair
+  sz[8] = (size_t)d.P * 4;                // inv
+  sz[9] = (size_t)max_mfma_tiles(d) * 8;  // tiles
+  sz[10] = (size_t)d.P * d.I * 4;         // h (fp32 bound; MFMA family uses half)
+  sz[11] = (size_t)d.P * d.H * 4;         // y
 }
 
 size_t workspace_bytes(const Dims& d) {
-  size_t sz[11], b = 0;
+  size_t sz[kRegions], b = 0;
   region_sizes(d, sz);
   for (size_t v : sz) b += al(v);
   return b;
 }
 
 Work carve(const Dims& d, void* base) {
-  size_t sz[11];
+  size_t sz[kRegions];
   region_sizes(d, sz);
   char* p = static_cast<char*>(base);
-  void* r[11];
-  for (int i = 0; i < 11; ++i) {
+  void* r[kRegions];
+  for (int i = 0; i < kRegions; ++i) {
     r[i] = p;
     p += al(sz[i]);
   }
@@ -50,12 +54,13 @@ Work carve(const Dims& d, void* base) {
   w.gates = static_cast<float*>(r[2]);
   w.offsets = static_cast<int32_t*>(r[3]);
   w.meta = static_cast<int32_t*>(r[4]);
-  w.active = static_cast<int32_t*>(r[5]);
-  w.pair = static_cast<int32_t*>(r[6]);
-  w.inv = static_cast<int32_t*>(r[7]);
-  w.tiles = static_cast<int32_t*>(r[8]);
-  w.h = r[9];
-  w.y = static_cast<float*>(r[10]);
+  w.gdesc = static_cast<int32_t*>(r[5]);
+  w.rtok = static_cast<int32_t*>(r[6]);
+  w.pair = static_cast<int32_t*>(r[7]);
+  w.inv = static_cast<int32_t*>(r[8]);
+  w.tiles = static_cast<int32_t*>(r[9]);
+  w.h = r[10];
+  w.y = static_cast<float*>(r[11]);
   return w;
 }
 
@@ -150,10 +155,20 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
   hipEvent_t ev_gate_up =
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr;
   if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
-  if (launch_router(d, x, router_w, router_bias, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_topk(d, w.logits, w.topk, w.gates, s) != hipSuccess) return MOE_ERR_HIP;
-  if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
-  if (launch_permute(d, w.topk, w, d.mfma ? kMfmaBM : 0, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
+  const int tile_rows = d.mfma ? kMfmaBM : 0;
+  if (small_select_permute(d)) {
+    // decode sizes: selection and permutation share one launch, so ROUTED
+    // marks the end of the router logits here
+    if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
+    if (launch_select_permute_small(d, w.logits, router_bias, w, tile_rows, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    if (launch_topk(d, w.logits, router_bias, w.topk, w.gates, nullptr, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
+    if (launch_permute(d, w.topk, w, tile_rows, s) != hipSuccess) return MOE_ERR_HIP;
+  }
   if (!rec(events, MOE_EV_PERMUTED, s)) return MOE_ERR_HIP;
   const moe_expert_bank* sh = d.S ? shared : nullptr;
   const hipError_t e = d.mfma ? launch_experts_mfma(d, x, *experts, sh, w, s, ev_gate_up)
@@ -177,9 +192,9 @@ moe_status moe_route(const void* x, const float* router_w, const float* router_b
   if (st != MOE_OK) return st;
   const Work w = carve(d, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* l = logits ? logits : w.logits;
-  if (launch_router(d, x, router_w, router_bias, l, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_topk(d, l, topk_idx, gates, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_topk(d, w.logits, router_bias, topk_idx, gates, logits, s) != hipSuccess)
+    return MOE_ERR_HIP;
   return MOE_OK;
 }
 

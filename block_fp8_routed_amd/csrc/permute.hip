@@ -1,194 +1,64 @@
-// permute.hip — token -> expert permutation (the per-expert fan-out of the
-// colizig page's "Features": experts are evaluated one group at a time, and
-// the threaded result is bit-identical to the serial one).
-//
-// Slot s = t*k + j is the j-th choice of token t. The permutation groups the
-// slots by expert; inside a group the slots stay in ascending order (stable),
-// so a group's rows are its tokens in ascending order. The always-on shared
-// expert, when present, is group E with slots T*k + t.
-//
-// One workgroup does it in four passes over LDS:
-//   1. count:   wave w takes a contiguous slot range and adds 1 per slot to its
-//               own counter row cnt[w][e] (LDS integer atomics, order-free);
-//   2. scan:    exclusive scan over (expert-major, wave-minor) gives each
-//               (wave, expert) its first row;
-//   3. scatter: each wave walks its slots in order, 64 at a time; lanes with
-//               the same expert find each other with one ballot per expert-id
-//               bit, take their rank among lower lanes, and the group's first
-//               lane advances the counter, so rows keep slot order;
-//   4. lists:   the non-empty groups (ascending, shared last) and, for the MFMA
-//               family, one (group, first row) entry per tile of tile_rows rows.
-// Expert ids outside [0, E) (possible only through moe_permute's caller) are
-// left out of every group with inv = -1; the shared group then starts right
-// after the last valid routed row. Nothing is accessed out of bounds.
-#include "device.hpp"
+// permute.hip — the token -> expert permutation kernels (permute_body), and
+// the fused decode kernel that selects every token's experts and permutes in
+// one workgroup.
 #include "layer.hpp"
+#include "permute.hpp"
+#include "select.hpp"
 
 namespace moe {
-
-template <int W>
-__device__ int block_excl_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += n;
-  }
-  if (lane == 63) tmp[w] = inc;
-  __syncthreads();
-  if (w == 0) {
-    const int t = lane < W ? tmp[lane] : 0;
-    int ti = t;
-#pragma unroll
-    for (int o = 1; o < W; o <<= 1) {
-      const int n = __shfl_up(ti, o, 64);
-      if (lane >= o) ti += n;
-    }
-    if (lane < W) tmp[32 + lane] = ti - t;
-    if (lane == W - 1) tmp[63] = ti;
-  }
-  __syncthreads();
-  const int res = inc - v + tmp[32 + w];
-  *total = tmp[63];
-  __syncthreads();
-  return res;
-}
 
 template <int W>
 __global__ __launch_bounds__(64 * W) void permute_kernel(
     const int32_t* __restrict__ topk, int64_t T, int k, int E, int S,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
-    int32_t* __restrict__ meta, int32_t* __restrict__ active, int32_t* __restrict__ tiles,
-    int tile_rows) {
+    int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
+    int32_t* __restrict__ tiles, int tile_rows) {
   extern __shared__ int32_t lds[];
-  int32_t* cnt = lds;          // [W][E]
-  int32_t* base = lds + W * E; // [E]
-  int32_t* tmp = base + E;     // [64]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  constexpr int NTH = 64 * W;
-  const int64_t TK = T * k;
+  permute_body<W>(topk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, lds);
+}
 
-  for (int i = tid; i < W * E; i += NTH) cnt[i] = 0;
+// Decode sizes (T <= 16, E <= 512): wavefront t selects token t's experts
+// (select_token), the selection goes to LDS, and all 16 wavefronts then run
+// the permutation on it. Same arithmetic as topk_softmax + permute_kernel.
+template <int NV>
+__global__ __launch_bounds__(1024) void select_permute_small(
+    const float* __restrict__ plog, int slices, const float* __restrict__ bias, int64_t T, int k,
+    int E, int S, int32_t* __restrict__ topk, float* __restrict__ gates,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
+    int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
+    int32_t* __restrict__ tiles, int tile_rows) {
+  extern __shared__ int32_t lds[];
+  int32_t* stk = lds + 16 * E + E + 64;  // [T][k]
+  const int64_t t = threadIdx.x >> 6;
+  if (t < T) select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, nullptr, stk);
   __syncthreads();
+  permute_body<16>(stk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, lds);
+}
 
-  // 1. count
-  const int64_t per = (TK + W - 1) / W;
-  const int64_t lo = min(TK, (int64_t)w * per), hi = min(TK, lo + per);
-  for (int64_t s = lo + lane; s < hi; s += 64) {
-    const int e = topk[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w * E + e], 1);
-  }
-  __syncthreads();
+bool small_select_permute(const Dims& d) {
+  return d.T <= kGemvMaxTokens && d.E <= 512;
+}
 
-  // 2. scan: column prefix over waves, then over experts
-  for (int e = tid; e < E; e += NTH) {
-    int run = 0;
-    for (int ww = 0; ww < W; ++ww) {
-      const int c = cnt[ww * E + e];
-      cnt[ww * E + e] = run;
-      run += c;
-    }
-    base[e] = run;  // count of e, for now
-  }
-  __syncthreads();
-  const int ept = (E + NTH - 1) / NTH;
-  const int e0 = tid * ept;
-  int local = 0;
-  for (int i = 0; i < ept; ++i)
-    if (e0 + i < E) local += base[e0 + i];
-  int total;
-  int run = block_excl_scan<W>(local, tmp, &total);
-  for (int i = 0; i < ept; ++i) {
-    if (e0 + i < E) {
-      const int c = base[e0 + i];
-      offsets[e0 + i] = run;
-      base[e0 + i] = run;
-      run += c;
-    }
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    offsets[E + 1] = (int)(total + S * T);
-  }
-  __syncthreads();
-  for (int i = tid; i < W * E; i += NTH) cnt[i] += base[i % E];
-  __syncthreads();
-
-  // 3. stable scatter
-  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
-  for (int64_t b0 = lo; b0 < hi; b0 += 64) {
-    const int64_t s = b0 + lane;
-    const int e_in = s < hi ? topk[s] : 0;
-    const bool ok = s < hi && (unsigned)e_in < (unsigned)E;
-    const int e = ok ? e_in : 0;
-    if (s < hi && !ok) inv[s] = -1;
-    unsigned long long peers = __ballot(ok);
-    for (int b = 0; b < ebits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const unsigned long long m = __ballot(ok && bit);
-      peers &= bit ? m : ~m;
-    }
-    if (!ok) peers = 0;
-    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    const int leader = ok ? (__ffsll((long long)peers) - 1) : lane;
-    int old = 0;
-    if (ok && lane == leader) old = atomicAdd(&cnt[w * E + e], __popcll(peers));
-    old = __shfl(old, leader, 64);
-    if (ok) {
-      const int pos = old + rank;
-      pair[pos] = (int)s;
-      inv[s] = pos;
-    }
-  }
-  if (S) {
-    for (int64_t t = tid; t < T; t += NTH) {
-      pair[total + t] = (int)(TK + t);
-      inv[TK + t] = (int)(total + t);
-    }
-  }
-
-  // 4. non-empty groups and MFMA row tiles
-  int nf = 0, nt = 0;
-  for (int i = 0; i < ept; ++i) {
-    const int e = e0 + i;
-    if (e < E) {
-      const int c = (e + 1 < E ? base[e + 1] : total) - base[e];
-      nf += c > 0;
-      if (tile_rows > 0) nt += (c + tile_rows - 1) / tile_rows;
-    }
-  }
-  int nact;
-  int apos = block_excl_scan<W>(nf, tmp, &nact);
-  int ntile = 0;
-  int tpos = tile_rows > 0 ? block_excl_scan<W>(nt, tmp, &ntile) : 0;
-  for (int i = 0; i < ept; ++i) {
-    const int e = e0 + i;
-    if (e < E) {
-      const int c = (e + 1 < E ? base[e + 1] : total) - base[e];
-      if (c > 0) active[apos++] = e;
-      if (tile_rows > 0) {
-        for (int m = 0; m < c; m += tile_rows) {
-          tiles[2 * tpos] = e;
-          tiles[2 * tpos + 1] = base[e] + m;
-          ++tpos;
-        }
-      }
-    }
-  }
-  int nshared_tiles = 0;
-  if (S && tile_rows > 0) {
-    nshared_tiles = (int)((T + tile_rows - 1) / tile_rows);
-    for (int i = tid; i < nshared_tiles; i += NTH) {
-      tiles[2 * (ntile + i)] = E;
-      tiles[2 * (ntile + i) + 1] = (int)(total + (int64_t)i * tile_rows);
-    }
-  }
-  if (tid == 0) {
-    if (S) active[nact] = E;
-    meta[0] = nact + S;
-    meta[1] = ntile + nshared_tiles;
-  }
+hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
+                                       const Work& w, int tile_rows, hipStream_t s) {
+  const int ns = router_slices(d) > 0 ? router_slices(d) : 1;
+  const size_t lds = (size_t)(16 * d.E + d.E + 64 + d.T * d.k) * sizeof(int32_t);
+  const int nv = (d.E + 63) / 64;
+#define MOE_SP(NV)                                                                            \
+  select_permute_small<NV><<<1, 1024, lds, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk,  \
+                                                w.gates, w.offsets, w.pair, w.inv, w.rtok,   \
+                                                w.meta, reinterpret_cast<int4*>(w.gdesc),     \
+                                                w.tiles, tile_rows)
+  if (nv <= 1)
+    MOE_SP(1);
+  else if (nv <= 2)
+    MOE_SP(2);
+  else if (nv <= 4)
+    MOE_SP(4);
+  else
+    MOE_SP(8);
+#undef MOE_SP
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
@@ -196,11 +66,13 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int
   if (d.E <= 512) {
     const size_t lds = (size_t)(16 * d.E + d.E + 64) * sizeof(int32_t);
     permute_kernel<16><<<1, 1024, lds, s>>>(topk, d.T, d.k, d.E, d.S, w.offsets, w.pair, w.inv,
-                                            w.meta, w.active, w.tiles, tile_rows);
+                                            w.rtok, w.meta, reinterpret_cast<int4*>(w.gdesc),
+                                            w.tiles, tile_rows);
   } else {
     const size_t lds = (size_t)(8 * d.E + d.E + 64) * sizeof(int32_t);
     permute_kernel<8><<<1, 512, lds, s>>>(topk, d.T, d.k, d.E, d.S, w.offsets, w.pair, w.inv,
-                                          w.meta, w.active, w.tiles, tile_rows);
+                                          w.rtok, w.meta, reinterpret_cast<int4*>(w.gdesc),
+                                          w.tiles, tile_rows);
   }
   return hipGetLastError();
 }

@@ -1,74 +1,111 @@
-// router.hip — router logits l[t][e] = sum_h x[t][h] * Wr[e][h] (+ b[e]), fp32.
+// router.hip — router logits l[t][e] = sum_h x[t][h] * Wr[e][h], fp32.
 //
 // The router is small and always resident (colizig page, "Features" and
 // "Architecture & how it works": attention/router/norms stay resident, experts
 // are streamed). Its cost is reading Wr at decode sizes and E*T*H FMAs at
 // prefill sizes, so there are two kernels:
-//  * router_gemv (T <= 16): one wavefront per expert row, coalesced 16-byte
-//    loads of Wr, every token's dot product accumulated from the same load;
-//  * router_gemm (T > 16): 64x64 LDS-tiled fp32 GEMM.
-// Both accumulate in fp32 in two levels (short per-lane or per-128-column
-// partial sums added into a running total), which keeps the rounding error of
-// a 4096-term logit near 1e-6, well inside the 1e-5 band within which two
-// logits count as tied.
+//  * router_slices (T <= 16): H is cut into slices of 512 columns; a
+//    workgroup stages its slice of x in LDS and four wavefronts each stream
+//    four expert rows of the slice with coalesced 16-byte loads. Partial sums
+//    per slice are written out; the top-k kernel adds them in slice order.
+//  * router_gemm (T > 16): 64x64 LDS-tiled fp32 GEMM, one slice.
+// Both accumulate in fp32 in two levels (short partial sums added into a
+// running total), which keeps the rounding error of a 4096-term logit near
+// 1e-6, well inside the 1e-5 band within which two logits count as tied.
+// The bias is added by the top-k kernel.
 #include "device.hpp"
 #include "layer.hpp"
 
 namespace moe {
 
 template <int NT, bool XBF16>
-__global__ __launch_bounds__(256) void router_gemv(const void* __restrict__ x,
-                                                  const float* __restrict__ wr,
-                                                  const float* __restrict__ bias,
-                                                  float* __restrict__ logits, int T, int H,
-                                                  int E) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  const float* wrow = wr + (size_t)e * H;
-  float acc[NT];
+__global__ __launch_bounds__(256) void router_slices_kernel(const void* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           float* __restrict__ plog, int T,
+                                                           int H, int E, int HS) {
+  __shared__ float xs[NT * kRouterSlice];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h0 = blockIdx.y * HS;
+  const int e0 = blockIdx.x * 16 + wave * 4;
+
+  // expert rows first: the loads are in flight while x is staged
+  constexpr int J = kRouterSlice / 256;
+  float4 w[4][J];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-  for (int c = 4 * lane; c < H; c += 256) {
-    const float4 w = *reinterpret_cast<const float4*>(wrow + c);
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < T) {
-        float xv[4];
-        if (XBF16) {
-          const uint2 v = *reinterpret_cast<const uint2*>(
-              reinterpret_cast<const uint16_t*>(x) + (size_t)t * H + c);
-          xv[0] = bf16_lo(v.x);
-          xv[1] = bf16_hi(v.x);
-          xv[2] = bf16_lo(v.y);
-          xv[3] = bf16_hi(v.y);
-        } else {
-          const float4 v = *reinterpret_cast<const float4*>(
-              reinterpret_cast<const float*>(x) + (size_t)t * H + c);
-          xv[0] = v.x;
-          xv[1] = v.y;
-          xv[2] = v.z;
-          xv[3] = v.w;
-        }
-        acc[t] = fmaf(w.x, xv[0], acc[t]);
-        acc[t] = fmaf(w.y, xv[1], acc[t]);
-        acc[t] = fmaf(w.z, xv[2], acc[t]);
-        acc[t] = fmaf(w.w, xv[3], acc[t]);
+    for (int j = 0; j < J; ++j) {
+      const int c = 4 * lane + 256 * j;
+      w[r][j] = (e0 + r < E && c < HS)
+                    ? *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * H + h0 + c)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  // stage the T x HS slice of x: all loads first (compile-time trip count)
+  constexpr int IT = (NT * kRouterSlice + 1023) / 1024;
+  float4 xv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = 4 * tid + 1024 * it;
+    const int t = i / HS, c = i - t * HS;
+    xv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < T * HS) {
+      if (XBF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) +
+                                                        (size_t)t * H + h0 + c);
+        xv[it] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+      } else {
+        xv[it] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) +
+                                                  (size_t)t * H + h0 + c);
       }
     }
   }
-  const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float s = group_sum<64>(acc[t]);
-    if (t < T && lane == t) logits[(size_t)t * E + e] = s + b;
+  for (int it = 0; it < IT; ++it) {
+    const int i = 4 * tid + 1024 * it;
+    if (i < T * HS) *reinterpret_cast<float4*>(&xs[i]) = xv[it];
   }
+  __syncthreads();
+  if (e0 >= E) return;
+
+  float acc[4][NT];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = 4 * lane + 256 * j;
+    const bool cin = c < HS;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      // token rows past T (NT rounds T up) contribute zero
+      const float4 xv = (cin && t < T) ? *reinterpret_cast<const float4*>(&xs[t * HS + c])
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a = acc[r][t];
+        a = fmaf(w[r][j].x, xv.x, a);
+        a = fmaf(w[r][j].y, xv.y, a);
+        a = fmaf(w[r][j].z, xv.z, a);
+        a = fmaf(w[r][j].w, xv.w, a);
+        acc[r][t] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float v = group_sum<64>(acc[r][t]);
+      const int q = r * NT + t;
+      if (t < T && e0 + r < E && lane == (q & 63))
+        plog[((size_t)blockIdx.y * T + t) * E + e0 + r] = v;
+    }
 }
 
 template <bool XBF16>
 __global__ __launch_bounds__(256) void router_gemm(const void* __restrict__ x,
                                                   const float* __restrict__ wr,
-                                                  const float* __restrict__ bias,
                                                   float* __restrict__ logits, int64_t T, int H,
                                                   int E) {
   __shared__ float As[16][68];
@@ -147,40 +184,42 @@ __global__ __launch_bounds__(256) void router_gemm(const void* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + 4 * tx + j;
-      if (n < E) logits[m * E + n] = outer[i][j] + (bias ? bias[n] : 0.f);
+      if (n < E) logits[m * E + n] = outer[i][j];
     }
   }
 }
 
 template <int NT>
-static void gemv_launch(const Dims& d, const void* x, const float* wr, const float* bias,
-                        float* logits, hipStream_t s) {
-  const dim3 grid((d.E + 3) / 4);
+static void slices_launch(const Dims& d, const void* x, const float* wr, float* plog,
+                          hipStream_t s) {
+  const int ns = router_slices(d);
+  const int HS = d.H < kRouterSlice ? d.H : kRouterSlice;
+  const dim3 grid((d.E + 15) / 16, ns);
   if (d.x_bf16)
-    router_gemv<NT, true><<<grid, 256, 0, s>>>(x, wr, bias, logits, (int)d.T, d.H, d.E);
+    router_slices_kernel<NT, true><<<grid, 256, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
   else
-    router_gemv<NT, false><<<grid, 256, 0, s>>>(x, wr, bias, logits, (int)d.T, d.H, d.E);
+    router_slices_kernel<NT, false><<<grid, 256, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
 }
 
-hipError_t launch_router(const Dims& d, const void* x, const float* wr, const float* bias,
-                         float* logits, hipStream_t s) {
-  if (d.T <= 16) {
+hipError_t launch_router(const Dims& d, const void* x, const float* wr, float* plog,
+                         hipStream_t s) {
+  if (router_slices(d) > 0) {
     if (d.T <= 1)
-      gemv_launch<1>(d, x, wr, bias, logits, s);
+      slices_launch<1>(d, x, wr, plog, s);
     else if (d.T <= 2)
-      gemv_launch<2>(d, x, wr, bias, logits, s);
+      slices_launch<2>(d, x, wr, plog, s);
     else if (d.T <= 4)
-      gemv_launch<4>(d, x, wr, bias, logits, s);
+      slices_launch<4>(d, x, wr, plog, s);
     else if (d.T <= 8)
-      gemv_launch<8>(d, x, wr, bias, logits, s);
+      slices_launch<8>(d, x, wr, plog, s);
     else
-      gemv_launch<16>(d, x, wr, bias, logits, s);
+      slices_launch<16>(d, x, wr, plog, s);
   } else {
     const dim3 grid((unsigned)((d.T + 63) / 64), (d.E + 63) / 64);
     if (d.x_bf16)
-      router_gemm<true><<<grid, 256, 0, s>>>(x, wr, bias, logits, d.T, d.H, d.E);
+      router_gemm<true><<<grid, 256, 0, s>>>(x, wr, plog, d.T, d.H, d.E);
     else
-      router_gemm<false><<<grid, 256, 0, s>>>(x, wr, bias, logits, d.T, d.H, d.E);
+      router_gemm<false><<<grid, 256, 0, s>>>(x, wr, plog, d.T, d.H, d.E);
   }
   return hipGetLastError();
 }

@@ -106,7 +106,9 @@ typedef struct {
  * skipped; pass NULL for the whole struct to record nothing. */
 typedef enum {
   MOE_EV_START = 0,        /* before the router                            */
-  MOE_EV_ROUTED = 1,       /* after logits + top-k + gates                 */
+  MOE_EV_ROUTED = 1,       /* after logits + top-k + gates (at decode sizes,  */
+                           /* where selection and permutation share one      */
+                           /* launch: after the logits)                      */
   MOE_EV_PERMUTED = 2,     /* after the token→expert permutation           */
   MOE_EV_GATE_UP = 3,      /* after gate/up + SwiGLU (routed and shared)   */
   MOE_EV_DOWN = 4,         /* after the down projection                    */
