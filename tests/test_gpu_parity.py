@@ -113,6 +113,12 @@ FWD_CASES = [  # (config, tokens, path, overrides)
     ("c1", 40, "gemv", {"experts": 8, "top_k": 8}),
     ("c3", None, "auto", {}),
     ("c3", 3, "auto", {}),
+    # grouped bf16 MFMA family: several 64-row tiles per group, ragged tails
+    ("c1", 5, "mfma", {}),
+    ("c1", 37, "mfma", {}),
+    ("c1", 300, "mfma", {"experts": 16, "top_k": 4}),
+    ("c2", None, "auto", {}),
+    ("c3", 100, "mfma", {}),
 ]
 
 
@@ -174,3 +180,32 @@ def test_expert_relabelling_invariance():
                            router_bias=bias)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+def test_prefill_e512_full_size_sampled():
+    """The 512-expert prefill workload at full size (4096 tokens, 16 hot
+    experts) in the launch configuration the benchmark uses: routing of every
+    token and the whole permutation against the oracle; outputs on a sample of
+    tokens (hot-expert, cold-expert and shared rows) computed one by one."""
+    import block_fp8_routed_amd as moe
+    shape = C["c4"]
+    layer = DevLayer(shape)
+    log("c4: routing all 4096 tokens")
+    idx, gates = layer.route()
+    accepted, ties = check_routing(layer, idx, gates)
+    off, pair, inv = moe.moe_permute(idx, shape.experts, True, shape.hidden, shape.inter,
+                                     shape.block)
+    r_off, r_pair, r_inv = oracle.permutation(accepted, shape.experts, True)
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(pair.cpu().numpy(), r_pair)
+    assert np.array_equal(inv.cpu().numpy(), r_inv)
+    out = layer.forward()
+    torch.cuda.synchronize()
+    counts = np.bincount(accepted.reshape(-1), minlength=shape.experts)
+    hot = set(np.argsort(-counts)[:16].tolist())
+    rng = np.random.default_rng(11)
+    sample = sorted(set(rng.choice(shape.tokens, 24, replace=False).tolist()) | {0, 4095})
+    n_hot = sum(1 for t in sample if hot & set(accepted[t].tolist()))
+    log(f"c4: oracle on {len(sample)} sampled tokens ({n_hot} touch a hot expert), ties={ties}")
+    ref = layer.oracle(routing=accepted, tokens=np.array(sample))
+    check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 sampled")
