@@ -37,6 +37,26 @@ __device__ __forceinline__ float dot2_bf16(bf16x2_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two E4M3FN bytes to an fp16 pair (exact: every E4M3FN value is an fp16 value).
+template <bool HI>
+__device__ __forceinline__ f16x2_t e4m3x2_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI);
+}
+
+// c + a.lo * b.lo + a.hi * b.hi with fp16 inputs and an fp32 accumulator
+// (v_dot2c_f32_f16); b is a dword holding two fp16 values.
+__device__ __forceinline__ float dot2_f16(f16x2_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// fp32 -> fp16 bits, round to nearest even, saturated to the finite range.
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
+  v = fminf(fmaxf(v, -65504.f), 65504.f);
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
 // bf16 halves of a dword to fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

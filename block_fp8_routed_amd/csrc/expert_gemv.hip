@@ -22,8 +22,10 @@
 //            bf16 activations, weights become exact bf16 pairs
 //            (v_cvt_scalef32_pk_bf16_fp8, unit scale) and meet the packed
 //            activations in v_dot2c_f32_bf16; fp32 activations use fp32 FMA.
-//            h is written in fp32, row-major [P][I] in permuted row order.
-//   down:    y[row][n] = sum_i h[row][i] * Wd[n][i], fp32 FMA, fp32 [P][H].
+//            h is written as fp16 (saturated at +-65504), row-major [P][I] in
+//            permuted row order, the same form the MFMA family uses.
+//   down:    y[row][n] = sum_i h[row][i] * Wd[n][i]: weights become exact fp16
+//            pairs and meet h in v_dot2c_f32_f16; y is fp32 [P][H].
 // Tokens of a group are taken NT at a time; a larger group takes several
 // passes over the weights already held in registers.
 #include <algorithm>
@@ -101,7 +103,7 @@ template <int H, int I, int NT, int RP, bool XBF16>
 __device__ __forceinline__ void gate_up_compute(const GateUpSlab<H, I, RP>& sl,
                                                 const void* __restrict__ x,
                                                 const int32_t* __restrict__ rtok,
-                                                float* __restrict__ h, int lane) {
+                                                uint16_t* __restrict__ h, int lane) {
   using M = RowMap<H>;
   const bool act = M::active(lane);
   const int roff = M::row(lane);
@@ -208,7 +210,8 @@ __device__ __forceinline__ void gate_up_compute(const GateUpSlab<H, I, RP>& sl,
         const float u = group_sum<M::RED>(au[r][t]);
         const int q = r * NT + t;
         const bool writer = M::RED == 64 ? lane == (q & 63) : (lane % M::RED) == (q % M::RED);
-        if (writer) h[(size_t)(sl.r0 + t0 + t) * I + sl.i0 + r * M::RPL + roff] = silu(a) * u;
+        if (writer)
+          h[(size_t)(sl.r0 + t0 + t) * I + sl.i0 + r * M::RPL + roff] = f32_to_f16_sat(silu(a) * u);
       }
     }
   }
@@ -219,7 +222,7 @@ template <int H, int I, int B, int NT, int RP, bool XBF16>
 __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, BankPtrs bk,
                                                    const int4* __restrict__ gdesc,
                                                    const int32_t* __restrict__ rtok, int E,
-                                                   float* __restrict__ h) {
+                                                   uint16_t* __restrict__ h) {
   using M = RowMap<H>;
   static_assert(I % (RP * M::RPL) == 0, "gate rows must split evenly into slabs");
   constexpr int SPG = I / (RP * M::RPL);
@@ -270,8 +273,8 @@ __device__ __forceinline__ void down_load(DownSlab<H, I, RD>& sl, int s, const B
 
 template <int H, int I, int NT, int RD>
 __device__ __forceinline__ void down_compute(const DownSlab<H, I, RD>& sl,
-                                             const float* __restrict__ h, float* __restrict__ y,
-                                             int lane) {
+                                             const uint16_t* __restrict__ h,
+                                             float* __restrict__ y, int lane) {
   using M = RowMap<I>;
   const bool act = M::active(lane);
   const int roff = M::row(lane);
@@ -285,31 +288,43 @@ __device__ __forceinline__ void down_compute(const DownSlab<H, I, RD>& sl,
 #pragma unroll
     for (int c = 0; c < M::CH; ++c) {
       const int col = M::col(lane, c);
-      float hv[NT][16];
+      uint32_t hr[NT][8];  // 16 fp16 values of h per token
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t < nv && act) {
-          const float* p = h + (size_t)(sl.r0 + t0 + t) * I + col;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(p + 4 * q);
-            hv[t][4 * q] = v.x;
-            hv[t][4 * q + 1] = v.y;
-            hv[t][4 * q + 2] = v.z;
-            hv[t][4 * q + 3] = v.w;
-          }
+          const uint16_t* p = h + (size_t)(sl.r0 + t0 + t) * I + col;
+          const uint4 a = ld16(p), b = ld16(p + 8);
+          hr[t][0] = a.x;
+          hr[t][1] = a.y;
+          hr[t][2] = a.z;
+          hr[t][3] = a.w;
+          hr[t][4] = b.x;
+          hr[t][5] = b.y;
+          hr[t][6] = b.z;
+          hr[t][7] = b.w;
         } else {
 #pragma unroll
-          for (int q = 0; q < 16; ++q) hv[t][q] = 0.f;
+          for (int q = 0; q < 8; ++q) hr[t][q] = 0u;
         }
       }
 #pragma unroll
       for (int r = 0; r < RD; ++r) {
-        float d[16];
-        dec16(sl.w[r][c], d);
+        const uint32_t wd[4] = {sl.w[r][c].x, sl.w[r][c].y, sl.w[r][c].z, sl.w[r][c].w};
+        f16x2_t wf[8];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (t < nv) acc[r][t] = fmaf(sl.sd[r][c], dot16(d, hv[t]), acc[r][t]);
+        for (int q = 0; q < 4; ++q) {
+          wf[2 * q] = e4m3x2_to_f16x2<false>(wd[q]);
+          wf[2 * q + 1] = e4m3x2_to_f16x2<true>(wd[q]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t < nv) {
+            float p = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p = dot2_f16(wf[j], hr[t][j], p);
+            acc[r][t] = fmaf(sl.sd[r][c], p, acc[r][t]);
+          }
+        }
       }
     }
 #pragma unroll
@@ -328,7 +343,7 @@ __device__ __forceinline__ void down_compute(const DownSlab<H, I, RD>& sl,
 
 template <int H, int I, int B, int NT, int RD>
 __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __restrict__ gdesc,
-                                                int E, const float* __restrict__ h,
+                                                int E, const uint16_t* __restrict__ h,
                                                 float* __restrict__ y) {
   using M = RowMap<I>;
   static_assert(H % (RD * M::RPL) == 0, "down rows must split evenly into slabs");
@@ -360,13 +375,14 @@ static void run_gemv(const Dims& d, const void* x, const BankPtrs& bk, const Wor
   constexpr int RD0 = rows_for<I>(8192) > 8 ? 8 : rows_for<I>(8192);
   constexpr int RD = H / MD::RPL < RD0 ? H / MD::RPL : RD0;
   constexpr int SPG1 = I / (RP * MG::RPL), SPG2 = H / (RD * MD::RPL);
+  constexpr int NTD = NT;  // tokens per down pass (h fragments are packed fp16)
   const int4* gdesc = reinterpret_cast<const int4*>(w.gdesc);
   const int groups = (int)std::min<int64_t>(d.E, d.T * d.k) + d.S;
   gemv_gate_up<H, I, B, NT, RP, XBF16><<<dim3((SPG1 + 3) / 4, groups), 256, 0, s>>>(
-      x, bk, gdesc, w.rtok, d.E, reinterpret_cast<float*>(w.h));
+      x, bk, gdesc, w.rtok, d.E, reinterpret_cast<uint16_t*>(w.h));
   if (after_gate_up) (void)hipEventRecord(after_gate_up, s);
-  gemv_down<H, I, B, 1, RD><<<dim3((SPG2 + 3) / 4, groups), 256, 0, s>>>(
-      bk, gdesc, d.E, reinterpret_cast<const float*>(w.h), w.y);
+  gemv_down<H, I, B, NTD, RD><<<dim3((SPG2 + 3) / 4, groups), 256, 0, s>>>(
+      bk, gdesc, d.E, reinterpret_cast<const uint16_t*>(w.h), w.y);
 }
 
 template <int H, int I, int B>

@@ -43,7 +43,6 @@
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -79,10 +78,8 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 
 // 8 E4M3 bytes (two dwords) to 8 fp16 (exact: E4M3 values are fp16 values).
 __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
-  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 1.0f, false);
-  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 1.0f, true);
-  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 1.0f, false);
-  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 1.0f, true);
+  const f16x2_t a = e4m3x2_to_f16x2<false>(lo), b = e4m3x2_to_f16x2<true>(lo);
+  const f16x2_t c = e4m3x2_to_f16x2<false>(hi), d = e4m3x2_to_f16x2<true>(hi);
   f16x8_t r;
   r[0] = a[0];
   r[1] = a[1];
@@ -101,12 +98,6 @@ __device__ __forceinline__ f16x8_t lds_f16x8(const uint16_t* p) {
 
 __device__ __forceinline__ f32x4_t mfma16_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// fp32 -> fp16 bits, round to nearest even, saturated to the finite range.
-__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
-  v = fminf(fmaxf(v, -65504.f), 65504.f);
-  return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
 __device__ __forceinline__ bf16x8_t lds_bf16x8(const uint16_t* p) {

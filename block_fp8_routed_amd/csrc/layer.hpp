@@ -48,7 +48,7 @@ struct Work {
   int32_t* pair;     // [P] row -> slot
   int32_t* inv;      // [P] slot -> row
   int32_t* tiles;    // [max_tiles][2] (group, first row) of each MFMA row tile
-  void* h;           // [P][I] fp32 (GEMV family) or bf16 (MFMA family)
+  void* h;           // [P][I] fp16 SwiGLU output
   float* y;          // [P][H] fp32
 };
 

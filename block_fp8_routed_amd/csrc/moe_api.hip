@@ -28,7 +28,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[7] = (size_t)d.P * 4;                // pair
   sz[8] = (size_t)d.P * 4;                // inv
   sz[9] = (size_t)max_mfma_tiles(d) * 8;  // tiles
-  sz[10] = (size_t)d.P * d.I * 4;         // h (fp32 bound; MFMA family uses half)
+  sz[10] = (size_t)d.P * d.I * 2;         // h (fp16)
   sz[11] = (size_t)d.P * d.H * 4;         // y
 }
 

@@ -1,6 +1,6 @@
 // permute.hip — the token -> expert permutation kernels (permute_body), and
 // the fused decode kernel that selects every token's experts and permutes in
-// one workgroup.
+// one workgroup (permute_wave).
 #include "layer.hpp"
 #include "permute.hpp"
 #include "select.hpp"
@@ -18,8 +18,8 @@ __global__ __launch_bounds__(64 * W) void permute_kernel(
 }
 
 // Decode sizes (T <= 16, E <= 512): wavefront t selects token t's experts
-// (select_token), the selection goes to LDS, and all 16 wavefronts then run
-// the permutation on it. Same arithmetic as topk_softmax + permute_kernel.
+// (select_token) into LDS; after one barrier, wavefront 0 alone builds the
+// permutation (permute_wave). Same results as topk_softmax + permute_kernel.
 template <int NV>
 __global__ __launch_bounds__(1024) void select_permute_small(
     const float* __restrict__ plog, int slices, const float* __restrict__ bias, int64_t T, int k,
@@ -27,28 +27,29 @@ __global__ __launch_bounds__(1024) void select_permute_small(
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
     int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
     int32_t* __restrict__ tiles, int tile_rows) {
-  extern __shared__ int32_t lds[];
-  int32_t* stk = lds + 16 * E + E + 64;  // [T][k]
+  __shared__ int32_t stk[kGemvMaxTokens * kMaxTopK];
+  __shared__ int32_t cnt[64 * kWaveExpertsPerLane];
   const int64_t t = threadIdx.x >> 6;
   if (t < T) select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, nullptr, stk);
   __syncthreads();
-  permute_body<16>(stk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, lds);
+  if (t != 0) return;
+  permute_wave(stk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, cnt);
 }
 
 bool small_select_permute(const Dims& d) {
-  return d.T <= kGemvMaxTokens && d.E <= 512;
+  return d.T <= kGemvMaxTokens && d.E <= 64 * kWaveExpertsPerLane;
 }
 
 hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
                                        const Work& w, int tile_rows, hipStream_t s) {
   const int ns = router_slices(d) > 0 ? router_slices(d) : 1;
-  const size_t lds = (size_t)(16 * d.E + d.E + 64 + d.T * d.k) * sizeof(int32_t);
   const int nv = (d.E + 63) / 64;
-#define MOE_SP(NV)                                                                            \
-  select_permute_small<NV><<<1, 1024, lds, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk,  \
-                                                w.gates, w.offsets, w.pair, w.inv, w.rtok,   \
-                                                w.meta, reinterpret_cast<int4*>(w.gdesc),     \
-                                                w.tiles, tile_rows)
+  const int threads = 64 * (int)d.T;
+#define MOE_SP(NV)                                                                             \
+  select_permute_small<NV><<<1, threads, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk,  \
+                                                 w.gates, w.offsets, w.pair, w.inv, w.rtok,   \
+                                                 w.meta, reinterpret_cast<int4*>(w.gdesc),     \
+                                                 w.tiles, tile_rows)
   if (nv <= 1)
     MOE_SP(1);
   else if (nv <= 2)

@@ -5,9 +5,9 @@
 // are streamed). Its cost is reading Wr at decode sizes and E*T*H FMAs at
 // prefill sizes, so there are two kernels:
 //  * router_slices (T <= 16): H is cut into slices of 512 columns; a
-//    workgroup stages its slice of x in LDS and four wavefronts each stream
-//    four expert rows of the slice with coalesced 16-byte loads. Partial sums
-//    per slice are written out; the top-k kernel adds them in slice order.
+//    wavefront dots four expert rows of a slice with four tokens using
+//    coalesced 16-byte loads. Partial sums per slice are written out; the
+//    top-k kernel adds them in slice order.
 //  * router_gemm (T > 16): 64x64 LDS-tiled fp32 GEMM, one slice.
 // Both accumulate in fp32 in two levels (short partial sums added into a
 // running total), which keeps the rounding error of a 4096-term logit near
@@ -18,17 +18,21 @@
 
 namespace moe {
 
+// Decode sizes: workgroup (expert quad q, slice s) has one wavefront per
+// group of 4 tokens; each wavefront dots 4 expert rows with its 4 tokens over
+// the slice's columns (lane L takes columns 4L + 256j) and reduces the 16
+// partial sums across the wave. Token rows are read straight from global
+// memory; the expert rows are shared by the workgroup's wavefronts through the
+// cache.
 template <int NT, bool XBF16>
 __global__ __launch_bounds__(256) void router_slices_kernel(const void* __restrict__ x,
                                                            const float* __restrict__ wr,
                                                            float* __restrict__ plog, int T,
                                                            int H, int E, int HS) {
-  __shared__ float xs[NT * kRouterSlice];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t0 = (threadIdx.x >> 6) * NT;
   const int h0 = blockIdx.y * HS;
-  const int e0 = blockIdx.x * 16 + wave * 4;
-
-  // expert rows first: the loads are in flight while x is staged
+  const int e0 = blockIdx.x * 4;
   constexpr int J = kRouterSlice / 256;
   float4 w[4][J];
 #pragma unroll
@@ -40,66 +44,40 @@ __global__ __launch_bounds__(256) void router_slices_kernel(const void* __restri
                     ? *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * H + h0 + c)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  // stage the T x HS slice of x: all loads first (compile-time trip count)
-  constexpr int IT = (NT * kRouterSlice + 1023) / 1024;
-  float4 xv[IT];
+  float4 xv[NT][J];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int i = 4 * tid + 1024 * it;
-    const int t = i / HS, c = i - t * HS;
-    xv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < T * HS) {
-      if (XBF16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) +
-                                                        (size_t)t * H + h0 + c);
-        xv[it] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
-      } else {
-        xv[it] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) +
-                                                  (size_t)t * H + h0 + c);
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = 4 * lane + 256 * j;
+      xv[t][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t0 + t < T && c < HS) {
+        if (XBF16) {
+          const uint2 u = *reinterpret_cast<const uint2*>(
+              reinterpret_cast<const uint16_t*>(x) + (size_t)(t0 + t) * H + h0 + c);
+          xv[t][j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+        } else {
+          xv[t][j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) +
+                                                      (size_t)(t0 + t) * H + h0 + c);
+        }
       }
     }
-  }
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int i = 4 * tid + 1024 * it;
-    if (i < T * HS) *reinterpret_cast<float4*>(&xs[i]) = xv[it];
-  }
-  __syncthreads();
-  if (e0 >= E) return;
-
-  float acc[4][NT];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int c = 4 * lane + 256 * j;
-    const bool cin = c < HS;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      // token rows past T (NT rounds T up) contribute zero
-      const float4 xv = (cin && t < T) ? *reinterpret_cast<const float4*>(&xs[t * HS + c])
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float a = acc[r][t];
-        a = fmaf(w[r][j].x, xv.x, a);
-        a = fmaf(w[r][j].y, xv.y, a);
-        a = fmaf(w[r][j].z, xv.z, a);
-        a = fmaf(w[r][j].w, xv.w, a);
-        acc[r][t] = a;
-      }
-    }
-  }
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const float v = group_sum<64>(acc[r][t]);
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        a = fmaf(w[r][j].x, xv[t][j].x, a);
+        a = fmaf(w[r][j].y, xv[t][j].y, a);
+        a = fmaf(w[r][j].z, xv[t][j].z, a);
+        a = fmaf(w[r][j].w, xv[t][j].w, a);
+      }
+      const float v = group_sum<64>(a);
       const int q = r * NT + t;
-      if (t < T && e0 + r < E && lane == (q & 63))
-        plog[((size_t)blockIdx.y * T + t) * E + e0 + r] = v;
+      if (t0 + t < T && e0 + r < E && lane == (q & 63))
+        plog[((size_t)blockIdx.y * T + t0 + t) * E + e0 + r] = v;
     }
 }
 
@@ -194,26 +172,24 @@ static void slices_launch(const Dims& d, const void* x, const float* wr, float* 
                           hipStream_t s) {
   const int ns = router_slices(d);
   const int HS = d.H < kRouterSlice ? d.H : kRouterSlice;
-  const dim3 grid((d.E + 15) / 16, ns);
+  const dim3 grid((d.E + 3) / 4, ns);
+  const int threads = 64 * (int)((d.T + NT - 1) / NT);
   if (d.x_bf16)
-    router_slices_kernel<NT, true><<<grid, 256, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
+    router_slices_kernel<NT, true><<<grid, threads, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
   else
-    router_slices_kernel<NT, false><<<grid, 256, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
+    router_slices_kernel<NT, false><<<grid, threads, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
 }
 
 hipError_t launch_router(const Dims& d, const void* x, const float* wr, float* plog,
                          hipStream_t s) {
   if (router_slices(d) > 0) {
+    // tokens per wavefront (T <= 16 here: at most 4 wavefronts per workgroup)
     if (d.T <= 1)
       slices_launch<1>(d, x, wr, plog, s);
     else if (d.T <= 2)
       slices_launch<2>(d, x, wr, plog, s);
-    else if (d.T <= 4)
-      slices_launch<4>(d, x, wr, plog, s);
-    else if (d.T <= 8)
-      slices_launch<8>(d, x, wr, plog, s);
     else
-      slices_launch<16>(d, x, wr, plog, s);
+      slices_launch<4>(d, x, wr, plog, s);
   } else {
     const dim3 grid((unsigned)((d.T + 63) / 64), (d.E + 63) / 64);
     if (d.x_bf16)

@@ -209,3 +209,30 @@ def test_prefill_e512_full_size_sampled():
     log(f"c4: oracle on {len(sample)} sampled tokens ({n_hot} touch a hot expert), ties={ties}")
     ref = layer.oracle(routing=accepted, tokens=np.array(sample))
     check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 sampled")
+
+
+WS_CASES = [("c1", 16, "auto"), ("c1", 4, "auto"), ("c0", 4, "auto"), ("c1", 16, "mfma"),
+            ("c2", 512, "auto"), ("c3", 8, "auto")]
+
+
+@pytest.mark.parametrize("name,T,path", WS_CASES, ids=[f"{n}-T{t}-{p}" for n, t, p in WS_CASES])
+def test_forward_does_not_depend_on_workspace_contents(name, T, path):
+    """Every workspace byte the layer reads is written by the same call first,
+    and nothing is written past the workspace: results are bit-identical for a
+    zeroed and a garbage-filled workspace, and a canary band after the
+    workspace is untouched."""
+    import block_fp8_routed_amd as moe
+    layer = DevLayer(C[name], tokens=T)
+    s = layer.shape
+    cfg = moe.make_config(T, s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
+                          layer.x.dtype, torch.float32, path)
+    n = moe.workspace_bytes(cfg)
+    guard = 1 << 20
+    outs = []
+    for fill in (0x00, 0xA5):
+        buf = torch.full((n + guard,), fill, dtype=torch.uint8, device="cuda")
+        ws = buf[:n]
+        outs.append(layer.forward(path=path, workspace=ws).clone())
+        torch.cuda.synchronize()
+        assert bool((buf[n:] == fill).all()), "write past the end of the workspace"
+    assert torch.equal(outs[0], outs[1])
