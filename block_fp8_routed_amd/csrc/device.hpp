@@ -102,6 +102,26 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sum over aligned segments of W lanes (W = 1, 2, 4, 8, 16, 32 or 64). The
+// segment's last lane always holds the sum (for W <= 16 every lane of the
+// segment does; W = 32 adds the even 16-lane row into the odd one with
+// row_bcast:15; W = 64 is group_sum<64>). One call reduces every segment of
+// the wavefront at once. Fixed order of additions.
+constexpr int kDppRowBcast15 = 0x142;
+template <int W>
+__device__ __forceinline__ float seg_sum(float v) {
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "width");
+  if (W == 64) return group_sum<64>(v);
+  if (W >= 2) v += dpp_f<kDppXor1>(v);
+  if (W >= 4) v += dpp_f<kDppXor2>(v);
+  if (W >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (W >= 16) v += dpp_f<kDppMirror>(v);
+  if (W == 32)  // rows 1 and 3 receive lane 15 of rows 0 and 2; rows 0 and 2 keep v
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               kDppRowBcast15, 0xA, 0xF, false));
+  return v;
+}
+
 // Larger value wins; equal values go to the lower index.
 __device__ __forceinline__ void take_max(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) {
