@@ -158,24 +158,13 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Lanes of a 64-wide wave laid over rows of K bytes, 16 bytes per lane per
-// load. K >= 1024: the whole wave covers 1024 bytes of one row per load and a
-// lane takes CH = K/1024 chunks. K < 1024: LPR = K/16 lanes share a row and a
-// load covers RPL rows (RPL = 64/LPR when that divides, else 1 with idle
-// lanes). RED is the width of the lane groups whose partial sums are added.
-template <int K>
-struct RowMap {
-  static_assert(K % 16 == 0, "row length must be a multiple of 16 bytes");
-  static_assert(K < 1024 || K % 1024 == 0, "rows of 1024+ bytes must be whole KiB");
-  static constexpr int LPR = K >= 1024 ? 64 : K / 16;
-  static constexpr int RPL = K >= 1024 ? 1 : (64 % LPR == 0 ? 64 / LPR : 1);
-  static constexpr int CH = K >= 1024 ? K / 1024 : 1;
-  static constexpr int RED = (K >= 1024 || 64 % LPR != 0) ? 64 : LPR;
-  __device__ static bool active(int lane) { return lane < LPR * RPL; }
-  __device__ static int row(int lane) { return RPL == 1 ? 0 : lane / LPR; }
-  __device__ static int col(int lane, int c) {
-    return K >= 1024 ? 16 * lane + 1024 * c : 16 * (lane % LPR);
-  }
-};
+// Workgroup barrier that orders LDS accesses only: global loads still in
+// flight (streamed weights) stay in flight across it, where __syncthreads()
+// would first wait for every outstanding load of the wavefront.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace moe

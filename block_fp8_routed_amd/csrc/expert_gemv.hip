@@ -77,17 +77,44 @@ __device__ __forceinline__ void dec16(const uint4 w, float* d) {
   e4m3x4_to_f32(w.w, d + 12);
 }
 
-// Stage the activations of tokens tok[0..nv) (rows of L elements of ELEM
-// bytes) into consecutive LDS rows. All 256 threads take part.
-template <int L, int ELEM>
-__device__ __forceinline__ void stage_rows(void* lds, const void* src, const int* tok, int nv) {
-  constexpr int CPR = L * ELEM / 16;  // 16-byte chunks per row
-  for (int i = threadIdx.x; i < nv * CPR; i += 256) {
-    const int t = i / CPR, c = i - t * CPR;
-    const uint4 v = ld16(reinterpret_cast<const uint8_t*>(src) + ((size_t)tok[t] * CPR + c) * 16);
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(lds) + ((size_t)t * CPR + c) * 16) = v;
+// One pass's activation rows (gate/up: x rows of the pass's tokens; down: the
+// group's h rows), moved global -> registers -> LDS in two steps so that the
+// kernels can place their loads against the weight stream. Thread i takes the
+// 16-byte chunks i, i + 256, ... of the pass's NT rows of L elements of ELEM
+// bytes; row_of(t) gives the source row of pass token t. A pass with fewer
+// than NT tokens repeats its last row in the unused entries, and chunks past
+// the NT rows (when 256 does not divide their count) repeat the last chunk
+// into a pad of the LDS buffer, so no load or store is conditional (a
+// conditional one would make the compiler wait for every load in flight).
+// When a row spans whole multiples of 256 chunks, t is the same for every
+// thread of a step (UNIFORM) and known at compile time after unrolling.
+// LDS row t starts at byte t * L * ELEM; the buffer takes BYTES.
+template <int L, int ELEM, int NT>
+struct RowStage {
+  static constexpr int CPR = L * ELEM / 16;  // chunks per row
+  static constexpr int N = (NT * CPR + 255) / 256;
+  static constexpr int BYTES = N * 256 * 16;
+  static constexpr bool UNIFORM = CPR % 256 == 0;
+  static_assert((L * ELEM) % 16 == 0, "rows must be whole 16-byte chunks");
+  uint4 v[N];
+  template <class RowOf>
+  __device__ __forceinline__ void load(const void* src, RowOf row_of) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      int i = threadIdx.x + 256 * j;
+      if (i >= NT * CPR) i = NT * CPR - 1;
+      const int t = UNIFORM ? (256 * j) / CPR : i / CPR;
+      const int c = i - t * CPR;
+      v[j] = ld16(reinterpret_cast<const uint8_t*>(src) + ((size_t)row_of(t) * CPR + c) * 16);
+    }
   }
-}
+  __device__ __forceinline__ void store(void* lds) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(lds) +
+                                (size_t)(threadIdx.x + 256 * j) * 16) = v[j];
+  }
+};
 
 // ------------------------------------------------------------- gate/up ---
 // grid: (slabs of PPW row pairs, 4 per workgroup; group slots). Slots past
@@ -101,11 +128,11 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
   constexpr int LPP = G::LPP, PPW = G::PPW, SPG = I / PPW;
   static_assert(I % PPW == 0, "row pairs must split evenly into slabs");
   constexpr int XB = XBF16 ? 2 : 4;  // bytes per activation
-  __shared__ __attribute__((aligned(16))) uint8_t xs[NT * H * XB];
-  __shared__ int toks[NT];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[RowStage<H, XBF16 ? 2 : 4, NT>::BYTES];
   const int4 gd = gdesc[blockIdx.y];
   const int g = gd.x;
   if (g < 0) return;  // uniform over the workgroup
+  const int r0 = gd.y, n = gd.z;
   const int lane = threadIdx.x & 63;
   const int slab = blockIdx.x * 4 + (threadIdx.x >> 6);
   const bool live = slab < SPG;
@@ -115,92 +142,110 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
   const uint8_t* W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
   const float* Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / B) * (H / B);
 
+  // Issue order: the first pass's token ids (a vector load: lane u < NT
+  // fetches id u), then the weights and scales, then the token rows, which
+  // wait for the ids only (vector loads complete in issue order), so the
+  // weights are in flight meanwhile. (A wavefront past the last slab loads
+  // slab 0 again and computes nothing: no load is conditional.)
+  RowStage<H, XB, NT> st;
+  int nv = n < NT ? n : NT;  // tokens in this pass (uniform)
+  int mytok = rtok[r0 + (lane < nv ? lane : nv - 1)];
+  __builtin_amdgcn_sched_barrier(0);
   uint4 wg[M], wu[M];
   float sg[M], su[M];
-  if (live) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int c = m * LPP + sub;
-      wg[m] = ld16_nt(W + (size_t)i * H + 16 * c);
-      wu[m] = ld16_nt(W + (size_t)(I + i) * H + 16 * c);
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int c = m * LPP + sub;
-      sg[m] = Sc[(i / B) * (H / B) + (16 * c) / B];
-      su[m] = Sc[((I + i) / B) * (H / B) + (16 * c) / B];
-    }
+  for (int m = 0; m < M; ++m) {
+    const int c = m * LPP + sub;
+    wg[m] = ld16_nt(W + (size_t)i * H + 16 * c);
+    wu[m] = ld16_nt(W + (size_t)(I + i) * H + 16 * c);
   }
-  const int r0 = gd.y, n = gd.z;
-  for (int t0 = 0; t0 < n; t0 += NT) {
-    const int nv = n - t0 < NT ? n - t0 : NT;  // tokens in this pass (uniform)
-    __syncthreads();  // the previous pass's LDS reads are done
-    if (threadIdx.x < nv) toks[threadIdx.x] = rtok[r0 + t0 + threadIdx.x];
-    __syncthreads();
-    stage_rows<H, XB>(xs, x, toks, nv);
-    __syncthreads();
-    if (!live) continue;
-    float ag[NT], au[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
+  for (int m = 0; m < M; ++m) {
+    const int c = m * LPP + sub;
+    sg[m] = Sc[(i / B) * (H / B) + (16 * c) / B];
+    su[m] = Sc[((I + i) / B) * (H / B) + (16 * c) / B];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // lane t of mytok holds the row of token t of the pass
+  const auto token_row = [&](int t) {
+    return decltype(st)::UNIFORM ? __builtin_amdgcn_readlane(mytok, t) : __shfl(mytok, t, 64);
+  };
+  st.load(x, token_row);
+  __builtin_amdgcn_sched_barrier(0);
+  st.store(xs);
+  lds_barrier();
+  for (int t0 = 0;;) {
+    if (live) {
+      float ag[NT], au[NT];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int c = m * LPP + sub;
-      if (XBF16) {
-        const uint32_t gq[4] = {wg[m].x, wg[m].y, wg[m].z, wg[m].w};
-        const uint32_t uq[4] = {wu[m].x, wu[m].y, wu[m].z, wu[m].w};
-        bf16x2_t gb[8], ub[8];
+      for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          gb[2 * q] = e4m3x2_to_bf16x2<false>(gq[q]);
-          gb[2 * q + 1] = e4m3x2_to_bf16x2<true>(gq[q]);
-          ub[2 * q] = e4m3x2_to_bf16x2<false>(uq[q]);
-          ub[2 * q + 1] = e4m3x2_to_bf16x2<true>(uq[q]);
-        }
+      for (int m = 0; m < M; ++m) {
+        const int c = m * LPP + sub;
+        if (XBF16) {
+          const uint32_t gq[4] = {wg[m].x, wg[m].y, wg[m].z, wg[m].w};
+          const uint32_t uq[4] = {wu[m].x, wu[m].y, wu[m].z, wu[m].w};
+          bf16x2_t gb[8], ub[8];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t < nv) {
-            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs) + t * H + 16 * c;
-            const uint4 a = *reinterpret_cast<const uint4*>(xr);
-            const uint4 b = *reinterpret_cast<const uint4*>(xr + 8);
-            const uint32_t xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-            float pg = 0.f, pu = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              pg = dot2_bf16(gb[j], xv[j], pg);
-              pu = dot2_bf16(ub[j], xv[j], pu);
-            }
-            ag[t] = fmaf(sg[m], pg, ag[t]);
-            au[t] = fmaf(su[m], pu, au[t]);
+          for (int q = 0; q < 4; ++q) {
+            gb[2 * q] = e4m3x2_to_bf16x2<false>(gq[q]);
+            gb[2 * q + 1] = e4m3x2_to_bf16x2<true>(gq[q]);
+            ub[2 * q] = e4m3x2_to_bf16x2<false>(uq[q]);
+            ub[2 * q + 1] = e4m3x2_to_bf16x2<true>(uq[q]);
           }
-        }
-      } else {
-        float gd16[16], ud16[16];
-        dec16(wg[m], gd16);
-        dec16(wu[m], ud16);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t < nv) {
-            const float* xr = reinterpret_cast<const float*>(xs) + t * H + 16 * c;
-            float pg = 0.f, pu = 0.f;
+          for (int t = 0; t < NT; ++t) {
+            if (t < nv) {
+              const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs) + t * H + 16 * c;
+              const uint4 a = *reinterpret_cast<const uint4*>(xr);
+              const uint4 b = *reinterpret_cast<const uint4*>(xr + 8);
+              const uint32_t xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+              float pg = 0.f, pu = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              pg = fmaf(gd16[j], xr[j], pg);
-              pu = fmaf(ud16[j], xr[j], pu);
+              for (int j = 0; j < 8; ++j) {
+                pg = dot2_bf16(gb[j], xv[j], pg);
+                pu = dot2_bf16(ub[j], xv[j], pu);
+              }
+              ag[t] = fmaf(sg[m], pg, ag[t]);
+              au[t] = fmaf(su[m], pu, au[t]);
             }
-            ag[t] = fmaf(sg[m], pg, ag[t]);
-            au[t] = fmaf(su[m], pu, au[t]);
+          }
+        } else {
+          float gd16[16], ud16[16];
+          dec16(wg[m], gd16);
+          dec16(wu[m], ud16);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (t < nv) {
+              const float* xr = reinterpret_cast<const float*>(xs) + t * H + 16 * c;
+              float pg = 0.f, pu = 0.f;
+#pragma unroll
+              for (int j = 0; j < 16; ++j) {
+                pg = fmaf(gd16[j], xr[j], pg);
+                pu = fmaf(ud16[j], xr[j], pu);
+              }
+              ag[t] = fmaf(sg[m], pg, ag[t]);
+              au[t] = fmaf(su[m], pu, au[t]);
+            }
           }
         }
       }
-    }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t >= nv) continue;
-      const float a = seg_sum<LPP>(ag[t]);
-      const float u = seg_sum<LPP>(au[t]);
-      if (sub == LPP - 1) h[(size_t)(r0 + t0 + t) * I + i] = f32_to_f16_sat(silu(a) * u);
+      for (int t = 0; t < NT; ++t) {
+        if (t >= nv) continue;
+        const float a = seg_sum<LPP>(ag[t]);
+        const float u = seg_sum<LPP>(au[t]);
+        if (sub == LPP - 1) h[(size_t)(r0 + t0 + t) * I + i] = f32_to_f16_sat(silu(a) * u);
+      }
     }
+    t0 += NT;
+    if (t0 >= n) break;
+    nv = n - t0 < NT ? n - t0 : NT;
+    mytok = rtok[r0 + t0 + (lane < nv ? lane : nv - 1)];
+    st.load(x, token_row);
+    lds_barrier();  // every wavefront is done with the previous pass
+    st.store(xs);
+    lds_barrier();
   }
 }
 
@@ -212,10 +257,11 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
   using D = DownMap<I>;
   constexpr int LPR = D::LPR, MD = D::MD, RW = D::RW, SPG = H / RW;
   static_assert(H % RW == 0, "rows must split evenly into slabs");
-  __shared__ __attribute__((aligned(16))) uint16_t hs[NT * I];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[RowStage<I, 2, NT>::BYTES / 2];
   const int4 gd = gdesc[blockIdx.y];
   const int g = gd.x;
   if (g < 0) return;  // uniform over the workgroup
+  const int r0 = gd.y, n = gd.z;
   const int lane = threadIdx.x & 63;
   const int slab = blockIdx.x * 4 + (threadIdx.x >> 6);
   const bool live = slab < SPG;
@@ -225,55 +271,66 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
   const uint8_t* W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
   const float* Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / B) * (I / B);
 
+  // the group's h rows are contiguous (rows r0 .. r0 + n - 1); the first
+  // pass's rows are requested before the weights and scales, so storing them
+  // to LDS does not wait for the weights. No load is conditional, as in
+  // gemv_gate_up.
+  RowStage<I, 2, NT> st;
+  int nv = n < NT ? n : NT;  // tokens in this pass (uniform)
+  const auto seq_row = [&](int t) { return t < nv ? t : nv - 1; };
+  st.load(h + (size_t)r0 * I, seq_row);
+  __builtin_amdgcn_sched_barrier(0);
   uint4 w[MD];
   float sd[MD];
-  if (live) {
 #pragma unroll
-    for (int m = 0; m < MD; ++m) w[m] = ld16_nt(W + (size_t)row * I + 16 * (m * LPR + sub));
+  for (int m = 0; m < MD; ++m) w[m] = ld16_nt(W + (size_t)row * I + 16 * (m * LPR + sub));
 #pragma unroll
-    for (int m = 0; m < MD; ++m) sd[m] = Sc[(row / B) * (I / B) + (16 * (m * LPR + sub)) / B];
-  }
-  const int r0 = gd.y, n = gd.z;
-  for (int t0 = 0; t0 < n; t0 += NT) {
-    const int nv = n - t0 < NT ? n - t0 : NT;  // tokens in this pass (uniform)
-    __syncthreads();
-    // the group's h rows are contiguous: rows r0 + t0 .. r0 + t0 + nv - 1
-    for (int q = threadIdx.x; q < nv * I / 8; q += 256)
-      *reinterpret_cast<uint4*>(hs + 8 * q) = ld16(h + (size_t)(r0 + t0) * I + 8 * q);
-    __syncthreads();
-    if (!live) continue;
-    float acc[NT];
+  for (int m = 0; m < MD; ++m) sd[m] = Sc[(row / B) * (I / B) + (16 * (m * LPR + sub)) / B];
+  __builtin_amdgcn_sched_barrier(0);
+  st.store(hs);
+  lds_barrier();
+  for (int t0 = 0;;) {
+    if (live) {
+      float acc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+      for (int t = 0; t < NT; ++t) acc[t] = 0.f;
 #pragma unroll
-    for (int m = 0; m < MD; ++m) {
-      const int c = m * LPR + sub;
-      const uint32_t wq[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
-      f16x2_t wf[8];
+      for (int m = 0; m < MD; ++m) {
+        const int c = m * LPR + sub;
+        const uint32_t wq[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
+        f16x2_t wf[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        wf[2 * q] = e4m3x2_to_f16x2<false>(wq[q]);
-        wf[2 * q + 1] = e4m3x2_to_f16x2<true>(wq[q]);
+        for (int q = 0; q < 4; ++q) {
+          wf[2 * q] = e4m3x2_to_f16x2<false>(wq[q]);
+          wf[2 * q + 1] = e4m3x2_to_f16x2<true>(wq[q]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t < nv) {
+            const uint4 a = *reinterpret_cast<const uint4*>(hs + t * I + 16 * c);
+            const uint4 b = *reinterpret_cast<const uint4*>(hs + t * I + 16 * c + 8);
+            const uint32_t hv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            float p = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p = dot2_f16(wf[j], hv[j], p);
+            acc[t] = fmaf(sd[m], p, acc[t]);
+          }
+        }
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (t < nv) {
-          const uint4 a = *reinterpret_cast<const uint4*>(hs + t * I + 16 * c);
-          const uint4 b = *reinterpret_cast<const uint4*>(hs + t * I + 16 * c + 8);
-          const uint32_t hv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          float p = 0.f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) p = dot2_f16(wf[j], hv[j], p);
-          acc[t] = fmaf(sd[m], p, acc[t]);
-        }
+        if (t >= nv) continue;
+        const float v = seg_sum<LPR>(acc[t]);
+        if (sub == LPR - 1) y[(size_t)(r0 + t0 + t) * H + row] = v;
       }
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t >= nv) continue;
-      const float v = seg_sum<LPR>(acc[t]);
-      if (sub == LPR - 1) y[(size_t)(r0 + t0 + t) * H + row] = v;
-    }
+    t0 += NT;
+    if (t0 >= n) break;
+    nv = n - t0 < NT ? n - t0 : NT;
+    st.load(h + (size_t)(r0 + t0) * I, seq_row);
+    lds_barrier();  // every wavefront is done with the previous pass
+    st.store(hs);
+    lds_barrier();
   }
 }
 

@@ -34,15 +34,17 @@ __global__ __launch_bounds__(256) void router_slices_kernel(const void* __restri
   const int h0 = blockIdx.y * HS;
   const int e0 = blockIdx.x * 4;
   constexpr int J = kRouterSlice / 256;
+  // Loads are unconditional, with row and column indices clamped into range
+  // (out-of-range terms are zeroed afterwards), so that all of them are in
+  // flight together.
   float4 w[4][J];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = 4 * lane + 256 * j;
-      w[r][j] = (e0 + r < E && c < HS)
-                    ? *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * H + h0 + c)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int e = e0 + r < E ? e0 + r : E - 1;
+      w[r][j] = *reinterpret_cast<const float4*>(wr + (size_t)e * H + h0 + (c < HS ? c : HS - 4));
     }
   float4 xv[NT][J];
 #pragma unroll
@@ -50,18 +52,22 @@ __global__ __launch_bounds__(256) void router_slices_kernel(const void* __restri
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = 4 * lane + 256 * j;
-      xv[t][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t0 + t < T && c < HS) {
-        if (XBF16) {
-          const uint2 u = *reinterpret_cast<const uint2*>(
-              reinterpret_cast<const uint16_t*>(x) + (size_t)(t0 + t) * H + h0 + c);
-          xv[t][j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
-        } else {
-          xv[t][j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) +
-                                                      (size_t)(t0 + t) * H + h0 + c);
-        }
+      const size_t off = (size_t)(t0 + t < T ? t0 + t : T - 1) * H + h0 + (c < HS ? c : HS - 4);
+      if (XBF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + off);
+        xv[t][j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+      } else {
+        xv[t][j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
       }
     }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (4 * lane + 256 * j < HS) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xv[t][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll

@@ -26,28 +26,44 @@ __device__ __forceinline__ void select_token(const float* __restrict__ plog, int
                                              float* gates_out, float* logits_out,
                                              int32_t* topk_lds) {
   const int lane = threadIdx.x & 63;
+  // Every partial logit (up to kMaxUnrolled slices) and bias term of the
+  // lane's experts is requested before any is used: the addresses are
+  // clamped into range instead of branched around, so the loads go out
+  // together and the token pays one memory latency, not one per expert.
+  constexpr int kMaxUnrolled = 8;
+  float part[NV][kMaxUnrolled];
+  float bv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i < E ? lane + 64 * i : E - 1;
+#pragma unroll
+    for (int s = 0; s < kMaxUnrolled; ++s) {
+      const int sc = s < slices ? s : slices - 1;
+      part[i][s] = plog[((size_t)sc * T + t) * E + e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i < E ? lane + 64 * i : E - 1;
+    bv[i] = bias ? bias[e] : 0.f;
+  }
   float v[NV];
   uint32_t avail = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    float val = -INFINITY;
+    float val = part[i][0];  // slices summed in slice order
+#pragma unroll
+    for (int s = 1; s < kMaxUnrolled; ++s)
+      if (s < slices) val += part[i][s];
     if (e < E) {
-      // slices summed in order; the first kMaxUnrolled loads go out together
-      constexpr int kMaxUnrolled = 8;
-      float part[kMaxUnrolled];
-#pragma unroll
-      for (int s = 0; s < kMaxUnrolled; ++s)
-        part[s] = s < slices ? plog[((size_t)s * T + t) * E + e] : 0.f;
-      val = part[0];
-#pragma unroll
-      for (int s = 1; s < kMaxUnrolled; ++s)
-        if (s < slices) val += part[s];
       for (int s = kMaxUnrolled; s < slices; ++s) val += plog[((size_t)s * T + t) * E + e];
-      if (bias) val += bias[e];
+      if (bias) val += bv[i];
       if (logits_out) logits_out[t * E + e] = val;
       if (val != val) val = -INFINITY;  // NaN never outranks a number
       avail |= 1u << i;
+    } else {
+      val = -INFINITY;
     }
     v[i] = val;
   }
