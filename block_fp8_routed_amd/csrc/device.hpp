@@ -122,27 +122,51 @@ __device__ __forceinline__ float seg_sum(float v) {
   return v;
 }
 
-// Larger value wins; equal values go to the lower index.
-__device__ __forceinline__ void take_max(float& v, int& i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
+// Inclusive prefix sum over the 64 lanes of a wavefront, by DPP: row_shr 1,
+// 2, 4, 8 inside each 16-lane row, then row_bcast:15 (rows 1 and 3 add the
+// last lane of the row before) and row_bcast:31 (rows 2 and 3 add lane 31).
+// Lanes whose DPP source is outside the row, and rows outside a row mask, add
+// the zero passed as the instruction's old value.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast31 = 0x143;
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+  return v;
 }
 
-// Wave-wide argmax of (v, i); the result is uniform across the wave.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  take_max(v, i, dpp_f<kDppXor1>(v), dpp_i<kDppXor1>(i));
-  take_max(v, i, dpp_f<kDppXor2>(v), dpp_i<kDppXor2>(i));
-  take_max(v, i, dpp_f<kDppHalfMirror>(v), dpp_i<kDppHalfMirror>(i));
-  take_max(v, i, dpp_f<kDppMirror>(v), dpp_i<kDppMirror>(i));
-  float bv = readlane_f(v, 0);
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16)
-    take_max(bv, bi, readlane_f(v, r), __builtin_amdgcn_readlane(i, r));
-  v = bv;
-  i = bi;
+// Wave-wide maximum of a 64-bit key, uniform on return: DPP exchanges inside
+// 16-lane rows, then the row maxima are folded with row_bcast:15 / :31 into
+// lane 63, which is read back. Rows outside a row mask compare against zero,
+// so keys must be non-negative as unsigned (they are).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, ROWS, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, ROWS, 0xF,
+                                                  false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  uint64_t o;
+  o = dpp_u64<kDppXor1, 0xF>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppXor2, 0xF>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppHalfMirror, 0xF>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppMirror, 0xF>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppRowBcast15, 0xA>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppRowBcast31, 0xC>(k);
+  k = o > k ? o : k;
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

@@ -35,13 +35,16 @@ inline int router_slices(const Dims& d) {
   return d.H % kRouterSlice == 0 ? d.H / kRouterSlice : 0;
 }
 
+constexpr int kMetaSelectCounter = 8;
+
 // Carved workspace. Every region is kAlign-aligned.
 struct Work {
   float* logits;     // [slices][T][E] partial router logits (bias not added)
   int32_t* topk;     // [T][k]
   float* gates;      // [T][k]
   int32_t* offsets;  // [E+2]
-  int32_t* meta;     // [16]: meta[0] = active groups, meta[1] = MFMA tiles
+  int32_t* meta;     // [16]: meta[0] = active groups, meta[1] = MFMA tiles,
+                     // meta[kMetaSelectCounter]: decode select completion count
   int32_t* gdesc;    // [E+2][4] per non-empty group: (group, first row, rows, 0);
                      // group = -1 past the last one (shared group = E)
   int32_t* rtok;     // [P] token of each permuted row
@@ -61,15 +64,18 @@ size_t workspace_bytes(const Dims& d);
 Work carve(const Dims& d, void* base);
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
+// zero_word (may be null): a workspace word the decode kernel (T <= 16) uses
+// as its completion counter; the router zeroes it.
 hipError_t launch_router(const Dims& d, const void* x, const float* wr, float* plogits,
-                         hipStream_t s);
+                         int32_t* zero_word, hipStream_t s);
 // Sums the router slices, adds the bias, selects and gates; optionally writes
 // the final logits.
 hipError_t launch_topk(const Dims& d, const float* plogits, const float* bias, int32_t* topk,
                        float* gates, float* logits_out, hipStream_t s);
 hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
                           hipStream_t s);
-// Decode sizes: top-k + gates + permutation in one workgroup.
+// Decode sizes: top-k + gates + permutation in one kernel, one workgroup per
+// token; the counter must be zero at launch (launch_router zeroes it).
 bool small_select_permute(const Dims& d);
 hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
                                        const Work& w, int tile_rows, hipStream_t s);

@@ -156,9 +156,12 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
   hipEvent_t ev_gate_up =
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr;
   if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
-  if (launch_router(d, x, router_w, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
+  const bool small = small_select_permute(d);
+  if (launch_router(d, x, router_w, w.logits, small ? w.meta + kMetaSelectCounter : nullptr, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
   const int tile_rows = d.mfma ? kMfmaBM : 0;
-  if (small_select_permute(d)) {
+  if (small) {
     // decode sizes: selection and permutation share one launch, so ROUTED
     // marks the end of the router logits here
     if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
@@ -193,7 +196,7 @@ moe_status moe_route(const void* x, const float* router_w, const float* router_b
   if (st != MOE_OK) return st;
   const Work w = carve(d, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_router(d, x, router_w, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, w.logits, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_topk(d, w.logits, router_bias, topk_idx, gates, logits, s) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;

@@ -17,23 +17,34 @@ __global__ __launch_bounds__(64 * W) void permute_kernel(
   permute_body<W>(topk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, lds);
 }
 
-// Decode sizes (T <= 16, E <= 512): wavefront t selects token t's experts
-// (select_token) into LDS; after one barrier, wavefront 0 alone builds the
-// permutation (permute_wave). Same results as topk_softmax + permute_kernel.
+// Decode sizes (T <= 16, E <= 512): workgroup t (one wavefront) selects token
+// t's experts and gates (select_token) and writes them out. Selection is most
+// of the kernel's work, so the tokens run on as many compute units. Each
+// workgroup then publishes its result (release fence, then one atomic
+// increment of *counter at device scope); the workgroup that brings the count
+// to T is the last, and after an acquire fence it reads every token's
+// selection back and builds the permutation alone (permute_wave). No
+// workgroup ever waits for another. *counter must be zero at launch (the
+// router kernel, launched just before on the same stream, zeroes it). Same
+// results as topk_softmax + permute_kernel.
 template <int NV>
-__global__ __launch_bounds__(1024) void select_permute_small(
+__global__ __launch_bounds__(64) void select_permute_small(
     const float* __restrict__ plog, int slices, const float* __restrict__ bias, int64_t T, int k,
-    int E, int S, int32_t* __restrict__ topk, float* __restrict__ gates,
+    int E, int S, int32_t* topk, float* __restrict__ gates, int32_t* counter,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
     int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
     int32_t* __restrict__ tiles, int tile_rows) {
-  __shared__ int32_t stk[kGemvMaxTokens * kMaxTopK];
   __shared__ int32_t cnt[64 * kWaveExpertsPerLane];
-  const int64_t t = threadIdx.x >> 6;
-  if (t < T) select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, nullptr, stk);
-  __syncthreads();
-  if (t != 0) return;
-  permute_wave(stk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, cnt);
+  select_token<NV>(plog, slices, bias, T, blockIdx.x, E, k, topk, gates, nullptr, nullptr);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_wave_barrier();
+  int done = 0;
+  if (threadIdx.x == 0) done = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+  done = __builtin_amdgcn_readfirstlane(done);
+  if (done != T - 1) return;  // uniform: not the last token
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  permute_wave(topk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, cnt);
 }
 
 bool small_select_permute(const Dims& d) {
@@ -44,12 +55,13 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
                                        const Work& w, int tile_rows, hipStream_t s) {
   const int ns = router_slices(d) > 0 ? router_slices(d) : 1;
   const int nv = (d.E + 63) / 64;
-  const int threads = 64 * (int)d.T;
-#define MOE_SP(NV)                                                                             \
-  select_permute_small<NV><<<1, threads, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk,  \
-                                                 w.gates, w.offsets, w.pair, w.inv, w.rtok,   \
-                                                 w.meta, reinterpret_cast<int4*>(w.gdesc),     \
-                                                 w.tiles, tile_rows)
+  const unsigned grid = (unsigned)d.T;
+#define MOE_SP(NV)                                                                          \
+  select_permute_small<NV><<<grid, 64, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk, \
+                                               w.gates, w.meta + kMetaSelectCounter,       \
+                                               w.offsets, w.pair, w.inv, w.rtok, w.meta,   \
+                                               reinterpret_cast<int4*>(w.gdesc), w.tiles,  \
+                                               tile_rows)
   if (nv <= 1)
     MOE_SP(1);
   else if (nv <= 2)

@@ -203,14 +203,8 @@ __device__ __forceinline__ void permute_body(
 
 // Exclusive prefix sum over the 64 lanes of a wavefront; *total gets the sum.
 __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
-  const int lane = threadIdx.x & 63;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += n;
-  }
-  *total = __shfl(inc, 63, 64);
+  const int inc = wave_incl_scan(v);
+  *total = __builtin_amdgcn_readlane(inc, 63);
   return inc - v;
 }
 

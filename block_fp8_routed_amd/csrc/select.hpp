@@ -10,9 +10,9 @@
 //
 // Lane L owns experts L, L+64, ...; it sums the router's partial logits over
 // the H slices in slice order and adds the bias. Each of the k rounds is a
-// local scan plus a wave argmax (DPP inside 16-lane rows, readlane across
-// rows) whose comparison (larger value, then lower index) is order-
-// independent, so the result is deterministic. Must be called by all 64 lanes.
+// lane-local maximum plus a wave maximum (DPP) of 64-bit keys that order by
+// logit, then by lower expert index; the order is total, so the result does
+// not depend on reduction order. Must be called by all 64 lanes.
 #pragma once
 
 #include "device.hpp"
@@ -67,22 +67,40 @@ __device__ __forceinline__ void select_token(const float* __restrict__ plog, int
     }
     v[i] = val;
   }
-  float my_v = 0.f, top = 0.f;
-  int my_i = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  // k rounds of a wave-wide maximum over 64-bit order keys: the high word is
+  // the logit's bits mapped to an unsigned order (negatives reversed, -0
+  // taken as +0 so that equal logits compare equal), the low word the
+  // complemented expert index, so the larger logit wins and equal logits go
+  // to the lower index. Absent experts have key 0, below every logit. The
+  // round's winner is cleared in the lane that holds it.
+  uint64_t key[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if ((avail >> i) & 1u) take_max(bv, bi, v[i], lane + 64 * i);
-    wave_argmax(bv, bi);
-    if (bi < E && (bi & 63) == lane) avail &= ~(1u << (bi >> 6));
-    if (lane == j) {
-      my_v = bv;
-      my_i = bi;
-    }
-    if (j == 0) top = bv;
+  for (int i = 0; i < NV; ++i) {
+    uint32_t b = __float_as_uint(v[i]);
+    if (b == 0x80000000u) b = 0u;
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    key[i] = ((avail >> i) & 1u) ? (((uint64_t)b << 32) | (uint32_t)~(lane + 64 * i)) : 0ull;
   }
+  uint64_t mine = 0;  // lane j < k ends with the j-th winner
+  uint64_t first = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t lm = key[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) lm = key[i] > lm ? key[i] : lm;
+    const uint64_t m = wave_max_u64(lm);
+    if (j == 0) first = m;
+    mine = lane == j ? m : mine;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) key[i] = key[i] == m ? 0ull : key[i];
+  }
+  // back from keys to (logit, expert)
+  const auto key_logit = [](uint64_t kk) {
+    const uint32_t hb = (uint32_t)(kk >> 32);
+    return __uint_as_float((hb & 0x80000000u) ? (hb & 0x7fffffffu) : ~hb);
+  };
+  const float top = key_logit(first);
+  const float my_v = key_logit(mine);
+  const int my_i = (int)~(uint32_t)mine;
   const float ex = lane < k ? expf(my_v - top) : 0.f;
   const float den = group_sum<64>(ex);
   if (lane < k) {
