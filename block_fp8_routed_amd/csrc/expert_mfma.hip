@@ -2,41 +2,31 @@
 // bf16 MFMA GEMMs over block-FP8 weights.
 //
 // With tens to thousands of tokens per expert the passes are dense
-// contractions, so they run on the matrix cores (v_mfma_f32_16x16x32_bf16).
+// contractions, so they run on the matrix cores (v_mfma_f32_32x32x16_bf16 and
+// _f16).
 // Following the colizig page ("Features": dequantisation fused into the dot
-// products), E4M3 weights are converted in registers right after their
-// 16-byte global load; every E4M3 value is a bf16 value, so the conversion
-// (v_cvt_scalef32_pk_bf16_fp8 with a unit scale) is exact and the products
-// are exact in fp32. A block's fp32 scale multiplies the partial sum of its
+// products), E4M3 weight tiles are staged in LDS as bytes and converted in
+// registers as each MFMA operand is read; every E4M3 value is a bf16 (and an
+// fp16) value, so the conversion (v_cvt_scalef32_pk_bf16_fp8 with a unit
+// scale) is exact and the products are exact in fp32. A block's fp32 scale multiplies the partial sum of its
 // 128 columns (one accumulator per scale block, folded into the running
 // total), never single weights.
 //
 // Work list: the permutation emits one (group, first row) entry per tile of
-// kMfmaBM = 64 rows of a group; blockIdx.y indexes it (entries past the count
-// exit at once) and blockIdx.x picks a block of output columns.
+// kMfmaBM = 128 rows of a group; each workgroup takes one (tile, block of
+// output columns) pair (entries past the count exit at once).
 //
-//   gate/up: a workgroup owns 64 gate columns and the 64 matching up columns;
-//            each of its 4 wavefronts owns 16 of each, so SwiGLU is applied to
-//            accumulator registers directly. bf16 MFMA: activations are bf16
-//            and the weights exact in bf16, so nothing is rounded on the way
-//            in. h is written as fp16 [P][I] (11-bit significand; saturated
-//            at +-65504).
-//   down:    fp16 MFMA on h (weights are exact in fp16 as well); a workgroup
-//            owns 128 output columns (32 per wavefront); y is written as fp32
-//            [P][H].
-// h is the one intermediate rounded below fp32. fp16 rather than bf16 keeps
-// its relative error at 2^-11, which leaves the layer's output well inside
-// its tolerance (max error <= 1e-2 x RMS); bf16 would use up most of it.
-// The 64 x 128 activation tile of the current scale block is staged in LDS
-// (rows padded by 16 bytes, so the 16 rows a wavefront reads in one step fall
-// in different banks); each wavefront loads its weight rows directly.
+// gate/up runs bf16 MFMA: activations are bf16 and the weights exact in bf16,
+// so nothing is rounded on the way in; SwiGLU is applied to the accumulator
+// registers and h is written as fp16 [P][I] (11-bit significand, saturated at
+// +-65504). down runs fp16 MFMA on h (the weights are exact in fp16 as well)
+// and writes y as fp32 [P][H]. h is the one intermediate rounded below fp32:
+// fp16 keeps its relative error at 2^-11, which leaves the layer's output well
+// inside its tolerance (max error <= 1e-2 x RMS); bf16 would use up most of it.
 //
-// MFMA operand layout (16x16x32 bf16): lane L supplies row L%16 of A and
-// column L%16 of B, each as 8 consecutive k of the 32 (k = 8*(L/16) .. +7).
-// The contraction is the same for any permutation of k applied to A and B
-// alike, so a lane loads 16 consecutive bytes of a weight row (k = 16*(L/16)
-// .. +15 of a 64-wide span) and uses them for two MFMA steps; its A reads use
-// the same k positions.
+// MFMA operand layout (32x32x16): lane L supplies row L%32 of A and column
+// L%32 of B, each as 8 k of the 16 (k = 8*(L/32) .. +7); lane L of the result
+// holds column L%32, value v being row 8*(v/4) + 4*(L/32) + v%4.
 #include "device.hpp"
 #include "layer.hpp"
 
@@ -44,7 +34,6 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct MfmaBank {
   const uint8_t* wgu;
@@ -58,7 +47,6 @@ struct MfmaBank {
 };
 
 constexpr int kBK = 128;            // K per scale block (the block edge)
-constexpr int kLda = kBK + 8;       // LDS row stride of the A tile, in bf16
 
 // 8 E4M3 bytes (two dwords) to 8 bf16 (exact).
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
@@ -92,207 +80,260 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-__device__ __forceinline__ f16x8_t lds_f16x8(const uint16_t* p) {
-  return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(p));
-}
+// Grouped pass, one template for both projections.
+//
+// Tile: kMfmaBM = 128 rows of one group x 512 weight rows, 512 threads as 2 x
+// 4 wavefronts; wavefront (wm, wn) owns rows [64 wm, 64 wm + 64) and 128
+// weight rows, as 2 x 4 MFMA tiles of 32 x 32 (v_mfma_f32_32x32x16_*, which
+// keeps the matrix pipe busy with four accumulators per wavefront).
+//   gate/up (GU): the 512 weight rows are gate rows n0 .. n0 + 255 then the
+//     matching up rows; wavefront wn takes gate rows 64 wn .. 64 wn + 63 of
+//     those and the matching up rows, so SwiGLU pairs accumulator tiles of the
+//     same wavefront. A = bf16 activation rows gathered by token; bf16 MFMA.
+//   down: weight rows n0 .. n0 + 511 are output columns; wavefront wn takes
+//     128 of them. A = fp16 h rows (a group's rows are contiguous); fp16 MFMA.
+// K runs in stages of 64 (half a scale block). A stage's A (128 x 64) and B
+// (512 x 64 bytes) tiles are fetched global -> registers one stage ahead and
+// written into the other of two LDS buffers after the current stage's MFMAs,
+// so global latency overlaps the matrix work; one barrier per stage. In LDS
+// the 16-byte chunks of a row are XOR-swizzled with the row index (A: chunk c
+// of row r at slot c ^ ((r >> 1) & 7); B: c ^ ((r >> 2) & 3)), which makes the
+// 32-row fragment reads and the tile writes free of bank conflicts.
+//
+// K order inside a stage: the contraction does not depend on the order of k,
+// as long as A and B use the same one. Lane group q = lane / 32 reads 16 B
+// bytes (16 k) of chunk 2p + q for step pair p and uses its halves in steps
+// 2p and 2p + 1; the A fragment of step 2p + h for group q is then 8 k at
+// chunk 4p + 2q + h (8 bf16 per A chunk).
+//
+// Block scales: one accumulator per output, kept in units of the current
+// block's scale. Entering scale block kb, the accumulators of a 32-column
+// tile are multiplied by s(kb-1) / s(kb) before its products are added, and
+// by the last scale at the end; the result equals sum_kb s(kb) * P(kb) up to
+// fp32 rounding (one extra rounding per block). A block with scale 0 adds
+// nothing and is skipped.
+// Rows of a tile past the group's end repeat its last row (no load is
+// conditional); 32-row MFMA tiles wholly past the end are skipped, and rows
+// past the end are never stored.
+constexpr int kTN = 512;            // weight rows per tile
+constexpr int kXcds = 8;            // accelerator complex dies (one L2 each)
+constexpr int kPassThreads = 512;
+constexpr int kKS = 64;             // k per pipeline stage
+constexpr int kAStage = kMfmaBM * kKS * 2;  // bytes: 128 rows x 64 bf16/fp16
+constexpr int kBStage = kTN * kKS;          // bytes: 512 rows x 64 E4M3
+static_assert(kMfmaBM == 128, "tile geometry assumes 128-row tiles");
 
-__device__ __forceinline__ f32x4_t mfma16_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
+template <bool GU, int H, int I>
+struct PassShape {
+  static constexpr int K = GU ? H : I;         // contraction length
+  static constexpr int COLS = GU ? 256 : 512;  // output columns per tile
+  static constexpr int NOUT = GU ? I : H;      // output row length
+};
 
-__device__ __forceinline__ bf16x8_t lds_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
-}
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Stage rows [0, 64) x k-columns [k0, k0 + 128) of the tile's activations into
-// LDS; rows at or past `valid` are zero. src(row) gives the row's base.
-template <typename RowPtr>
-__device__ __forceinline__ void stage_a(uint16_t* As, RowPtr src, int valid, int k0) {
-  const int tid = threadIdx.x;
-  uint4 v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + 256 * j;        // 16-byte chunk: 64 rows x 16 chunks
-    const int row = c >> 4, c16 = c & 15;
-    v[j] = row < valid ? ld16(src(row) + k0 + 8 * c16) : make_uint4(0, 0, 0, 0);
+// 8 E4M3 bytes to the MFMA operand type (bf16 for GU, fp16 for down) and the
+// 32x32x16 MFMA of that type
+template <bool GU>
+struct Op;
+template <>
+struct Op<true> {
+  typedef bf16x8_t T;
+  static __device__ __forceinline__ T cvt(uint32_t lo, uint32_t hi) { return e4m3x8_to_bf16x8(lo, hi); }
+  static __device__ __forceinline__ f32x16_t mma(uint4 a, T b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), b, c, 0, 0, 0);
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + 256 * j;
-    const int row = c >> 4, c16 = c & 15;
-    *reinterpret_cast<uint4*>(As + row * kLda + 8 * c16) = v[j];
+};
+template <>
+struct Op<false> {
+  typedef f16x8_t T;
+  static __device__ __forceinline__ T cvt(uint32_t lo, uint32_t hi) { return e4m3x8_to_f16x8(lo, hi); }
+  static __device__ __forceinline__ f32x16_t mma(uint4 a, T b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), b, c, 0, 0, 0);
   }
-}
+};
 
-template <int H, int I, int B>
-__global__ __launch_bounds__(256) void mfma_gate_up(const uint16_t* __restrict__ x, MfmaBank bk,
-                                                   const int32_t* __restrict__ meta,
-                                                   const int32_t* __restrict__ tiles,
-                                                   const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ rtok, int E,
-                                                   uint16_t* __restrict__ h) {
-  static_assert(B == kBK && H % kBK == 0 && I % 64 == 0, "MFMA tiling");
-  __shared__ uint16_t As[kMfmaBM * kLda];
-  __shared__ int toks[kMfmaBM];
-  const int tile = blockIdx.y;
+template <bool GU, int H, int I>
+__global__ __launch_bounds__(kPassThreads) void mfma_pass(const uint16_t* __restrict__ act,
+                                                        MfmaBank bk,
+                                                        const int32_t* __restrict__ meta,
+                                                        const int32_t* __restrict__ tiles,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ rtok, int E,
+                                                        void* __restrict__ out) {
+  using P = PassShape<GU, H, I>;
+  using O = Op<GU>;
+  constexpr int K = P::K, NS = K / kKS;
+  static_assert(K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kAStage + kBStage)];
+  __shared__ int arow[kMfmaBM];
+  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
+  // (each with its own L2), so workgroup L runs on XCD L % 8. XCD x takes row
+  // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
+  // tile's activation rows are fetched into one L2 and reused from it.
+  constexpr int NCB = P::NOUT / P::COLS;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int tile = (j / NCB) * kXcds + xcd;
   if (tile >= meta[1]) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 64 + wave * 16;  // this wavefront's 16 gate columns
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int n0 = (j % NCB) * P::COLS;
   const bool sh = g == E;
-  const uint8_t* W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
-  const float* Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / B) * (H / B);
-  if (threadIdx.x < kMfmaBM) toks[threadIdx.x] = threadIdx.x < valid ? rtok[r0 + threadIdx.x] : 0;
+  const uint8_t* W;
+  const float* Sc;
+  if (GU) {
+    W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
+    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
+  } else {
+    W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
+    Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / kBK) * (I / kBK);
+  }
+  // source row of each tile row
+  if (tid < kMfmaBM) {
+    const int rr = tid < valid ? tid : valid - 1;
+    arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
+  }
   __syncthreads();
 
-  const uint8_t* wg_row = W + (size_t)(n0 + (lane & 15)) * H + 16 * (lane >> 4);
-  const uint8_t* wu_row = W + (size_t)(I + n0 + (lane & 15)) * H + 16 * (lane >> 4);
-  const float* sg_row = Sc + (size_t)(n0 / B) * (H / B);
-  const float* su_row = Sc + (size_t)((I + n0) / B) * (H / B);
-  auto xrow = [&](int row) { return x + (size_t)toks[row] * H; };
+  // Stage fetch: A chunk q = tid + 512 i (i < 2) is row q / 8, chunk q % 8;
+  // B chunk q = tid + 512 i (i < 4) is weight row q / 4, chunk q % 4.
+  const uint8_t* asrc[2];
+  const uint8_t* bsrc[4];
+  int adst[2], bdst[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + kPassThreads * i, r = q >> 3, c = q & 7;
+    asrc[i] = reinterpret_cast<const uint8_t*>(act) + (size_t)arow[r] * K * 2 + 16 * c;
+    adst[i] = r * (kKS * 2) + 16 * (c ^ ((r >> 1) & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + kPassThreads * i, r = q >> 2, c = q & 3;
+    const int wrow = GU ? (r < 256 ? n0 + r : I + n0 + r - 256) : n0 + r;
+    bsrc[i] = W + (size_t)wrow * K + 16 * c;
+    bdst[i] = r * kKS + 16 * (c ^ ((r >> 2) & 3));
+  }
+  uint4 av[2], bv[4];
+  auto fetch = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) av[i] = ld16(asrc[i] + st * kKS * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[i] = ld16(bsrc[i] + st * kKS);
+  };
+  auto put = [&](int buf) {
+    uint8_t* A = lds + buf * (kAStage + kBStage);
+    uint8_t* B = A + kAStage;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(A + adst[i]) = av[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + bdst[i]) = bv[i];
+  };
 
-  f32x4_t accg[4], accu[4];
+  // this wavefront's fragments: A rows 64 wm + 32 m + lane % 32; B (tile)
+  // rows brow(nb) + lane % 32
+  const int q = lane >> 5, l32 = lane & 31;
+  int arw[2], brw[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) accg[m] = accu[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < 2; ++m) arw[m] = 64 * wm + 32 * m + l32;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    brw[nb] = (GU ? (nb < 2 ? 64 * wn + 32 * nb : 256 + 64 * wn + 32 * (nb - 2)) : 128 * wn + 32 * nb) + l32;
+  // scale row of each 32-column tile
+  const float* srow[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int wrow = GU ? (nb < 2 ? n0 + 64 * wn : I + n0 + 64 * wn) : n0 + 128 * wn;
+    srow[nb] = Sc + (size_t)(wrow / kBK) * (K / kBK);
+  }
+  int mlive = (valid - 64 * wm + 31) / 32;  // 32-row tiles of this wavefront with rows
+  mlive = mlive < 0 ? 0 : (mlive > 2 ? 2 : mlive);
 
-  for (int kb = 0; kb < H / kBK; ++kb) {
-    const int k0 = kb * kBK;
-    uint4 wgv[2], wuv[2];
+  f32x16_t acc[2][4];
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-      wgv[sp] = ld16(wg_row + k0 + 64 * sp);
-      wuv[sp] = ld16(wu_row + k0 + 64 * sp);
-    }
-    const float sg = sg_row[kb], su = su_row[kb];
-    __syncthreads();  // the previous block's LDS reads are done
-    stage_a(As, xrow, valid, k0);
-    __syncthreads();
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[m][nb][v] = 0.f;
+  float unit[4] = {0.f, 0.f, 0.f, 0.f};  // scale the accumulators are expressed in
+  bool on[4] = {false, false, false, false};
+  float snext[4];  // scales of the next block, read one block ahead
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) snext[nb] = srow[nb][0];
 
-    f32x4_t bg[4], bu[4];
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int st = 0; st < NS; ++st) {
+    if (st + 1 < NS) fetch(st + 1);
+    if ((st & 1) == 0) {  // entering scale block st / 2
 #pragma unroll
-    for (int m = 0; m < 4; ++m) bg[m] = bu[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 4; ++nb) {
+        const float sn = snext[nb];
+        if (st + 2 < NS) snext[nb] = srow[nb][(st >> 1) + 1];
+        on[nb] = sn != 0.f;
+        if (on[nb]) {
+          const float r = unit[nb] / sn;  // unit 0 (nothing added yet): the accumulators are 0
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
+          for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8_t bgf = st ? e4m3x8_to_bf16x8(wgv[sp].z, wgv[sp].w)
-                                : e4m3x8_to_bf16x8(wgv[sp].x, wgv[sp].y);
-        const bf16x8_t buf = st ? e4m3x8_to_bf16x8(wuv[sp].z, wuv[sp].w)
-                                : e4m3x8_to_bf16x8(wuv[sp].x, wuv[sp].y);
-        const int kc = 64 * sp + 16 * (lane >> 4) + 8 * st;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bf16x8_t af = lds_bf16x8(As + (16 * m + (lane & 15)) * kLda + kc);
-          bg[m] = mfma16(af, bgf, bg[m]);
-          bu[m] = mfma16(af, buf, bu[m]);
+            for (int v = 0; v < 16; ++v) acc[m][nb][v] *= r;
+          unit[nb] = sn;
         }
       }
     }
+    const uint8_t* A = lds + (st & 1) * (kAStage + kBStage);
+    const uint8_t* B = A + kAStage;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int p = 0; p < 2; ++p) {
+      uint4 braw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        accg[m][i] = fmaf(sg, bg[m][i], accg[m][i]);
-        accu[m][i] = fmaf(su, bu[m][i], accu[m][i]);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int r = brw[nb], c = 2 * p + q;
+        braw[nb] = *reinterpret_cast<const uint4*>(B + r * kKS + 16 * (c ^ ((r >> 2) & 3)));
       }
-  }
-  // D layout: lane L holds rows 4*(L/16) + i of column L%16
-  const int col = n0 + (lane & 15);
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+      for (int hh = 0; hh < 2; ++hh) {
+        typename O::T bf[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * m + 4 * (lane >> 4) + i;
-      if (row < valid) h[(size_t)(r0 + row) * I + col] = f32_to_f16_sat(silu(accg[m][i]) * accu[m][i]);
-    }
-}
-
-template <int H, int I, int B>
-__global__ __launch_bounds__(256) void mfma_down(MfmaBank bk, const int32_t* __restrict__ meta,
-                                                const int32_t* __restrict__ tiles,
-                                                const int32_t* __restrict__ offsets, int E,
-                                                const uint16_t* __restrict__ h,
-                                                float* __restrict__ y) {
-  static_assert(B == kBK && I % kBK == 0 && H % 128 == 0, "MFMA tiling");
-  __shared__ uint16_t As[kMfmaBM * kLda];
-  const int tile = blockIdx.y;
-  if (tile >= meta[1]) return;
-  const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
-  const int valid = min(kMfmaBM, offsets[g + 1] - r0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 128 + wave * 32;  // this wavefront's 32 output columns
-  const bool sh = g == E;
-  const uint8_t* W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
-  const float* Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / B) * (I / B);
-  const uint8_t* w_row[2];
+        for (int nb = 0; nb < 4; ++nb)
+          bf[nb] = hh ? O::cvt(braw[nb].z, braw[nb].w) : O::cvt(braw[nb].x, braw[nb].y);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-    w_row[nb] = W + (size_t)(n0 + 16 * nb + (lane & 15)) * I + 16 * (lane >> 4);
-  const float* s_row = Sc + (size_t)(n0 / B) * (I / B);  // 32 columns share a scale row
-  auto hrow = [&](int row) { return h + (size_t)(r0 + row) * I; };
-
-  f32x4_t acc[4][2];
+        for (int m = 0; m < 2; ++m) {
+          if (m < mlive) {
+            const int r = arw[m], c = 4 * p + 2 * q + hh;
+            const uint4 af = *reinterpret_cast<const uint4*>(A + r * (kKS * 2) + 16 * (c ^ ((r >> 1) & 7)));
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = 0; kb < I / kBK; ++kb) {
-    const int k0 = kb * kBK;
-    uint4 wv[2][2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) wv[nb][sp] = ld16(w_row[nb] + k0 + 64 * sp);
-    const float sc = s_row[kb];
-    __syncthreads();
-    stage_a(As, hrow, valid, k0);
-    __syncthreads();
-
-    f32x4_t b[4][2];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f16x8_t bf[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          bf[nb] = st ? e4m3x8_to_f16x8(wv[nb][sp].z, wv[nb][sp].w)
-                      : e4m3x8_to_f16x8(wv[nb][sp].x, wv[nb][sp].y);
-        const int kc = 64 * sp + 16 * (lane >> 4) + 8 * st;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f16x8_t af = lds_f16x8(As + (16 * m + (lane & 15)) * kLda + kc);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) b[m][nb] = mfma16_f16(af, bf[nb], b[m][nb]);
+            for (int nb = 0; nb < 4; ++nb)
+              if (on[nb]) acc[m][nb] = O::mma(af, bf[nb], acc[m][nb]);
+          }
         }
       }
     }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][nb][i] = fmaf(sc, b[m][nb][i], acc[m][nb][i]);
+    if (st + 1 < NS) put((st + 1) & 1);
+    __syncthreads();
   }
+
+  // D layout (32x32): lane L holds column L % 32; value v is row
+  // 8 (v / 4) + 4 (L / 32) + v % 4
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * m + 4 * (lane >> 4) + i;
-      if (row < valid) {
+    for (int v = 0; v < 16; ++v) {
+      const int row = 64 * wm + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
+      if (row >= valid) continue;
+      if (GU) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + row) * I;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          y[(size_t)(r0 + row) * H + n0 + 16 * nb + (lane & 15)] = acc[m][nb][i];
+        for (int jj = 0; jj < 2; ++jj)
+          h[n0 + 64 * wn + 32 * jj + l32] = f32_to_f16_sat(silu(acc[m][jj][v] * unit[jj]) *
+                                                           (acc[m][jj + 2][v] * unit[jj + 2]));
+      } else {
+        float* y = reinterpret_cast<float*>(out) + (size_t)(r0 + row) * H;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) y[n0 + 128 * wn + 32 * nb + l32] = acc[m][nb][v] * unit[nb];
       }
     }
 }
@@ -301,13 +342,14 @@ __global__ __launch_bounds__(256) void mfma_down(MfmaBank bk, const int32_t* __r
 template <int H, int I, int B>
 static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Work& w,
                      hipStream_t s, hipEvent_t after_gate_up) {
-  const unsigned ntiles = (unsigned)max_mfma_tiles(d);
-  mfma_gate_up<H, I, B><<<dim3(I / 64, ntiles), 256, 0, s>>>(
-      reinterpret_cast<const uint16_t*>(x), bk, w.meta, w.tiles, w.offsets, w.rtok, d.E,
-      reinterpret_cast<uint16_t*>(w.h));
+  static_assert(B == kBK, "MFMA passes take 128 x 128 scale blocks");
+  // tile slots rounded up to whole rounds of the XCDs (extra slots exit)
+  const unsigned nt8 = (unsigned)((max_mfma_tiles(d) + kXcds - 1) / kXcds * kXcds);
+  mfma_pass<true, H, I><<<nt8 * (I / PassShape<true, H, I>::COLS), kPassThreads, 0, s>>>(
+      reinterpret_cast<const uint16_t*>(x), bk, w.meta, w.tiles, w.offsets, w.rtok, d.E, w.h);
   if (after_gate_up) (void)hipEventRecord(after_gate_up, s);
-  mfma_down<H, I, B><<<dim3(H / 128, ntiles), 256, 0, s>>>(
-      bk, w.meta, w.tiles, w.offsets, d.E, reinterpret_cast<const uint16_t*>(w.h), w.y);
+  mfma_pass<false, H, I><<<nt8 * (H / PassShape<false, H, I>::COLS), kPassThreads, 0, s>>>(
+      reinterpret_cast<const uint16_t*>(w.h), bk, w.meta, w.tiles, w.offsets, w.rtok, d.E, w.y);
 }
 
 #define MOE_MFMA_SHAPES(X) \

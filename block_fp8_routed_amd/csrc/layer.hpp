@@ -13,7 +13,7 @@ namespace moe {
 constexpr int kMaxExperts = 1024;  // permute keeps per-wave expert counters in LDS
 constexpr int kMaxTopK = 16;       // top-k keeps the selection in registers
 constexpr int kGemvMaxTokens = 16; // AUTO path: wavefront GEMV up to this many tokens
-constexpr int kMfmaBM = 64;        // rows (tokens) of one grouped-MFMA tile
+constexpr int kMfmaBM = 128;       // rows (tokens) of one grouped-MFMA tile
 constexpr size_t kAlign = 256;
 
 struct Dims {

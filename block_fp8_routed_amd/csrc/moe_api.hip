@@ -101,7 +101,7 @@ static moe_status basic_dims(const moe_config* c, Dims* d) {
 static moe_status expert_family_ok(const Dims& d) {
   if (d.mfma) {
     if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
-    if (max_mfma_tiles(d) > 65535) return MOE_ERR_UNSUPPORTED;  // tile grid dimension
+    if (max_mfma_tiles(d) > 65535) return MOE_ERR_UNSUPPORTED;  // bounded tile list
     return has_mfma_instance(d) ? MOE_OK : MOE_ERR_UNSUPPORTED;
   }
   return has_gemv_instance(d) ? MOE_OK : MOE_ERR_UNSUPPORTED;
