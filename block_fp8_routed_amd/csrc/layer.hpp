@@ -25,14 +25,34 @@ struct Dims {
   bool mfma;     // expert family: grouped bf16 MFMA (true) or wavefront GEMV
 };
 
-// Router partial logits: decode-sized calls split H into slices of
-// kRouterSlice columns (or one slice of H < kRouterSlice) and the top-k kernel
-// sums the slices in order. 0 = the tiled-GEMM router (one full slice).
+// Router kernels and partial logits. The router writes partial logits per
+// slice of H; the top-k kernel sums the slices in slice order.
+//  * decode (T <= 16): wavefront dot products over slices of kRouterSlice
+//    columns (one slice when H < kRouterSlice);
+//  * prefill with bf16 activations (H a multiple of 32): MFMA tiles over the
+//    router weights split exactly into three bf16 planes, slices of
+//    kRouterSlice columns when H is a multiple of it, else one;
+//  * otherwise (fp32 activations at prefill sizes): the fp32 tiled GEMM, one
+//    slice.
 constexpr int kRouterSlice = 512;
+enum RouterKind { kRouterDecode, kRouterMfma, kRouterGemm, kRouterNone };
+inline RouterKind router_kind(const Dims& d) {
+  if (d.T <= kGemvMaxTokens) {
+    if (d.H < kRouterSlice || d.H % kRouterSlice == 0) return kRouterDecode;
+    return kRouterGemm;
+  }
+  if (d.x_bf16 && d.H % 32 == 0) return kRouterMfma;
+  return kRouterGemm;
+}
+// number of partial-logit slices (>= 1)
 inline int router_slices(const Dims& d) {
-  if (d.T > kGemvMaxTokens) return 0;
-  if (d.H < kRouterSlice) return 1;
-  return d.H % kRouterSlice == 0 ? d.H / kRouterSlice : 0;
+  switch (router_kind(d)) {
+    case kRouterDecode:
+    case kRouterMfma:
+      return d.H % kRouterSlice == 0 ? d.H / kRouterSlice : 1;
+    default:
+      return 1;
+  }
 }
 
 constexpr int kMetaSelectCounter = 8;
@@ -53,6 +73,7 @@ struct Work {
   int32_t* tiles;    // [max_tiles][2] (group, first row) of each MFMA row tile
   void* h;           // [P][I] fp16 SwiGLU output
   float* y;          // [P][H] fp32
+  uint16_t* rsplit;  // [3][E][H] bf16 planes of the router weights (MFMA router)
 };
 
 inline int64_t max_mfma_tiles(const Dims& d) {
@@ -66,7 +87,7 @@ Work carve(const Dims& d, void* base);
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
 // zero_word (may be null): a workspace word the decode kernel (T <= 16) uses
 // as its completion counter; the router zeroes it.
-hipError_t launch_router(const Dims& d, const void* x, const float* wr, float* plogits,
+hipError_t launch_router(const Dims& d, const void* x, const float* wr, const Work& w,
                          int32_t* zero_word, hipStream_t s);
 // Sums the router slices, adds the bias, selects and gates; optionally writes
 // the final logits.

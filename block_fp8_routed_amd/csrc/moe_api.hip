@@ -14,11 +14,10 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 12;
+constexpr int kRegions = 13;
 
 static void region_sizes(const Dims& d, size_t* sz) {
-  const int ns = router_slices(d) > 0 ? router_slices(d) : 1;
-  sz[0] = (size_t)ns * d.T * d.E * 4;     // partial router logits
+  sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
   sz[1] = (size_t)d.T * d.k * 4;          // topk
   sz[2] = (size_t)d.T * d.k * 4;          // gates
   sz[3] = (size_t)(d.E + 2) * 4;          // offsets
@@ -30,6 +29,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[9] = (size_t)max_mfma_tiles(d) * 8;  // tiles
   sz[10] = (size_t)d.P * d.I * 2;         // h (fp16)
   sz[11] = (size_t)d.P * d.H * 4;         // y
+  sz[12] = router_kind(d) == kRouterMfma ? (size_t)3 * d.E * d.H * 2 : 0;  // router planes
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -61,6 +61,7 @@ Work carve(const Dims& d, void* base) {
   w.tiles = static_cast<int32_t*>(r[9]);
   w.h = r[10];
   w.y = static_cast<float*>(r[11]);
+  w.rsplit = static_cast<uint16_t*>(r[12]);
   return w;
 }
 
@@ -157,7 +158,7 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr;
   if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
   const bool small = small_select_permute(d);
-  if (launch_router(d, x, router_w, w.logits, small ? w.meta + kMetaSelectCounter : nullptr, s) !=
+  if (launch_router(d, x, router_w, w, small ? w.meta + kMetaSelectCounter : nullptr, s) !=
       hipSuccess)
     return MOE_ERR_HIP;
   const int tile_rows = d.mfma ? kMfmaBM : 0;
@@ -196,7 +197,7 @@ moe_status moe_route(const void* x, const float* router_w, const float* router_b
   if (st != MOE_OK) return st;
   const Work w = carve(d, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_router(d, x, router_w, w.logits, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_topk(d, w.logits, router_bias, topk_idx, gates, logits, s) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;

@@ -53,7 +53,7 @@ bool small_select_permute(const Dims& d) {
 
 hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
                                        const Work& w, int tile_rows, hipStream_t s) {
-  const int ns = router_slices(d) > 0 ? router_slices(d) : 1;
+  const int ns = router_slices(d);
   const int nv = (d.E + 63) / 64;
   const unsigned grid = (unsigned)d.T;
 #define MOE_SP(NV)                                                                          \

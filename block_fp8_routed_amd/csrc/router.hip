@@ -2,17 +2,19 @@
 //
 // The router is small and always resident (colizig page, "Features" and
 // "Architecture & how it works": attention/router/norms stay resident, experts
-// are streamed). Its cost is reading Wr at decode sizes and E*T*H FMAs at
-// prefill sizes, so there are two kernels:
+// are streamed). Its cost is reading Wr at decode sizes and E*T*H MACs at
+// prefill sizes, so there are three kernels:
 //  * router_slices (T <= 16): H is cut into slices of 512 columns; a
 //    wavefront dots four expert rows of a slice with four tokens using
-//    coalesced 16-byte loads. Partial sums per slice are written out; the
-//    top-k kernel adds them in slice order.
-//  * router_gemm (T > 16): 64x64 LDS-tiled fp32 GEMM, one slice.
-// Both accumulate in fp32 in two levels (short partial sums added into a
-// running total), which keeps the rounding error of a 4096-term logit near
-// 1e-6, well inside the 1e-5 band within which two logits count as tied.
-// The bias is added by the top-k kernel.
+//    coalesced 16-byte loads.
+//  * router_mfma (T > 16, bf16 activations): bf16 MFMA tiles over an exact
+//    three-plane bf16 split of Wr, per slice of 512 columns.
+//  * router_gemm (otherwise): 64x64 LDS-tiled fp32 GEMM, one slice.
+// Partial sums per slice are written out and the top-k kernel adds them in
+// slice order. Every path accumulates in fp32 in two levels (short partial
+// sums added into a running total), which keeps the rounding error of a
+// 4096-term logit near 1e-6, well inside the 1e-5 band within which two
+// logits count as tied. The bias is added by the top-k kernel.
 #include "device.hpp"
 #include "layer.hpp"
 
@@ -192,22 +194,165 @@ static void slices_launch(const Dims& d, const void* x, const float* wr, float* 
                                                             zero_word);
 }
 
-hipError_t launch_router(const Dims& d, const void* x, const float* wr, float* plog,
+// ------------------------------------------------------------ MFMA router --
+// Prefill sizes with bf16 activations. Each fp32 router weight is split into
+// three bf16 planes, w = hi + mid + lo (hi = bf16(w), mid = bf16(w - hi),
+// lo = bf16(w - hi - mid), each difference exact in fp32), which leaves a
+// remainder below 2^-24 |w|. A logit is then the sum of three bf16 MFMA
+// contractions of the (exact) bf16 activations, each product exact in fp32.
+__global__ __launch_bounds__(256) void router_split(const float* __restrict__ wr, int64_t n,
+                                                    uint16_t* __restrict__ planes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float w = wr[i];
+  const uint32_t hb = f32_to_bf16_bits(w);
+  const float r1 = w - __uint_as_float(hb << 16);
+  const uint32_t mb = f32_to_bf16_bits(r1);
+  const float r2 = r1 - __uint_as_float(mb << 16);
+  const uint32_t lb = f32_to_bf16_bits(r2);
+  planes[i] = (uint16_t)hb;
+  planes[n + i] = (uint16_t)mb;
+  planes[2 * n + i] = (uint16_t)lb;
+}
+
+// Tile of 128 tokens x 128 experts over one slice of H (blockIdx.z), 256
+// threads as 2 x 2 wavefronts of 64 x 64 (2 x 2 MFMA tiles of 32 x 32). K runs
+// in stages of 32: the stage's activation tile and three weight-plane tiles
+// are fetched global -> registers one stage ahead and stored into the other
+// of two LDS buffers after the stage's MFMAs. 16-byte chunks are
+// XOR-swizzled by row (chunk c of row r at slot c ^ ((r >> 2) & 3)) against
+// bank conflicts. Rows past T and experts past E repeat the last one (loads
+// stay unconditional) and are not stored.
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kRtBM = 128, kRtBN = 128, kRtKS = 32;
+constexpr int kRtRow = kRtKS * 2;                // bytes per tile row per stage
+constexpr int kRtA = kRtBM * kRtRow;             // 8 KiB
+constexpr int kRtStage = kRtA + 3 * kRtBN * kRtRow;  // 32 KiB
+
+__global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ x,
+                                                  const uint16_t* __restrict__ planes,
+                                                  float* __restrict__ plog, int T, int H, int E,
+                                                  int HS) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kRtStage];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.x * kRtBM, e0 = blockIdx.y * kRtBN, h0 = blockIdx.z * HS;
+  const size_t plane = (size_t)E * H;
+  // fetch map: A chunk q = tid + 256 i (i < 2): row q / 4, chunk q % 4;
+  // B chunk q = tid + 256 i (i < 6): plane q / 512, row (q % 512) / 4, chunk q % 4
+  const uint16_t* src[8];
+  int dst[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+    const int row = m0 + r < T ? m0 + r : T - 1;
+    src[i] = x + (size_t)row * H + h0 + 8 * c;
+    dst[i] = r * kRtRow + 16 * (c ^ ((r >> 2) & 3));
+  }
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int q = tid + 256 * i, p = q >> 9, r = (q & 511) >> 2, c = q & 3;
+    const int e = e0 + r < E ? e0 + r : E - 1;
+    src[2 + i] = planes + p * plane + (size_t)e * H + h0 + 8 * c;
+    dst[2 + i] = kRtA + p * (kRtBN * kRtRow) + r * kRtRow + 16 * (c ^ ((r >> 2) & 3));
+  }
+  uint4 v[8];
+  auto fetch = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ld16(src[i] + st * kRtKS);
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(lds + buf * kRtStage + dst[i]) = v[i];
+  };
+  const int q = lane >> 5, l32 = lane & 31;
+  rf32x16_t acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
+  const int NS = HS / kRtKS;
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int st = 0; st < NS; ++st) {
+    if (st + 1 < NS) fetch(st + 1);
+    const uint8_t* L = lds + (st & 1) * kRtStage;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {  // k16 steps; lane group q takes chunk 2t + q
+      const int c = 2 * t + q;
+      rbf16x8_t a[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int r = 64 * wm + 32 * m + l32;
+        a[m] = __builtin_bit_cast(rbf16x8_t,
+                                  *reinterpret_cast<const uint4*>(L + r * kRtRow + 16 * (c ^ ((r >> 2) & 3))));
+      }
+#pragma unroll
+      for (int p = 2; p >= 0; --p) {  // lo, mid, hi: the small terms first
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int r = 64 * wn + 32 * n + l32;
+          const rbf16x8_t b = __builtin_bit_cast(
+              rbf16x8_t, *reinterpret_cast<const uint4*>(L + kRtA + p * (kRtBN * kRtRow) + r * kRtRow +
+                                                         16 * (c ^ ((r >> 2) & 3))));
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b, acc[m][n], 0, 0, 0);
+        }
+      }
+    }
+    if (st + 1 < NS) put((st + 1) & 1);
+    __syncthreads();
+  }
+  // D layout (32x32): lane L holds column L % 32, value j row 8 (j / 4) + 4 (L / 32) + j % 4
+  float* out = plog + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int t = m0 + 64 * wm + 32 * m + 8 * (j >> 2) + 4 * q + (j & 3);
+      if (t >= T) continue;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int e = e0 + 64 * wn + 32 * n + l32;
+        if (e < E) out[(size_t)t * E + e] = acc[m][n][j];
+      }
+    }
+}
+
+hipError_t launch_router(const Dims& d, const void* x, const float* wr, const Work& w,
                          int32_t* zero_word, hipStream_t s) {
-  if (router_slices(d) > 0) {
-    // tokens per wavefront (T <= 16 here: at most 4 wavefronts per workgroup)
-    if (d.T <= 1)
-      slices_launch<1>(d, x, wr, plog, zero_word, s);
-    else if (d.T <= 2)
-      slices_launch<2>(d, x, wr, plog, zero_word, s);
-    else
-      slices_launch<4>(d, x, wr, plog, zero_word, s);
-  } else {
-    const dim3 grid((unsigned)((d.T + 63) / 64), (d.E + 63) / 64);
-    if (d.x_bf16)
-      router_gemm<true><<<grid, 256, 0, s>>>(x, wr, plog, d.T, d.H, d.E);
-    else
-      router_gemm<false><<<grid, 256, 0, s>>>(x, wr, plog, d.T, d.H, d.E);
+  float* plog = w.logits;
+  switch (router_kind(d)) {
+    case kRouterDecode:
+      // tokens per wavefront (T <= 16 here: at most 4 wavefronts per workgroup)
+      if (d.T <= 1)
+        slices_launch<1>(d, x, wr, plog, zero_word, s);
+      else if (d.T <= 2)
+        slices_launch<2>(d, x, wr, plog, zero_word, s);
+      else
+        slices_launch<4>(d, x, wr, plog, zero_word, s);
+      break;
+    case kRouterMfma: {
+      const int64_t n = (int64_t)d.E * d.H;
+      router_split<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(wr, n, w.rsplit);
+      const int ns = router_slices(d);
+      const dim3 grid((unsigned)((d.T + kRtBM - 1) / kRtBM), (d.E + kRtBN - 1) / kRtBN, ns);
+      router_mfma<<<grid, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(x), w.rsplit, plog,
+                                       (int)d.T, d.H, d.E, d.H / ns);
+      break;
+    }
+    default: {
+      const dim3 grid((unsigned)((d.T + 63) / 64), (d.E + 63) / 64);
+      if (d.x_bf16)
+        router_gemm<true><<<grid, 256, 0, s>>>(x, wr, plog, d.T, d.H, d.E);
+      else
+        router_gemm<false><<<grid, 256, 0, s>>>(x, wr, plog, d.T, d.H, d.E);
+    }
   }
   return hipGetLastError();
 }

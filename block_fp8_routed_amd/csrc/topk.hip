@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ pl
 hipError_t launch_topk(const Dims& d, const float* plog, const float* bias, int32_t* topk,
                        float* gates, float* logits_out, hipStream_t s) {
   const dim3 grid((unsigned)((d.T + 3) / 4));
-  const int ns = router_slices(d) > 0 ? router_slices(d) : 1;
+  const int ns = router_slices(d);
   const int nv = (d.E + 63) / 64;
 #define MOE_TOPK(NV) \
   topk_softmax<NV><<<grid, 256, 0, s>>>(plog, ns, bias, topk, gates, logits_out, d.T, d.E, d.k)
