@@ -82,23 +82,32 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 
 // Grouped pass, one template for both projections.
 //
-// Tile: kMfmaBM = 128 rows of one group x 512 weight rows, 512 threads as 2 x
-// 4 wavefronts; wavefront (wm, wn) owns rows [64 wm, 64 wm + 64) and 128
-// weight rows, as 2 x 4 MFMA tiles of 32 x 32 (v_mfma_f32_32x32x16_*, which
-// keeps the matrix pipe busy with four accumulators per wavefront).
+// A workgroup (512 threads, 8 wavefronts) computes one tile: up to kMfmaBM =
+// 128 rows of one group against 512 weight rows, on 32x32x16 MFMAs
+// (v_mfma_f32_32x32x16_*, which keeps the matrix pipe busy with four
+// accumulators per wavefront).
 //   gate/up (GU): the 512 weight rows are gate rows n0 .. n0 + 255 then the
-//     matching up rows; wavefront wn takes gate rows 64 wn .. 64 wn + 63 of
-//     those and the matching up rows, so SwiGLU pairs accumulator tiles of the
-//     same wavefront. A = bf16 activation rows gathered by token; bf16 MFMA.
-//   down: weight rows n0 .. n0 + 511 are output columns; wavefront wn takes
-//     128 of them. A = fp16 h rows (a group's rows are contiguous); fp16 MFMA.
-// K runs in stages of 64 (half a scale block). A stage's A (128 x 64) and B
-// (512 x 64 bytes) tiles are fetched global -> registers one stage ahead and
-// written into the other of two LDS buffers after the current stage's MFMAs,
-// so global latency overlaps the matrix work; one barrier per stage. In LDS
-// the 16-byte chunks of a row are XOR-swizzled with the row index (A: chunk c
-// of row r at slot c ^ ((r >> 1) & 7); B: c ^ ((r >> 2) & 3)), which makes the
-// 32-row fragment reads and the tile writes free of bank conflicts.
+//     matching up rows; every wavefront holds gate and up tiles of the same
+//     columns, so SwiGLU pairs accumulator tiles of one wavefront. A = bf16
+//     activation rows gathered by token; bf16 MFMA.
+//   down: weight rows n0 .. n0 + 511 are output columns. A = fp16 h rows (a
+//     group's rows are contiguous); fp16 MFMA.
+// Two tile shapes, chosen per tile:
+//   full (more than 64 rows): 2 x 4 wavefronts, each 64 rows x 128 weight
+//     rows (2 x 4 MFMA tiles); stages fetched one ahead.
+//   thin (at most 64 rows, where the pass streams weights): 1 x 8
+//     wavefronts, each 64 rows x 64 weight rows (2 x 2 MFMA tiles); the A
+//     tile has 64 rows, and stages are fetched two ahead, so twice the bytes
+//     are in flight while the weights stream.
+// K runs in stages of 64 (half a scale block). A stage's A tile and B (512 x
+// 64 bytes) tile are fetched global -> registers ahead of use and written into
+// the other of two LDS buffers after the current stage's MFMAs; one barrier
+// per stage. Loads are never conditional (a stage index past the end is
+// clamped, rows past the group's end repeat its last row), so the compiler
+// can wait for exactly the loads a write needs. In LDS the 16-byte chunks of a
+// row are XOR-swizzled with the row index (A: chunk c of row r at slot c ^
+// ((r >> 1) & 7); B: c ^ ((r >> 2) & 3)), which makes the 32-row fragment
+// reads and the tile writes free of bank conflicts.
 //
 // K order inside a stage: the contraction does not depend on the order of k,
 // as long as A and B use the same one. Lane group q = lane / 32 reads 16 B
@@ -112,9 +121,8 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 // by the last scale at the end; the result equals sum_kb s(kb) * P(kb) up to
 // fp32 rounding (one extra rounding per block). A block with scale 0 adds
 // nothing and is skipped.
-// Rows of a tile past the group's end repeat its last row (no load is
-// conditional); 32-row MFMA tiles wholly past the end are skipped, and rows
-// past the end are never stored.
+// 32-row MFMA tiles wholly past the group's end are skipped, and rows past
+// the end are never stored.
 constexpr int kTN = 512;            // weight rows per tile
 constexpr int kXcds = 8;            // accelerator complex dies (one L2 each)
 constexpr int kPassThreads = 512;
@@ -153,124 +161,114 @@ struct Op<false> {
   }
 };
 
-template <bool GU, int H, int I>
-__global__ __launch_bounds__(kPassThreads) void mfma_pass(const uint16_t* __restrict__ act,
-                                                        MfmaBank bk,
-                                                        const int32_t* __restrict__ meta,
-                                                        const int32_t* __restrict__ tiles,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ rtok, int E,
-                                                        void* __restrict__ out) {
+// Tile geometry of one shape (THIN: at most 64 rows).
+template <bool GU, bool THIN>
+struct TileShape {
+  static constexpr int RA = THIN ? 64 : 128;  // A rows fetched per stage
+  static constexpr int AC = RA * 8 / kPassThreads;  // A chunks per thread per stage
+  static constexpr int NBW = THIN ? 2 : 4;    // 32-column MFMA tiles per wavefront
+  static constexpr int DEPTH = THIN ? 2 : 1;  // stages fetched ahead
+  // tile-relative weight row of this wavefront's MFMA tile nb (lane 0)
+  static __device__ __forceinline__ int brow(int wn, int nb) {
+    if (GU) {
+      if (THIN) return nb == 0 ? 32 * wn : 256 + 32 * wn;
+      return nb < 2 ? 64 * wn + 32 * nb : 256 + 64 * wn + 32 * (nb - 2);
+    }
+    return (THIN ? 64 : 128) * wn + 32 * nb;
+  }
+};
+
+template <bool GU, int H, int I, bool THIN>
+__device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, const uint8_t* W,
+                                          const float* Sc, const int* arow, int valid, int r0,
+                                          int n0, uint8_t* lds, void* __restrict__ out) {
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
-  constexpr int K = P::K, NS = K / kKS;
-  static_assert(K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kAStage + kBStage)];
-  __shared__ int arow[kMfmaBM];
-  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
-  // (each with its own L2), so workgroup L runs on XCD L % 8. XCD x takes row
-  // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
-  // tile's activation rows are fetched into one L2 and reused from it.
-  constexpr int NCB = P::NOUT / P::COLS;
-  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int tile = (j / NCB) * kXcds + xcd;
-  if (tile >= meta[1]) return;
-  const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
-  const int valid = min(kMfmaBM, offsets[g + 1] - r0);
+  using S = TileShape<GU, THIN>;
+  constexpr int K = P::K, NS = K / kKS, AC = S::AC, NBW = S::NBW;
+  static_assert(NS % 2 == 0, "stages come in pairs (one scale block)");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int n0 = (j % NCB) * P::COLS;
-  const bool sh = g == E;
-  const uint8_t* W;
-  const float* Sc;
-  if (GU) {
-    W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
-    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
-  } else {
-    W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
-    Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / kBK) * (I / kBK);
-  }
-  // source row of each tile row
-  if (tid < kMfmaBM) {
-    const int rr = tid < valid ? tid : valid - 1;
-    arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
-  }
-  __syncthreads();
+  const int wm = THIN ? 0 : wave >> 2, wn = THIN ? wave : wave & 3;
 
-  // Stage fetch: A chunk q = tid + 512 i (i < 2) is row q / 8, chunk q % 8;
-  // B chunk q = tid + 512 i (i < 4) is weight row q / 4, chunk q % 4.
-  const uint8_t* asrc[2];
-  const uint8_t* bsrc[4];
-  int adst[2], bdst[4];
+  // fetch map: A chunk qq = tid + 512 i is row qq / 8, chunk qq % 8; B chunk
+  // qq = tid + 512 i (i < 4) is weight row qq / 4, chunk qq % 4
+  // (byte offsets from the wave-uniform bases fit in 32 bits: checked on the
+  // host for the activation rows, and a weight matrix is below 2 GiB)
+  const uint8_t* abase = reinterpret_cast<const uint8_t*>(act);
+  uint32_t asrc[AC], bsrc[4];
+  int adst[AC], bdst[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = tid + kPassThreads * i, r = q >> 3, c = q & 7;
-    asrc[i] = reinterpret_cast<const uint8_t*>(act) + (size_t)arow[r] * K * 2 + 16 * c;
+  for (int i = 0; i < AC; ++i) {
+    const int qq = tid + kPassThreads * i, r = qq >> 3, c = qq & 7;
+    asrc[i] = (uint32_t)arow[r] * (K * 2) + 16 * c;
     adst[i] = r * (kKS * 2) + 16 * (c ^ ((r >> 1) & 7));
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = tid + kPassThreads * i, r = q >> 2, c = q & 3;
+    const int qq = tid + kPassThreads * i, r = qq >> 2, c = qq & 3;
     const int wrow = GU ? (r < 256 ? n0 + r : I + n0 + r - 256) : n0 + r;
-    bsrc[i] = W + (size_t)wrow * K + 16 * c;
+    bsrc[i] = (uint32_t)wrow * K + 16 * c;
     bdst[i] = r * kKS + 16 * (c ^ ((r >> 2) & 3));
   }
-  uint4 av[2], bv[4];
-  auto fetch = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) av[i] = ld16(asrc[i] + st * kKS * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bv[i] = ld16(bsrc[i] + st * kKS);
+  struct Regs {
+    uint4 a[AC], b[4];
   };
-  auto put = [&](int buf) {
+  auto fetch = [&](Regs& R, int st) {
+    st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
+#pragma unroll
+    for (int i = 0; i < AC; ++i) R.a[i] = ld16(abase + (asrc[i] + (uint32_t)(st * kKS * 2)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R.b[i] = ld16(W + (bsrc[i] + (uint32_t)(st * kKS)));
+  };
+  auto put = [&](const Regs& R, int buf) {
     uint8_t* A = lds + buf * (kAStage + kBStage);
     uint8_t* B = A + kAStage;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(A + adst[i]) = av[i];
+    for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + adst[i]) = R.a[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + bdst[i]) = bv[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + bdst[i]) = R.b[i];
   };
 
-  // this wavefront's fragments: A rows 64 wm + 32 m + lane % 32; B (tile)
-  // rows brow(nb) + lane % 32
+  // this wavefront's fragments: A rows 64 wm + 32 m + lane % 32; B rows
+  // brow(nb) + lane % 32
   const int q = lane >> 5, l32 = lane & 31;
-  int arw[2], brw[4];
+  int arw[2], brw[NBW];
 #pragma unroll
   for (int m = 0; m < 2; ++m) arw[m] = 64 * wm + 32 * m + l32;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    brw[nb] = (GU ? (nb < 2 ? 64 * wn + 32 * nb : 256 + 64 * wn + 32 * (nb - 2)) : 128 * wn + 32 * nb) + l32;
-  // scale row of each 32-column tile
-  const float* srow[4];
+  for (int nb = 0; nb < NBW; ++nb) brw[nb] = S::brow(wn, nb) + l32;
+  // scale row of each MFMA tile
+  const float* srow[NBW];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int wrow = GU ? (nb < 2 ? n0 + 64 * wn : I + n0 + 64 * wn) : n0 + 128 * wn;
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int br = S::brow(wn, nb);
+    const int wrow = GU ? (br < 256 ? n0 + br : I + n0 + br - 256) : n0 + br;
     srow[nb] = Sc + (size_t)(wrow / kBK) * (K / kBK);
   }
   int mlive = (valid - 64 * wm + 31) / 32;  // 32-row tiles of this wavefront with rows
   mlive = mlive < 0 ? 0 : (mlive > 2 ? 2 : mlive);
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[2][NBW];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[m][nb][v] = 0.f;
-  float unit[4] = {0.f, 0.f, 0.f, 0.f};  // scale the accumulators are expressed in
-  bool on[4] = {false, false, false, false};
-  float snext[4];  // scales of the next block, read one block ahead
+  float unit[NBW];  // scale the accumulators are expressed in
+  bool on[NBW];
+  float snext[NBW];  // scales of the next block, read one block ahead
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) snext[nb] = srow[nb][0];
+  for (int nb = 0; nb < NBW; ++nb) {
+    unit[nb] = 0.f;
+    on[nb] = false;
+    snext[nb] = srow[nb][0];
+  }
 
-  fetch(0);
-  put(0);
-  __syncthreads();
-  for (int st = 0; st < NS; ++st) {
-    if (st + 1 < NS) fetch(st + 1);
+  auto compute = [&](int st) {
     if ((st & 1) == 0) {  // entering scale block st / 2
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NBW; ++nb) {
         const float sn = snext[nb];
         if (st + 2 < NS) snext[nb] = srow[nb][(st >> 1) + 1];
         on[nb] = sn != 0.f;
@@ -288,17 +286,17 @@ __global__ __launch_bounds__(kPassThreads) void mfma_pass(const uint16_t* __rest
     const uint8_t* B = A + kAStage;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      uint4 braw[4];
+      uint4 braw[NBW];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NBW; ++nb) {
         const int r = brw[nb], c = 2 * p + q;
         braw[nb] = *reinterpret_cast<const uint4*>(B + r * kKS + 16 * (c ^ ((r >> 2) & 3)));
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        typename O::T bf[4];
+        typename O::T bf[NBW];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NBW; ++nb)
           bf[nb] = hh ? O::cvt(braw[nb].z, braw[nb].w) : O::cvt(braw[nb].x, braw[nb].y);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -306,14 +304,43 @@ __global__ __launch_bounds__(kPassThreads) void mfma_pass(const uint16_t* __rest
             const int r = arw[m], c = 4 * p + 2 * q + hh;
             const uint4 af = *reinterpret_cast<const uint4*>(A + r * (kKS * 2) + 16 * (c ^ ((r >> 1) & 7)));
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < NBW; ++nb)
               if (on[nb]) acc[m][nb] = O::mma(af, bf[nb], acc[m][nb]);
           }
         }
       }
     }
-    if (st + 1 < NS) put((st + 1) & 1);
+  };
+
+  if (S::DEPTH == 1) {
+    Regs R;
+    fetch(R, 0);
+    put(R, 0);
     __syncthreads();
+    for (int st = 0; st < NS; ++st) {
+      fetch(R, st + 1);
+      compute(st);
+      if (st + 1 < NS) put(R, (st + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    // stage st + 1 is in flight while stage st is computed and stage st + 2
+    // is requested; the register sets alternate, so the loop runs in pairs
+    Regs R0, R1;
+    fetch(R0, 0);
+    fetch(R1, 1);
+    put(R0, 0);
+    __syncthreads();
+    for (int st = 0; st < NS; st += 2) {
+      fetch(R0, st + 2);
+      compute(st);
+      put(R1, 1);
+      __syncthreads();
+      fetch(R1, st + 3);
+      compute(st + 1);
+      if (st + 2 < NS) put(R0, 0);
+      __syncthreads();
+    }
   }
 
   // D layout (32x32): lane L holds column L % 32; value v is row
@@ -327,15 +354,61 @@ __global__ __launch_bounds__(kPassThreads) void mfma_pass(const uint16_t* __rest
       if (GU) {
         uint16_t* h = reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + row) * I;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          h[n0 + 64 * wn + 32 * jj + l32] = f32_to_f16_sat(silu(acc[m][jj][v] * unit[jj]) *
-                                                           (acc[m][jj + 2][v] * unit[jj + 2]));
+        for (int jj = 0; jj < NBW / 2; ++jj)
+          h[n0 + S::brow(wn, jj) + l32] = f32_to_f16_sat(silu(acc[m][jj][v] * unit[jj]) *
+                                                         (acc[m][jj + NBW / 2][v] * unit[jj + NBW / 2]));
       } else {
         float* y = reinterpret_cast<float*>(out) + (size_t)(r0 + row) * H;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) y[n0 + 128 * wn + 32 * nb + l32] = acc[m][nb][v] * unit[nb];
+        for (int nb = 0; nb < NBW; ++nb) y[n0 + S::brow(wn, nb) + l32] = acc[m][nb][v] * unit[nb];
       }
     }
+}
+
+template <bool GU, int H, int I>
+__global__ __launch_bounds__(kPassThreads) void mfma_pass(const uint16_t* __restrict__ act,
+                                                        MfmaBank bk,
+                                                        const int32_t* __restrict__ meta,
+                                                        const int32_t* __restrict__ tiles,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ rtok, int E,
+                                                        void* __restrict__ out) {
+  using P = PassShape<GU, H, I>;
+  static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kAStage + kBStage)];
+  __shared__ int arow[kMfmaBM];
+  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
+  // (each with its own L2), so workgroup L runs on XCD L % 8. XCD x takes row
+  // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
+  // tile's activation rows are fetched into one L2 and reused from it.
+  constexpr int NCB = P::NOUT / P::COLS;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int tile = (j / NCB) * kXcds + xcd;
+  if (tile >= meta[1]) return;
+  const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
+  const int valid = min(kMfmaBM, offsets[g + 1] - r0);
+  const int tid = threadIdx.x;
+  const int n0 = (j % NCB) * P::COLS;
+  const bool sh = g == E;
+  const uint8_t* W;
+  const float* Sc;
+  if (GU) {
+    W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
+    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
+  } else {
+    W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
+    Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / kBK) * (I / kBK);
+  }
+  // source row of each tile row (GU: the token; down: the h row)
+  if (tid < kMfmaBM) {
+    const int rr = tid < valid ? tid : valid - 1;
+    arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
+  }
+  __syncthreads();
+  if (valid <= 64)
+    pass_tile<GU, H, I, true>(act, W, Sc, arow, valid, r0, n0, lds, out);
+  else
+    pass_tile<GU, H, I, false>(act, W, Sc, arow, valid, r0, n0, lds, out);
 }
 
 // ---------------------------------------------------------------------------

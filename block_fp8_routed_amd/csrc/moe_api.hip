@@ -103,6 +103,9 @@ static moe_status expert_family_ok(const Dims& d) {
   if (d.mfma) {
     if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
     if (max_mfma_tiles(d) > 65535) return MOE_ERR_UNSUPPORTED;  // bounded tile list
+    // the passes address activation and h rows with 32-bit byte offsets
+    if ((uint64_t)d.T * d.H * 2 > 0xffffffffull || (uint64_t)d.P * d.I * 2 > 0xffffffffull)
+      return MOE_ERR_UNSUPPORTED;
     return has_mfma_instance(d) ? MOE_OK : MOE_ERR_UNSUPPORTED;
   }
   return has_gemv_instance(d) ? MOE_OK : MOE_ERR_UNSUPPORTED;
