@@ -82,24 +82,24 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 
 // Grouped pass, one template for both projections.
 //
-// A workgroup (512 threads, 8 wavefronts) computes one tile: up to kMfmaBM =
-// 128 rows of one group against 512 weight rows, on 32x32x16 MFMAs
-// (v_mfma_f32_32x32x16_*, which keeps the matrix pipe busy with four
-// accumulators per wavefront).
-//   gate/up (GU): the 512 weight rows are gate rows n0 .. n0 + 255 then the
-//     matching up rows; every wavefront holds gate and up tiles of the same
-//     columns, so SwiGLU pairs accumulator tiles of one wavefront. A = bf16
-//     activation rows gathered by token; bf16 MFMA.
-//   down: weight rows n0 .. n0 + 511 are output columns. A = fp16 h rows (a
-//     group's rows are contiguous); fp16 MFMA.
+// A workgroup (512 threads, 8 wavefronts as 2 x 4) computes one tile: up to
+// kMfmaBM = 128 rows of one group against 256 weight rows, on 32x32x16 MFMAs
+// (v_mfma_f32_32x32x16_*). Registers are held to 128 per lane and LDS to 64
+// KiB per workgroup, so two workgroups (four wavefronts per SIMD) share a
+// compute unit and hide each other's LDS and memory latency.
+//   gate/up (GU): the 256 weight rows are gate rows n0 .. n0 + 127 then the
+//     matching up rows; wavefront wn holds gate rows 32 wn .. 32 wn + 31 and
+//     the matching up rows, so SwiGLU pairs accumulator tiles of one
+//     wavefront. A = bf16 activation rows gathered by token; bf16 MFMA.
+//   down: weight rows n0 .. n0 + 255 are output columns; wavefront wn holds
+//     64 of them. A = fp16 h rows (a group's rows are contiguous); fp16 MFMA.
 // Two tile shapes, chosen per tile:
-//   full (more than 64 rows): 2 x 4 wavefronts, each 64 rows x 128 weight
-//     rows (2 x 4 MFMA tiles); stages fetched one ahead.
-//   thin (at most 64 rows, where the pass streams weights): 1 x 8
-//     wavefronts, each 64 rows x 64 weight rows (2 x 2 MFMA tiles); the A
-//     tile has 64 rows, and stages are fetched two ahead, so twice the bytes
-//     are in flight while the weights stream.
-// K runs in stages of 64 (half a scale block). A stage's A tile and B (512 x
+//   full (more than 64 rows): wavefront (wm, wn) takes rows 64 wm .. + 63
+//     (two 32-row MFMA tiles); stages fetched one ahead.
+//   thin (at most 64 rows, where the pass streams weights): rows 32 wm ..
+//     + 31 (one MFMA tile); the A tile has 64 rows, and stages are fetched
+//     two ahead, so more bytes are in flight while the weights stream.
+// K runs in stages of 64 (half a scale block). A stage's A tile and B (256 x
 // 64 bytes) tile are fetched global -> registers ahead of use and written into
 // the other of two LDS buffers after the current stage's MFMAs; one barrier
 // per stage. Loads are never conditional (a stage index past the end is
@@ -120,21 +120,21 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 // tile are multiplied by s(kb-1) / s(kb) before its products are added, and
 // by the last scale at the end; the result equals sum_kb s(kb) * P(kb) up to
 // fp32 rounding (one extra rounding per block). A block with scale 0 adds
-// nothing and is skipped.
-// 32-row MFMA tiles wholly past the group's end are skipped, and rows past
-// the end are never stored.
-constexpr int kTN = 512;            // weight rows per tile
+// nothing: its codes are masked to +0.
+// Rows past the group's end are computed with the rest (they repeat the last
+// row) and never stored.
+constexpr int kTN = 256;            // weight rows per tile
 constexpr int kXcds = 8;            // accelerator complex dies (one L2 each)
 constexpr int kPassThreads = 512;
 constexpr int kKS = 64;             // k per pipeline stage
 constexpr int kAStage = kMfmaBM * kKS * 2;  // bytes: 128 rows x 64 bf16/fp16
-constexpr int kBStage = kTN * kKS;          // bytes: 512 rows x 64 E4M3
+constexpr int kBStage = kTN * kKS;          // bytes: 256 rows x 64 E4M3
 static_assert(kMfmaBM == 128, "tile geometry assumes 128-row tiles");
 
 template <bool GU, int H, int I>
 struct PassShape {
   static constexpr int K = GU ? H : I;         // contraction length
-  static constexpr int COLS = GU ? 256 : 512;  // output columns per tile
+  static constexpr int COLS = GU ? 128 : 256;  // output columns per tile
   static constexpr int NOUT = GU ? I : H;      // output row length
 };
 
@@ -166,15 +166,16 @@ template <bool GU, bool THIN>
 struct TileShape {
   static constexpr int RA = THIN ? 64 : 128;  // A rows fetched per stage
   static constexpr int AC = RA * 8 / kPassThreads;  // A chunks per thread per stage
-  static constexpr int NBW = THIN ? 2 : 4;    // 32-column MFMA tiles per wavefront
+  static constexpr int BC = kTN * 4 / kPassThreads; // B chunks per thread per stage
+  static constexpr int MW = THIN ? 1 : 2;     // 32-row MFMA tiles per wavefront
+  static constexpr int NBW = 2;               // 32-column MFMA tiles per wavefront
   static constexpr int DEPTH = THIN ? 2 : 1;  // stages fetched ahead
-  // tile-relative weight row of this wavefront's MFMA tile nb (lane 0)
+  // tile-relative first row of this wavefront's rows
+  static __device__ __forceinline__ int arow0(int wm) { return (THIN ? 32 : 64) * wm; }
+  // tile-relative weight row of this wavefront's MFMA tile nb
   static __device__ __forceinline__ int brow(int wn, int nb) {
-    if (GU) {
-      if (THIN) return nb == 0 ? 32 * wn : 256 + 32 * wn;
-      return nb < 2 ? 64 * wn + 32 * nb : 256 + 64 * wn + 32 * (nb - 2);
-    }
-    return (THIN ? 64 : 128) * wn + 32 * nb;
+    if (GU) return nb == 0 ? 32 * wn : kTN / 2 + 32 * wn;
+    return 64 * wn + 32 * nb;
   }
 };
 
@@ -185,101 +186,98 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
   using S = TileShape<GU, THIN>;
-  constexpr int K = P::K, NS = K / kKS, AC = S::AC, NBW = S::NBW;
+  constexpr int K = P::K, NS = K / kKS, AC = S::AC, BC = S::BC, MW = S::MW, NBW = S::NBW;
   static_assert(NS % 2 == 0, "stages come in pairs (one scale block)");
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = THIN ? 0 : wave >> 2, wn = THIN ? wave : wave & 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches only
+  const int wm = wave >> 2, wn = wave & 3;
 
   // fetch map: A chunk qq = tid + 512 i is row qq / 8, chunk qq % 8; B chunk
-  // qq = tid + 512 i (i < 4) is weight row qq / 4, chunk qq % 4
-  // (byte offsets from the wave-uniform bases fit in 32 bits: checked on the
-  // host for the activation rows, and a weight matrix is below 2 GiB)
+  // qq = tid + 512 i is weight row qq / 4, chunk qq % 4. Moving qq by 512
+  // moves the row by 64 (A) or 128 (B), which leaves the swizzle alone, so
+  // the LDS targets and the weight sources of i > 0 are constant offsets from
+  // those of i = 0 (GU: B rows 128 .. 255 are the up rows). Byte offsets from
+  // the wave-uniform bases fit in 32 bits (checked on the host for the
+  // activation rows; a weight matrix is below 2 GiB).
   const uint8_t* abase = reinterpret_cast<const uint8_t*>(act);
-  uint32_t asrc[AC], bsrc[4];
-  int adst[AC], bdst[4];
+  uint32_t asrc[AC];
+  const int ar0 = tid >> 3, ac0 = tid & 7;
+  const int adst0 = ar0 * (kKS * 2) + 16 * (ac0 ^ ((ar0 >> 1) & 7));
 #pragma unroll
-  for (int i = 0; i < AC; ++i) {
-    const int qq = tid + kPassThreads * i, r = qq >> 3, c = qq & 7;
-    asrc[i] = (uint32_t)arow[r] * (K * 2) + 16 * c;
-    adst[i] = r * (kKS * 2) + 16 * (c ^ ((r >> 1) & 7));
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qq = tid + kPassThreads * i, r = qq >> 2, c = qq & 3;
-    const int wrow = GU ? (r < 256 ? n0 + r : I + n0 + r - 256) : n0 + r;
-    bsrc[i] = (uint32_t)wrow * K + 16 * c;
-    bdst[i] = r * kKS + 16 * (c ^ ((r >> 2) & 3));
-  }
+  for (int i = 0; i < AC; ++i) asrc[i] = (uint32_t)arow[ar0 + 64 * i] * (K * 2) + 16 * ac0;
+  const int br0 = tid >> 2, bc0 = tid & 3;
+  const int bdst0 = br0 * kKS + 16 * (bc0 ^ ((br0 >> 2) & 3));
+  const uint32_t bsrc0 = (uint32_t)(n0 + br0) * K + 16 * bc0;
+  auto bstep = [](int i) -> uint32_t { return (uint32_t)(GU ? I * i : 128 * i) * K; };
   struct Regs {
-    uint4 a[AC], b[4];
+    uint4 a[AC], b[BC];
   };
   auto fetch = [&](Regs& R, int st) {
     st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
 #pragma unroll
     for (int i = 0; i < AC; ++i) R.a[i] = ld16(abase + (asrc[i] + (uint32_t)(st * kKS * 2)));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R.b[i] = ld16(W + (bsrc[i] + (uint32_t)(st * kKS)));
+    for (int i = 0; i < BC; ++i) R.b[i] = ld16(W + (bsrc0 + bstep(i) + (uint32_t)(st * kKS)));
   };
   auto put = [&](const Regs& R, int buf) {
     uint8_t* A = lds + buf * (kAStage + kBStage);
     uint8_t* B = A + kAStage;
 #pragma unroll
-    for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + adst[i]) = R.a[i];
+    for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + adst0 + 64 * (kKS * 2) * i) = R.a[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + bdst[i]) = R.b[i];
+    for (int i = 0; i < BC; ++i) *reinterpret_cast<uint4*>(B + bdst0 + 128 * kKS * i) = R.b[i];
   };
 
-  // this wavefront's fragments: A rows 64 wm + 32 m + lane % 32; B rows
-  // brow(nb) + lane % 32
+  // this wavefront's fragments: A rows arow0 + 32 m + lane % 32; B rows
+  // brow(nb) + lane % 32. The row offsets are multiples of 32, so the swizzle
+  // of a fragment read depends on lane % 32 only.
   const int q = lane >> 5, l32 = lane & 31;
-  int arw[2], brw[NBW];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) arw[m] = 64 * wm + 32 * m + l32;
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) brw[nb] = S::brow(wn, nb) + l32;
+  const int afr = (S::arow0(wm) + l32) * (kKS * 2), asw = (l32 >> 1) & 7;
+  const int bfr = l32 * kKS, bsw = (l32 >> 2) & 3;
   // scale row of each MFMA tile
   const float* srow[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     const int br = S::brow(wn, nb);
-    const int wrow = GU ? (br < 256 ? n0 + br : I + n0 + br - 256) : n0 + br;
+    const int wrow = GU ? (br < kTN / 2 ? n0 + br : I + n0 + br - kTN / 2) : n0 + br;
     srow[nb] = Sc + (size_t)(wrow / kBK) * (K / kBK);
   }
-  int mlive = (valid - 64 * wm + 31) / 32;  // 32-row tiles of this wavefront with rows
-  mlive = mlive < 0 ? 0 : (mlive > 2 ? 2 : mlive);
 
-  f32x16_t acc[2][NBW];
+  f32x16_t acc[MW][NBW];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MW; ++m)
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[m][nb][v] = 0.f;
-  float unit[NBW];  // scale the accumulators are expressed in
-  bool on[NBW];
-  float snext[NBW];  // scales of the next block, read one block ahead
+  float unit[NBW];     // scale the accumulators are expressed in
+  uint32_t keep[NBW];  // all ones, or 0 for a block of scale 0 (its codes are masked to +0)
+  float snext[NBW];    // scales of the next block, read one block ahead
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     unit[nb] = 0.f;
-    on[nb] = false;
+    keep[nb] = 0u;
     snext[nb] = srow[nb][0];
   }
 
-  auto compute = [&](int st) {
-    if ((st & 1) == 0) {  // entering scale block st / 2
+  // One stage. Every MFMA tile is computed even when rows past the group's
+  // end fill it (their results are not stored); nothing inside is
+  // conditional, so the compiler schedules the MFMAs and LDS reads freely.
+  auto compute = [&](int st, bool block_start) {
+    if (block_start) {  // entering scale block st / 2
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         const float sn = snext[nb];
         if (st + 2 < NS) snext[nb] = srow[nb][(st >> 1) + 1];
-        on[nb] = sn != 0.f;
-        if (on[nb]) {
-          const float r = unit[nb] / sn;  // unit 0 (nothing added yet): the accumulators are 0
+        const bool on = sn != 0.f;
+        // unit 0 (nothing added yet): the accumulators are 0 and stay 0
+        const float r = on ? unit[nb] / sn : 1.f;
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < MW; ++m)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[m][nb][v] *= r;
-          unit[nb] = sn;
-        }
+          for (int v = 0; v < 16; ++v) acc[m][nb][v] *= r;
+        unit[nb] = on ? sn : unit[nb];
+        keep[nb] = on ? 0xffffffffu : 0u;
       }
     }
     const uint8_t* A = lds + (st & 1) * (kAStage + kBStage);
@@ -288,25 +286,22 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     for (int p = 0; p < 2; ++p) {
       uint4 braw[NBW];
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        const int r = brw[nb], c = 2 * p + q;
-        braw[nb] = *reinterpret_cast<const uint4*>(B + r * kKS + 16 * (c ^ ((r >> 2) & 3)));
-      }
+      for (int nb = 0; nb < NBW; ++nb)
+        braw[nb] = *reinterpret_cast<const uint4*>(B + S::brow(wn, nb) * kKS + bfr +
+                                                   16 * ((2 * p + q) ^ bsw));
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         typename O::T bf[NBW];
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
-          bf[nb] = hh ? O::cvt(braw[nb].z, braw[nb].w) : O::cvt(braw[nb].x, braw[nb].y);
+          bf[nb] = hh ? O::cvt(braw[nb].z & keep[nb], braw[nb].w & keep[nb])
+                      : O::cvt(braw[nb].x & keep[nb], braw[nb].y & keep[nb]);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          if (m < mlive) {
-            const int r = arw[m], c = 4 * p + 2 * q + hh;
-            const uint4 af = *reinterpret_cast<const uint4*>(A + r * (kKS * 2) + 16 * (c ^ ((r >> 1) & 7)));
+        for (int m = 0; m < MW; ++m) {
+          const uint4 af = *reinterpret_cast<const uint4*>(A + afr + 32 * m * (kKS * 2) +
+                                                           16 * ((4 * p + 2 * q + hh) ^ asw));
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-              if (on[nb]) acc[m][nb] = O::mma(af, bf[nb], acc[m][nb]);
-          }
+          for (int nb = 0; nb < NBW; ++nb) acc[m][nb] = O::mma(af, bf[nb], acc[m][nb]);
         }
       }
     }
@@ -317,10 +312,14 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     fetch(R, 0);
     put(R, 0);
     __syncthreads();
-    for (int st = 0; st < NS; ++st) {
+    for (int st = 0; st < NS; st += 2) {
       fetch(R, st + 1);
-      compute(st);
-      if (st + 1 < NS) put(R, (st + 1) & 1);
+      compute(st, true);
+      put(R, 1);
+      __syncthreads();
+      fetch(R, st + 2);
+      compute(st + 1, false);
+      if (st + 2 < NS) put(R, 0);
       __syncthreads();
     }
   } else {
@@ -333,11 +332,11 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     __syncthreads();
     for (int st = 0; st < NS; st += 2) {
       fetch(R0, st + 2);
-      compute(st);
+      compute(st, true);
       put(R1, 1);
       __syncthreads();
       fetch(R1, st + 3);
-      compute(st + 1);
+      compute(st + 1, false);
       if (st + 2 < NS) put(R0, 0);
       __syncthreads();
     }
@@ -346,17 +345,15 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   // D layout (32x32): lane L holds column L % 32; value v is row
   // 8 (v / 4) + 4 (L / 32) + v % 4
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MW; ++m)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = 64 * wm + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
+      const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
       if (row >= valid) continue;
       if (GU) {
         uint16_t* h = reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + row) * I;
-#pragma unroll
-        for (int jj = 0; jj < NBW / 2; ++jj)
-          h[n0 + S::brow(wn, jj) + l32] = f32_to_f16_sat(silu(acc[m][jj][v] * unit[jj]) *
-                                                         (acc[m][jj + NBW / 2][v] * unit[jj + NBW / 2]));
+        h[n0 + S::brow(wn, 0) + l32] =
+            f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
       } else {
         float* y = reinterpret_cast<float*>(out) + (size_t)(r0 + row) * H;
 #pragma unroll
@@ -366,7 +363,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
 }
 
 template <bool GU, int H, int I>
-__global__ __launch_bounds__(kPassThreads) void mfma_pass(const uint16_t* __restrict__ act,
+__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void mfma_pass(const uint16_t* __restrict__ act,
                                                         MfmaBank bk,
                                                         const int32_t* __restrict__ meta,
                                                         const int32_t* __restrict__ tiles,
