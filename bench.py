@@ -14,8 +14,16 @@ Prints one JSON line: MoE-layer tokens/s, plus
                 algorithmic FLOPs for MFMA-bound workloads;
   cpu_baseline: the CPU oracle (fp64 NumPy) timed on a bounded sample of the
                 same workload on this host.
+  roofline.traffic: HBM bytes per launch of that kernel, from rocprofv3 PMC
+                runs (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by
+                the bytes a plain copy kernel of known size moves per KiB the
+                same counter reports), read from profiles/traffic.json when its
+                recorded source hash matches the kernel's current sources;
+                null otherwise.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--tokens 16]
+       python bench.py --copy-calibration            (the copy kernel for the counters)
+       python bench.py --traffic-report FETCH.csv WRITE.csv COPYF.csv COPYW.csv --config c1
 """
 from __future__ import annotations
 
@@ -107,6 +115,96 @@ def cpu_baseline(shape, host, x_batches, seconds):
     }
 
 
+# sources that define each dominant kernel (its traffic is void once they change)
+KERNEL_SOURCES = {
+    "gemv": ["expert_gemv.hip", "device.hpp", "layer.hpp"],
+    "mfma": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
+}
+KERNEL_MATCH = {"gemv": "gemv_gate_up<", "mfma": "mfma_pass<true"}
+COPY_MATCH = "MulFunctor"  # the copy kernel of --copy-calibration (dst = src * 1)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_MIB = 512
+
+
+def sources_sha(family):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "block_fp8_routed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_key(config, tokens, family):
+    return f"{config}:T{tokens}:{family}"
+
+
+def copy_calibration():
+    """The plain copy kernel the counters are calibrated on: an elementwise
+    kernel reading COPY_MIB MiB and writing as many, five times."""
+    import torch
+    n = COPY_MIB * 2**20 // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda")  # contents do not matter
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+
+
+def counter_means(path, match):
+    """Mean counter value (KiB) per dispatch of the kernels whose name holds match."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if match in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no dispatch of {match!r} in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_report(args):
+    fetch_csv, write_csv, copy_f_csv, copy_w_csv = args.traffic_report
+    import workloads as W
+    shape = W.CONFIGS[args.config]
+    T = args.tokens if args.tokens is not None else shape.tokens
+    family = "mfma" if (args.path == "mfma" or (args.path == "auto" and shape.x_dtype == "bf16"
+                                                and T > 16)) else "gemv"
+    f_kib, nf = counter_means(fetch_csv, KERNEL_MATCH[family])
+    w_kib, nw = counter_means(write_csv, KERNEL_MATCH[family])
+    cf_kib, _ = counter_means(copy_f_csv, COPY_MATCH)
+    cw_kib, _ = counter_means(copy_w_csv, COPY_MATCH)
+    copy_bytes = COPY_MIB * 2**20
+    fetch_scale, write_scale = copy_bytes / (cf_kib * 1024), copy_bytes / (cw_kib * 1024)
+    entry = {
+        "kernel": KERNEL_MATCH[family], "config": args.config, "tokens": T,
+        "sources_sha256": sources_sha(family),
+        "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+        "dispatches": [nf, nw],
+        "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib": round(cf_kib, 1),
+                             "write_kib": round(cw_kib, 1), "fetch_bytes_per_kib": fetch_scale,
+                             "write_bytes_per_kib": write_scale},
+        "traffic_bytes_per_launch": round(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale),
+    }
+    table = {}
+    if os.path.exists(TRAFFIC_FILE):
+        table = json.load(open(TRAFFIC_FILE))
+    table[traffic_key(args.config, T, family)] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(entry))
+
+
+def recorded_traffic(config, tokens, family):
+    """Traffic per launch from profiles/traffic.json, if taken on the current sources."""
+    try:
+        entry = json.load(open(TRAFFIC_FILE)).get(traffic_key(config, tokens, family))
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("sources_sha256") != sources_sha(family):
+        return None
+    return entry["traffic_bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,7 +217,18 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="device copies of the bank (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the copy kernel the PMC counters are calibrated on")
+    ap.add_argument("--traffic-report", nargs=4, metavar="CSV",
+                    help="FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter CSVs: "
+                         "record the dominant kernel's traffic in profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic_report:
+        traffic_report(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -253,6 +362,7 @@ def main():
                 "algorithmic_per_launch": round(gu_bytes),
                 "mfma_TFLOPs": round(tflops, 2)}
     roof["avg_launch_us"] = round(gu_avg_ms * 1e3, 2)
+    roof["traffic"] = recorded_traffic(args.config, T, "mfma" if mfma else "gemv")
 
     res = {
         "metric": "MoE-layer tokens/s; decode HBM GB/s vs peak, prefill MFMA util",

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import DevLayer, check_output, check_routing, log
+from parity import DevLayer, check_output, check_routing, host_bank, log
 
 pytestmark = pytest.mark.gpu
 
@@ -138,6 +138,60 @@ def test_forward_matches_oracle(name, T, path, ov):
     torch.cuda.synchronize()
     ref = layer.oracle(routing=accepted)
     check_output(out, ref["out"], what=f"{name} T={layer.T} {path} ties={ties}")
+
+
+def _constructed_routing_layer():
+    """A 16-expert layer at the 2048/768 shape whose routing is fixed by
+    construction: router row e is 10 * (unit vector e), so a token's logits
+    are 10 * x[t, :16], and each token carries four chosen experts at
+    x = 4, 3, 2, 1 (all other of the first 16 entries 0; the rest N(0,1)).
+    Group sizes hit the grouped-MFMA tile edges: 129 and 128 (two tiles, the
+    second of 1 / 0 rows), 65 and 64 (the full/thin boundary), 33 (two
+    32-row MFMA tiles, the second of 1 row), 1, and ~38-row fill groups.
+    Some block scales are 0 over nonzero codes (their weights dequantise
+    to 0)."""
+    shape = C["c1"].with_(experts=16, top_k=4, name="c1e16_tiles")
+    T, E, k, H = 200, 16, 4, shape.hidden
+    ranges = {0: (0, 129), 1: (0, 128), 2: (129, 194), 3: (0, 64), 4: (64, 97), 5: (197, 198)}
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, :E] = 0.0
+    fill = 6
+    for t in range(T):
+        chosen = [e for e, (lo, hi) in ranges.items() if lo <= t < hi]
+        while len(chosen) < k:
+            if fill not in chosen:
+                chosen.append(fill)
+            fill = 6 + (fill - 5) % 10
+        for j, e in enumerate(chosen):
+            x[t, e] = float(k - j)
+    x = W.round_to_bf16(x)
+    wr = np.zeros((E, H), np.float32)
+    wr[np.arange(E), np.arange(E)] = 10.0
+    bank, _ = host_bank(shape.with_(tokens=0))
+    bank = {key: v.copy() for key, v in bank.items()}
+    I = shape.inter
+    bank["s_gate_up"][0, 1, 3] = 0.0            # gate rows 128..255, k 384..511
+    bank["s_gate_up"][1, I // 128 + 2, 5] = 0.0  # up rows 256..383 of expert 1
+    bank["s_gate_up"][6, 0, 0] = 0.0            # a thin fill group
+    bank["s_down"][2, 4, 1] = 0.0
+    return shape, x, wr, bank
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_forward_tile_edges_and_zero_scales(path):
+    import block_fp8_routed_amd as moe
+    shape, x, wr, bank = _constructed_routing_layer()
+    k = shape.top_k
+    ref_idx = oracle.select_topk(oracle.router_logits(x, wr, None), k)
+    counts = np.bincount(ref_idx.reshape(-1), minlength=shape.experts)
+    assert list(counts[:6]) == [129, 128, 65, 64, 33, 1], counts
+    out = moe.moe_forward(torch.from_numpy(x).to(torch.bfloat16).cuda(), torch.from_numpy(wr).cuda(),
+                          moe.Bank.from_numpy(bank), k, shape.block, path=path)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(x, wr, None, lambda e: W.bank_expert(bank, e), k, shape.inter,
+                           shape.block)
+    check_output(out, ref["out"], what=f"constructed routing, zero scales, {path}")
 
 
 def test_forward_bf16_output():
