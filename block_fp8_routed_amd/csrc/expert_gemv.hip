@@ -58,12 +58,12 @@ struct GateUpMap {
                     LPP == 64, "lanes per pair");
 };
 
-// down lane map: C chunks per row, LPR lanes per row (4 for wide rows), MD
-// chunks per lane, RW rows per wavefront.
+// down lane map: C chunks per row, LPR lanes per row (8 for rows of 512+
+// bytes), MD chunks per lane, RW rows per wavefront.
 template <int I>
 struct DownMap {
   static constexpr int C = I / 16;
-  static constexpr int LPR = C >= 64 ? C / 16 : (C >= 4 ? 4 : C);
+  static constexpr int LPR = C >= 32 ? 8 : (C >= 4 ? 4 : C);
   static constexpr int MD = C / LPR;
   static constexpr int RW = 64 / LPR;
   static_assert(I % 16 == 0 && LPR * MD == C, "chunking");
@@ -335,11 +335,12 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Chunks per lane per row of gate/up: 8 for rows of 2048+ bytes (16 KiB of
-// weights per wavefront), else one chunk per lane.
+// Chunks per lane per row of gate/up: 4 for rows of 2048+ bytes (8 KiB of
+// weights per wavefront, ~108 VGPRs: four wavefronts per SIMD keep enough
+// loads in flight to stream at the read ceiling), else one chunk per lane.
 template <int H>
 constexpr int gate_up_chunks() {
-  return H >= 2048 ? 8 : 1;
+  return H >= 2048 ? 4 : 1;
 }
 
 template <int H, int I, int B, int NT, bool XBF16>
