@@ -55,7 +55,9 @@ inline int router_slices(const Dims& d) {
   }
 }
 
-constexpr int kMetaSelectCounter = 8;
+constexpr int kMetaSelectCounter = 8;  // decode selection's completion counter
+constexpr int kMetaPermCounter = 9;    // multi-block permutation's completion counter
+constexpr int kPermMaxBlocksHost = 16; // blocks of the multi-block permutation (at most)
 
 // Carved workspace. Every region is kAlign-aligned.
 struct Work {
@@ -74,6 +76,7 @@ struct Work {
   void* h;           // [P][I] fp16 SwiGLU output
   float* y;          // [P][H] fp32
   uint16_t* rsplit;  // [3][E][H] bf16 planes of the router weights (MFMA router)
+  int32_t* pblock;   // [2][16][E] per-block expert counts, then per-block bases
 };
 
 inline int64_t max_mfma_tiles(const Dims& d) {
@@ -91,10 +94,14 @@ hipError_t launch_router(const Dims& d, const void* x, const float* wr, const Wo
                          int32_t* zero_word, hipStream_t s);
 // Sums the router slices, adds the bias, selects and gates; optionally writes
 // the final logits.
+// zero_word (may be null): a workspace word the multi-block permutation that
+// follows uses as its completion counter; the top-k kernel zeroes it.
 hipError_t launch_topk(const Dims& d, const float* plogits, const float* bias, int32_t* topk,
-                       float* gates, float* logits_out, hipStream_t s);
+                       float* gates, float* logits_out, int32_t* zero_word, hipStream_t s);
+// counter_zeroed: the completion counter (meta[kMetaPermCounter]) was zeroed
+// by an earlier kernel on the stream; otherwise a one-thread kernel zeroes it.
 hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
-                          hipStream_t s);
+                          bool counter_zeroed, hipStream_t s);
 // Decode sizes: top-k + gates + permutation in one kernel, one workgroup per
 // token; the counter must be zero at launch (launch_router zeroes it).
 bool small_select_permute(const Dims& d);

@@ -14,7 +14,7 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 13;
+constexpr int kRegions = 14;
 
 static void region_sizes(const Dims& d, size_t* sz) {
   sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
@@ -30,6 +30,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[10] = (size_t)d.P * d.I * 2;         // h (fp16)
   sz[11] = (size_t)d.P * d.H * 4;         // y
   sz[12] = router_kind(d) == kRouterMfma ? (size_t)3 * d.E * d.H * 2 : 0;  // router planes
+  sz[13] = (size_t)2 * kPermMaxBlocksHost * d.E * 4;  // permutation block counts and bases
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -62,6 +63,7 @@ Work carve(const Dims& d, void* base) {
   w.h = r[10];
   w.y = static_cast<float*>(r[11]);
   w.rsplit = static_cast<uint16_t*>(r[12]);
+  w.pblock = static_cast<int32_t*>(r[13]);
   return w;
 }
 
@@ -172,10 +174,11 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
     if (launch_select_permute_small(d, w.logits, router_bias, w, tile_rows, s) != hipSuccess)
       return MOE_ERR_HIP;
   } else {
-    if (launch_topk(d, w.logits, router_bias, w.topk, w.gates, nullptr, s) != hipSuccess)
+    if (launch_topk(d, w.logits, router_bias, w.topk, w.gates, nullptr,
+                    w.meta + kMetaPermCounter, s) != hipSuccess)
       return MOE_ERR_HIP;
     if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
-    if (launch_permute(d, w.topk, w, tile_rows, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_permute(d, w.topk, w, tile_rows, true, s) != hipSuccess) return MOE_ERR_HIP;
   }
   if (!rec(events, MOE_EV_PERMUTED, s)) return MOE_ERR_HIP;
   const moe_expert_bank* sh = d.S ? shared : nullptr;
@@ -201,7 +204,7 @@ moe_status moe_route(const void* x, const float* router_w, const float* router_b
   const Work w = carve(d, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_router(d, x, router_w, w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_topk(d, w.logits, router_bias, topk_idx, gates, logits, s) != hipSuccess)
+  if (launch_topk(d, w.logits, router_bias, topk_idx, gates, logits, nullptr, s) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -220,7 +223,7 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t* offsets, int32_t* pair,
   w.offsets = offsets;
   w.pair = pair;
   w.inv = inv;
-  if (launch_permute(d, topk_idx, w, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_permute(d, topk_idx, w, 0, false, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }

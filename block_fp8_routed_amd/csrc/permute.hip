@@ -1,21 +1,12 @@
-// permute.hip — the token -> expert permutation kernels (permute_body), and
-// the fused decode kernel that selects every token's experts and permutes in
-// one workgroup (permute_wave).
+// permute.hip — the token -> expert permutation: the multi-block kernels for
+// larger batches (perm_count, perm_scatter), and the fused decode kernel that
+// selects every token's experts and permutes in the last token's workgroup
+// (permute_wave).
 #include "layer.hpp"
 #include "permute.hpp"
 #include "select.hpp"
 
 namespace moe {
-
-template <int W>
-__global__ __launch_bounds__(64 * W) void permute_kernel(
-    const int32_t* __restrict__ topk, int64_t T, int k, int E, int S,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
-    int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
-    int32_t* __restrict__ tiles, int tile_rows) {
-  extern __shared__ int32_t lds[];
-  permute_body<W>(topk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, lds);
-}
 
 // Decode sizes (T <= 16, E <= 512): workgroup t (one wavefront) selects token
 // t's experts and gates (select_token) and writes them out. Selection is most
@@ -26,7 +17,7 @@ __global__ __launch_bounds__(64 * W) void permute_kernel(
 // selection back and builds the permutation alone (permute_wave). No
 // workgroup ever waits for another. *counter must be zero at launch (the
 // router kernel, launched just before on the same stream, zeroes it). Same
-// results as topk_softmax + permute_kernel.
+// results as topk_softmax + the multi-block permutation.
 template <int NV>
 __global__ __launch_bounds__(64) void select_permute_small(
     const float* __restrict__ plog, int slices, const float* __restrict__ bias, int64_t T, int k,
@@ -74,19 +65,184 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
-                          hipStream_t s) {
-  if (d.E <= 512) {
-    const size_t lds = (size_t)(16 * d.E + d.E + 64) * sizeof(int32_t);
-    permute_kernel<16><<<1, 1024, lds, s>>>(topk, d.T, d.k, d.E, d.S, w.offsets, w.pair, w.inv,
-                                            w.rtok, w.meta, reinterpret_cast<int4*>(w.gdesc),
-                                            w.tiles, tile_rows);
-  } else {
-    const size_t lds = (size_t)(8 * d.E + d.E + 64) * sizeof(int32_t);
-    permute_kernel<8><<<1, 512, lds, s>>>(topk, d.T, d.k, d.E, d.S, w.offsets, w.pair, w.inv,
-                                          w.rtok, w.meta, reinterpret_cast<int4*>(w.gdesc),
-                                          w.tiles, tile_rows);
+// ------------------------------------------------------ multi-block (T > 16)
+// The same permutation as permute_body, spread over NB blocks of consecutive
+// slots so that large batches are not serialised on one compute unit.
+//   perm_count: block b histograms its slots (LDS counters) into
+//     bcnt[b][E]; then it publishes them (device-scope release, one atomic
+//     increment of *counter) and the block that completes the count
+//     (acquire) turns the histograms into offsets, per-block bases
+//     bbase[b][e] = offsets[e] + (rows of e in blocks before b), group
+//     descriptors and MFMA row tiles. No block waits for another. *counter
+//     must be zero at launch.
+//   perm_scatter: block b places its slots: its wavefronts take consecutive
+//     sub-ranges, count per (wavefront, expert), take exclusive prefixes over
+//     wavefronts on top of bbase[b][e], and walk their slots in order with
+//     ballot peer ranks (as permute_body), so rows keep slot order.
+constexpr int kPermBlockSlots = 512;  // slots per block (at most kPermMaxBlocks blocks)
+constexpr int kPermMaxBlocks = kPermMaxBlocksHost;
+
+inline int perm_blocks(int64_t TK) {
+  int64_t nb = (TK + kPermBlockSlots - 1) / kPermBlockSlots;
+  return (int)(nb < 1 ? 1 : (nb > kPermMaxBlocks ? kPermMaxBlocks : nb));
+}
+
+__global__ __launch_bounds__(1024) void perm_count(
+    const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb,
+    int32_t* bcnt, int32_t* counter, int32_t* __restrict__ offsets, int32_t* bbase,
+    int32_t* __restrict__ meta, int4* __restrict__ gdesc, int32_t* __restrict__ tiles,
+    int tile_rows) {
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t tmp[64];
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int64_t TK = T * k;
+  const int64_t per = (TK + nb - 1) / nb;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = lo + per < TK ? lo + per : TK;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  for (int64_t s = lo + tid; s < hi; s += 1024) {
+    const int e = topk[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
   }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) bcnt[(size_t)blockIdx.x * E + e] = cnt[e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nb - 1;
+  __syncthreads();
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // one expert per thread (E <= 1024): prefix over blocks, in block order
+  const int e = tid;
+  int c = 0;
+  int32_t pre[kPermMaxBlocks];
+#pragma unroll
+  for (int b = 0; b < kPermMaxBlocks; ++b) {
+    const int v = (e < E && b < nb) ? bcnt[(size_t)b * E + e] : 0;
+    pre[b] = c;
+    c += v;
+  }
+  int total;
+  const int off = block_excl_scan<16>(c, tmp, &total);
+  if (e < E) {
+    offsets[e] = off;
+#pragma unroll
+    for (int b = 0; b < kPermMaxBlocks; ++b)
+      if (b < nb) bbase[(size_t)b * E + e] = off + pre[b];
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    offsets[E + 1] = (int)(total + S * T);
+  }
+  // non-empty groups and MFMA row tiles, ascending expert, shared last
+  const int nf = (e < E && c > 0) ? 1 : 0;
+  const int nt = (e < E && tile_rows > 0) ? (c + tile_rows - 1) / tile_rows : 0;
+  int nact, ntile = 0;
+  const int apos = block_excl_scan<16>(nf, tmp, &nact);
+  const int tpos = tile_rows > 0 ? block_excl_scan<16>(nt, tmp, &ntile) : 0;
+  if (nf) gdesc[apos] = make_int4(e, off, c, 0);
+  for (int m = 0, tp = tpos; m < nt; ++m, ++tp) {
+    tiles[2 * tp] = e;
+    tiles[2 * tp + 1] = off + m * tile_rows;
+  }
+  int nshared_tiles = 0;
+  if (S && tile_rows > 0) {
+    nshared_tiles = (int)((T + tile_rows - 1) / tile_rows);
+    for (int i = tid; i < nshared_tiles; i += 1024) {
+      tiles[2 * (ntile + i)] = E;
+      tiles[2 * (ntile + i) + 1] = (int)(total + (int64_t)i * tile_rows);
+    }
+  }
+  if (tid == 0) {
+    if (S) gdesc[nact] = make_int4(E, total, (int)T, 0);
+    meta[0] = nact + S;
+    meta[1] = ntile + nshared_tiles;
+  }
+  for (int y = nact + S + tid; y < E + 2; y += 1024) gdesc[y] = make_int4(-1, 0, 0, 0);
+}
+
+// lds: (16 * E) int32 of shared memory
+__global__ __launch_bounds__(1024) void perm_scatter(
+    const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb,
+    const int32_t* __restrict__ bbase, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ pair, int32_t* __restrict__ inv, int32_t* __restrict__ rtok) {
+  extern __shared__ int32_t wcnt[];  // [16][E]
+  constexpr int W = 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t TK = T * k;
+  const int64_t per = (TK + nb - 1) / nb;
+  const int64_t blo = (int64_t)blockIdx.x * per, bhi = blo + per < TK ? blo + per : TK;
+  const int64_t wper = (bhi - blo + W - 1) / W;
+  const int64_t lo = blo + w * wper < bhi ? blo + w * wper : bhi;
+  const int64_t hi = lo + wper < bhi ? lo + wper : bhi;
+  for (int i = tid; i < W * E; i += 1024) wcnt[i] = 0;
+  __syncthreads();
+  for (int64_t s = lo + lane; s < hi; s += 64) {
+    const int e = topk[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&wcnt[w * E + e], 1);
+  }
+  __syncthreads();
+  // exclusive prefix over wavefronts on top of the block's base
+  for (int e = tid; e < E; e += 1024) {
+    int run = bbase[(size_t)blockIdx.x * E + e];
+    for (int ww = 0; ww < W; ++ww) {
+      const int c = wcnt[ww * E + e];
+      wcnt[ww * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
+  for (int64_t b0 = lo; b0 < hi; b0 += 64) {
+    const int64_t s = b0 + lane;
+    const int e_in = s < hi ? topk[s] : 0;
+    const bool ok = s < hi && (unsigned)e_in < (unsigned)E;
+    const int e = ok ? e_in : 0;
+    if (s < hi && !ok) inv[s] = -1;
+    unsigned long long peers = __ballot(ok);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long m = __ballot(ok && bit);
+      peers &= bit ? m : ~m;
+    }
+    if (!ok) peers = 0;
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    const int leader = ok ? (__ffsll((long long)peers) - 1) : lane;
+    int old = 0;
+    if (ok && lane == leader) old = atomicAdd(&wcnt[w * E + e], __popcll(peers));
+    old = __shfl(old, leader, 64);
+    if (ok) {
+      const int pos = old + rank;
+      pair[pos] = (int)s;
+      inv[s] = pos;
+      rtok[pos] = (int)(s / k);
+    }
+  }
+  if (S && blockIdx.x == 0) {  // the shared group: slot TK + t is token t
+    const int total = offsets[E];
+    for (int64_t t = tid; t < T; t += 1024) {
+      pair[total + t] = (int)(TK + t);
+      inv[TK + t] = (int)(total + t);
+      rtok[total + t] = (int)t;
+    }
+  }
+}
+
+__global__ void zero_word(int32_t* p) { *p = 0; }
+
+hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
+                          bool counter_zeroed, hipStream_t s) {
+  int32_t* counter = w.meta + kMetaPermCounter;
+  if (!counter_zeroed) zero_word<<<1, 1, 0, s>>>(counter);
+  const int nb = perm_blocks(d.T * d.k);
+  perm_count<<<nb, 1024, 0, s>>>(topk, d.T, d.k, d.E, d.S, nb, w.pblock, counter, w.offsets,
+                                 w.pblock + (size_t)kPermMaxBlocks * d.E, w.meta,
+                                 reinterpret_cast<int4*>(w.gdesc), w.tiles, tile_rows);
+  perm_scatter<<<nb, 1024, (size_t)16 * d.E * sizeof(int32_t), s>>>(
+      topk, d.T, d.k, d.E, d.S, nb, w.pblock + (size_t)kPermMaxBlocks * d.E, w.offsets, w.pair,
+      w.inv, w.rtok);
   return hipGetLastError();
 }
 

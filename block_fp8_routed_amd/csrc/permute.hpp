@@ -1,27 +1,20 @@
-// permute.hpp — token -> expert permutation (the per-expert fan-out of the
-// colizig page's "Features": experts are evaluated one group at a time, and
-// the threaded result is bit-identical to the serial one).
+// permute.hpp — token -> expert permutation helpers (the per-expert fan-out of
+// the colizig page's "Features": experts are evaluated one group at a time,
+// and the threaded result is bit-identical to the serial one).
 //
 // Slot s = t*k + j is the j-th choice of token t. The permutation groups the
 // slots by expert; inside a group the slots stay in ascending order (stable),
 // so a group's rows are its tokens in ascending order. The always-on shared
 // expert, when present, is group E with slots T*k + t.
 //
-// One workgroup does it in four passes over LDS:
-//   1. count:   wave w takes a contiguous slot range and adds 1 per slot to its
-//               own counter row cnt[w][e] (LDS integer atomics, order-free);
-//   2. scan:    exclusive scan over (expert-major, wave-minor) gives each
-//               (wave, expert) its first row;
-//   3. scatter: each wave walks its slots in order, 64 at a time; lanes with
-//               the same expert find each other with one ballot per expert-id
-//               bit, take their rank among lower lanes, and the group's first
-//               lane advances the counter, so rows keep slot order;
-//   4. lists:   a descriptor (group, first row, rows) per non-empty group
-//               (ascending, shared last, then group = -1 up to E+2 entries)
-//               and, for the MFMA family, one (group, first row) entry per
-//               tile of tile_rows rows.
-// Every permuted row also gets its token id (rtok), so the expert kernels
-// gather activations without dividing slot ids.
+// Every kernel that builds it counts per expert (LDS counters), takes
+// exclusive scans for the groups' first rows, and places slots in slot order:
+// lanes with the same expert find each other with one ballot per expert-id
+// bit and take their rank among lower lanes, and the group's first lane
+// advances the counter. It also emits a descriptor (group, first row, rows)
+// per non-empty group (ascending, shared last, then group = -1 up to E+2
+// entries) and, for the MFMA family, one (group, first row) entry per tile of
+// tile_rows rows, and the token of every permuted row (rtok).
 // Expert ids outside [0, E) (possible only through moe_permute's caller) are
 // left out of every group with inv = -1; the shared group then starts right
 // after the last valid routed row. Nothing is accessed out of bounds.
@@ -59,147 +52,6 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
   __syncthreads();
   return res;
 }
-
-// lds: (W*E + E + 64) int32 of shared memory. topk may live in global or
-// shared memory (it is only read).
-template <int W>
-__device__ __forceinline__ void permute_body(
-    const int32_t* topk, int64_t T, int k, int E, int S, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ pair, int32_t* __restrict__ inv, int32_t* __restrict__ rtok,
-    int32_t* __restrict__ meta, int4* __restrict__ gdesc, int32_t* __restrict__ tiles,
-    int tile_rows, int32_t* lds) {
-  int32_t* cnt = lds;          // [W][E]
-  int32_t* base = lds + W * E; // [E]
-  int32_t* tmp = base + E;     // [64]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  constexpr int NTH = 64 * W;
-  const int64_t TK = T * k;
-
-  for (int i = tid; i < W * E; i += NTH) cnt[i] = 0;
-  __syncthreads();
-
-  // 1. count
-  const int64_t per = (TK + W - 1) / W;
-  const int64_t lo = min(TK, (int64_t)w * per), hi = min(TK, lo + per);
-  for (int64_t s = lo + lane; s < hi; s += 64) {
-    const int e = topk[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w * E + e], 1);
-  }
-  __syncthreads();
-
-  // 2. scan: column prefix over waves, then over experts
-  for (int e = tid; e < E; e += NTH) {
-    int run = 0;
-    for (int ww = 0; ww < W; ++ww) {
-      const int c = cnt[ww * E + e];
-      cnt[ww * E + e] = run;
-      run += c;
-    }
-    base[e] = run;  // count of e, for now
-  }
-  __syncthreads();
-  const int ept = (E + NTH - 1) / NTH;
-  const int e0 = tid * ept;
-  int local = 0;
-  for (int i = 0; i < ept; ++i)
-    if (e0 + i < E) local += base[e0 + i];
-  int total;
-  int run = block_excl_scan<W>(local, tmp, &total);
-  for (int i = 0; i < ept; ++i) {
-    if (e0 + i < E) {
-      const int c = base[e0 + i];
-      offsets[e0 + i] = run;
-      base[e0 + i] = run;
-      run += c;
-    }
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    offsets[E + 1] = (int)(total + S * T);
-  }
-  __syncthreads();
-  for (int i = tid; i < W * E; i += NTH) cnt[i] += base[i % E];
-  __syncthreads();
-
-  // 3. stable scatter
-  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
-  for (int64_t b0 = lo; b0 < hi; b0 += 64) {
-    const int64_t s = b0 + lane;
-    const int e_in = s < hi ? topk[s] : 0;
-    const bool ok = s < hi && (unsigned)e_in < (unsigned)E;
-    const int e = ok ? e_in : 0;
-    if (s < hi && !ok) inv[s] = -1;
-    unsigned long long peers = __ballot(ok);
-    for (int b = 0; b < ebits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const unsigned long long m = __ballot(ok && bit);
-      peers &= bit ? m : ~m;
-    }
-    if (!ok) peers = 0;
-    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    const int leader = ok ? (__ffsll((long long)peers) - 1) : lane;
-    int old = 0;
-    if (ok && lane == leader) old = atomicAdd(&cnt[w * E + e], __popcll(peers));
-    old = __shfl(old, leader, 64);
-    if (ok) {
-      const int pos = old + rank;
-      pair[pos] = (int)s;
-      inv[s] = pos;
-      rtok[pos] = (int)(s / k);
-    }
-  }
-  if (S) {
-    for (int64_t t = tid; t < T; t += NTH) {
-      pair[total + t] = (int)(TK + t);
-      inv[TK + t] = (int)(total + t);
-      rtok[total + t] = (int)t;
-    }
-  }
-
-  // 4. non-empty groups and MFMA row tiles
-  int nf = 0, nt = 0;
-  for (int i = 0; i < ept; ++i) {
-    const int e = e0 + i;
-    if (e < E) {
-      const int c = (e + 1 < E ? base[e + 1] : total) - base[e];
-      nf += c > 0;
-      if (tile_rows > 0) nt += (c + tile_rows - 1) / tile_rows;
-    }
-  }
-  int nact;
-  int apos = block_excl_scan<W>(nf, tmp, &nact);
-  int ntile = 0;
-  int tpos = tile_rows > 0 ? block_excl_scan<W>(nt, tmp, &ntile) : 0;
-  for (int i = 0; i < ept; ++i) {
-    const int e = e0 + i;
-    if (e < E) {
-      const int c = (e + 1 < E ? base[e + 1] : total) - base[e];
-      if (c > 0) gdesc[apos++] = make_int4(e, base[e], c, 0);
-      if (tile_rows > 0) {
-        for (int m = 0; m < c; m += tile_rows) {
-          tiles[2 * tpos] = e;
-          tiles[2 * tpos + 1] = base[e] + m;
-          ++tpos;
-        }
-      }
-    }
-  }
-  int nshared_tiles = 0;
-  if (S && tile_rows > 0) {
-    nshared_tiles = (int)((T + tile_rows - 1) / tile_rows);
-    for (int i = tid; i < nshared_tiles; i += NTH) {
-      tiles[2 * (ntile + i)] = E;
-      tiles[2 * (ntile + i) + 1] = (int)(total + (int64_t)i * tile_rows);
-    }
-  }
-  if (tid == 0) {
-    if (S) gdesc[nact] = make_int4(E, total, (int)T, 0);
-    meta[0] = nact + S;
-    meta[1] = ntile + nshared_tiles;
-  }
-  for (int y = nact + S + tid; y < E + 2; y += NTH) gdesc[y] = make_int4(-1, 0, 0, 0);
-}
-
 
 // Exclusive prefix sum over the 64 lanes of a wavefront; *total gets the sum.
 __device__ __forceinline__ int wave_excl_scan(int v, int* total) {

@@ -11,19 +11,21 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ pl
                                                    int32_t* __restrict__ topk,
                                                    float* __restrict__ gates,
                                                    float* __restrict__ logits_out, int64_t T,
-                                                   int E, int k) {
+                                                   int E, int k, int32_t* __restrict__ zero_word) {
+  if (zero_word && blockIdx.x == 0 && threadIdx.x == 0) *zero_word = 0;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, logits_out, nullptr);
 }
 
 hipError_t launch_topk(const Dims& d, const float* plog, const float* bias, int32_t* topk,
-                       float* gates, float* logits_out, hipStream_t s) {
+                       float* gates, float* logits_out, int32_t* zero_word, hipStream_t s) {
   const dim3 grid((unsigned)((d.T + 3) / 4));
   const int ns = router_slices(d);
   const int nv = (d.E + 63) / 64;
 #define MOE_TOPK(NV) \
-  topk_softmax<NV><<<grid, 256, 0, s>>>(plog, ns, bias, topk, gates, logits_out, d.T, d.E, d.k)
+  topk_softmax<NV><<<grid, 256, 0, s>>>(plog, ns, bias, topk, gates, logits_out, d.T, d.E, d.k, \
+                                        zero_word)
   if (nv <= 1)
     MOE_TOPK(1);
   else if (nv <= 2)
