@@ -4,49 +4,63 @@
 // expert with weight 1 (colizig page, model table: "top-10 + 1 shared").
 // Summed in fp32 in a fixed order (slots j = 0..k-1, then the shared expert),
 // so the result does not depend on how the expert passes were scheduled; one
-// rounding to the output dtype at the end.
+// rounding to the output dtype at the end. y rows are fp16 (written so by the
+// down passes).
 #include "device.hpp"
 #include "layer.hpp"
 
 namespace moe {
 
+// Thread i of a workgroup sums 8 consecutive outputs of one token (16-byte
+// fp16 loads of y, fp32 accumulation).
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                      const float* __restrict__ gates,
                                                      const int32_t* __restrict__ inv, int64_t T,
                                                      int H, int k, int S, void* __restrict__ out) {
   const int64_t t = blockIdx.x;
-  const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (n >= H) return;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float g = gates[t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)inv[t * k + j] * H + n);
-    a0 = fmaf(g, v.x, a0);
-    a1 = fmaf(g, v.y, a1);
-    a2 = fmaf(g, v.z, a2);
-    a3 = fmaf(g, v.w, a3);
-  }
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = 0.f;
+  auto add = [&](const uint4 v, float g) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t p = __builtin_bit_cast(f16x2_t, w[i]);
+      a[2 * i] = fmaf(g, (float)p[0], a[2 * i]);
+      a[2 * i + 1] = fmaf(g, (float)p[1], a[2 * i + 1]);
+    }
+  };
+  for (int j = 0; j < k; ++j)
+    add(ld16(y + (size_t)inv[t * k + j] * H + n), gates[t * k + j]);
   if (S) {
-    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)inv[T * k + t] * H + n);
-    a0 += v.x;
-    a1 += v.y;
-    a2 += v.z;
-    a3 += v.w;
+    const uint4 v = ld16(y + (size_t)inv[T * k + t] * H + n);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t p = __builtin_bit_cast(f16x2_t, w[i]);
+      a[2 * i] += (float)p[0];
+      a[2 * i + 1] += (float)p[1];
+    }
   }
   if (OUT_BF16) {
-    uint2 o;
-    o.x = f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16);
-    o.y = f32_to_bf16_bits(a2) | (f32_to_bf16_bits(a3) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + t * H + n) = o;
+    uint4 o;
+    o.x = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+    o.y = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+    o.z = f32_to_bf16_bits(a[4]) | (f32_to_bf16_bits(a[5]) << 16);
+    o.w = f32_to_bf16_bits(a[6]) | (f32_to_bf16_bits(a[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * H + n) = o;
   } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * H + n) =
-        make_float4(a0, a1, a2, a3);
+    float* o = reinterpret_cast<float*>(out) + t * H + n;
+    *reinterpret_cast<float4*>(o) = make_float4(a[0], a[1], a[2], a[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(a[4], a[5], a[6], a[7]);
   }
 }
 
 hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s) {
-  const dim3 grid((unsigned)d.T, (d.H + 1023) / 1024);
+  const dim3 grid((unsigned)d.T, (d.H + 2047) / 2048);
   if (d.out_bf16)
     combine_kernel<true><<<grid, 256, 0, s>>>(w.y, w.gates, w.inv, d.T, d.H, d.k, d.S, out);
   else

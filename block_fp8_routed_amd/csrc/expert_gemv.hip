@@ -25,7 +25,8 @@
 //            use fp32 FMA. h is written as fp16 (saturated at +-65504), row-
 //            major [P][I] in permuted row order, the form the MFMA family uses.
 //   down:    y[row][n] = sum_i h[row][i] * Wd[n][i]: exact fp16 weight pairs
-//            meet h in v_dot2c_f32_f16; y is fp32 [P][H].
+//            meet h in v_dot2c_f32_f16; y is written as fp16 [P][H] (saturated
+//            at +-65504), the form the combine reads.
 // Tokens of a group are taken NT at a time; a larger group takes several
 // passes over the weights already held in registers.
 #include <algorithm>
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
 template <int H, int I, int B, int NT>
 __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __restrict__ gdesc,
                                                 int E, const uint16_t* __restrict__ h,
-                                                float* __restrict__ y) {
+                                                uint16_t* __restrict__ y) {
   using D = DownMap<I>;
   constexpr int LPR = D::LPR, MD = D::MD, RW = D::RW, SPG = H / RW;
   static_assert(H % RW == 0, "rows must split evenly into slabs");
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
       for (int t = 0; t < NT; ++t) {
         if (t >= nv) continue;
         const float v = seg_sum<LPR>(acc[t]);
-        if (sub == LPR - 1) y[(size_t)(r0 + t0 + t) * H + row] = v;
+        if (sub == LPR - 1) y[(size_t)(r0 + t0 + t) * H + row] = f32_to_f16_sat(v);
       }
     }
     t0 += NT;

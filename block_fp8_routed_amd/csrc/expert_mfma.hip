@@ -20,9 +20,10 @@
 // so nothing is rounded on the way in; SwiGLU is applied to the accumulator
 // registers and h is written as fp16 [P][I] (11-bit significand, saturated at
 // +-65504). down runs fp16 MFMA on h (the weights are exact in fp16 as well)
-// and writes y as fp32 [P][H]. h is the one intermediate rounded below fp32:
-// fp16 keeps its relative error at 2^-11, which leaves the layer's output well
-// inside its tolerance (max error <= 1e-2 x RMS); bf16 would use up most of it.
+// and writes y as fp16 [P][H] (saturated the same way). h and y are the two
+// intermediates rounded below fp32: fp16 keeps their relative error at 2^-11,
+// which leaves the layer's output well inside its tolerance (max error <=
+// 1e-2 x RMS); bf16 would use up most of it.
 //
 // MFMA operand layout (32x32x16): lane L supplies row L%32 of A and column
 // L%32 of B, each as 8 k of the 16 (k = 8*(L/32) .. +7); lane L of the result
@@ -355,9 +356,10 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         h[n0 + S::brow(wn, 0) + l32] =
             f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
       } else {
-        float* y = reinterpret_cast<float*>(out) + (size_t)(r0 + row) * H;
+        uint16_t* y = reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + row) * H;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) y[n0 + S::brow(wn, nb) + l32] = acc[m][nb][v] * unit[nb];
+        for (int nb = 0; nb < NBW; ++nb)
+          y[n0 + S::brow(wn, nb) + l32] = f32_to_f16_sat(acc[m][nb][v] * unit[nb]);
       }
     }
 }

@@ -28,7 +28,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[8] = (size_t)d.P * 4;                // inv
   sz[9] = (size_t)max_mfma_tiles(d) * 8;  // tiles
   sz[10] = (size_t)d.P * d.I * 2;         // h (fp16)
-  sz[11] = (size_t)d.P * d.H * 4;         // y
+  sz[11] = (size_t)d.P * d.H * 2;         // y (fp16)
   sz[12] = router_kind(d) == kRouterMfma ? (size_t)3 * d.E * d.H * 2 : 0;  // router planes
   sz[13] = (size_t)2 * kPermMaxBlocksHost * d.E * 4;  // permutation block counts and bases
 }
@@ -61,7 +61,7 @@ Work carve(const Dims& d, void* base) {
   w.inv = static_cast<int32_t*>(r[8]);
   w.tiles = static_cast<int32_t*>(r[9]);
   w.h = r[10];
-  w.y = static_cast<float*>(r[11]);
+  w.y = static_cast<uint16_t*>(r[11]);
   w.rsplit = static_cast<uint16_t*>(r[12]);
   w.pblock = static_cast<int32_t*>(r[13]);
   return w;
