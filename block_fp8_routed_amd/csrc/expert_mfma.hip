@@ -120,8 +120,9 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 // block's scale. Entering scale block kb, the accumulators of a 32-column
 // tile are multiplied by s(kb-1) / s(kb) before its products are added, and
 // by the last scale at the end; the result equals sum_kb s(kb) * P(kb) up to
-// fp32 rounding (one extra rounding per block). A block with scale 0 adds
-// nothing: its codes are masked to +0.
+// fp32 rounding (the ratio costs about two roundings per block). A block
+// with scale 0 adds nothing: its codes are zeroed when the tile is written to
+// LDS.
 // Rows past the group's end are computed with the rest (they repeat the last
 // row) and never stored.
 constexpr int kTN = 256;            // weight rows per tile
@@ -200,7 +201,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   // those of i = 0 (GU: B rows 128 .. 255 are the up rows). Byte offsets from
   // the wave-uniform bases fit in 32 bits (checked on the host for the
   // activation rows; a weight matrix is below 2 GiB).
-  const uint8_t* abase = reinterpret_cast<const uint8_t*>(act);
+  const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(act, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(W, (uint32_t)((GU ? 2 * I : H) * K));
   uint32_t asrc[AC];
   const int ar0 = tid >> 3, ac0 = tid & 7;
   const int adst0 = ar0 * (kKS * 2) + 16 * (ac0 ^ ((ar0 >> 1) & 7));
@@ -213,16 +215,34 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   struct Regs {
     uint4 a[AC], b[BC];
   };
+  // scale rows of this thread's B chunks: chunk i of every thread lies in the
+  // same 128-row block (GU: the gate block, then the up block), so these are
+  // uniform; a block of scale 0 has its codes zeroed when written to LDS
+  const float* bscale[BC];
+#pragma unroll
+  for (int i = 0; i < BC; ++i) {
+    const int wrow = GU ? (i == 0 ? n0 : I + n0) : n0 + 128 * i;
+    bscale[i] = Sc + (size_t)(wrow / kBK) * (K / kBK);
+  }
   auto fetch = [&](Regs& R, int st) {
     st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
 #pragma unroll
-    for (int i = 0; i < AC; ++i) R.a[i] = ld16(abase + (asrc[i] + (uint32_t)(st * kKS * 2)));
+    for (int i = 0; i < AC; ++i) R.a[i] = buffer_ld16(arsrc, asrc[i], (uint32_t)(st * kKS * 2));
 #pragma unroll
-    for (int i = 0; i < BC; ++i) R.b[i] = ld16(W + (bsrc0 + bstep(i) + (uint32_t)(st * kKS)));
+    for (int i = 0; i < BC; ++i)
+      R.b[i] = buffer_ld16(brsrc, bsrc0, bstep(i) + (uint32_t)(st * kKS));
   };
-  auto put = [&](const Regs& R, int buf) {
+  auto put = [&](Regs& R, int buf, int st) {
     uint8_t* A = lds + buf * (kAStage + kBStage);
     uint8_t* B = A + kAStage;
+    bool zero = false;
+#pragma unroll
+    for (int i = 0; i < BC; ++i) zero |= bscale[i][st >> 1] == 0.f;
+    if (zero) {  // rare: a zero block scale (uniform branch)
+#pragma unroll
+      for (int i = 0; i < BC; ++i)
+        if (bscale[i][st >> 1] == 0.f) R.b[i] = make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + adst0 + 64 * (kKS * 2) * i) = R.a[i];
 #pragma unroll
@@ -251,13 +271,11 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[m][nb][v] = 0.f;
-  float unit[NBW];     // scale the accumulators are expressed in
-  uint32_t keep[NBW];  // all ones, or 0 for a block of scale 0 (its codes are masked to +0)
-  float snext[NBW];    // scales of the next block, read one block ahead
+  float unit[NBW];   // scale the accumulators are expressed in
+  float snext[NBW];  // scales of the next block, read one block ahead
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     unit[nb] = 0.f;
-    keep[nb] = 0u;
     snext[nb] = srow[nb][0];
   }
 
@@ -271,14 +289,14 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         const float sn = snext[nb];
         if (st + 2 < NS) snext[nb] = srow[nb][(st >> 1) + 1];
         const bool on = sn != 0.f;
-        // unit 0 (nothing added yet): the accumulators are 0 and stay 0
-        const float r = on ? unit[nb] / sn : 1.f;
+        // unit 0 (nothing added yet): the accumulators are 0 and stay 0; a
+        // block of scale 0 (codes zeroed in LDS) leaves the unit as it is
+        const float r = on ? unit[nb] * __builtin_amdgcn_rcpf(sn) : 1.f;
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[m][nb][v] *= r;
         unit[nb] = on ? sn : unit[nb];
-        keep[nb] = on ? 0xffffffffu : 0u;
       }
     }
     const uint8_t* A = lds + (st & 1) * (kAStage + kBStage);
@@ -295,8 +313,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         typename O::T bf[NBW];
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
-          bf[nb] = hh ? O::cvt(braw[nb].z & keep[nb], braw[nb].w & keep[nb])
-                      : O::cvt(braw[nb].x & keep[nb], braw[nb].y & keep[nb]);
+          bf[nb] = hh ? O::cvt(braw[nb].z, braw[nb].w) : O::cvt(braw[nb].x, braw[nb].y);
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
           const uint4 af = *reinterpret_cast<const uint4*>(A + afr + 32 * m * (kKS * 2) +
@@ -311,16 +328,16 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   if (S::DEPTH == 1) {
     Regs R;
     fetch(R, 0);
-    put(R, 0);
+    put(R, 0, 0);
     __syncthreads();
     for (int st = 0; st < NS; st += 2) {
       fetch(R, st + 1);
       compute(st, true);
-      put(R, 1);
+      put(R, 1, st + 1);
       __syncthreads();
       fetch(R, st + 2);
       compute(st + 1, false);
-      if (st + 2 < NS) put(R, 0);
+      if (st + 2 < NS) put(R, 0, st + 2);
       __syncthreads();
     }
   } else {
@@ -329,16 +346,16 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     Regs R0, R1;
     fetch(R0, 0);
     fetch(R1, 1);
-    put(R0, 0);
+    put(R0, 0, 0);
     __syncthreads();
     for (int st = 0; st < NS; st += 2) {
       fetch(R0, st + 2);
       compute(st, true);
-      put(R1, 1);
+      put(R1, 1, st + 1);
       __syncthreads();
       fetch(R1, st + 3);
       compute(st + 1, false);
-      if (st + 2 < NS) put(R0, 0);
+      if (st + 2 < NS) put(R0, 0, st + 2);
       __syncthreads();
     }
   }
