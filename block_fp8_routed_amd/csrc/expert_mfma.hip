@@ -99,7 +99,7 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 //     (two 32-row MFMA tiles); stages fetched one ahead.
 //   thin (at most 64 rows, where the pass streams weights): rows 32 wm ..
 //     + 31 (one MFMA tile); the A tile has 64 rows, and stages are fetched
-//     two ahead, so more bytes are in flight while the weights stream.
+//     four ahead, so more bytes are in flight while the weights stream.
 // K runs in stages of 64 (half a scale block). A stage's A tile and B (256 x
 // 64 bytes) tile are fetched global -> registers ahead of use and written into
 // the other of two LDS buffers after the current stage's MFMAs; one barrier
@@ -171,7 +171,7 @@ struct TileShape {
   static constexpr int BC = kTN * 4 / kPassThreads; // B chunks per thread per stage
   static constexpr int MW = THIN ? 1 : 2;     // 32-row MFMA tiles per wavefront
   static constexpr int NBW = 2;               // 32-column MFMA tiles per wavefront
-  static constexpr int DEPTH = THIN ? 2 : 1;  // stages fetched ahead
+  static constexpr int DEPTH = THIN ? 4 : 1;  // stages fetched ahead
   // tile-relative first row of this wavefront's rows
   static __device__ __forceinline__ int arow0(int wm) { return (THIN ? 32 : 64) * wm; }
   // tile-relative weight row of this wavefront's MFMA tile nb
@@ -341,22 +341,25 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
       __syncthreads();
     }
   } else {
-    // stage st + 1 is in flight while stage st is computed and stage st + 2
-    // is requested; the register sets alternate, so the loop runs in pairs
-    Regs R0, R1;
-    fetch(R0, 0);
-    fetch(R1, 1);
-    put(R0, 0, 0);
+    // a ring of DEPTH register sets: while stage st is computed, stages
+    // st + 1 .. st + DEPTH are in flight (stage s lives in set s % DEPTH);
+    // the loop is unrolled by DEPTH so the sets are fixed registers
+    constexpr int D = S::DEPTH;
+    static_assert(NS % D == 0, "stage count must be a multiple of the prefetch depth");
+    Regs R[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) fetch(R[j], j);
+    put(R[0], 0, 0);
     __syncthreads();
-    for (int st = 0; st < NS; st += 2) {
-      fetch(R0, st + 2);
-      compute(st, true);
-      put(R1, 1, st + 1);
-      __syncthreads();
-      fetch(R1, st + 3);
-      compute(st + 1, false);
-      if (st + 2 < NS) put(R0, 0, st + 2);
-      __syncthreads();
+    for (int st0 = 0; st0 < NS; st0 += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int st = st0 + j;
+        fetch(R[j], st + D);  // set j held stage st, written to LDS before this stage
+        compute(st, (st & 1) == 0);
+        if (st + 1 < NS) put(R[(j + 1) % D], (st + 1) & 1, st + 1);
+        __syncthreads();
+      }
     }
   }
 
