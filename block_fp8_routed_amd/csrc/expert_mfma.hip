@@ -122,7 +122,10 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 // by the last scale at the end; the result equals sum_kb s(kb) * P(kb) up to
 // fp32 rounding (the ratio costs about two roundings per block). A block
 // with scale 0 adds nothing: its codes are zeroed when the tile is written to
-// LDS.
+// LDS. The tile's scales (two scale rows, K / 128 each) are copied to LDS
+// once at the start: read from global memory inside the loop, each would be
+// a vector load issued behind the weight prefetches, and as vector loads
+// complete in order, waiting for it would wait for every stage in flight.
 // Rows past the group's end are computed with the rest (they repeat the last
 // row) and never stored.
 constexpr int kTN = 256;            // weight rows per tile
@@ -183,7 +186,7 @@ struct TileShape {
 
 template <bool GU, int H, int I, bool THIN>
 __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, const uint8_t* W,
-                                          const float* Sc, const int* arow, int valid, int r0,
+                                          const float* ss, const int* arow, int valid, int r0,
                                           int n0, uint8_t* lds, void* __restrict__ out) {
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
@@ -215,15 +218,13 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   struct Regs {
     uint4 a[AC], b[BC];
   };
-  // scale rows of this thread's B chunks: chunk i of every thread lies in the
-  // same 128-row block (GU: the gate block, then the up block), so these are
-  // uniform; a block of scale 0 has its codes zeroed when written to LDS
+  // scale rows (in LDS) of this thread's B chunks: chunk i of every thread
+  // lies in the tile's scale row i (GU: the gate block, then the up block;
+  // down: rows n0 .. + 127, then n0 + 128 .. + 255), so these are uniform; a
+  // block of scale 0 has its codes zeroed when written to LDS
   const float* bscale[BC];
 #pragma unroll
-  for (int i = 0; i < BC; ++i) {
-    const int wrow = GU ? (i == 0 ? n0 : I + n0) : n0 + 128 * i;
-    bscale[i] = Sc + (size_t)(wrow / kBK) * (K / kBK);
-  }
+  for (int i = 0; i < BC; ++i) bscale[i] = ss + i * (K / kBK);
   auto fetch = [&](Regs& R, int st) {
     st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
 #pragma unroll
@@ -255,14 +256,11 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   const int q = lane >> 5, l32 = lane & 31;
   const int afr = (S::arow0(wm) + l32) * (kKS * 2), asw = (l32 >> 1) & 7;
   const int bfr = l32 * kKS, bsw = (l32 >> 2) & 3;
-  // scale row of each MFMA tile
+  // scale row (in LDS) of each MFMA tile: its weight rows lie in the tile's
+  // scale row brow / 128
   const float* srow[NBW];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int br = S::brow(wn, nb);
-    const int wrow = GU ? (br < kTN / 2 ? n0 + br : I + n0 + br - kTN / 2) : n0 + br;
-    srow[nb] = Sc + (size_t)(wrow / kBK) * (K / kBK);
-  }
+  for (int nb = 0; nb < NBW; ++nb) srow[nb] = ss + (S::brow(wn, nb) / kBK) * (K / kBK);
 
   f32x16_t acc[MW][NBW];
 #pragma unroll
@@ -397,6 +395,8 @@ void mfma_pass(const uint16_t* __restrict__ act,
   static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kAStage + kBStage)];
   __shared__ int arow[kMfmaBM];
+  constexpr int NKB = P::K / kBK;  // scale blocks along K
+  __shared__ float ss[2 * NKB];    // the tile's two scale rows
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
   // (each with its own L2), so workgroup L runs on XCD L % 8. XCD x takes row
   // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
@@ -424,11 +424,18 @@ void mfma_pass(const uint16_t* __restrict__ act,
     const int rr = tid < valid ? tid : valid - 1;
     arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
   }
+  // scale rows of the tile's weight rows: GU: the gate block of rows n0 ..
+  // n0 + 127 and the matching up block; down: rows n0 .. and n0 + 128 ..
+  if (tid >= 256 && tid < 256 + 2 * NKB) {
+    const int i = (tid - 256) / NKB, kb = (tid - 256) % NKB;
+    const int wrow = GU ? (i == 0 ? n0 : I + n0) : n0 + 128 * i;
+    ss[i * NKB + kb] = Sc[(size_t)(wrow / kBK) * NKB + kb];
+  }
   __syncthreads();
   if (valid <= 64)
-    pass_tile<GU, H, I, true>(act, W, Sc, arow, valid, r0, n0, lds, out);
+    pass_tile<GU, H, I, true>(act, W, ss, arow, valid, r0, n0, lds, out);
   else
-    pass_tile<GU, H, I, false>(act, W, Sc, arow, valid, r0, n0, lds, out);
+    pass_tile<GU, H, I, false>(act, W, ss, arow, valid, r0, n0, lds, out);
 }
 
 // ---------------------------------------------------------------------------
