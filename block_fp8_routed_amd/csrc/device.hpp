@@ -169,6 +169,19 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Wave-wide maximum of a 32-bit unsigned key, uniform on return (the same
+// DPP steps as wave_max_u64, one word wide). Keys must be non-negative as
+// unsigned, as rows outside a row mask compare against zero.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppXor1, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppXor2, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppHalfMirror, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppMirror, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppRowBcast15, 0xA, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppRowBcast31, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)k, 63);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // 16-byte global load through the vector memory path.

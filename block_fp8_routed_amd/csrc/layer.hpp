@@ -55,7 +55,6 @@ inline int router_slices(const Dims& d) {
   }
 }
 
-constexpr int kMetaSelectCounter = 8;  // decode selection's completion counter
 constexpr int kMetaPermCounter = 9;    // multi-block permutation's completion counter
 constexpr int kPermMaxBlocksHost = 16; // blocks of the multi-block permutation (at most)
 
@@ -66,7 +65,7 @@ struct Work {
   float* gates;      // [T][k]
   int32_t* offsets;  // [E+2]
   int32_t* meta;     // [16]: meta[0] = active groups, meta[1] = MFMA tiles,
-                     // meta[kMetaSelectCounter]: decode select completion count
+                     // meta[kMetaPermCounter]: multi-block permutation's completion count
   int32_t* gdesc;    // [E+2][4] per non-empty group: (group, first row, rows, 0);
                      // group = -1 past the last one (shared group = E)
   int32_t* rtok;     // [P] token of each permuted row
@@ -88,10 +87,8 @@ size_t workspace_bytes(const Dims& d);
 Work carve(const Dims& d, void* base);
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
-// zero_word (may be null): a workspace word the decode kernel (T <= 16) uses
-// as its completion counter; the router zeroes it.
 hipError_t launch_router(const Dims& d, const void* x, const float* wr, const Work& w,
-                         int32_t* zero_word, hipStream_t s);
+                         hipStream_t s);
 // Sums the router slices, adds the bias, selects and gates; optionally writes
 // the final logits.
 // zero_word (may be null): a workspace word the multi-block permutation that
@@ -102,8 +99,8 @@ hipError_t launch_topk(const Dims& d, const float* plogits, const float* bias, i
 // by an earlier kernel on the stream; otherwise a one-thread kernel zeroes it.
 hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int tile_rows,
                           bool counter_zeroed, hipStream_t s);
-// Decode sizes: top-k + gates + permutation in one kernel, one workgroup per
-// token; the counter must be zero at launch (launch_router zeroes it).
+// Decode sizes: top-k + gates + permutation in one kernel of one workgroup
+// (one wavefront per token).
 bool small_select_permute(const Dims& d);
 hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
                                        const Work& w, int tile_rows, hipStream_t s);

@@ -163,9 +163,7 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr;
   if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
   const bool small = small_select_permute(d);
-  if (launch_router(d, x, router_w, w, small ? w.meta + kMetaSelectCounter : nullptr, s) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, w, s) != hipSuccess) return MOE_ERR_HIP;
   const int tile_rows = d.mfma ? kMfmaBM : 0;
   if (small) {
     // decode sizes: selection and permutation share one launch, so ROUTED
@@ -203,7 +201,7 @@ moe_status moe_route(const void* x, const float* router_w, const float* router_b
   if (st != MOE_OK) return st;
   const Work w = carve(d, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_router(d, x, router_w, w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, w, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_topk(d, w.logits, router_bias, topk_idx, gates, logits, nullptr, s) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;

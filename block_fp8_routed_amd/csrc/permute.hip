@@ -1,58 +1,123 @@
 // permute.hip — the token -> expert permutation: the multi-block kernels for
 // larger batches (perm_count, perm_scatter), and the fused decode kernel that
-// selects every token's experts and permutes in the last token's workgroup
-// (permute_wave).
+// selects every token's experts and then permutes them.
 #include "layer.hpp"
 #include "permute.hpp"
 #include "select.hpp"
 
 namespace moe {
 
-// Decode sizes (T <= 16, E <= 512): workgroup t (one wavefront) selects token
-// t's experts and gates (select_token) and writes them out. Selection is most
-// of the kernel's work, so the tokens run on as many compute units. Each
-// workgroup then publishes its result (release fence, then one atomic
-// increment of *counter at device scope); the workgroup that brings the count
-// to T is the last, and after an acquire fence it reads every token's
-// selection back and builds the permutation alone (permute_wave). No
-// workgroup ever waits for another. *counter must be zero at launch (the
-// router kernel, launched just before on the same stream, zeroes it). Same
-// results as topk_softmax + the multi-block permutation.
+// Decode sizes (T <= 16, E <= 512): one workgroup of T wavefronts, which
+// selects and permutes without any result leaving the compute unit between
+// the steps.
+//   1. wavefront t selects token t's experts and gates (select_token); lane
+//      j < k sets bit t of its expert's token mask (LDS). With at most 16
+//      tokens a mask holds an expert's whole token set, and since a token's
+//      experts are distinct every (expert, token) bit is set once.
+//   2. wavefront 0: lane L owns experts NV L .. NV L + NV - 1 (ascending
+//      with L); the group sizes are the masks' popcounts, their exclusive
+//      scan gives the groups' first rows, and a scan of the non-empty flags
+//      places the group descriptors (and, for the MFMA family, one row tile
+//      per group: a group has at most 16 < tile_rows rows).
+//   3. the slot of token t's j-th choice e goes to row first[e] + (tokens
+//      below t in e's mask): rows keep ascending token order (stable).
+// Same results as topk_softmax + the multi-block permutation.
 template <int NV>
-__global__ __launch_bounds__(64) void select_permute_small(
+__global__ __launch_bounds__(64 * kGemvMaxTokens) void select_permute_small(
     const float* __restrict__ plog, int slices, const float* __restrict__ bias, int64_t T, int k,
-    int E, int S, int32_t* topk, float* __restrict__ gates, int32_t* counter,
+    int E, int S, int32_t* __restrict__ topk, float* __restrict__ gates,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
     int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
     int32_t* __restrict__ tiles, int tile_rows) {
-  __shared__ int32_t cnt[64 * kWaveExpertsPerLane];
-  select_token<NV>(plog, slices, bias, T, blockIdx.x, E, k, topk, gates, nullptr, nullptr);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __builtin_amdgcn_wave_barrier();
-  int done = 0;
-  if (threadIdx.x == 0) done = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-  done = __builtin_amdgcn_readfirstlane(done);
-  if (done != T - 1) return;  // uniform: not the last token
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  permute_wave(topk, T, k, E, S, offsets, pair, inv, rtok, meta, gdesc, tiles, tile_rows, cnt);
+  static_assert(kGemvMaxTokens <= 32, "a token mask is one 32-bit word");
+  __shared__ uint32_t tmask[64 * NV];  // bit t: token t chose the expert
+  __shared__ int32_t first[64 * NV];   // first row of each expert's group
+  __shared__ int32_t routed_rows;
+  const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;  // blockDim.x = 64 T
+  for (int e = threadIdx.x; e < 64 * NV; e += blockDim.x) tmask[e] = 0u;
+  __syncthreads();
+  const int my_e = select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, nullptr);
+  if (lane < k) atomicOr(&tmask[my_e], 1u << t);
+  __syncthreads();
+  if (t == 0) {
+    uint32_t m[NV];
+    int local = 0, nz = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = NV * lane + i;
+      m[i] = e < E ? tmask[e] : 0u;
+      local += __popc(m[i]);
+      nz += m[i] != 0u;
+    }
+    int total, nact;
+    int run = wave_excl_scan(local, &total);
+    int apos = wave_excl_scan(nz, &nact);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = NV * lane + i;
+      if (e < E) {
+        const int c = __popc(m[i]);
+        offsets[e] = run;
+        first[e] = run;
+        if (c > 0) {
+          gdesc[apos] = make_int4(e, run, c, 0);
+          if (tile_rows > 0) {
+            tiles[2 * apos] = e;
+            tiles[2 * apos + 1] = run;
+          }
+          ++apos;
+        }
+        run += c;
+      }
+    }
+    if (lane == 0) {
+      offsets[E] = total;
+      offsets[E + 1] = total + S * (int)T;
+      if (S) {
+        gdesc[nact] = make_int4(E, total, (int)T, 0);
+        if (tile_rows > 0) {
+          tiles[2 * nact] = E;
+          tiles[2 * nact + 1] = total;
+        }
+      }
+      meta[0] = nact + S;
+      meta[1] = tile_rows > 0 ? nact + S : 0;
+      routed_rows = total;
+    }
+    for (int y = nact + S + lane; y < E + 2; y += 64) gdesc[y] = make_int4(-1, 0, 0, 0);
+  }
+  __syncthreads();
+  const int TK = (int)(T * k);
+  if (lane < k) {
+    const int row = first[my_e] + __popc(tmask[my_e] & ((1u << t) - 1u));
+    const int s = t * k + lane;
+    pair[row] = s;
+    inv[s] = row;
+    rtok[row] = t;
+  }
+  if (S && lane == 0) {  // the shared group: slot TK + t is token t
+    const int row = routed_rows + t;
+    pair[row] = TK + t;
+    inv[TK + t] = row;
+    rtok[row] = t;
+  }
 }
 
 bool small_select_permute(const Dims& d) {
-  return d.T <= kGemvMaxTokens && d.E <= 64 * kWaveExpertsPerLane;
+  static_assert(kGemvMaxTokens <= kMfmaBM, "a decode group fits one MFMA row tile");
+  return d.T <= kGemvMaxTokens && d.E <= 64 * 8;
 }
 
 hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
                                        const Work& w, int tile_rows, hipStream_t s) {
   const int ns = router_slices(d);
   const int nv = (d.E + 63) / 64;
-  const unsigned grid = (unsigned)d.T;
-#define MOE_SP(NV)                                                                          \
-  select_permute_small<NV><<<grid, 64, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk, \
-                                               w.gates, w.meta + kMetaSelectCounter,       \
-                                               w.offsets, w.pair, w.inv, w.rtok, w.meta,   \
-                                               reinterpret_cast<int4*>(w.gdesc), w.tiles,  \
-                                               tile_rows)
+  const unsigned threads = (unsigned)(64 * d.T);
+#define MOE_SP(NV)                                                                             \
+  select_permute_small<NV><<<1, threads, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk,  \
+                                                 w.gates, w.offsets, w.pair, w.inv, w.rtok,   \
+                                                 w.meta, reinterpret_cast<int4*>(w.gdesc),    \
+                                                 w.tiles, tile_rows)
   if (nv <= 1)
     MOE_SP(1);
   else if (nv <= 2)

@@ -30,12 +30,8 @@ template <int NT, bool XBF16>
 __global__ __launch_bounds__(256) void router_slices_kernel(const void* __restrict__ x,
                                                            const float* __restrict__ wr,
                                                            float* __restrict__ plog, int T,
-                                                           int H, int E, int HS,
-                                                           int32_t* __restrict__ zero_word) {
+                                                           int H, int E, int HS) {
   const int lane = threadIdx.x & 63;
-  // arms the completion counter of the kernel that follows (see
-  // select_permute_small); every later kernel sees it after this one ends
-  if (zero_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *zero_word = 0;
   const int t0 = (threadIdx.x >> 6) * NT;
   const int h0 = blockIdx.y * HS;
   const int e0 = blockIdx.x * 4;
@@ -181,17 +177,15 @@ __global__ __launch_bounds__(256) void router_gemm(const void* __restrict__ x,
 
 template <int NT>
 static void slices_launch(const Dims& d, const void* x, const float* wr, float* plog,
-                          int32_t* zero_word, hipStream_t s) {
+                          hipStream_t s) {
   const int ns = router_slices(d);
   const int HS = d.H < kRouterSlice ? d.H : kRouterSlice;
   const dim3 grid((d.E + 3) / 4, ns);
   const int threads = 64 * (int)((d.T + NT - 1) / NT);
   if (d.x_bf16)
-    router_slices_kernel<NT, true><<<grid, threads, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS,
-                                                           zero_word);
+    router_slices_kernel<NT, true><<<grid, threads, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
   else
-    router_slices_kernel<NT, false><<<grid, threads, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS,
-                                                            zero_word);
+    router_slices_kernel<NT, false><<<grid, threads, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
 }
 
 // ------------------------------------------------------------ MFMA router --
@@ -325,17 +319,17 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
 }
 
 hipError_t launch_router(const Dims& d, const void* x, const float* wr, const Work& w,
-                         int32_t* zero_word, hipStream_t s) {
+                         hipStream_t s) {
   float* plog = w.logits;
   switch (router_kind(d)) {
     case kRouterDecode:
       // tokens per wavefront (T <= 16 here: at most 4 wavefronts per workgroup)
       if (d.T <= 1)
-        slices_launch<1>(d, x, wr, plog, zero_word, s);
+        slices_launch<1>(d, x, wr, plog, s);
       else if (d.T <= 2)
-        slices_launch<2>(d, x, wr, plog, zero_word, s);
+        slices_launch<2>(d, x, wr, plog, s);
       else
-        slices_launch<4>(d, x, wr, plog, zero_word, s);
+        slices_launch<4>(d, x, wr, plog, s);
       break;
     case kRouterMfma: {
       const int64_t n = (int64_t)d.E * d.H;

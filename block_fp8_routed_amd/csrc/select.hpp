@@ -9,10 +9,12 @@
 // exp(l_i - l_0) over the selected logits only (l_0 the largest).
 //
 // Lane L owns experts L, L+64, ...; it sums the router's partial logits over
-// the H slices in slice order and adds the bias. Each of the k rounds is a
-// lane-local maximum plus a wave maximum (DPP) of 64-bit keys that order by
-// logit, then by lower expert index; the order is total, so the result does
-// not depend on reduction order. Must be called by all 64 lanes.
+// the H slices in slice order and adds the bias. Each of the k rounds takes
+// the wave-wide maximum (DPP) of 32-bit keys that order the logits exactly,
+// then the lowest expert index holding it (one ballot per expert row of the
+// lanes, lowest row first); the order is total, so the result does not
+// depend on reduction order. Must be called by all 64 lanes; returns, in lane
+// j < k, the j-th selected expert (other lanes: -1).
 #pragma once
 
 #include "device.hpp"
@@ -20,11 +22,10 @@
 namespace moe {
 
 template <int NV>
-__device__ __forceinline__ void select_token(const float* __restrict__ plog, int slices,
-                                             const float* __restrict__ bias, int64_t T,
-                                             int64_t t, int E, int k, int32_t* topk_out,
-                                             float* gates_out, float* logits_out,
-                                             int32_t* topk_lds) {
+__device__ __forceinline__ int select_token(const float* __restrict__ plog, int slices,
+                                            const float* __restrict__ bias, int64_t T, int64_t t,
+                                            int E, int k, int32_t* topk_out, float* gates_out,
+                                            float* logits_out) {
   const int lane = threadIdx.x & 63;
   // Every partial logit (up to kMaxUnrolled slices) and bias term of the
   // lane's experts is requested before any is used: the addresses are
@@ -47,8 +48,11 @@ __device__ __forceinline__ void select_token(const float* __restrict__ plog, int
     const int e = lane + 64 * i < E ? lane + 64 * i : E - 1;
     bv[i] = bias ? bias[e] : 0.f;
   }
-  float v[NV];
-  uint32_t avail = 0;
+  // order keys: the logit's bits mapped to an unsigned order (negatives
+  // reversed, -0 taken as +0 so that equal logits compare equal, NaN taken as
+  // -inf so that it never outranks a number). Every logit maps above zero
+  // (-inf to 0x007fffff), so 0 marks an absent or already chosen expert.
+  uint32_t key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
@@ -56,58 +60,56 @@ __device__ __forceinline__ void select_token(const float* __restrict__ plog, int
 #pragma unroll
     for (int s = 1; s < kMaxUnrolled; ++s)
       if (s < slices) val += part[i][s];
+    key[i] = 0u;
     if (e < E) {
       for (int s = kMaxUnrolled; s < slices; ++s) val += plog[((size_t)s * T + t) * E + e];
       if (bias) val += bv[i];
       if (logits_out) logits_out[t * E + e] = val;
-      if (val != val) val = -INFINITY;  // NaN never outranks a number
-      avail |= 1u << i;
-    } else {
-      val = -INFINITY;
+      if (val != val) val = -INFINITY;
+      uint32_t b = __float_as_uint(val);
+      if (b == 0x80000000u) b = 0u;
+      key[i] = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
     }
-    v[i] = val;
   }
-  // k rounds of a wave-wide maximum over 64-bit order keys: the high word is
-  // the logit's bits mapped to an unsigned order (negatives reversed, -0
-  // taken as +0 so that equal logits compare equal), the low word the
-  // complemented expert index, so the larger logit wins and equal logits go
-  // to the lower index. Absent experts have key 0, below every logit. The
-  // round's winner is cleared in the lane that holds it.
-  uint64_t key[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    uint32_t b = __float_as_uint(v[i]);
-    if (b == 0x80000000u) b = 0u;
-    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    key[i] = ((avail >> i) & 1u) ? (((uint64_t)b << 32) | (uint32_t)~(lane + 64 * i)) : 0ull;
-  }
-  uint64_t mine = 0;  // lane j < k ends with the j-th winner
-  uint64_t first = 0;
+  uint32_t mine = 0;  // lane j < k ends with the j-th winner's key and expert
+  int mine_e = -1;
+  uint32_t first = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t lm = key[0];
+    uint32_t lm = key[0];
 #pragma unroll
-    for (int i = 1; i < NV; ++i) lm = key[i] > lm ? key[i] : lm;
-    const uint64_t m = wave_max_u64(lm);
+    for (int i = 1; i < NV; ++i) lm = max(lm, key[i]);
+    const uint32_t m = wave_max_u32(lm);
     if (j == 0) first = m;
-    mine = lane == j ? m : mine;
+    // the lowest expert index holding the maximum: experts 64 i + lane, so
+    // the first row i with a holder, then its lowest lane
+    int win = -1;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) key[i] = key[i] == m ? 0ull : key[i];
+    for (int i = 0; i < NV; ++i) {
+      const unsigned long long b = __ballot(key[i] == m);
+      if (win < 0 && b != 0ull) {
+        const int wl = __ffsll((long long)b) - 1;
+        win = 64 * i + wl;
+        if (lane == wl) key[i] = 0u;
+      }
+    }
+    if (lane == j) {
+      mine = m;
+      mine_e = win;
+    }
   }
-  // back from keys to (logit, expert)
-  const auto key_logit = [](uint64_t kk) {
-    const uint32_t hb = (uint32_t)(kk >> 32);
+  // back from keys to logits
+  const auto key_logit = [](uint32_t hb) {
     return __uint_as_float((hb & 0x80000000u) ? (hb & 0x7fffffffu) : ~hb);
   };
   const float top = key_logit(first);
   const float my_v = key_logit(mine);
-  const int my_i = (int)~(uint32_t)mine;
   const float ex = lane < k ? expf(my_v - top) : 0.f;
   const float den = group_sum<64>(ex);
   if (lane < k) {
-    topk_out[t * k + lane] = my_i;
+    topk_out[t * k + lane] = mine_e;
     gates_out[t * k + lane] = ex / den;
-    if (topk_lds) topk_lds[t * k + lane] = my_i;
   }
+  return lane < k ? mine_e : -1;
 }
 
 }  // namespace moe

@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ pl
   if (zero_word && blockIdx.x == 0 && threadIdx.x == 0) *zero_word = 0;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, logits_out, nullptr);
+  select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, logits_out);
 }
 
 hipError_t launch_topk(const Dims& d, const float* plog, const float* bias, int32_t* topk,

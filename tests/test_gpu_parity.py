@@ -194,6 +194,32 @@ def test_forward_tile_edges_and_zero_scales(path):
     check_output(out, ref["out"], what=f"constructed routing, zero scales, {path}")
 
 
+@pytest.mark.parametrize("T,path", [(16, "gemv"), (5, "mfma"), (40, "gemv")])
+def test_exact_ties_go_to_the_lower_index(T, path):
+    """A router of zeros, its odd rows -0, makes every logit exactly +0 or -0
+    (the activations are positive): the selection is fixed by the tie rule
+    alone (experts 0 .. k-1 in that order, -0 equal to +0, gates 1/k), and
+    every token lands in the same k groups."""
+    import block_fp8_routed_amd as moe
+    shape = C["c1"].with_(experts=16, top_k=4, name="c1e16_ties")
+    E, k, H = shape.experts, shape.top_k, shape.hidden
+    x = np.abs(W.gen_x(shape, T))
+    wr = np.zeros((E, H), np.float32)
+    wr[1::2] = -0.0
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    idx, gates = moe.moe_route(xd, torch.from_numpy(wr).cuda(), k, shape.inter, shape.block)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(k), (T, 1)))
+    assert np.array_equal(gates.cpu().numpy(), np.full((T, k), 1.0 / k, np.float32))
+    bank, _ = host_bank(shape.with_(tokens=0))
+    out = moe.moe_forward(xd, torch.from_numpy(wr).cuda(), moe.Bank.from_numpy(bank), k,
+                          shape.block, path=path)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(x, wr, None, lambda e: W.bank_expert(bank, e), k, shape.inter,
+                           shape.block)
+    assert np.array_equal(ref["topk_idx"], np.tile(np.arange(k), (T, 1)))
+    check_output(out, ref["out"], what=f"exact ties T={T} {path}")
+
+
 def test_forward_bf16_output():
     layer = DevLayer(C["c1"], tokens=16)
     idx, gates = layer.route()
