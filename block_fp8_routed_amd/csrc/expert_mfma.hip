@@ -96,19 +96,25 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 //     64 of them. A = fp16 h rows (a group's rows are contiguous); fp16 MFMA.
 // Two tile shapes, chosen per tile:
 //   full (more than 64 rows): wavefront (wm, wn) takes rows 64 wm .. + 63
-//     (two 32-row MFMA tiles); stages fetched one ahead.
+//     (two 32-row MFMA tiles). K runs in stages of 64 (half a scale block):
+//     a stage's A tile (128 rows) and B tile (256 x 64 bytes) are fetched
+//     global -> registers one stage ahead and written into the other of two
+//     LDS buffers after the current stage's MFMAs; one barrier per stage.
 //   thin (at most 64 rows, where the pass streams weights): rows 32 wm ..
-//     + 31 (one MFMA tile); the A tile has 64 rows, and stages are fetched
-//     four ahead, so more bytes are in flight while the weights stream.
-// K runs in stages of 64 (half a scale block). A stage's A tile and B (256 x
-// 64 bytes) tile are fetched global -> registers ahead of use and written into
-// the other of two LDS buffers after the current stage's MFMAs; one barrier
-// per stage. Loads are never conditional (a stage index past the end is
-// clamped, rows past the group's end repeat its last row), so the compiler
-// can wait for exactly the loads a write needs. In LDS the 16-byte chunks of a
-// row are XOR-swizzled with the row index (A: chunk c of row r at slot c ^
-// ((r >> 1) & 7); B: c ^ ((r >> 2) & 3)), which makes the 32-row fragment
-// reads and the tile writes free of bank conflicts.
+//     + 31 (one MFMA tile); the A tile has 64 rows. gate/up: K runs in
+//     stages of 128 (one scale block), so every weight row is read 128
+//     bytes at a time, which the memory system streams faster than 64-byte
+//     pieces of 256 rows; two stages are in flight in registers, and the
+//     stage (16 KiB of A, 32 KiB of B) goes through one LDS buffer, with a
+//     barrier before and after its MFMAs. down (K = I, a few stages): 64-k
+//     stages in two LDS buffers, four fetched ahead.
+// Loads are never conditional (a stage index past the end is clamped, rows
+// past the group's end repeat its last row), so the compiler can wait for
+// exactly the loads a write needs. In LDS the 16-byte chunks of a row are
+// XOR-swizzled with the row index (64-k stages: A chunk c of row r at slot
+// c ^ ((r >> 1) & 7), B at c ^ ((r >> 2) & 3); 128-k stages: A at c ^ (r &
+// 15), B at c ^ ((r >> 1) & 7)), which makes the 32-row fragment reads and
+// the tile writes free of bank conflicts.
 //
 // K order inside a stage: the contraction does not depend on the order of k,
 // as long as A and B use the same one. Lane group q = lane / 32 reads 16 B
@@ -131,9 +137,7 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 constexpr int kTN = 256;            // weight rows per tile
 constexpr int kXcds = 8;            // accelerator complex dies (one L2 each)
 constexpr int kPassThreads = 512;
-constexpr int kKS = 64;             // k per pipeline stage
-constexpr int kAStage = kMfmaBM * kKS * 2;  // bytes: 128 rows x 64 bf16/fp16
-constexpr int kBStage = kTN * kKS;          // bytes: 256 rows x 64 E4M3
+constexpr int kLdsBytes = 65536;    // stage buffers of one workgroup
 static_assert(kMfmaBM == 128, "tile geometry assumes 128-row tiles");
 
 template <bool GU, int H, int I>
@@ -169,12 +173,24 @@ struct Op<false> {
 // Tile geometry of one shape (THIN: at most 64 rows).
 template <bool GU, bool THIN>
 struct TileShape {
+  // thin gate/up tiles (K = H) take 128-k stages through one LDS buffer; the
+  // down pass's K (= I) is short enough that the deeper pipeline of 64-k
+  // stages in two buffers pays more than the longer row pieces
+  static constexpr bool WIDE = THIN && GU;
   static constexpr int RA = THIN ? 64 : 128;  // A rows fetched per stage
-  static constexpr int AC = RA * 8 / kPassThreads;  // A chunks per thread per stage
-  static constexpr int BC = kTN * 4 / kPassThreads; // B chunks per thread per stage
+  static constexpr int KS = WIDE ? 128 : 64;  // k per stage
+  static constexpr int CA = KS * 2 / 16;      // 16-byte chunks per A row (bf16/fp16)
+  static constexpr int CB = KS / 16;          // 16-byte chunks per B row (E4M3)
+  static constexpr int AC = RA * CA / kPassThreads;   // A chunks per thread per stage
+  static constexpr int BC = kTN * CB / kPassThreads;  // B chunks per thread per stage
+  static constexpr int ASTAGE = RA * KS * 2;  // bytes of a stage's A tile
+  static constexpr int BSTAGE = kTN * KS;     // bytes of a stage's B tile
+  static constexpr int BUFS = WIDE ? 1 : 2;   // LDS stage buffers
   static constexpr int MW = THIN ? 1 : 2;     // 32-row MFMA tiles per wavefront
   static constexpr int NBW = 2;               // 32-column MFMA tiles per wavefront
-  static constexpr int DEPTH = THIN ? 4 : 1;  // stages fetched ahead
+  static constexpr int DEPTH = WIDE ? 2 : (THIN ? 4 : 1);  // stages fetched ahead
+  static_assert(BUFS * (ASTAGE + BSTAGE) <= kLdsBytes, "stage buffers exceed the LDS block");
+  static_assert(AC * kPassThreads == RA * CA && BC * kPassThreads == kTN * CB, "fetch map");
   // tile-relative first row of this wavefront's rows
   static __device__ __forceinline__ int arow0(int wm) { return (THIN ? 32 : 64) * wm; }
   // tile-relative weight row of this wavefront's MFMA tile nb
@@ -182,6 +198,9 @@ struct TileShape {
     if (GU) return nb == 0 ? 32 * wn : kTN / 2 + 32 * wn;
     return 64 * wn + 32 * nb;
   }
+  // LDS slot of chunk c of A row r / B row r
+  static __device__ __forceinline__ int aswz(int r) { return CA == 16 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int bswz(int r) { return CB == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 };
 
 template <bool GU, int H, int I, bool THIN>
@@ -191,76 +210,84 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
   using S = TileShape<GU, THIN>;
-  constexpr int K = P::K, NS = K / kKS, AC = S::AC, BC = S::BC, MW = S::MW, NBW = S::NBW;
-  static_assert(NS % 2 == 0, "stages come in pairs (one scale block)");
+  constexpr int K = P::K, KS = S::KS, NS = K / KS, AC = S::AC, BC = S::BC, MW = S::MW,
+                NBW = S::NBW, CA = S::CA, CB = S::CB;
+  constexpr int NKB = K / kBK;
+  static_assert(K % KS == 0 && kBK % KS == 0, "stages must tile the scale blocks");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches only
   const int wm = wave >> 2, wn = wave & 3;
 
-  // fetch map: A chunk qq = tid + 512 i is row qq / 8, chunk qq % 8; B chunk
-  // qq = tid + 512 i is weight row qq / 4, chunk qq % 4. Moving qq by 512
-  // moves the row by 64 (A) or 128 (B), which leaves the swizzle alone, so
-  // the LDS targets and the weight sources of i > 0 are constant offsets from
-  // those of i = 0 (GU: B rows 128 .. 255 are the up rows). Byte offsets from
-  // the wave-uniform bases fit in 32 bits (checked on the host for the
-  // activation rows; a weight matrix is below 2 GiB).
+  // fetch map: A chunk qq = tid + 512 i is row qq / CA, chunk qq % CA; B chunk
+  // qq = tid + 512 i is tile weight row qq / CB, chunk qq % CB. Moving qq by
+  // 512 moves the row by a multiple of 32, which leaves the swizzle alone, so
+  // the LDS targets and the sources of i > 0 are constant offsets from those
+  // of i = 0 (GU: tile rows 128 .. 255 are the up rows I + n0 ..). Byte
+  // offsets from the wave-uniform bases fit in 32 bits (checked on the host
+  // for the activation rows; a weight matrix is below 2 GiB).
   const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(act, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(W, (uint32_t)((GU ? 2 * I : H) * K));
+  constexpr int ARS = kPassThreads / CA, BRS = kPassThreads / CB;  // row step per i
   uint32_t asrc[AC];
-  const int ar0 = tid >> 3, ac0 = tid & 7;
-  const int adst0 = ar0 * (kKS * 2) + 16 * (ac0 ^ ((ar0 >> 1) & 7));
+  const int ar0 = tid / CA, ac0 = tid % CA;
+  const int adst0 = ar0 * (KS * 2) + 16 * (ac0 ^ S::aswz(ar0));
 #pragma unroll
-  for (int i = 0; i < AC; ++i) asrc[i] = (uint32_t)arow[ar0 + 64 * i] * (K * 2) + 16 * ac0;
-  const int br0 = tid >> 2, bc0 = tid & 3;
-  const int bdst0 = br0 * kKS + 16 * (bc0 ^ ((br0 >> 2) & 3));
+  for (int i = 0; i < AC; ++i) asrc[i] = (uint32_t)arow[ar0 + ARS * i] * (K * 2) + 16 * ac0;
+  const int br0 = tid / CB, bc0 = tid % CB;
+  const int bdst0 = br0 * KS + 16 * (bc0 ^ S::bswz(br0));
   const uint32_t bsrc0 = (uint32_t)(n0 + br0) * K + 16 * bc0;
-  auto bstep = [](int i) -> uint32_t { return (uint32_t)(GU ? I * i : 128 * i) * K; };
+  // weight row offset (in rows) of chunk group i's tile row BRS i
+  auto brow_of = [](int i) -> int {
+    const int tr = BRS * i;
+    return GU ? (tr < kTN / 2 ? tr : I + tr - kTN / 2) : tr;
+  };
   struct Regs {
     uint4 a[AC], b[BC];
   };
-  // scale rows (in LDS) of this thread's B chunks: chunk i of every thread
-  // lies in the tile's scale row i (GU: the gate block, then the up block;
+  // scale rows (in LDS) of this thread's B chunks: chunk group i lies in the
+  // tile's scale row (BRS i) / 128 (GU: the gate block, then the up block;
   // down: rows n0 .. + 127, then n0 + 128 .. + 255), so these are uniform; a
   // block of scale 0 has its codes zeroed when written to LDS
   const float* bscale[BC];
 #pragma unroll
-  for (int i = 0; i < BC; ++i) bscale[i] = ss + i * (K / kBK);
+  for (int i = 0; i < BC; ++i) bscale[i] = ss + (BRS * i / kBK) * NKB;
   auto fetch = [&](Regs& R, int st) {
     st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
 #pragma unroll
-    for (int i = 0; i < AC; ++i) R.a[i] = buffer_ld16(arsrc, asrc[i], (uint32_t)(st * kKS * 2));
+    for (int i = 0; i < AC; ++i) R.a[i] = buffer_ld16(arsrc, asrc[i], (uint32_t)(st * KS * 2));
 #pragma unroll
     for (int i = 0; i < BC; ++i)
-      R.b[i] = buffer_ld16(brsrc, bsrc0, bstep(i) + (uint32_t)(st * kKS));
+      R.b[i] = buffer_ld16(brsrc, bsrc0, (uint32_t)(brow_of(i) * K + st * KS));
   };
   auto put = [&](Regs& R, int buf, int st) {
-    uint8_t* A = lds + buf * (kAStage + kBStage);
-    uint8_t* B = A + kAStage;
+    uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
+    uint8_t* B = A + S::ASTAGE;
+    const int kb = st * KS / kBK;
     bool zero = false;
 #pragma unroll
-    for (int i = 0; i < BC; ++i) zero |= bscale[i][st >> 1] == 0.f;
+    for (int i = 0; i < BC; ++i) zero |= bscale[i][kb] == 0.f;
     if (zero) {  // rare: a zero block scale (uniform branch)
 #pragma unroll
       for (int i = 0; i < BC; ++i)
-        if (bscale[i][st >> 1] == 0.f) R.b[i] = make_uint4(0, 0, 0, 0);
+        if (bscale[i][kb] == 0.f) R.b[i] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + adst0 + 64 * (kKS * 2) * i) = R.a[i];
+    for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + adst0 + ARS * (KS * 2) * i) = R.a[i];
 #pragma unroll
-    for (int i = 0; i < BC; ++i) *reinterpret_cast<uint4*>(B + bdst0 + 128 * kKS * i) = R.b[i];
+    for (int i = 0; i < BC; ++i) *reinterpret_cast<uint4*>(B + bdst0 + BRS * KS * i) = R.b[i];
   };
 
   // this wavefront's fragments: A rows arow0 + 32 m + lane % 32; B rows
   // brow(nb) + lane % 32. The row offsets are multiples of 32, so the swizzle
   // of a fragment read depends on lane % 32 only.
   const int q = lane >> 5, l32 = lane & 31;
-  const int afr = (S::arow0(wm) + l32) * (kKS * 2), asw = (l32 >> 1) & 7;
-  const int bfr = l32 * kKS, bsw = (l32 >> 2) & 3;
+  const int afr = (S::arow0(wm) + l32) * (KS * 2), asw = S::aswz(l32);
+  const int bfr = l32 * KS, bsw = S::bswz(l32);
   // scale row (in LDS) of each MFMA tile: its weight rows lie in the tile's
   // scale row brow / 128
   const float* srow[NBW];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) srow[nb] = ss + (S::brow(wn, nb) / kBK) * (K / kBK);
+  for (int nb = 0; nb < NBW; ++nb) srow[nb] = ss + (S::brow(wn, nb) / kBK) * NKB;
 
   f32x16_t acc[MW][NBW];
 #pragma unroll
@@ -280,12 +307,18 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   // One stage. Every MFMA tile is computed even when rows past the group's
   // end fill it (their results are not stored); nothing inside is
   // conditional, so the compiler schedules the MFMAs and LDS reads freely.
-  auto compute = [&](int st, bool block_start) {
-    if (block_start) {  // entering scale block st / 2
+  // K order inside a stage: the contraction does not depend on the order of
+  // k, as long as A and B use the same one. Lane group q = lane / 32 reads
+  // 16 B bytes (16 k) of chunk 2p + q for step pair p and uses its halves in
+  // steps 2p and 2p + 1; the A fragment of step 2p + h for group q is then 8
+  // k at chunk 4p + 2q + h (8 bf16 per A chunk).
+  auto compute = [&](int buf, int st) {
+    if ((st * KS) % kBK == 0) {  // entering scale block kb
+      const int kb = st * KS / kBK;
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         const float sn = snext[nb];
-        if (st + 2 < NS) snext[nb] = srow[nb][(st >> 1) + 1];
+        if (kb + 1 < NKB) snext[nb] = srow[nb][kb + 1];
         const bool on = sn != 0.f;
         // unit 0 (nothing added yet): the accumulators are 0 and stay 0; a
         // block of scale 0 (codes zeroed in LDS) leaves the unit as it is
@@ -297,14 +330,14 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         unit[nb] = on ? sn : unit[nb];
       }
     }
-    const uint8_t* A = lds + (st & 1) * (kAStage + kBStage);
-    const uint8_t* B = A + kAStage;
+    const uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
+    const uint8_t* B = A + S::ASTAGE;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < KS / 32; ++p) {
       uint4 braw[NBW];
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
-        braw[nb] = *reinterpret_cast<const uint4*>(B + S::brow(wn, nb) * kKS + bfr +
+        braw[nb] = *reinterpret_cast<const uint4*>(B + S::brow(wn, nb) * KS + bfr +
                                                    16 * ((2 * p + q) ^ bsw));
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -314,7 +347,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
           bf[nb] = hh ? O::cvt(braw[nb].z, braw[nb].w) : O::cvt(braw[nb].x, braw[nb].y);
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
-          const uint4 af = *reinterpret_cast<const uint4*>(A + afr + 32 * m * (kKS * 2) +
+          const uint4 af = *reinterpret_cast<const uint4*>(A + afr + 32 * m * (KS * 2) +
                                                            16 * ((4 * p + 2 * q + hh) ^ asw));
 #pragma unroll
           for (int nb = 0; nb < NBW; ++nb) acc[m][nb] = O::mma(af, bf[nb], acc[m][nb]);
@@ -324,24 +357,27 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   };
 
   if (S::DEPTH == 1) {
+    // two LDS buffers, one stage fetched ahead, one barrier per stage
+    static_assert(NS % 2 == 0, "stages come in pairs");
     Regs R;
     fetch(R, 0);
     put(R, 0, 0);
     __syncthreads();
     for (int st = 0; st < NS; st += 2) {
       fetch(R, st + 1);
-      compute(st, true);
+      compute(0, st);
       put(R, 1, st + 1);
       __syncthreads();
       fetch(R, st + 2);
-      compute(st + 1, false);
+      compute(1, st + 1);
       if (st + 2 < NS) put(R, 0, st + 2);
       __syncthreads();
     }
-  } else {
-    // a ring of DEPTH register sets: while stage st is computed, stages
-    // st + 1 .. st + DEPTH are in flight (stage s lives in set s % DEPTH);
-    // the loop is unrolled by DEPTH so the sets are fixed registers
+  } else if (S::BUFS == 2) {
+    // two LDS buffers and a ring of DEPTH register sets: while stage st is
+    // computed, stages st + 1 .. st + DEPTH are in flight (stage s lives in
+    // set s % DEPTH); the loop is unrolled by DEPTH so the sets are fixed
+    // registers; one barrier per stage
     constexpr int D = S::DEPTH;
     static_assert(NS % D == 0, "stage count must be a multiple of the prefetch depth");
     Regs R[D];
@@ -354,8 +390,27 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
       for (int j = 0; j < D; ++j) {
         const int st = st0 + j;
         fetch(R[j], st + D);  // set j held stage st, written to LDS before this stage
-        compute(st, (st & 1) == 0);
+        compute(st & 1, st);
         if (st + 1 < NS) put(R[(j + 1) % D], (st + 1) & 1, st + 1);
+        __syncthreads();
+      }
+    }
+  } else {
+    // one LDS buffer and a ring of DEPTH register sets (as above), with a
+    // barrier before and after each stage's MFMAs
+    constexpr int D = S::DEPTH;
+    static_assert(NS % D == 0, "stage count must be a multiple of the prefetch depth");
+    Regs R[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) fetch(R[j], j);
+    for (int st0 = 0; st0 < NS; st0 += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int st = st0 + j;
+        put(R[j], 0, st);     // the previous stage's reads ended at the last barrier
+        fetch(R[j], st + D);  // set j is free once written
+        __syncthreads();
+        compute(0, st);
         __syncthreads();
       }
     }
@@ -393,7 +448,7 @@ void mfma_pass(const uint16_t* __restrict__ act,
                                                         void* __restrict__ out) {
   using P = PassShape<GU, H, I>;
   static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kAStage + kBStage)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ int arow[kMfmaBM];
   constexpr int NKB = P::K / kBK;  // scale blocks along K
   __shared__ float ss[2 * NKB];    // the tile's two scale rows
