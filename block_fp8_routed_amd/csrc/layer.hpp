@@ -29,27 +29,41 @@ struct Dims {
 // slice of H; the top-k kernel sums the slices in slice order.
 //  * decode (T <= 16): wavefront dot products over slices of kRouterSlice
 //    columns (one slice when H < kRouterSlice);
-//  * prefill with bf16 activations (H a multiple of 32): MFMA tiles over the
-//    router weights split exactly into three bf16 planes, slices of
-//    kRouterSlice columns when H is a multiple of it, else one;
+//  * prefill with bf16 activations (H a multiple of 64): MFMA tiles of
+//    kRouterTile tokens x kRouterTile experts over the router weights split
+//    exactly into three bf16 planes; H is cut into as many slices (a power of
+//    two, each a multiple of 128 columns, at most kMaxSlicesUnrolled) as
+//    brings the tile count x slices to about 512 workgroups, so that small
+//    batches still spread over the compute units;
 //  * otherwise (fp32 activations at prefill sizes): the fp32 tiled GEMM, one
 //    slice.
 constexpr int kRouterSlice = 512;
+constexpr int kRouterTile = 128;
 enum RouterKind { kRouterDecode, kRouterMfma, kRouterGemm, kRouterNone };
 inline RouterKind router_kind(const Dims& d) {
   if (d.T <= kGemvMaxTokens) {
     if (d.H < kRouterSlice || d.H % kRouterSlice == 0) return kRouterDecode;
     return kRouterGemm;
   }
-  if (d.x_bf16 && d.H % 32 == 0) return kRouterMfma;
+  if (d.x_bf16 && d.H % 64 == 0) return kRouterMfma;
   return kRouterGemm;
 }
+// slices the top-k kernel sums without a loop: 16 when a lane holds at most
+// two experts (E <= 128), else 8
+inline int max_router_slices(const Dims& d) { return d.E <= 128 ? 16 : 8; }
 // number of partial-logit slices (>= 1)
 inline int router_slices(const Dims& d) {
   switch (router_kind(d)) {
     case kRouterDecode:
-    case kRouterMfma:
       return d.H % kRouterSlice == 0 ? d.H / kRouterSlice : 1;
+    case kRouterMfma: {
+      const int64_t tiles = ((d.T + kRouterTile - 1) / kRouterTile) *
+                            ((d.E + kRouterTile - 1) / kRouterTile);
+      int ns = 1;
+      while (2 * ns <= max_router_slices(d) && tiles * ns < 512 && d.H % (2 * ns * 128) == 0)
+        ns *= 2;
+      return ns;
+    }
     default:
       return 1;
   }

@@ -212,14 +212,15 @@ __global__ __launch_bounds__(256) void router_split(const float* __restrict__ wr
 // Tile of 128 tokens x 128 experts over one slice of H (blockIdx.z), 256
 // threads as 2 x 2 wavefronts of 64 x 64 (2 x 2 MFMA tiles of 32 x 32). K runs
 // in stages of 32: the stage's activation tile and three weight-plane tiles
-// are fetched global -> registers one stage ahead and stored into the other
-// of two LDS buffers after the stage's MFMAs. 16-byte chunks are
-// XOR-swizzled by row (chunk c of row r at slot c ^ ((r >> 2) & 3)) against
-// bank conflicts. Rows past T and experts past E repeat the last one (loads
-// stay unconditional) and are not stored.
+// are fetched global -> registers two stages ahead (a ring of two register
+// sets) and stored into the other of two LDS buffers after the stage's MFMAs.
+// 16-byte chunks are XOR-swizzled by row (chunk c of row r at slot c ^ ((r >>
+// 2) & 3)) against bank conflicts. Rows past T and experts past E repeat the
+// last one, and a stage index past the slice's end repeats its last stage
+// (loads stay unconditional); none of those is stored.
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rf32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kRtBM = 128, kRtBN = 128, kRtKS = 32;
+constexpr int kRtBM = kRouterTile, kRtBN = kRouterTile, kRtKS = 32;
 constexpr int kRtRow = kRtKS * 2;                // bytes per tile row per stage
 constexpr int kRtA = kRtBM * kRtRow;             // 8 KiB
 constexpr int kRtStage = kRtA + 3 * kRtBN * kRtRow;  // 32 KiB
@@ -251,12 +252,14 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
     src[2 + i] = planes + p * plane + (size_t)e * H + h0 + 8 * c;
     dst[2 + i] = kRtA + p * (kRtBN * kRtRow) + r * kRtRow + 16 * (c ^ ((r >> 2) & 3));
   }
-  uint4 v[8];
-  auto fetch = [&](int st) {
+  const int NS = HS / kRtKS;
+  typedef uint4 StageRegs[8];
+  auto fetch = [&](StageRegs& v, int st) {
+    st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = ld16(src[i] + st * kRtKS);
   };
-  auto put = [&](int buf) {
+  auto put = [&](const StageRegs& v, int buf) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(lds + buf * kRtStage + dst[i]) = v[i];
   };
@@ -268,13 +271,8 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
-  const int NS = HS / kRtKS;
-  fetch(0);
-  put(0);
-  __syncthreads();
-  for (int st = 0; st < NS; ++st) {
-    if (st + 1 < NS) fetch(st + 1);
-    const uint8_t* L = lds + (st & 1) * kRtStage;
+  auto compute = [&](int buf) {
+    const uint8_t* L = lds + buf * kRtStage;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // k16 steps; lane group q takes chunk 2t + q
       const int c = 2 * t + q;
@@ -299,8 +297,22 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
         }
       }
     }
-    if (st + 1 < NS) put((st + 1) & 1);
-    __syncthreads();
+  };
+  // stage s lives in register set s % 2 until it is stored to LDS buffer s % 2
+  StageRegs v[2];
+  fetch(v[0], 0);
+  fetch(v[1], 1);
+  put(v[0], 0);
+  __syncthreads();
+  for (int st0 = 0; st0 < NS; st0 += 2) {  // NS is even: slices are multiples of 128 columns
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      fetch(v[j], st0 + j + 2);  // set j held stage st0 + j, stored before this stage
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the stage's MFMAs
+      compute(j);
+      put(v[j ^ 1], j ^ 1);  // stage st0 + j + 1 (a repeat past the end)
+      __syncthreads();
+    }
   }
   // D layout (32x32): lane L holds column L % 32, value j row 8 (j / 4) + 4 (L / 32) + j % 4
   float* out = plog + (size_t)blockIdx.z * T * E;
@@ -333,8 +345,11 @@ hipError_t launch_router(const Dims& d, const void* x, const float* wr, const Wo
       break;
     case kRouterMfma: {
       const int64_t n = (int64_t)d.E * d.H;
-      router_split<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(wr, n, w.rsplit);
       const int ns = router_slices(d);
+      // stages come in pairs (router_kind takes this kernel only for H a
+      // multiple of 64, and slices of more than one are multiples of 128)
+      if ((d.H / ns) % (2 * kRtKS) != 0) return hipErrorInvalidValue;
+      router_split<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(wr, n, w.rsplit);
       const dim3 grid((unsigned)((d.T + kRtBM - 1) / kRtBM), (d.E + kRtBN - 1) / kRtBN, ns);
       router_mfma<<<grid, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(x), w.rsplit, plog,
                                        (int)d.T, d.H, d.E, d.H / ns);

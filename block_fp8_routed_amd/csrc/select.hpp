@@ -27,11 +27,12 @@ __device__ __forceinline__ int select_token(const float* __restrict__ plog, int 
                                             int E, int k, int32_t* topk_out, float* gates_out,
                                             float* logits_out) {
   const int lane = threadIdx.x & 63;
-  // Every partial logit (up to kMaxUnrolled slices) and bias term of the
-  // lane's experts is requested before any is used: the addresses are
-  // clamped into range instead of branched around, so the loads go out
-  // together and the token pays one memory latency, not one per expert.
-  constexpr int kMaxUnrolled = 8;
+  // Every partial logit (up to kMaxUnrolled slices: 16 for up to two
+  // experts per lane, else 8) and bias term of the lane's experts is
+  // requested before any is used: the addresses are clamped into range
+  // instead of branched around, so the loads go out together and the token
+  // pays one memory latency, not one per expert.
+  constexpr int kMaxUnrolled = NV <= 2 ? 16 : 8;
   float part[NV][kMaxUnrolled];
   float bv[NV];
 #pragma unroll
