@@ -8,8 +8,9 @@ expert bank, so that repeated calls cannot be served from the 256 MB MALL.
 
 Prints one JSON line: MoE-layer tokens/s, plus
   roofline:     the dominant kernel (gate/up expert pass) timed with HIP events
-                recorded around its launch on the layer's stream during the
-                timed steps; algorithmic bytes = the bytes of the experts the
+                recorded around its launch on the layer's stream during every
+                7th timed step (an event record costs the stream a few us, so
+                the other steps run without); algorithmic bytes = the bytes of the experts the
                 step's routing touches (E4M3 weights + fp32 scales), or
                 algorithmic FLOPs for MFMA-bound workloads;
   cpu_baseline: the CPU oracle (fp64 NumPy) timed on a bounded sample of the
@@ -39,6 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+EV_EVERY = 7                   # timed steps per step that records the gate/up events (coprime
+                               # with the input batches and bank copies, so the samples rotate)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
@@ -295,15 +298,18 @@ def main():
         if st != 0:
             raise moe.MoeError(st, "moe_forward")
 
-    # per-step events around the gate/up launch (PERMUTED -> GATE_UP)
+    # events around the gate/up launch (PERMUTED -> GATE_UP) on every
+    # EV_EVERY-th timed step: each event record costs the stream a few us, so
+    # recording on every step would slow the steps being timed
     K, Wm = args.steps, args.warmup
-    ev_pairs = [(hip.event(), hip.event()) for _ in range(K)]
-    ev_structs = []
-    for a, b in ev_pairs:
+    sampled = list(range(0, K, EV_EVERY))
+    ev_pairs = [(hip.event(), hip.event()) for _ in sampled]
+    ev_structs = {}
+    for i, (a, b) in zip(sampled, ev_pairs):
         s = moe.MoePhaseEvents()
         s.ev[moe.MOE_EV_PERMUTED] = a
         s.ev[moe.MOE_EV_GATE_UP] = b
-        ev_structs.append(s)
+        ev_structs[i] = s
     start, stop = hip.event(), hip.event()
 
     log(f"warmup {Wm} steps (T={T}, copies={copies}, batches={len(xs)}, path={'mfma' if mfma else 'gemv'})")
@@ -313,16 +319,16 @@ def main():
     log(f"timing {K} steps")
     hip.record(start, sp)
     for i in range(K):
-        call(Wm + i, ev_structs[i])
+        call(Wm + i, ev_structs.get(i))
     hip.record(stop, sp)
     torch.cuda.synchronize()
     total_ms = hip.elapsed_ms(start, stop)
     ms = total_ms / K
     gu_ms = [hip.elapsed_ms(a, b) for a, b in ev_pairs]
-    gu_avg_ms = sum(gu_ms) / K
-    steps_uniq = [uniq[(Wm + i) % len(xs)] for i in range(K)]
-    mean_uniq = sum(steps_uniq) / K
-    gu_bytes = mean_uniq * gu_bytes_per_expert
+    gu_avg_ms = sum(gu_ms) / len(gu_ms)
+    # the bytes of the sampled steps (for the kernel) and of all steps (for the layer)
+    gu_bytes = sum(uniq[(Wm + i) % len(xs)] for i in sampled) / len(sampled) * gu_bytes_per_expert
+    mean_uniq = sum(uniq[(Wm + i) % len(xs)] for i in range(K)) / K
     layer_bytes = mean_uniq * all_bytes_per_expert
 
     # phase breakdown (outside the timed region): all phase events on a few steps
@@ -362,6 +368,7 @@ def main():
                 "algorithmic_per_launch": round(gu_bytes),
                 "mfma_TFLOPs": round(tflops, 2)}
     roof["avg_launch_us"] = round(gu_avg_ms * 1e3, 2)
+    roof["launch_samples"] = len(sampled)
     roof["traffic"] = recorded_traffic(args.config, T, "mfma" if mfma else "gemv")
 
     res = {

@@ -1,11 +1,12 @@
-// combine.hip — out[t] = sum_j g[t][j] * y[inv[t*k+j]] (+ y[inv[T*k+t]]).
+// combine.hip — out[t] = sum_j g[t][j] * y[t*k+j] (+ y[T*k+t]).
 //
 // The gate-weighted sum of a token's expert outputs, plus the always-on shared
 // expert with weight 1 (colizig page, model table: "top-10 + 1 shared").
 // Summed in fp32 in a fixed order (slots j = 0..k-1, then the shared expert),
 // so the result does not depend on how the expert passes were scheduled; one
-// rounding to the output dtype at the end. y rows are fp16 (written so by the
-// down passes).
+// rounding to the output dtype at the end. y rows are fp16, stored by slot
+// (the down passes write row r's output to y row pair[r]), so a token's
+// outputs are rows t*k .. t*k + k - 1 (and T*k + t for the shared expert).
 #include "device.hpp"
 #include "layer.hpp"
 
@@ -15,8 +16,7 @@ namespace moe {
 // fp16 loads of y, fp32 accumulation).
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
-                                                     const float* __restrict__ gates,
-                                                     const int32_t* __restrict__ inv, int64_t T,
+                                                     const float* __restrict__ gates, int64_t T,
                                                      int H, int k, int S, void* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
@@ -34,9 +34,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
   };
   for (int j = 0; j < k; ++j)
-    add(ld16(y + (size_t)inv[t * k + j] * H + n), gates[t * k + j]);
+    add(ld16(y + (size_t)(t * k + j) * H + n), gates[t * k + j]);
   if (S) {
-    const uint4 v = ld16(y + (size_t)inv[T * k + t] * H + n);
+    const uint4 v = ld16(y + (size_t)(T * k + t) * H + n);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -62,9 +62,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s) {
   const dim3 grid((unsigned)d.T, (d.H + 2047) / 2048);
   if (d.out_bf16)
-    combine_kernel<true><<<grid, 256, 0, s>>>(w.y, w.gates, w.inv, d.T, d.H, d.k, d.S, out);
+    combine_kernel<true><<<grid, 256, 0, s>>>(w.y, w.gates, d.T, d.H, d.k, d.S, out);
   else
-    combine_kernel<false><<<grid, 256, 0, s>>>(w.y, w.gates, w.inv, d.T, d.H, d.k, d.S, out);
+    combine_kernel<false><<<grid, 256, 0, s>>>(w.y, w.gates, d.T, d.H, d.k, d.S, out);
   return hipGetLastError();
 }
 

@@ -254,6 +254,7 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
 template <int H, int I, int B, int NT>
 __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __restrict__ gdesc,
                                                 int E, const uint16_t* __restrict__ h,
+                                                const int32_t* __restrict__ pair,
                                                 uint16_t* __restrict__ y) {
   using D = DownMap<I>;
   constexpr int LPR = D::LPR, MD = D::MD, RW = D::RW, SPG = H / RW;
@@ -291,6 +292,11 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
   st.store(hs);
   lds_barrier();
   for (int t0 = 0;;) {
+    // y is stored by slot (row r's output goes to y row pair[r]), so the
+    // combine reads a token's outputs without the inverse permutation
+    int oslot[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oslot[t] = pair[r0 + t0 + (t < nv ? t : nv - 1)];
     if (live) {
       float acc[NT];
 #pragma unroll
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
       for (int t = 0; t < NT; ++t) {
         if (t >= nv) continue;
         const float v = seg_sum<LPR>(acc[t]);
-        if (sub == LPR - 1) y[(size_t)(r0 + t0 + t) * H + row] = f32_to_f16_sat(v);
+        if (sub == LPR - 1) y[(size_t)oslot[t] * H + row] = f32_to_f16_sat(v);
       }
     }
     t0 += NT;
@@ -355,7 +361,7 @@ static void run_gemv(const Dims& d, const void* x, const BankPtrs& bk, const Wor
       x, bk, gdesc, w.rtok, d.E, reinterpret_cast<uint16_t*>(w.h));
   if (after_gate_up) (void)hipEventRecord(after_gate_up, s);
   gemv_down<H, I, B, NT><<<dim3((SPG2 + 3) / 4, groups), 256, 0, s>>>(
-      bk, gdesc, d.E, reinterpret_cast<const uint16_t*>(w.h), w.y);
+      bk, gdesc, d.E, reinterpret_cast<const uint16_t*>(w.h), w.pair, w.y);
 }
 
 template <int H, int I, int B>

@@ -205,8 +205,9 @@ struct TileShape {
 
 template <bool GU, int H, int I, bool THIN>
 __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, const uint8_t* W,
-                                          const float* ss, const int* arow, int valid, int r0,
-                                          int n0, uint8_t* lds, void* __restrict__ out) {
+                                          const float* ss, const int* arow, const int* orow,
+                                          int valid, int r0, int n0, uint8_t* lds,
+                                          void* __restrict__ out) {
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
   using S = TileShape<GU, THIN>;
@@ -429,7 +430,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         h[n0 + S::brow(wn, 0) + l32] =
             f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
       } else {
-        uint16_t* y = reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + row) * H;
+        uint16_t* y = reinterpret_cast<uint16_t*>(out) + (size_t)orow[row] * H;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
           y[n0 + S::brow(wn, nb) + l32] = f32_to_f16_sat(acc[m][nb][v] * unit[nb]);
@@ -444,12 +445,14 @@ void mfma_pass(const uint16_t* __restrict__ act,
                                                         const int32_t* __restrict__ meta,
                                                         const int32_t* __restrict__ tiles,
                                                         const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ rtok, int E,
+                                                        const int32_t* __restrict__ rtok,
+                                                        const int32_t* __restrict__ pair, int E,
                                                         void* __restrict__ out) {
   using P = PassShape<GU, H, I>;
   static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ int arow[kMfmaBM];
+  __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
   constexpr int NKB = P::K / kBK;  // scale blocks along K
   __shared__ float ss[2 * NKB];    // the tile's two scale rows
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
@@ -478,6 +481,9 @@ void mfma_pass(const uint16_t* __restrict__ act,
   if (tid < kMfmaBM) {
     const int rr = tid < valid ? tid : valid - 1;
     arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
+    // y is stored by slot (row r's output goes to y row pair[r]), so the
+    // combine reads a token's outputs without the inverse permutation
+    if (!GU) orow[tid] = pair[r0 + rr];
   }
   // scale rows of the tile's weight rows: GU: the gate block of rows n0 ..
   // n0 + 127 and the matching up block; down: rows n0 .. and n0 + 128 ..
@@ -488,9 +494,9 @@ void mfma_pass(const uint16_t* __restrict__ act,
   }
   __syncthreads();
   if (valid <= 64)
-    pass_tile<GU, H, I, true>(act, W, ss, arow, valid, r0, n0, lds, out);
+    pass_tile<GU, H, I, true>(act, W, ss, arow, orow, valid, r0, n0, lds, out);
   else
-    pass_tile<GU, H, I, false>(act, W, ss, arow, valid, r0, n0, lds, out);
+    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, valid, r0, n0, lds, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -501,10 +507,12 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
   // tile slots rounded up to whole rounds of the XCDs (extra slots exit)
   const unsigned nt8 = (unsigned)((max_mfma_tiles(d) + kXcds - 1) / kXcds * kXcds);
   mfma_pass<true, H, I><<<nt8 * (I / PassShape<true, H, I>::COLS), kPassThreads, 0, s>>>(
-      reinterpret_cast<const uint16_t*>(x), bk, w.meta, w.tiles, w.offsets, w.rtok, d.E, w.h);
+      reinterpret_cast<const uint16_t*>(x), bk, w.meta, w.tiles, w.offsets, w.rtok, w.pair, d.E,
+      w.h);
   if (after_gate_up) (void)hipEventRecord(after_gate_up, s);
   mfma_pass<false, H, I><<<nt8 * (H / PassShape<false, H, I>::COLS), kPassThreads, 0, s>>>(
-      reinterpret_cast<const uint16_t*>(w.h), bk, w.meta, w.tiles, w.offsets, w.rtok, d.E, w.y);
+      reinterpret_cast<const uint16_t*>(w.h), bk, w.meta, w.tiles, w.offsets, w.rtok, w.pair, d.E,
+      w.y);
 }
 
 #define MOE_MFMA_SHAPES(X) \
