@@ -8,9 +8,10 @@ expert bank, so that repeated calls cannot be served from the 256 MB MALL.
 
 Prints one JSON line: MoE-layer tokens/s, plus
   roofline:     the dominant kernel (gate/up expert pass) timed with HIP events
-                recorded around its launch on the layer's stream during every
-                7th timed step (an event record costs the stream a few us, so
-                the other steps run without); algorithmic bytes = the bytes of the experts the
+                attached to its own dispatch (the library launches it with
+                hipExtLaunchKernel when the caller passes them) on every 21st
+                timed step; recording them costs the stream about 1 us, so the
+                other steps run without; algorithmic bytes = the bytes of the experts the
                 step's routing touches (E4M3 weights + fp32 scales), or
                 algorithmic FLOPs for MFMA-bound workloads;
   cpu_baseline: the CPU oracle (fp64 NumPy) timed on a bounded sample of the
@@ -40,8 +41,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-EV_EVERY = 7                   # timed steps per step that records the gate/up events (coprime
-                               # with the input batches and bank copies, so the samples rotate)
+EV_EVERY = 21                  # default: timed steps per step that records the gate/up events
+                               # (coprime with the input batches and bank copies: samples rotate)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
@@ -219,6 +220,9 @@ def main():
     ap.add_argument("--batches", type=int, default=8, help="distinct input batches rotated")
     ap.add_argument("--copies", type=int, default=0, help="device copies of the bank (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--event-every", type=int, default=EV_EVERY,
+                    help="record the gate/up kernel events on every N-th timed step "
+                         "(0: none, no roofline figure)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the copy kernel the PMC counters are calibrated on")
@@ -298,11 +302,12 @@ def main():
         if st != 0:
             raise moe.MoeError(st, "moe_forward")
 
-    # events around the gate/up launch (PERMUTED -> GATE_UP) on every
-    # EV_EVERY-th timed step: each event record costs the stream a few us, so
-    # recording on every step would slow the steps being timed
+    # the gate/up kernel's own start and end (PERMUTED -> GATE_UP, attached to
+    # its dispatch) on every EV_EVERY-th timed step: recording them costs the
+    # stream about a microsecond, so recording on every step would slow the
+    # steps being timed
     K, Wm = args.steps, args.warmup
-    sampled = list(range(0, K, EV_EVERY))
+    sampled = list(range(0, K, args.event_every)) if args.event_every > 0 else []
     ev_pairs = [(hip.event(), hip.event()) for _ in sampled]
     ev_structs = {}
     for i, (a, b) in zip(sampled, ev_pairs):
@@ -325,13 +330,20 @@ def main():
     total_ms = hip.elapsed_ms(start, stop)
     ms = total_ms / K
     gu_ms = [hip.elapsed_ms(a, b) for a, b in ev_pairs]
+    if not gu_ms:  # --event-every 0: time the steps only
+        print(json.dumps({"ms_per_step": round(ms, 5), "steps": K, "tokens_per_s": T / (ms / 1e3)}))
+        return
     gu_avg_ms = sum(gu_ms) / len(gu_ms)
     # the bytes of the sampled steps (for the kernel) and of all steps (for the layer)
     gu_bytes = sum(uniq[(Wm + i) % len(xs)] for i in sampled) / len(sampled) * gu_bytes_per_expert
     mean_uniq = sum(uniq[(Wm + i) % len(xs)] for i in range(K)) / K
     layer_bytes = mean_uniq * all_bytes_per_expert
 
-    # phase breakdown (outside the timed region): all phase events on a few steps
+    # phase breakdown (outside the timed region): all phase events on a few
+    # steps. Each stream-marker event costs the stream ~3 us, and the kernel-
+    # attached pair starts ~6-10 us after a preceding marker, so "permute"
+    # (ROUTED marker -> gate/up kernel start) carries that overhead; the
+    # rocprofv3 kernel traces give the per-kernel times.
     phase = {n: [] for n in ("route", "permute", "gate_up", "down", "combine")}
     for i in range(min(20, K)):
         evs = [hip.event() for _ in range(moe.MOE_EV_COUNT)]

@@ -29,6 +29,8 @@
 //            at +-65504), the form the combine reads.
 // Tokens of a group are taken NT at a time; a larger group takes several
 // passes over the weights already held in registers.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "device.hpp"
@@ -352,21 +354,25 @@ constexpr int gate_up_chunks() {
 
 template <int H, int I, int B, int NT, bool XBF16>
 static void run_gemv(const Dims& d, const void* x, const BankPtrs& bk, const Work& w,
-                     hipStream_t s, hipEvent_t after_gate_up) {
+                     hipStream_t s, KernelEvents ev) {
   constexpr int M = gate_up_chunks<H>();
   constexpr int SPG1 = I / GateUpMap<H, M>::PPW, SPG2 = H / DownMap<I>::RW;
   const int4* gdesc = reinterpret_cast<const int4*>(w.gdesc);
   const int groups = (int)std::min<int64_t>(d.E, d.T * d.k) + d.S;
-  gemv_gate_up<H, I, B, NT, M, XBF16><<<dim3((SPG1 + 3) / 4, groups), 256, 0, s>>>(
-      x, bk, gdesc, w.rtok, d.E, reinterpret_cast<uint16_t*>(w.h));
-  if (after_gate_up) (void)hipEventRecord(after_gate_up, s);
+  const dim3 grid((SPG1 + 3) / 4, groups);
+  uint16_t* h = reinterpret_cast<uint16_t*>(w.h);
+  if (ev.any())  // the events take the kernel's own start and end times
+    hipExtLaunchKernelGGL(gemv_gate_up<H, I, B, NT, M, XBF16>, grid, dim3(256), 0, s, ev.begin,
+                          ev.end, 0, x, bk, gdesc, static_cast<const int32_t*>(w.rtok), d.E, h);
+  else
+    gemv_gate_up<H, I, B, NT, M, XBF16><<<grid, 256, 0, s>>>(x, bk, gdesc, w.rtok, d.E, h);
   gemv_down<H, I, B, NT><<<dim3((SPG2 + 3) / 4, groups), 256, 0, s>>>(
       bk, gdesc, d.E, reinterpret_cast<const uint16_t*>(w.h), w.pair, w.y);
 }
 
 template <int H, int I, int B>
 static void run_gemv_nt(const Dims& d, const void* x, const BankPtrs& bk, const Work& w,
-                        hipStream_t s, hipEvent_t ev) {
+                        hipStream_t s, KernelEvents ev) {
   // tokens per pass: up to 4 (fp32 activations of wide rows: 1, which keeps
   // their LDS stage at 16 KiB); larger groups take several passes over the
   // weights held in registers
@@ -396,13 +402,13 @@ bool has_gemv_instance(const Dims& d) {
 
 hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               hipEvent_t after_gate_up) {
+                               KernelEvents gate_up_events) {
   BankPtrs bk{routed.w_gate_up, routed.w_down, routed.s_gate_up, routed.s_down,
               shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
               shared ? shared->s_gate_up : nullptr, shared ? shared->s_down : nullptr};
 #define X(h, i, b)                                       \
   if (d.H == h && d.I == i && d.B == b) {                \
-    run_gemv_nt<h, i, b>(d, x, bk, w, s, after_gate_up); \
+    run_gemv_nt<h, i, b>(d, x, bk, w, s, gate_up_events); \
     return hipGetLastError();                            \
   }
   MOE_GEMV_SHAPES(X)

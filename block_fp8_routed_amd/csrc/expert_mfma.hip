@@ -28,6 +28,8 @@
 // MFMA operand layout (32x32x16): lane L supplies row L%32 of A and column
 // L%32 of B, each as 8 k of the 16 (k = 8*(L/32) .. +7); lane L of the result
 // holds column L%32, value v being row 8*(v/4) + 4*(L/32) + v%4.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 #include "layer.hpp"
 
@@ -502,14 +504,20 @@ void mfma_pass(const uint16_t* __restrict__ act,
 // ---------------------------------------------------------------------------
 template <int H, int I, int B>
 static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Work& w,
-                     hipStream_t s, hipEvent_t after_gate_up) {
+                     hipStream_t s, KernelEvents ev) {
   static_assert(B == kBK, "MFMA passes take 128 x 128 scale blocks");
   // tile slots rounded up to whole rounds of the XCDs (extra slots exit)
   const unsigned nt8 = (unsigned)((max_mfma_tiles(d) + kXcds - 1) / kXcds * kXcds);
-  mfma_pass<true, H, I><<<nt8 * (I / PassShape<true, H, I>::COLS), kPassThreads, 0, s>>>(
-      reinterpret_cast<const uint16_t*>(x), bk, w.meta, w.tiles, w.offsets, w.rtok, w.pair, d.E,
-      w.h);
-  if (after_gate_up) (void)hipEventRecord(after_gate_up, s);
+  const dim3 grid(nt8 * (I / PassShape<true, H, I>::COLS));
+  const uint16_t* xa = reinterpret_cast<const uint16_t*>(x);
+  const int32_t *meta = w.meta, *tiles = w.tiles, *offsets = w.offsets, *rtok = w.rtok,
+                *pair = w.pair;
+  if (ev.any())  // the events take the kernel's own start and end times
+    hipExtLaunchKernelGGL(mfma_pass<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin, ev.end,
+                          0, xa, bk, meta, tiles, offsets, rtok, pair, d.E, w.h);
+  else
+    mfma_pass<true, H, I><<<grid, kPassThreads, 0, s>>>(xa, bk, meta, tiles, offsets, rtok, pair,
+                                                        d.E, w.h);
   mfma_pass<false, H, I><<<nt8 * (H / PassShape<false, H, I>::COLS), kPassThreads, 0, s>>>(
       reinterpret_cast<const uint16_t*>(w.h), bk, w.meta, w.tiles, w.offsets, w.rtok, w.pair, d.E,
       w.y);
@@ -529,13 +537,13 @@ bool has_mfma_instance(const Dims& d) {
 
 hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               hipEvent_t after_gate_up) {
+                               KernelEvents gate_up_events) {
   MfmaBank bk{routed.w_gate_up, routed.w_down, routed.s_gate_up, routed.s_down,
               shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
               shared ? shared->s_gate_up : nullptr, shared ? shared->s_down : nullptr};
 #define X(hh, ii, bb)                                    \
   if (d.H == hh && d.I == ii && d.B == bb) {             \
-    run_mfma<hh, ii, bb>(d, x, bk, w, s, after_gate_up); \
+    run_mfma<hh, ii, bb>(d, x, bk, w, s, gate_up_events); \
     return hipGetLastError();                            \
   }
   MOE_MFMA_SHAPES(X)

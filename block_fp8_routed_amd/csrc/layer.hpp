@@ -118,13 +118,19 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int
 bool small_select_permute(const Dims& d);
 hipError_t launch_select_permute_small(const Dims& d, const float* plog, const float* bias,
                                        const Work& w, int tile_rows, hipStream_t s);
+// Events attached to the gate/up kernel's own dispatch (either may be null):
+// begin takes the kernel's start time, end its end time.
+struct KernelEvents {
+  hipEvent_t begin, end;
+  bool any() const { return begin != nullptr || end != nullptr; }
+};
 // expert passes; returns hipErrorInvalidValue if no instantiation matches
 hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               hipEvent_t after_gate_up);
+                               KernelEvents gate_up_events);
 hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               hipEvent_t after_gate_up);
+                               KernelEvents gate_up_events);
 bool has_gemv_instance(const Dims& d);
 bool has_mfma_instance(const Dims& d);
 hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s);

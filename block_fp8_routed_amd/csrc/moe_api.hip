@@ -159,8 +159,11 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
 
   const Work w = carve(d, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t ev_gate_up =
-      events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr;
+  // PERMUTED and GATE_UP are attached to the gate/up kernel's dispatch (its
+  // start and end times), so that pair times that kernel alone
+  const KernelEvents ev_gate_up{
+      events ? static_cast<hipEvent_t>(events->ev[MOE_EV_PERMUTED]) : nullptr,
+      events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr};
   if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
   const bool small = small_select_permute(d);
   if (launch_router(d, x, router_w, w, s) != hipSuccess) return MOE_ERR_HIP;
@@ -178,7 +181,6 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
     if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
     if (launch_permute(d, w.topk, w, tile_rows, true, s) != hipSuccess) return MOE_ERR_HIP;
   }
-  if (!rec(events, MOE_EV_PERMUTED, s)) return MOE_ERR_HIP;
   const moe_expert_bank* sh = d.S ? shared : nullptr;
   const hipError_t e = d.mfma ? launch_experts_mfma(d, x, *experts, sh, w, s, ev_gate_up)
                               : launch_experts_gemv(d, x, *experts, sh, w, s, ev_gate_up);

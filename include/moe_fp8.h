@@ -102,15 +102,21 @@ typedef struct {
 
 /* Optional per-phase HIP events (hipEvent_t passed as void*). Each non-NULL
  * event is recorded on `stream` at the named phase boundary, so a caller can
- * time the phases of a call with hipEventElapsedTime. NULL entries are
- * skipped; pass NULL for the whole struct to record nothing. */
+ * time the phases of a call with hipEventElapsedTime. PERMUTED and GATE_UP
+ * are attached to the gate/up kernel's own dispatch (hipExtLaunchKernel):
+ * they take that kernel's start and end times, so the pair times the kernel
+ * alone, without the dispatch gap before it (which falls in ROUTED ->
+ * PERMUTED). NULL entries are skipped; pass NULL for the whole struct to
+ * record nothing. */
 typedef enum {
   MOE_EV_START = 0,        /* before the router                            */
   MOE_EV_ROUTED = 1,       /* after logits + top-k + gates (at decode sizes,  */
                            /* where selection and permutation share one      */
                            /* launch: after the logits)                      */
-  MOE_EV_PERMUTED = 2,     /* after the token→expert permutation           */
-  MOE_EV_GATE_UP = 3,      /* after gate/up + SwiGLU (routed and shared)   */
+  MOE_EV_PERMUTED = 2,     /* start of the gate/up kernel (after the       */
+                           /* token→expert permutation)                     */
+  MOE_EV_GATE_UP = 3,      /* end of the gate/up + SwiGLU kernel (routed   */
+                           /* and shared)                                   */
   MOE_EV_DOWN = 4,         /* after the down projection                    */
   MOE_EV_END = 5,          /* after the combine                            */
   MOE_EV_COUNT = 6
