@@ -50,7 +50,7 @@ def test_device_dequant_block_grid():
 # ---------------------------------------------------------------- router ---
 ROUTE_CASES = [
     ("c0", None), ("c1", 1), ("c1", 4), ("c1", 16), ("c1", 17), ("c2", None),
-    ("c3", None), ("c3", 300), ("c4", None),
+    ("c3", None), ("c3", 300), ("c4", None), ("c0e1024k16", 16), ("c0e1024k16", 37),
 ]
 
 
@@ -58,7 +58,7 @@ ROUTE_CASES = [
 def test_route_matches_oracle(name, T):
     # routing needs no expert bank: build the inputs directly
     import block_fp8_routed_amd as moe
-    shape = C[name]
+    shape = C[name] if name in C else C["c0"].with_(experts=1024, top_k=16, name=name)
     T = shape.tokens if T is None else T
     x = W.gen_x(shape, T)
     wr, b = W.gen_router(shape), W.gen_bias(shape)
@@ -119,6 +119,12 @@ FWD_CASES = [  # (config, tokens, path, overrides)
     ("c1", 300, "mfma", {"experts": 16, "top_k": 4}),
     ("c2", None, "auto", {}),
     ("c3", 100, "mfma", {}),
+    # the limits: top-16 (the most a token may choose) of 512 experts through the
+    # one-workgroup decode selection, and 1024 experts (the most supported) with a
+    # shared expert through the multi-block path
+    ("c0", 16, "gemv", {"experts": 512, "top_k": 16}),
+    ("c0", 20, "gemv", {"experts": 1024, "top_k": 16, "shared": True}),
+    ("c0", 3, "gemv", {"experts": 1024, "top_k": 1}),
 ]
 
 
