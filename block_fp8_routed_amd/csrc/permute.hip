@@ -139,15 +139,19 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
 //     (acquire) turns the histograms into offsets, per-block bases
 //     bbase[b][e] = offsets[e] + (rows of e in blocks before b), group
 //     descriptors and MFMA row tiles. No block waits for another. *counter
-//     must be zero at launch.
+//     must be zero at launch. Up to kPermOneBlock slots run as one block,
+//     which takes the counts straight from LDS (no hand-over).
 //   perm_scatter: block b places its slots: its wavefronts take consecutive
 //     sub-ranges, count per (wavefront, expert), take exclusive prefixes over
 //     wavefronts on top of bbase[b][e], and walk their slots in order with
-//     ballot peer ranks (as permute_body), so rows keep slot order.
+//     ballot peer ranks, so rows keep slot order.
 constexpr int kPermBlockSlots = 512;  // slots per block (at most kPermMaxBlocks blocks)
+constexpr int kPermBatch = 4;         // slot loads per thread issued together
 constexpr int kPermMaxBlocks = kPermMaxBlocksHost;
 
+constexpr int kPermOneBlock = 4096;   // up to this many slots: one block, no hand-over
 inline int perm_blocks(int64_t TK) {
+  if (TK <= kPermOneBlock) return 1;
   int64_t nb = (TK + kPermBlockSlots - 1) / kPermBlockSlots;
   return (int)(nb < 1 ? 1 : (nb > kPermMaxBlocks ? kPermMaxBlocks : nb));
 }
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(1024) void perm_count(
     int32_t* __restrict__ meta, int4* __restrict__ gdesc, int32_t* __restrict__ tiles,
     int tile_rows) {
   __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t tmp[64];
+  __shared__ int32_t tmp[3 * 64];
   __shared__ int last;
   const int tid = threadIdx.x;
   const int64_t TK = T * k;
@@ -166,31 +170,57 @@ __global__ __launch_bounds__(1024) void perm_count(
   const int64_t lo = (int64_t)blockIdx.x * per, hi = lo + per < TK ? lo + per : TK;
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
-  for (int64_t s = lo + tid; s < hi; s += 1024) {
-    const int e = topk[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  // kPermBatch slots per thread are loaded before any is counted (indices
+  // clamped, so the loads are unconditional and go out together)
+  for (int64_t s0 = lo + tid; s0 < hi; s0 += 1024 * kPermBatch) {
+    int ev[kPermBatch];
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i) {
+      const int64_t s = s0 + 1024 * i;
+      ev[i] = topk[s < hi ? s : hi - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i)
+      if (s0 + 1024 * i < hi && (unsigned)ev[i] < (unsigned)E) atomicAdd(&cnt[ev[i]], 1);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) bcnt[(size_t)blockIdx.x * E + e] = cnt[e];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0)
-    last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nb - 1;
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // one expert per thread (E <= 1024): prefix over blocks, in block order
-  const int e = tid;
+  const int e = tid;  // from here on one expert per thread (E <= 1024)
   int c = 0;
   int32_t pre[kPermMaxBlocks];
+  if (nb == 1) {  // uniform: the one block holds every count
+    c = e < E ? cnt[e] : 0;
 #pragma unroll
-  for (int b = 0; b < kPermMaxBlocks; ++b) {
-    const int v = (e < E && b < nb) ? bcnt[(size_t)b * E + e] : 0;
-    pre[b] = c;
-    c += v;
+    for (int b = 0; b < kPermMaxBlocks; ++b) pre[b] = 0;
+  } else {
+    for (int i = tid; i < E; i += 1024) bcnt[(size_t)blockIdx.x * E + i] = cnt[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             nb - 1;
+    __syncthreads();
+    if (!last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // prefix over blocks, in block order; every count is requested before
+    // any is summed (clamped indices)
+#pragma unroll
+    for (int b = 0; b < kPermMaxBlocks; ++b)
+      pre[b] = bcnt[(size_t)(b < nb ? b : nb - 1) * E + (e < E ? e : E - 1)];
+#pragma unroll
+    for (int b = 0; b < kPermMaxBlocks; ++b) {
+      const int v = (e < E && b < nb) ? pre[b] : 0;
+      pre[b] = c;
+      c += v;
+    }
   }
-  int total;
-  const int off = block_excl_scan<16>(c, tmp, &total);
+  // non-empty groups and MFMA row tiles, ascending expert, shared last
+  const int nf = (e < E && c > 0) ? 1 : 0;
+  const int nt = (e < E && tile_rows > 0) ? (c + tile_rows - 1) / tile_rows : 0;
+  const int sv[3] = {c, nf, nt};
+  int sx[3], st[3];
+  block_excl_scan<16, 3>(sv, sx, st, tmp);
+  const int off = sx[0], apos = sx[1], tpos = sx[2];
+  const int total = st[0], nact = st[1], ntile = st[2];
   if (e < E) {
     offsets[e] = off;
 #pragma unroll
@@ -201,12 +231,6 @@ __global__ __launch_bounds__(1024) void perm_count(
     offsets[E] = total;
     offsets[E + 1] = (int)(total + S * T);
   }
-  // non-empty groups and MFMA row tiles, ascending expert, shared last
-  const int nf = (e < E && c > 0) ? 1 : 0;
-  const int nt = (e < E && tile_rows > 0) ? (c + tile_rows - 1) / tile_rows : 0;
-  int nact, ntile = 0;
-  const int apos = block_excl_scan<16>(nf, tmp, &nact);
-  const int tpos = tile_rows > 0 ? block_excl_scan<16>(nt, tmp, &ntile) : 0;
   if (nf) gdesc[apos] = make_int4(e, off, c, 0);
   for (int m = 0, tp = tpos; m < nt; ++m, ++tp) {
     tiles[2 * tp] = e;
@@ -228,13 +252,17 @@ __global__ __launch_bounds__(1024) void perm_count(
   for (int y = nact + S + tid; y < E + 2; y += 1024) gdesc[y] = make_int4(-1, 0, 0, 0);
 }
 
-// lds: (16 * E) int32 of shared memory
+// lds: (16 + prefix) * E int32 of shared memory. prefix (uniform): the block's base
+// per expert is offsets[e] + its own count of the slots before its range
+// (used when the counting kernel ran as one block and left no per-block
+// bases); otherwise bbase[b][e].
 __global__ __launch_bounds__(1024) void perm_scatter(
-    const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb,
+    const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb, int prefix,
     const int32_t* __restrict__ bbase, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ pair, int32_t* __restrict__ inv, int32_t* __restrict__ rtok) {
-  extern __shared__ int32_t wcnt[];  // [16][E]
+  extern __shared__ int32_t wcnt[];  // [16][E], then the prefix counts [E]
   constexpr int W = 16;
+  int32_t* pcnt = wcnt + W * E;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t TK = T * k;
   const int64_t per = (TK + nb - 1) / nb;
@@ -242,16 +270,41 @@ __global__ __launch_bounds__(1024) void perm_scatter(
   const int64_t wper = (bhi - blo + W - 1) / W;
   const int64_t lo = blo + w * wper < bhi ? blo + w * wper : bhi;
   const int64_t hi = lo + wper < bhi ? lo + wper : bhi;
-  for (int i = tid; i < W * E; i += 1024) wcnt[i] = 0;
+  for (int i = tid; i < (W + prefix) * E; i += 1024) wcnt[i] = 0;
   __syncthreads();
-  for (int64_t s = lo + lane; s < hi; s += 64) {
-    const int e = topk[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&wcnt[w * E + e], 1);
+  if (prefix) {  // count of each expert among slots [0, blo)
+    for (int64_t s0 = tid; s0 < blo; s0 += 1024 * kPermBatch) {
+      int pv[kPermBatch];
+#pragma unroll
+      for (int i = 0; i < kPermBatch; ++i) {
+        const int64_t s = s0 + 1024 * i;
+        pv[i] = topk[s < blo ? s : blo - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < kPermBatch; ++i)
+        if (s0 + 1024 * i < blo && (unsigned)pv[i] < (unsigned)E) atomicAdd(&pcnt[pv[i]], 1);
+    }
+  }
+  // the wavefront's slots, kPermBatch rounds of 64 at a time: loaded (clamped,
+  // unconditional) before any is used, kept for the scatter below when the
+  // wavefront has at most kPermBatch rounds
+  int ev[kPermBatch];
+#pragma unroll
+  for (int i = 0; i < kPermBatch; ++i) ev[i] = 0;
+  for (int64_t s0 = lo + lane; s0 < hi; s0 += 64 * kPermBatch) {
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i) {
+      const int64_t s = s0 + 64 * i;
+      ev[i] = topk[s < hi ? s : hi - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i)
+      if (s0 + 64 * i < hi && (unsigned)ev[i] < (unsigned)E) atomicAdd(&wcnt[w * E + ev[i]], 1);
   }
   __syncthreads();
   // exclusive prefix over wavefronts on top of the block's base
   for (int e = tid; e < E; e += 1024) {
-    int run = bbase[(size_t)blockIdx.x * E + e];
+    int run = prefix ? offsets[e] + pcnt[e] : bbase[(size_t)blockIdx.x * E + e];
     for (int ww = 0; ww < W; ++ww) {
       const int c = wcnt[ww * E + e];
       wcnt[ww * E + e] = run;
@@ -260,9 +313,17 @@ __global__ __launch_bounds__(1024) void perm_scatter(
   }
   __syncthreads();
   const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const bool held = hi - lo <= 64 * kPermBatch;  // uniform: ev holds every round
   for (int64_t b0 = lo; b0 < hi; b0 += 64) {
     const int64_t s = b0 + lane;
-    const int e_in = s < hi ? topk[s] : 0;
+    int e_in = 0;
+    if (held) {
+#pragma unroll
+      for (int i = 0; i < kPermBatch; ++i)
+        if (b0 == lo + 64 * i) e_in = ev[i];
+    } else if (s < hi) {
+      e_in = topk[s];
+    }
     const bool ok = s < hi && (unsigned)e_in < (unsigned)E;
     const int e = ok ? e_in : 0;
     if (s < hi && !ok) inv[s] = -1;
@@ -301,13 +362,20 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int
                           bool counter_zeroed, hipStream_t s) {
   int32_t* counter = w.meta + kMetaPermCounter;
   if (!counter_zeroed) zero_word<<<1, 1, 0, s>>>(counter);
-  const int nb = perm_blocks(d.T * d.k);
+  const int64_t TK = d.T * d.k;
+  const int nb = perm_blocks(TK);
   perm_count<<<nb, 1024, 0, s>>>(topk, d.T, d.k, d.E, d.S, nb, w.pblock, counter, w.offsets,
                                  w.pblock + (size_t)kPermMaxBlocks * d.E, w.meta,
                                  reinterpret_cast<int4*>(w.gdesc), w.tiles, tile_rows);
-  perm_scatter<<<nb, 1024, (size_t)16 * d.E * sizeof(int32_t), s>>>(
-      topk, d.T, d.k, d.E, d.S, nb, w.pblock + (size_t)kPermMaxBlocks * d.E, w.offsets, w.pair,
-      w.inv, w.rtok);
+  // one counting block leaves the bases of one placing block only: the
+  // placing blocks (1024 slots each, one round per wavefront) then count
+  // their own prefixes, as long as the extra LDS row keeps the block within
+  // 64 KiB of dynamic LDS (else one placing block takes every slot)
+  const int prefix = (nb == 1 && (size_t)17 * d.E * sizeof(int32_t) <= 65536) ? 1 : 0;
+  const int nbs = prefix ? (int)((TK + 1023) / 1024) : nb;
+  perm_scatter<<<nbs, 1024, (size_t)(16 + prefix) * d.E * sizeof(int32_t), s>>>(
+      topk, d.T, d.k, d.E, d.S, nbs, prefix, w.pblock + (size_t)kPermMaxBlocks * d.E, w.offsets,
+      w.pair, w.inv, w.rtok);
   return hipGetLastError();
 }
 

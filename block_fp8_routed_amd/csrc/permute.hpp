@@ -25,33 +25,37 @@
 
 namespace moe {
 
-template <int W>
-__device__ int block_excl_scan(int v, int* tmp, int* total) {
+// Exclusive prefix sums of N values per thread over a workgroup of W
+// wavefronts (W <= 32), all N at once: DPP scans inside each wavefront, then
+// a DPP scan of the wavefront totals by wavefront 0. tmp: N * 64 int32 of
+// shared memory; total[i] gets the workgroup's sum of value i.
+template <int W, int N>
+__device__ void block_excl_scan(const int (&v)[N], int (&res)[N], int (&total)[N], int* tmp) {
+  static_assert(W <= 32, "wavefront totals fit one scan");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = v;
+  int inc[N];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += n;
+  for (int i = 0; i < N; ++i) {
+    inc[i] = wave_incl_scan(v[i]);
+    if (lane == 63) tmp[64 * i + w] = inc[i];
   }
-  if (lane == 63) tmp[w] = inc;
   __syncthreads();
   if (w == 0) {
-    const int t = lane < W ? tmp[lane] : 0;
-    int ti = t;
 #pragma unroll
-    for (int o = 1; o < W; o <<= 1) {
-      const int n = __shfl_up(ti, o, 64);
-      if (lane >= o) ti += n;
+    for (int i = 0; i < N; ++i) {
+      const int t = lane < W ? tmp[64 * i + lane] : 0;
+      const int ti = wave_incl_scan(t);
+      if (lane < W) tmp[64 * i + 32 + lane] = ti - t;
+      if (lane == W - 1) tmp[64 * i + 63] = ti;
     }
-    if (lane < W) tmp[32 + lane] = ti - t;
-    if (lane == W - 1) tmp[63] = ti;
   }
   __syncthreads();
-  const int res = inc - v + tmp[32 + w];
-  *total = tmp[63];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    res[i] = inc[i] - v[i] + tmp[64 * i + 32 + w];
+    total[i] = tmp[64 * i + 63];
+  }
   __syncthreads();
-  return res;
 }
 
 // Exclusive prefix sum over the 64 lanes of a wavefront; *total gets the sum.
