@@ -88,7 +88,6 @@ struct Work {
   int32_t* tiles;    // [max_tiles][2] (group, first row) of each MFMA row tile
   void* h;           // [P][I] fp16 SwiGLU output
   uint16_t* y;       // [P][H] fp16 expert outputs by slot (saturated at +-65504)
-  uint16_t* rsplit;  // [3][E][H] bf16 planes of the router weights (MFMA router)
   int32_t* pblock;   // [2][16][E] per-block expert counts, then per-block bases
 };
 

@@ -14,7 +14,7 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 14;
+constexpr int kRegions = 13;
 
 static void region_sizes(const Dims& d, size_t* sz) {
   sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
@@ -29,8 +29,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[9] = (size_t)max_mfma_tiles(d) * 8;  // tiles
   sz[10] = (size_t)d.P * d.I * 2;         // h (fp16)
   sz[11] = (size_t)d.P * d.H * 2;         // y (fp16)
-  sz[12] = router_kind(d) == kRouterMfma ? (size_t)3 * d.E * d.H * 2 : 0;  // router planes
-  sz[13] = (size_t)2 * kPermMaxBlocksHost * d.E * 4;  // permutation block counts and bases
+  sz[12] = (size_t)2 * kPermMaxBlocksHost * d.E * 4;  // permutation block counts and bases
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -62,8 +61,7 @@ Work carve(const Dims& d, void* base) {
   w.tiles = static_cast<int32_t*>(r[9]);
   w.h = r[10];
   w.y = static_cast<uint16_t*>(r[11]);
-  w.rsplit = static_cast<uint16_t*>(r[12]);
-  w.pblock = static_cast<int32_t*>(r[13]);
+  w.pblock = static_cast<int32_t*>(r[12]);
   return w;
 }
 

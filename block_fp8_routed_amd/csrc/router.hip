@@ -194,26 +194,21 @@ static void slices_launch(const Dims& d, const void* x, const float* wr, float* 
 // lo = bf16(w - hi - mid), each difference exact in fp32), which leaves a
 // remainder below 2^-24 |w|. A logit is then the sum of three bf16 MFMA
 // contractions of the (exact) bf16 activations, each product exact in fp32.
-__global__ __launch_bounds__(256) void router_split(const float* __restrict__ wr, int64_t n,
-                                                    uint16_t* __restrict__ planes) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float w = wr[i];
-  const uint32_t hb = f32_to_bf16_bits(w);
+// The split is done in registers as the fp32 weights are staged into LDS.
+__device__ __forceinline__ void split3(float w, uint32_t& hb, uint32_t& mb, uint32_t& lb) {
+  hb = f32_to_bf16_bits(w);
   const float r1 = w - __uint_as_float(hb << 16);
-  const uint32_t mb = f32_to_bf16_bits(r1);
+  mb = f32_to_bf16_bits(r1);
   const float r2 = r1 - __uint_as_float(mb << 16);
-  const uint32_t lb = f32_to_bf16_bits(r2);
-  planes[i] = (uint16_t)hb;
-  planes[n + i] = (uint16_t)mb;
-  planes[2 * n + i] = (uint16_t)lb;
+  lb = f32_to_bf16_bits(r2);
 }
 
 // Tile of 128 tokens x 128 experts over one slice of H (blockIdx.z), 256
 // threads as 2 x 2 wavefronts of 64 x 64 (2 x 2 MFMA tiles of 32 x 32). K runs
-// in stages of 32: the stage's activation tile and three weight-plane tiles
+// in stages of 32: the stage's activation tile (bf16) and weight tile (fp32)
 // are fetched global -> registers two stages ahead (a ring of two register
-// sets) and stored into the other of two LDS buffers after the stage's MFMAs.
+// sets) and stored into the other of two LDS buffers after the stage's MFMAs,
+// the weights as their three bf16 planes.
 // 16-byte chunks are XOR-swizzled by row (chunk c of row r at slot c ^ ((r >>
 // 2) & 3)) against bank conflicts. Rows past T and experts past E repeat the
 // last one, and a stage index past the slice's end repeats its last stage
@@ -226,42 +221,61 @@ constexpr int kRtA = kRtBM * kRtRow;             // 8 KiB
 constexpr int kRtStage = kRtA + 3 * kRtBN * kRtRow;  // 32 KiB
 
 __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ x,
-                                                  const uint16_t* __restrict__ planes,
+                                                  const float* __restrict__ wr,
                                                   float* __restrict__ plog, int T, int H, int E,
                                                   int HS) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kRtStage];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.x * kRtBM, e0 = blockIdx.y * kRtBN, h0 = blockIdx.z * HS;
-  const size_t plane = (size_t)E * H;
-  // fetch map: A chunk q = tid + 256 i (i < 2): row q / 4, chunk q % 4;
-  // B chunk q = tid + 256 i (i < 6): plane q / 512, row (q % 512) / 4, chunk q % 4
-  const uint16_t* src[8];
-  int dst[8];
+  // fetch map: A chunk q = tid + 256 i (i < 2): row q / 4, chunk q % 4 (8 bf16);
+  // B chunk q = tid + 256 i (i < 4): weight row q / 8, chunk q % 8 (4 fp32),
+  // stored as 4 bf16 (8 bytes) at the same place of each of the three planes
+  const uint16_t* asrc[2];
+  int adst[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int q = tid + 256 * i, r = q >> 2, c = q & 3;
     const int row = m0 + r < T ? m0 + r : T - 1;
-    src[i] = x + (size_t)row * H + h0 + 8 * c;
-    dst[i] = r * kRtRow + 16 * (c ^ ((r >> 2) & 3));
+    asrc[i] = x + (size_t)row * H + h0 + 8 * c;
+    adst[i] = r * kRtRow + 16 * (c ^ ((r >> 2) & 3));
   }
+  const float* bsrc[4];
+  int bdst[4];
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int q = tid + 256 * i, p = q >> 9, r = (q & 511) >> 2, c = q & 3;
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + 256 * i, r = q >> 3, c8 = q & 7;
     const int e = e0 + r < E ? e0 + r : E - 1;
-    src[2 + i] = planes + p * plane + (size_t)e * H + h0 + 8 * c;
-    dst[2 + i] = kRtA + p * (kRtBN * kRtRow) + r * kRtRow + 16 * (c ^ ((r >> 2) & 3));
+    bsrc[i] = wr + (size_t)e * H + h0 + 4 * c8;
+    bdst[i] = kRtA + r * kRtRow + 16 * ((c8 >> 1) ^ ((r >> 2) & 3)) + 8 * (c8 & 1);
   }
   const int NS = HS / kRtKS;
-  typedef uint4 StageRegs[8];
+  struct StageRegs {
+    uint4 a[2], b[4];
+  };
   auto fetch = [&](StageRegs& v, int st) {
     st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ld16(src[i] + st * kRtKS);
+    for (int i = 0; i < 2; ++i) v.a[i] = ld16(asrc[i] + st * kRtKS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v.b[i] = ld16(bsrc[i] + st * kRtKS);
   };
   auto put = [&](const StageRegs& v, int buf) {
+    uint8_t* L = lds + buf * kRtStage;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(lds + buf * kRtStage + dst[i]) = v[i];
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(L + adst[i]) = v.a[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t f[4] = {v.b[i].x, v.b[i].y, v.b[i].z, v.b[i].w};
+      uint32_t hb[4], mb[4], lb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) split3(__uint_as_float(f[j]), hb[j], mb[j], lb[j]);
+      *reinterpret_cast<uint2*>(L + bdst[i]) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
+      *reinterpret_cast<uint2*>(L + bdst[i] + kRtBN * kRtRow) =
+          make_uint2(mb[0] | mb[1] << 16, mb[2] | mb[3] << 16);
+      *reinterpret_cast<uint2*>(L + bdst[i] + 2 * kRtBN * kRtRow) =
+          make_uint2(lb[0] | lb[1] << 16, lb[2] | lb[3] << 16);
+    }
   };
   const int q = lane >> 5, l32 = lane & 31;
   rf32x16_t acc[2][2];
@@ -344,15 +358,13 @@ hipError_t launch_router(const Dims& d, const void* x, const float* wr, const Wo
         slices_launch<4>(d, x, wr, plog, s);
       break;
     case kRouterMfma: {
-      const int64_t n = (int64_t)d.E * d.H;
       const int ns = router_slices(d);
       // stages come in pairs (router_kind takes this kernel only for H a
       // multiple of 64, and slices of more than one are multiples of 128)
       if ((d.H / ns) % (2 * kRtKS) != 0) return hipErrorInvalidValue;
-      router_split<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(wr, n, w.rsplit);
       const dim3 grid((unsigned)((d.T + kRtBM - 1) / kRtBM), (d.E + kRtBN - 1) / kRtBN, ns);
-      router_mfma<<<grid, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(x), w.rsplit, plog,
-                                       (int)d.T, d.H, d.E, d.H / ns);
+      router_mfma<<<grid, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(x), wr, plog, (int)d.T,
+                                       d.H, d.E, d.H / ns);
       break;
     }
     default: {
