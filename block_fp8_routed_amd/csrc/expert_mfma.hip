@@ -335,6 +335,9 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     }
     const uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
     const uint8_t* B = A + S::ASTAGE;
+    // the stage's MFMAs run at raised wave priority, so that a wavefront
+    // ready to compute issues ahead of those waiting on loads and barriers
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int p = 0; p < KS / 32; ++p) {
       uint4 braw[NBW];
@@ -357,6 +360,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (S::DEPTH == 1) {
