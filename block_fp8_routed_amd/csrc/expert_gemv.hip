@@ -26,7 +26,8 @@
 //            major [P][I] in permuted row order, the form the MFMA family uses.
 //   down:    y[row][n] = sum_i h[row][i] * Wd[n][i]: exact fp16 weight pairs
 //            meet h in v_dot2c_f32_f16; y is written as fp16 [P][H] (saturated
-//            at +-65504), the form the combine reads.
+//            at +-65504) by slot (row r's output to y row pair[r]), the form
+//            the combine reads.
 // Tokens of a group are taken NT at a time; a larger group takes several
 // passes over the weights already held in registers.
 #include <hip/hip_ext.h>

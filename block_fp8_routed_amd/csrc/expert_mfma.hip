@@ -20,7 +20,8 @@
 // so nothing is rounded on the way in; SwiGLU is applied to the accumulator
 // registers and h is written as fp16 [P][I] (11-bit significand, saturated at
 // +-65504). down runs fp16 MFMA on h (the weights are exact in fp16 as well)
-// and writes y as fp16 [P][H] (saturated the same way). h and y are the two
+// and writes y as fp16 [P][H] by slot (row r's output to y row pair[r]),
+// saturated the same way. h and y are the two
 // intermediates rounded below fp32: fp16 keeps their relative error at 2^-11,
 // which leaves the layer's output well inside its tolerance (max error <=
 // 1e-2 x RMS); bf16 would use up most of it.

@@ -131,7 +131,7 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
 }
 
 // ------------------------------------------------------ multi-block (T > 16)
-// The same permutation as permute_body, spread over NB blocks of consecutive
+// The token -> expert permutation, spread over NB blocks of consecutive
 // slots so that large batches are not serialised on one compute unit.
 //   perm_count: block b histograms its slots (LDS counters) into
 //     bcnt[b][E]; then it publishes them (device-scope release, one atomic
