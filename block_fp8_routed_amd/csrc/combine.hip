@@ -13,7 +13,8 @@
 namespace moe {
 
 // Thread i of a workgroup sums 8 consecutive outputs of one token (16-byte
-// fp16 loads of y, fp32 accumulation).
+// fp16 loads of y, fp32 accumulation). y is read once and out written once,
+// so both go through non-temporal accesses.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                      const float* __restrict__ gates, int64_t T,
@@ -34,9 +35,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
   };
   for (int j = 0; j < k; ++j)
-    add(ld16(y + (size_t)(t * k + j) * H + n), gates[t * k + j]);
+    add(ld16_nt(y + (size_t)(t * k + j) * H + n), gates[t * k + j]);
   if (S) {
-    const uint4 v = ld16(y + (size_t)(T * k + t) * H + n);
+    const uint4 v = ld16_nt(y + (size_t)(T * k + t) * H + n);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -51,11 +52,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     o.y = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
     o.z = f32_to_bf16_bits(a[4]) | (f32_to_bf16_bits(a[5]) << 16);
     o.w = f32_to_bf16_bits(a[6]) | (f32_to_bf16_bits(a[7]) << 16);
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * H + n) = o;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w},
+                                reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + t * H + n));
   } else {
-    float* o = reinterpret_cast<float*>(out) + t * H + n;
-    *reinterpret_cast<float4*>(o) = make_float4(a[0], a[1], a[2], a[3]);
-    *reinterpret_cast<float4*>(o + 4) = make_float4(a[4], a[5], a[6], a[7]);
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    f32x4v* o = reinterpret_cast<f32x4v*>(reinterpret_cast<float*>(out) + t * H + n);
+    __builtin_nontemporal_store(f32x4v{a[0], a[1], a[2], a[3]}, o);
+    __builtin_nontemporal_store(f32x4v{a[4], a[5], a[6], a[7]}, o + 1);
   }
 }
 
