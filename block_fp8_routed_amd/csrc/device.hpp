@@ -201,11 +201,15 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// AUX is the instruction's cache-policy field (gfx950: bit 1 = nt, a
+// non-temporal access for data read once).
+template <int AUX = 0>
 __device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+constexpr int kBufNonTemporal = 2;
 
 // Workgroup barrier that orders LDS accesses only: global loads still in
 // flight (streamed weights) stay in flight across it, where __syncthreads()

@@ -260,8 +260,12 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
 #pragma unroll
     for (int i = 0; i < AC; ++i) R.a[i] = buffer_ld16(arsrc, asrc[i], (uint32_t)(st * KS * 2));
 #pragma unroll
+    // thin gate/up tiles stream weights read once, a whole 128-byte line per
+    // row and stage: non-temporal. (64-k stages read half lines, whose other
+    // half the next stage finds in L2 only if the line was kept.)
     for (int i = 0; i < BC; ++i)
-      R.b[i] = buffer_ld16(brsrc, bsrc0, (uint32_t)(brow_of(i) * K + st * KS));
+      R.b[i] = buffer_ld16<S::WIDE ? kBufNonTemporal : 0>(brsrc, bsrc0,
+                                                          (uint32_t)(brow_of(i) * K + st * KS));
   };
   auto put = [&](Regs& R, int buf, int st) {
     uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
