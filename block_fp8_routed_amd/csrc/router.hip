@@ -287,6 +287,7 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
       for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
   auto compute = [&](int buf) {
     const uint8_t* L = lds + buf * kRtStage;
+    __builtin_amdgcn_s_setprio(1);  // a wavefront ready to compute issues first
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // k16 steps; lane group q takes chunk 2t + q
       const int c = 2 * t + q;
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // stage s lives in register set s % 2 until it is stored to LDS buffer s % 2
   StageRegs v[2];
