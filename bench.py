@@ -307,7 +307,9 @@ def main():
     # stream about a microsecond, so recording on every step would slow the
     # steps being timed
     K, Wm = args.steps, args.warmup
-    sampled = list(range(0, K, args.event_every)) if args.event_every > 0 else []
+    # (the first sample is step EV_EVERY-1: the first timed step follows the
+    # warm-up's synchronize and can run at a lower clock)
+    sampled = list(range(args.event_every - 1, K, args.event_every)) if args.event_every > 0 else []
     ev_pairs = [(hip.event(), hip.event()) for _ in sampled]
     ev_structs = {}
     for i, (a, b) in zip(sampled, ev_pairs):
