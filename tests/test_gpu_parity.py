@@ -80,6 +80,9 @@ PERM_CASES = [  # (T, E, k, shared, skew)
     (1, 8, 2, False, 0), (4, 8, 2, True, 0), (16, 128, 8, False, 0), (37, 16, 16, True, 0),
     (1, 1, 1, True, 0), (300, 512, 10, True, 0), (4096, 512, 10, True, 1),
     (2000, 1024, 4, False, 1), (1000, 513, 7, True, 0),
+    # either side of the one-block counting limit (4096 slots), skewed so some
+    # experts take many slots
+    (512, 128, 8, False, 1), (513, 128, 8, True, 1),
 ]
 
 
