@@ -320,7 +320,12 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   // 16 B bytes (16 k) of chunk 2p + q for step pair p and uses its halves in
   // steps 2p and 2p + 1; the A fragment of step 2p + h for group q is then 8
   // k at chunk 4p + 2q + h (8 bf16 per A chunk).
+  // a wavefront whose rows all lie past the group's end (a thin tile of at
+  // most 32 rows) skips its MFMAs; it still fetches and stores its share of
+  // the stage and takes part in every barrier (uniform per wavefront)
+  const bool idle = S::arow0(wm) >= valid;
   auto compute = [&](int buf, int st) {
+    if (idle) return;
     if ((st * KS) % kBK == 0) {  // entering scale block kb
       const int kb = st * KS / kBK;
 #pragma unroll
