@@ -1,0 +1,63 @@
+"""Host-side logic of bench.py (no GPU): the PMC traffic bookkeeping behind
+the JSON line's roofline.traffic."""
+import json
+import os
+import sys
+import types
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _csv(path, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (kernel, value) in enumerate(rows):
+            f.write(f'{i},"{kernel}",X,{value}\n')
+    return str(path)
+
+
+def test_traffic_report_scales_counters_by_the_copy_kernel(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gu = "void moe::gemv_gate_up<2048, 768, 128, 4, 4, true>(void const*, ...)"
+    fetch = _csv(tmp_path / "f.csv", [(gu, 1000.0), ("void moe::gemv_down<...>", 7.0), (gu, 3000.0)])
+    write = _csv(tmp_path / "w.csv", [(gu, 8.0), (gu, 12.0)])
+    mib = bench.COPY_MIB * 2 ** 20
+    # the copy kernel moves mib bytes each way: 2 bytes per fetch KiB, 1 per write KiB
+    copy_f = _csv(tmp_path / "cf.csv", [("MulFunctor<float>", mib / 2048)] * 3)
+    copy_w = _csv(tmp_path / "cw.csv", [("FillFunctor<float>", 1.0), ("MulFunctor<float>", mib / 1024)])
+    args = types.SimpleNamespace(traffic_report=[fetch, write, copy_f, copy_w], config="c1",
+                                 tokens=None, path="auto")
+    bench.traffic_report(args)
+
+    entry = json.load(open(tmp_path / "traffic.json"))["c1:T16:gemv"]
+    # only the gate/up dispatches count, averaged
+    assert entry["fetch_kib_per_dispatch"] == 2000.0
+    assert entry["write_kib_per_dispatch"] == 10.0
+    assert entry["dispatches"] == [2, 2]
+    assert entry["copy_calibration"]["fetch_bytes_per_kib"] == 2.0
+    assert entry["copy_calibration"]["write_bytes_per_kib"] == 1.0
+    assert entry["traffic_bytes_per_launch"] == 2000 * 1024 * 2 + 10 * 1024
+    assert bench.recorded_traffic("c1", 16, "gemv") == entry["traffic_bytes_per_launch"]
+    # other workloads have no record; changed kernel sources void this one
+    assert bench.recorded_traffic("c1", 4, "gemv") is None
+    monkeypatch.setattr(bench, "sources_sha", lambda family: "0" * 64)
+    assert bench.recorded_traffic("c1", 16, "gemv") is None
+
+
+def test_traffic_report_picks_the_mfma_kernel_at_prefill_sizes(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gu = "void moe::mfma_pass<true, 2048, 768>(unsigned short const*, ...)"
+    dn = "void moe::mfma_pass<false, 2048, 768>(unsigned short const*, ...)"
+    fetch = _csv(tmp_path / "f.csv", [(gu, 100.0), (dn, 900.0)])
+    write = _csv(tmp_path / "w.csv", [(gu, 1.0), (dn, 9.0)])
+    copy_f = _csv(tmp_path / "cf.csv", [("MulFunctor", bench.COPY_MIB * 1024.0)])
+    copy_w = _csv(tmp_path / "cw.csv", [("MulFunctor", bench.COPY_MIB * 1024.0)])
+    args = types.SimpleNamespace(traffic_report=[fetch, write, copy_f, copy_w], config="c2",
+                                 tokens=None, path="auto")
+    bench.traffic_report(args)
+    entry = json.load(open(tmp_path / "traffic.json"))["c2:T512:mfma"]
+    assert entry["kernel"] == "mfma_pass<true"
+    assert entry["traffic_bytes_per_launch"] == 100 * 1024 + 1 * 1024
