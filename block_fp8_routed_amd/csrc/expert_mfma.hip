@@ -136,7 +136,9 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 // a vector load issued behind the weight prefetches, and as vector loads
 // complete in order, waiting for it would wait for every stage in flight.
 // Rows past the group's end are computed with the rest (they repeat the last
-// row) and never stored.
+// row) and never stored; a wavefront whose rows all lie past it skips its
+// MFMAs. The results go out through LDS, so that every output row is stored
+// as whole 16-byte chunks.
 constexpr int kTN = 256;            // weight rows per tile
 constexpr int kXcds = 8;            // accelerator complex dies (one L2 each)
 constexpr int kPassThreads = 512;
@@ -433,25 +435,59 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     }
   }
 
-  // D layout (32x32): lane L holds column L % 32; value v is row
-  // 8 (v / 4) + 4 (L / 32) + v % 4
+  // Epilogue through LDS (free after the loop's last barrier): each wavefront
+  // writes its fp16 results into a row-major tile, then every output row is
+  // stored as 16-byte chunks. D layout (32x32): lane L holds column L % 32;
+  // value v is row 8 (v / 4) + 4 (L / 32) + v % 4. Lanes exchange one value
+  // with their neighbour (DPP quad_perm 1,0,3,2) so that each writes one
+  // dword: an even lane two columns of row R (value v), an odd lane two
+  // columns of row R + 1 (value v + 1). The 64-byte row pieces of one write
+  // (rows R, R + 1, R + 4, R + 5) are spread over the banks by XOR-ing the
+  // chunk index with (row & 1 | (row >> 2 & 1) << 1) << 2.
+  constexpr int OC = GU ? 128 : 256;  // output columns of the tile
+  constexpr int ORB = OC * 2;         // bytes per tile row in LDS
+  constexpr int OCH = ORB / 16;       // 16-byte chunks per row
+  static_assert(S::RA * ORB <= kLdsBytes, "output tile exceeds the LDS block");
+  auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
+  const bool odd = l32 & 1;
+  auto wput = [&](int m, int col0, uint32_t a, uint32_t b, int v) {
+    const uint32_t send = odd ? a : b;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
+    const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3) + (odd ? 1 : 0);
+    const int col = col0 + l32 - (odd ? 1 : 0);
+    const uint32_t word = odd ? (recv | (b << 16)) : (a | (recv << 16));
+    *reinterpret_cast<uint32_t*>(lds + row * ORB + 16 * (((2 * col) >> 4) ^ oswz(row)) +
+                                 ((2 * col) & 15)) = word;
+  };
+  if (!idle) {
 #pragma unroll
-  for (int m = 0; m < MW; ++m)
+    for (int m = 0; m < MW; ++m)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
-      if (row >= valid) continue;
-      if (GU) {
-        uint16_t* h = reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + row) * I;
-        h[n0 + S::brow(wn, 0) + l32] =
-            f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
-      } else {
-        uint16_t* y = reinterpret_cast<uint16_t*>(out) + (size_t)orow[row] * H;
+      for (int v = 0; v < 16; v += 2) {
+        if (GU) {
+          const uint32_t a = f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
+          const uint32_t b =
+              f32_to_f16_sat(silu(acc[m][0][v + 1] * unit[0]) * (acc[m][1][v + 1] * unit[1]));
+          wput(m, S::brow(wn, 0), a, b, v);
+        } else {
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-          y[n0 + S::brow(wn, nb) + l32] = f32_to_f16_sat(acc[m][nb][v] * unit[nb]);
+          for (int nb = 0; nb < NBW; ++nb)
+            wput(m, S::brow(wn, nb), f32_to_f16_sat(acc[m][nb][v] * unit[nb]),
+                 f32_to_f16_sat(acc[m][nb][v + 1] * unit[nb]), v);
+        }
       }
-    }
+  }
+  __syncthreads();
+  static_assert((S::RA * OCH) % kPassThreads == 0, "output chunks per thread");
+#pragma unroll
+  for (int i = 0; i < S::RA * OCH / kPassThreads; ++i) {
+    const int idx = tid + kPassThreads * i, r = idx / OCH, c = idx % OCH;
+    if (r >= valid) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
+    uint16_t* dst = GU ? reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + r) * I + n0 + 8 * c
+                       : reinterpret_cast<uint16_t*>(out) + (size_t)orow[r] * H + n0 + 8 * c;
+    *reinterpret_cast<uint4*>(dst) = val;
+  }
 }
 
 template <bool GU, int H, int I>
