@@ -25,6 +25,7 @@ Prints one JSON line: MoE-layer tokens/s, plus
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--tokens 16]
        python bench.py --copy-calibration            (the copy kernel for the counters)
+       python bench.py --gemm-calibration --config c4  (library bf16 GEMMs at the expert shapes)
        python bench.py --traffic-report FETCH.csv WRITE.csv COPYF.csv COPYW.csv --config c1
 """
 from __future__ import annotations
@@ -156,6 +157,41 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
 
 
+def gemm_calibration(shape):
+    """The vendor library's bf16 GEMM (torch.matmul -> hipBLASLt) at one
+    expert's gate/up (rows x H -> 2I) and down (rows x I -> H) shapes for
+    several group sizes, plus a large square product: a reference for what
+    a dense bf16 contraction of these sizes reaches on this chip, with bf16
+    weights (no dequantisation) and one launch per expert."""
+    import torch
+    torch.manual_seed(0)
+    H, I = shape.hidden, shape.inter
+
+    def rate(M, N, K, what, reps=50):
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+        bt = b.t()  # weights stored row-major [N][K], as the experts are
+        for _ in range(5):
+            c = a @ bt
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ bt
+        e1.record()
+        torch.cuda.synchronize()
+        del c
+        us = e0.elapsed_time(e1) / reps * 1e3
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        print(json.dumps({"what": what, "M": M, "N": N, "K": K, "us": round(us, 2),
+                          "TFLOPs": round(tf, 1), "frac_of_2.5PF": round(tf / 2500, 4)}), flush=True)
+
+    for rows in (64, 256, 1024, 2048, 4096):
+        rate(rows, 2 * I, H, "gate/up")
+        rate(rows, H, I, "down")
+    rate(8192, 8192, 8192, "square")
+
+
 def counter_means(path, match):
     """Mean counter value (KiB) per dispatch of the kernels whose name holds match."""
     import csv
@@ -226,6 +262,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the copy kernel the PMC counters are calibrated on")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="time the library bf16 GEMM at the workload's expert shapes")
     ap.add_argument("--traffic-report", nargs=4, metavar="CSV",
                     help="FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter CSVs: "
                          "record the dominant kernel's traffic in profiles/traffic.json")
@@ -235,6 +273,10 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_calibration:
+        import workloads as W
+        gemm_calibration(W.CONFIGS[args.config])
         return
 
     if args.gpus != 1:
