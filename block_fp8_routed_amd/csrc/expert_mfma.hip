@@ -400,8 +400,15 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     constexpr int D = S::DEPTH;
     static_assert(NS % D == 0, "stage count must be a multiple of the prefetch depth");
     Regs R[D];
+    // the prologue issues the stages in order, as the loop does: the waits the
+    // compiler places at the loop head must hold for both ways in, and loads
+    // of different stages interleaved here would make them wait for nearly
+    // every load in flight
 #pragma unroll
-    for (int j = 0; j < D; ++j) fetch(R[j], j);
+    for (int j = 0; j < D; ++j) {
+      fetch(R[j], j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     put(R[0], 0, 0);
     __syncthreads();
     for (int st0 = 0; st0 < NS; st0 += D) {
@@ -421,7 +428,10 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     static_assert(NS % D == 0, "stage count must be a multiple of the prefetch depth");
     Regs R[D];
 #pragma unroll
-    for (int j = 0; j < D; ++j) fetch(R[j], j);
+    for (int j = 0; j < D; ++j) {  // in stage order (see above)
+      fetch(R[j], j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     for (int st0 = 0; st0 < NS; st0 += D) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
