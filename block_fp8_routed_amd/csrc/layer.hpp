@@ -32,7 +32,7 @@ struct Dims {
 //  * prefill with bf16 activations (H a multiple of 64): MFMA tiles of
 //    kRouterTile tokens x kRouterTile experts over the router weights split
 //    exactly into three bf16 planes; H is cut into as many slices (a power of
-//    two, each a multiple of 128 columns, at most kMaxSlicesUnrolled) as
+//    two, each a multiple of 128 columns, at most max_router_slices) as
 //    brings the tile count x slices to about 512 workgroups, so that small
 //    batches still spread over the compute units;
 //  * otherwise (fp32 activations at prefill sizes): the fp32 tiled GEMM, one
