@@ -20,8 +20,8 @@ Prints one JSON line: MoE-layer tokens/s, plus
                 runs (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by
                 the bytes a plain copy kernel of known size moves per KiB the
                 same counter reports), read from profiles/traffic.json when its
-                recorded source hash matches the kernel's current sources;
-                null otherwise.
+                recorded hash of the kernel code (comments and whitespace left
+                out) matches the current sources; null otherwise.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--tokens 16]
        python bench.py --copy-calibration            (the copy kernel for the counters)
@@ -131,12 +131,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 512
 
 
+def code_text(src):
+    """Kernel source without its comments and with whitespace collapsed, so
+    that a recorded traffic figure survives edits that change no code."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def sources_sha(family):
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(ROOT, "block_fp8_routed_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_fp8_routed_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -61,3 +61,19 @@ def test_traffic_report_picks_the_mfma_kernel_at_prefill_sizes(tmp_path, monkeyp
     entry = json.load(open(tmp_path / "traffic.json"))["c2:T512:mfma"]
     assert entry["kernel"] == "mfma_pass<true"
     assert entry["traffic_bytes_per_launch"] == 100 * 1024 + 1 * 1024
+
+
+def test_traffic_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    src = tmp_path / "csrc"
+    src.mkdir()
+    (src / "k.hip").write_text("// header\n__global__ void k(int* p) { p[0] = 1; /* store */ }\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", {"gemv": ["k.hip"]})
+    (tmp_path / "block_fp8_routed_amd").mkdir()
+    (tmp_path / "block_fp8_routed_amd" / "csrc").symlink_to(src)
+    h0 = bench.sources_sha("gemv")
+    (src / "k.hip").write_text("// a longer header\n/* block\n comment */\n"
+                               "__global__ void k(int* p) {\n  p[0] = 1;  // store\n}\n")
+    assert bench.sources_sha("gemv") == h0
+    (src / "k.hip").write_text("// header\n__global__ void k(int* p) { p[0] = 2; }\n")
+    assert bench.sources_sha("gemv") != h0
