@@ -128,6 +128,13 @@ FWD_CASES = [  # (config, tokens, path, overrides)
     ("c0", 16, "gemv", {"experts": 512, "top_k": 16}),
     ("c0", 20, "gemv", {"experts": 1024, "top_k": 16, "shared": True}),
     ("c0", 3, "gemv", {"experts": 1024, "top_k": 1}),
+    # expert counts that leave part of a lane row empty in the one-workgroup
+    # decode selection (two and four experts per lane), and the first token
+    # count the automatic choice sends to the grouped MFMA family with the
+    # multi-kernel selection and permutation
+    ("c0", 9, "gemv", {"experts": 100, "top_k": 3, "shared": True}),
+    ("c0", 16, "auto", {"experts": 200, "top_k": 5}),
+    ("c1", 17, "auto", {}),
 ]
 
 
