@@ -35,6 +35,16 @@ silent (each restated at the function that uses it):
   R9 a token is tie-flagged when its k-th and (k+1)-th largest logits differ by
      less than 1e-5 (absolute, on these fp64 logits); its selection is then not
      unique at the kernel's precision.
+  R10 (a variant for prefill sizes, where both operands of the gate/up
+     contraction are E4M3; the pages describe E4M3 weights only, so the
+     activation side is this project's reading) each token's activation row
+     is cut into blocks of `block` columns; a block's scale is 2^e with e the
+     smallest integer such that its largest magnitude is at most 448 * 2^e
+     (e = 0 for an all-zero block, never below -127), and each value becomes
+     the nearest E4M3FN value of x * 2^-e (an exact tie goes to the even
+     mantissa; the sign is kept, so negative values that round to zero give
+     -0). Power-of-two scales are the block-scale form of gfx950's FP8
+     matrix instructions. The router still reads the unquantised x.
 Every function here is pinned by tests/test_oracle_pins.py; no function is
 parity-unpinned.
 """
@@ -74,6 +84,61 @@ def dequantise(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
     s_full = np.repeat(np.repeat(s, block, axis=0), block, axis=1)
     assert s_full.shape == w.shape, (s_full.shape, w.shape)
     return w * s_full
+
+
+# --------------------------------------------------------------------------
+# E4M3 activations for the gate/up contraction (R10)
+# --------------------------------------------------------------------------
+def e4m3fn_round(v) -> np.ndarray:
+    """The E4M3FN byte nearest to each finite v with |v| <= 448 (R10): the
+    candidates are the values of the non-negative finite codes 0x00 .. 0x7E
+    (increasing with the code), the nearest magnitude wins, an exact tie goes
+    to the code whose mantissa is even, and the sign bit is v's sign bit."""
+    v = np.asarray(v, np.float64)
+    if np.any(~np.isfinite(v)) or np.any(np.abs(v) > 448.0):
+        raise ValueError("e4m3fn_round takes finite values of magnitude at most 448")
+    mags = e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))  # 0x00 .. 0x7E
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)  # first value >= a
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def act_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e, at least -127; 0 where
+    amax is 0 (R10). A log2 estimate, corrected by exact comparisons."""
+    amax = np.asarray(amax, np.float64)
+    e = np.zeros(amax.shape, np.int64)
+    nz = amax > 0
+    a = amax[nz]
+    est = np.ceil(np.log2(a / 448.0)).astype(np.int64)
+    est = np.where(a > np.ldexp(448.0, est), est + 1, est)
+    est = np.where(a <= np.ldexp(448.0, est - 1), est - 1, est)
+    e[nz] = np.maximum(est, -127)
+    return e
+
+
+def quantise_activations(x: np.ndarray, block: int):
+    """x [T][H] -> (codes [T][H] uint8, exponents [T][H/block] int64), one
+    power-of-two scale per token and block of `block` columns (R10)."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    if H % block:
+        raise ValueError("block must divide the row length")
+    xb = x.reshape(T, H // block, block)
+    e = act_scale_exponent(np.abs(xb).max(axis=2))
+    scaled = xb * np.ldexp(1.0, -e)[:, :, None]  # exact: a power of two
+    return e4m3fn_round(scaled).reshape(T, H), e
+
+
+def dequantise_activations(codes: np.ndarray, exps: np.ndarray, block: int) -> np.ndarray:
+    """x^[t, h] = dec(codes[t, h]) * 2^exps[t, h // block] (R10), fp64."""
+    T, H = codes.shape
+    v = e4m3fn_decode(codes).reshape(T, H // block, block)
+    return (v * np.ldexp(1.0, np.asarray(exps, np.int64))[:, :, None]).reshape(T, H)
 
 
 def expert_matrices(expert: dict, inter: int, block: int):
@@ -180,7 +245,7 @@ def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray
 def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndarray],
               expert: Callable[[int], dict], top_k: int, inter: int, block: int,
               shared: Optional[dict] = None, routing: Optional[np.ndarray] = None,
-              tokens: Optional[np.ndarray] = None):
+              tokens: Optional[np.ndarray] = None, act_block: Optional[int] = None):
     """The whole layer in fp64.
 
     expert(e) returns expert e's block-FP8 dict (w_gate_up, s_gate_up, w_down,
@@ -188,13 +253,17 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndar
     overrides the selection (used to re-run the oracle with another valid set
     for a tie-flagged token); gates are then taken over those experts. With
     `tokens` given, only those rows of the output are computed (the logits of
-    every token are still formed, since they are cheap).
+    every token are still formed, since they are cheap). With `act_block`
+    given, the experts read the activations quantised to E4M3 in blocks of
+    that many columns (R10); the router reads x as it is.
 
     Returns dict(out [T'][H], logits [T][E], topk_idx [T][k], gates [T][k],
     ties [T]) where T' = len(tokens) or T.
     """
     x = np.asarray(x, np.float64)
     logits = router_logits(x, router_w, router_bias)
+    xe = x if act_block is None else dequantise_activations(
+        *quantise_activations(x, act_block), act_block)
     idx = select_topk(logits, top_k) if routing is None else np.asarray(routing, np.int64)
     gates = gate_weights(logits, idx)
     rows = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
@@ -203,13 +272,13 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndar
     for e in np.unique(sub_idx):
         wg, wu, wd = expert_matrices(expert(int(e)), inter, block)
         who, slot = np.nonzero(sub_idx == e)
-        y = swiglu_expert(x[rows[who]], wg, wu, wd)
+        y = swiglu_expert(xe[rows[who]], wg, wu, wd)
         # each (token, slot) pair appears once; in fp64 the order of the k
         # terms of a token is immaterial at the tolerances this oracle serves
         for r, (i, j) in enumerate(zip(who, slot)):
             out[i] += gates[rows[i], j] * y[r]
     if shared is not None:
         wg, wu, wd = expert_matrices(shared, inter, block)
-        out += swiglu_expert(x[rows], wg, wu, wd)
+        out += swiglu_expert(xe[rows], wg, wu, wd)
     return {"out": out, "logits": logits, "topk_idx": idx, "gates": gates,
             "ties": tie_flags(logits, top_k)}

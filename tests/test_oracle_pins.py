@@ -268,9 +268,94 @@ def pin_tie_flags(O):
     assert not O.tie_flags(l, 4).any()
 
 
+# ------------------------------------------ E4M3 activations (reading R10) ---
+def lib_round(v):
+    """E4M3FN bytes of fp64 values through torch's own float8_e4m3fn cast."""
+    return torch.from_numpy(np.asarray(v, np.float64)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def scalar_exponent(amax):
+    """Smallest integer e >= -127 with amax <= 448 * 2^e, by counting up."""
+    if amax == 0.0:
+        return 0
+    e = -127
+    while amax > math.ldexp(448.0, e):
+        e += 1
+    return e
+
+
+def pin_act_round_matches_library(O):
+    rng = np.random.default_rng(10)
+    mags = lib_decode(np.arange(0x7F, dtype=np.uint8))  # 0 .. 448, increasing
+    mids = (mags[:-1] + mags[1:]) / 2                  # exact ties in fp64
+    v = np.concatenate([mids, -mids, mags, -mags, rng.uniform(-448, 448, 4000),
+                        rng.uniform(-2e-2, 2e-2, 4000), [0.0, -0.0, -1e-30]])
+    assert np.array_equal(O.e4m3fn_round(v), lib_round(v))
+
+
+def pin_act_scale_closed_form(O):
+    for k in (-20, -1, 0, 3, 40):
+        b = math.ldexp(448.0, k)
+        got = O.act_scale_exponent(np.array([b, b * (1 + 2.0 ** -30), b * (1 - 2.0 ** -30)]))
+        assert list(got) == [k, k + 1, k]
+    assert list(O.act_scale_exponent(np.array([0.0, 1e-300, 1.0]))) == [0, -127, -8]
+
+
+def pin_act_quantise_blocks_bruteforce(O):
+    rng = np.random.default_rng(11)
+    B = 32
+    x = rng.normal(0, 1, (3, 4 * B)) * np.array([1e-3, 1.0, 1e3])[:, None]
+    x[1, B:2 * B] = 0.0                                # an all-zero block
+    x[2, 2 * B + 5] = 5e5                              # one large value: its block only
+    codes, exps = O.quantise_activations(x, B)
+    for t in range(x.shape[0]):
+        for b in range(x.shape[1] // B):
+            blk = x[t, b * B:(b + 1) * B]
+            e = scalar_exponent(float(np.abs(blk).max()))
+            assert exps[t, b] == e
+            assert np.array_equal(codes[t, b * B:(b + 1) * B], lib_round(blk * 2.0 ** -e))
+    xh = O.dequantise_activations(codes, exps, B)
+    ok = np.abs(xh - x) <= np.maximum(2.0 ** -4 * np.abs(x),
+                                      2.0 ** -10 * np.repeat(np.ldexp(1.0, exps), B, axis=1))
+    assert ok.all()
+    # idempotent in value (the exponent may drop by one when a block's
+    # largest value rounds down to 448 * 2^(e-1); the values stay the same)
+    assert np.array_equal(O.dequantise_activations(*O.quantise_activations(xh, B), B), xh)
+
+
+def pin_act_layer_uses_quantised_experts_only(O):
+    """With act_block, the experts see the E4M3 activations and the router the
+    original ones: against a torch evaluation that quantises with torch's cast."""
+    rng = np.random.default_rng(12)
+    H, I, B, E, k, T = 64, 32, 32, 4, 2, 5
+    experts = [random_expert(rng, H, I, B) for _ in range(E)]
+    shared = random_expert(rng, H, I, B)
+    x = rng.normal(0, 1, (T, H))
+    wr = rng.normal(0, 0.3, (E, H))
+    res = O.moe_layer(x, wr, None, lambda e: experts[e], k, I, B, shared=shared, act_block=B)
+    xh = np.empty_like(x)
+    for t in range(T):
+        for b in range(H // B):
+            blk = x[t, b * B:(b + 1) * B]
+            e = scalar_exponent(float(np.abs(blk).max()))
+            xh[t, b * B:(b + 1) * B] = lib_decode(lib_round(blk * 2.0 ** -e)) * 2.0 ** e
+    logits = torch.from_numpy(x) @ torch.from_numpy(wr).T
+    top = torch.topk(logits, k, dim=1).indices.numpy()
+    assert np.array_equal(res["topk_idx"], top)
+    want = torch_swiglu(xh, shared, I, B)
+    for t in range(T):
+        g = torch.softmax(logits[t, top[t]], 0).numpy()
+        for j in range(k):
+            want[t] += g[j] * torch_swiglu(xh[t:t + 1], experts[top[t, j]], I, B)[0]
+    assert np.allclose(res["out"], want, rtol=1e-9, atol=1e-12)
+
+
 PINS = [pin_decode_matches_library, pin_decode_anchors, pin_dequant_bruteforce,
         pin_topk_bruteforce, pin_gates, pin_permutation, pin_single_expert_is_dense,
-        pin_all_experts_equal_gates_is_dense_mean, pin_whole_layer_scalar, pin_tie_flags]
+        pin_all_experts_equal_gates_is_dense_mean, pin_whole_layer_scalar, pin_tie_flags,
+        pin_act_round_matches_library, pin_act_scale_closed_form,
+        pin_act_quantise_blocks_bruteforce, pin_act_layer_uses_quantised_experts_only]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -293,11 +378,19 @@ MUTATIONS = {
     "gates_not_renormalised": ("g[t] = sel / sel.sum()", "g[t] = sel"),
     "silu_sign": ("return z / (1.0 + np.exp(-z))", "return z / (1.0 + np.exp(z))"),
     "down_not_transposed": ("return (silu(a) * u) @ wd.T", "return (silu(a) * u) @ wd.T[::-1]"),
-    "shared_dropped": ("out += swiglu_expert(x[rows], wg, wu, wd)", "pass"),
+    "shared_dropped": ("out += swiglu_expert(xe[rows], wg, wu, wd)", "pass"),
     "permutation_ties_by_descending_slot": ('order = np.argsort(flat, kind="stable")',
                                             "order = np.lexsort((-np.arange(flat.size), flat))"),
     "tie_band_relative": ("return (srt[:, k - 1] - srt[:, k]) < band",
                           "return (srt[:, k - 1] - srt[:, k]) < band * np.abs(srt[:, k - 1])"),
+    "act_ties_to_odd": ("((d_hi == d_lo) & (hi % 2 == 0))", "((d_hi == d_lo) & (hi % 2 == 1))"),
+    "act_scale_one_too_large": ("e[nz] = np.maximum(est, -127)",
+                                "e[nz] = np.maximum(est + 1, -127)"),
+    "act_scale_floor_clamp": ("e[nz] = np.maximum(est, -127)", "e[nz] = np.maximum(est, -126)"),
+    "act_sign_dropped": ("return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)",
+                         "return code"),
+    "experts_read_unquantised_x": ("y = swiglu_expert(xe[rows[who]], wg, wu, wd)",
+                                   "y = swiglu_expert(x[rows[who]], wg, wu, wd)"),
 }
 
 
