@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     make_config,
     make_workspace,
     moe_dequant_e4m3,
+    moe_quantize_act_e4m3,
     moe_forward,
     moe_permute,
     moe_route,

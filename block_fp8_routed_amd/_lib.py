@@ -24,7 +24,7 @@ PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA}
  MOE_EV_END, MOE_EV_COUNT) = range(7)
 
 EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_route", "moe_permute",
-           "moe_dequant_e4m3", "moe_status_string", "moe_version")
+           "moe_dequant_e4m3", "moe_quantize_act_e4m3", "moe_status_string", "moe_version")
 
 
 class MoeConfig(ctypes.Structure):
@@ -87,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.moe_permute.restype = ctypes.c_int
     lib.moe_dequant_e4m3.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P]
     lib.moe_dequant_e4m3.restype = ctypes.c_int
+    lib.moe_quantize_act_e4m3.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P]
+    lib.moe_quantize_act_e4m3.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_version.argtypes = []
@@ -253,6 +255,24 @@ def moe_permute(topk_idx: torch.Tensor, experts: int, has_shared: bool, hidden: 
     if st != MOE_OK:
         raise MoeError(st, "moe_permute")
     return offsets, pair[:P], inv[:P]
+
+
+def moe_quantize_act_e4m3(x: torch.Tensor, stream=None):
+    """bf16 activations [T][H] -> (E4M3 codes [T][H] uint8, E8M0 exponents
+    [T][H/128] uint8, e + 127), one power-of-two scale per token and block of
+    128 columns."""
+    lib = load()
+    _dev(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    x = x.contiguous()
+    T, H = x.shape
+    codes = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    exps = torch.empty((T, max(H // 128, 1)), dtype=torch.uint8, device=x.device)
+    st = lib.moe_quantize_act_e4m3(_ptr(x), T, H, _ptr(codes), _ptr(exps), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_quantize_act_e4m3")
+    return codes, exps
 
 
 def moe_dequant_e4m3(w: torch.Tensor, scales: torch.Tensor, block: int,

@@ -1,0 +1,98 @@
+// quant_act.hip — moe_quantize_act_e4m3: bf16 activations to E4M3 bytes with
+// one power-of-two scale per token and block of 128 columns.
+//
+// This is the activation side of the variant that runs both operands of the
+// gate/up contraction in E4M3 at prefill sizes. The pages describe E4M3
+// weights only (colizig page, "What this project is trying to prove":
+// natively block-FP8 checkpoints); the activation side is a reading of this
+// project: a block's scale is 2^e with e the smallest integer such that the
+// block's largest magnitude is at most 448 * 2^e (0 for an all-zero block,
+// never below -127), and each value becomes the nearest E4M3FN value of
+// x * 2^-e, an exact tie going to the even mantissa, the sign kept (negative
+// values that round to zero give -0). Power-of-two scales are what gfx950's
+// block-scaled FP8 matrix instructions take (E8M0), so the scale can ride in
+// the instruction itself.
+//
+// x * 2^-e is exact in fp32 (a bf16 value times a power of two), except
+// below 2^-126, where fp32 rounds; such values are far below half of
+// E4M3's smallest subnormal (2^-10) and give a zero code either way, so
+// each code is decided exactly as an exact-arithmetic rounding would.
+//
+// One wavefront per block: lane L takes columns 2L and 2L + 1 (one dword of
+// bf16), the block's largest magnitude comes from a DPP maximum over the
+// lanes' fp32 bit patterns (non-negative floats order as unsigned integers).
+#include "device.hpp"
+#include "layer.hpp"
+
+namespace moe {
+
+constexpr int kActBlock = 128;  // columns per activation scale block
+
+// nearest E4M3FN byte to v, |v| <= 448 (ties to the even mantissa, sign kept)
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    // subnormal range: m * 2^-9 with m = 0 .. 8 (m = 8 is the smallest
+    // normal, code 0x08)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    int E = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;  // a is a normal fp32
+    const uint32_t r = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - E));  // 8 .. 16
+    const bool carry = r == 16;
+    E += carry ? 1 : 0;
+    code = ((uint32_t)(E + 7) << 3) | (carry ? 0u : r - 8);
+  }
+  return code | sign;
+}
+
+// smallest e >= -127 with amax <= 448 * 2^e; 0 for amax = 0
+__device__ __forceinline__ int act_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  if (amax < 0x1p-119f) return -127;  // exponent field <= -120: the floor
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xff) - 127;  // amax = (1 + f) 2^E, f < 1
+  // amax 2^-(E-8) = (1 + f) 256 <= 448 iff 1 + f <= 1.75 (mantissa bits 0x600000)
+  return (b & 0x7fffff) <= 0x600000u ? E - 8 : E - 7;
+}
+
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint32_t* __restrict__ x,
+                                                       int64_t nblocks,
+                                                       uint16_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ exps) {
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;  // uniform over the wavefront
+  const int lane = threadIdx.x & 63;
+  const uint32_t w = x[blk * (kActBlock / 2) + lane];  // columns 2 lane, 2 lane + 1
+  const float v0 = bf16_lo(w), v1 = bf16_hi(w);
+  const uint32_t m = max(__float_as_uint(fabsf(v0)), __float_as_uint(fabsf(v1)));
+  const int e = act_exponent(__uint_as_float(wave_max_u32(m)));
+  const uint32_t c0 = e4m3_rne(__builtin_ldexpf(v0, -e));
+  const uint32_t c1 = e4m3_rne(__builtin_ldexpf(v1, -e));
+  codes[blk * (kActBlock / 2) + lane] = (uint16_t)(c0 | (c1 << 8));
+  if (lane == 0) exps[blk] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_quant_act(const void* x, int64_t T, int H, uint8_t* codes, uint8_t* exps,
+                            hipStream_t s) {
+  const int64_t nb = T * (H / kActBlock);
+  quant_act_kernel<<<(unsigned)((nb + 3) / 4), 256, 0, s>>>(
+      static_cast<const uint32_t*>(x), nb, reinterpret_cast<uint16_t*>(codes), exps);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_quantize_act_e4m3(const void* x, int64_t tokens, int32_t hidden,
+                                            uint8_t* codes, uint8_t* exps, void* stream) {
+  if (!x || !codes || !exps) return MOE_ERR_NULL;
+  if (tokens < 0 || hidden <= 0) return MOE_ERR_SHAPE;
+  if (hidden % moe::kActBlock != 0) return MOE_ERR_UNSUPPORTED;
+  if (tokens * (int64_t)(hidden / moe::kActBlock) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (tokens == 0) return MOE_OK;
+  return moe::launch_quant_act(x, tokens, hidden, codes, exps, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}

@@ -177,6 +177,22 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t* offsets, int32_t* pair,
 moe_status moe_dequant_e4m3(const uint8_t* w, const float* scales, int64_t rows, int32_t cols,
                             int32_t block, float* out, void* stream);
 
+/* E4M3 activations for the variant that runs both operands of the gate/up
+ * contraction in FP8 (a reading of this project: the pages describe E4M3
+ * weights only, colizig page, "What this project is trying to prove").
+ * Each token's row of x is cut into blocks of 128 columns; block b of token t
+ * gets the scale 2^e, e the smallest integer with max|x| <= 448 * 2^e over the
+ * block (0 for an all-zero block, at least -127), and each value becomes the
+ * nearest OCP E4M3FN value of x * 2^-e (ties to the even mantissa, sign
+ * kept, so negatives that round to zero give 0x80).
+ *   x      [tokens][hidden] bf16, finite values only (device)
+ *   codes  [tokens][hidden] E4M3FN bytes (device, written)
+ *   exps   [tokens][hidden/128] uint8 E8M0 exponents, e + 127 (device, written)
+ * hidden must be a multiple of 128 (else MOE_ERR_UNSUPPORTED); tokens == 0
+ * enqueues nothing. */
+moe_status moe_quantize_act_e4m3(const void* x, int64_t tokens, int32_t hidden, uint8_t* codes,
+                                 uint8_t* exps, void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

@@ -5,12 +5,16 @@ import this package. The HIP library and its Python binding never do.
 """
 from .moe_oracle import (  # noqa: F401
     TIE_BAND,
+    act_scale_exponent,
     dequantise,
+    dequantise_activations,
     e4m3fn_decode,
+    e4m3fn_round,
     expert_matrices,
     gate_weights,
     moe_layer,
     permutation,
+    quantise_activations,
     router_logits,
     select_topk,
     silu,

@@ -146,3 +146,14 @@ def test_route_and_permute_validation():
     assert lib.moe_permute(FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE, 8,
                            None) == _lib.MOE_ERR_WORKSPACE
     assert lib.moe_permute(FAKE, FAKE, FAKE, FAKE, None, FAKE, n, None) == _lib.MOE_ERR_NULL
+
+
+def test_quantize_act_validation():
+    lib = moe.load()
+    q = lib.moe_quantize_act_e4m3
+    assert q(None, 4, 256, FAKE, FAKE, None) == _lib.MOE_ERR_NULL
+    assert q(FAKE, 4, 256, None, FAKE, None) == _lib.MOE_ERR_NULL
+    assert q(FAKE, -1, 256, FAKE, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert q(FAKE, 4, 0, FAKE, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert q(FAKE, 4, 200, FAKE, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert q(FAKE, 0, 256, FAKE, FAKE, None) == _lib.MOE_OK  # nothing enqueued

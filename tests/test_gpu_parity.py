@@ -47,6 +47,51 @@ def test_device_dequant_block_grid():
     assert np.array_equal(got.cpu().numpy(), want)
 
 
+def _act_rows(rng):
+    """bf16 rows that reach every branch of the activation quantiser: exact
+    midpoints between neighbouring E4M3 values (ties), signed zeros, an
+    all-zero block, blocks whose largest value sits at 448 * 2^k and just
+    above it, blocks at the -127 exponent floor, subnormal E4M3 results."""
+    mags = oracle.e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (mags[:-1] + mags[1:]) / 2
+    rows = []
+    r = np.zeros(512)
+    r[:126] = mids                      # block 0: max 440 -> e = 0, ties
+    r[128:254] = -mids
+    r[256:384] = 0.0                    # an all-zero block
+    r[384] = 448.0 * 4                  # largest value exactly 448 * 2^2
+    r[385:512] = -0.0
+    rows.append(r)
+    r = np.zeros(512)
+    r[0] = 448.0 * 2 ** -3 * (1 + 2 ** -7)   # just above 448 * 2^-3 (a bf16 value)
+    r[1:128] = rng.normal(0, 1e-3, 127)      # small values, E4M3 subnormals
+    r[128:256] = rng.normal(0, 1e-37, 128)   # tiny block: the -127 floor
+    r[256:384] = rng.normal(0, 1, 128) * 2.0 ** 60
+    r[384:512] = rng.normal(0, 1, 128) * 2.0 ** -100
+    rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("T,H", [(2, 512), (300, 2048), (4096, 4096)])
+def test_activation_quantiser_matches_oracle(T, H):
+    """E4M3 activation codes and E8M0 exponents bit-exact against the oracle
+    (reading R10), on crafted edge rows and random bf16 rows at the prefill
+    shapes."""
+    import block_fp8_routed_amd as moe
+    rng = np.random.default_rng(T + H)
+    x = rng.normal(0, 1, (T, H))
+    x[:, ::97] *= 50.0                                 # a few outliers per row
+    if H == 512:
+        x = _act_rows(rng)
+    xb = torch.from_numpy(x).to(torch.bfloat16)       # the values both sides see
+    codes, exps = moe.moe_quantize_act_e4m3(xb.cuda())
+    torch.cuda.synchronize()
+    r_codes, r_exps = oracle.quantise_activations(xb.to(torch.float64).numpy(), 128)
+    assert np.array_equal(codes.cpu().numpy(), r_codes)
+    assert np.array_equal(exps.cpu().numpy().astype(np.int64) - 127, r_exps)
+    log(f"quantise activations T={T} H={H}: codes and exponents bit-exact")
+
+
 # ---------------------------------------------------------------- router ---
 ROUTE_CASES = [
     ("c0", None), ("c1", 1), ("c1", 4), ("c1", 16), ("c1", 17), ("c2", None),
