@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(HERE, "libmoe_fp8.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA = 0, 1, 2
-PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA}
+MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA_FP8 = 0, 1, 2, 3
+PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA,
+         "mfma_fp8": MOE_PATH_MFMA_FP8}
 (MOE_EV_START, MOE_EV_ROUTED, MOE_EV_PERMUTED, MOE_EV_GATE_UP, MOE_EV_DOWN,
  MOE_EV_END, MOE_EV_COUNT) = range(7)
 

@@ -562,6 +562,295 @@ void mfma_pass(const uint16_t* __restrict__ act,
 }
 
 // ---------------------------------------------------------------------------
+// FP8 gate/up: the variant that runs both operands of the gate/up contraction
+// in E4M3 (activations quantised by moe_quantize_act_e4m3: one power-of-two
+// scale per token and 128 columns), on v_mfma_scale_f32_32x32x64_f8f6f4.
+//   Lane l supplies A row l % 32 and B column (weight row) l % 32, each as the
+//   32 bytes of K of its lane half (bytes 32 (l / 32) .. + 31 of the 64-k
+//   step: two 16-byte LDS chunks). A and B take K in the same order, so the
+//   contraction does not depend on the order in which the instruction walks K.
+//   The activation scale rides in the instruction: lane l's E8M0 byte scales A
+//   row l % 32 over its 32 K, all inside one 128-column block, so every lane
+//   of a row passes that block's exponent; B's scale byte is 127 (1). The
+//   weights' fp32 block scales are applied in the ratio form of the bf16 pass.
+// Tiles as in the bf16 pass with half the A bytes: full tiles (more than 64
+// rows) take 64-k stages through two LDS buffers (8 KiB of A, 16 KiB of B),
+// one stage fetched ahead; thin tiles take 128-k stages (one scale block)
+// through one 40 KiB buffer, two stages in flight in registers. A and B rows
+// are both KS bytes of E4M3 and share one swizzle (chunk c of row r at slot
+// c ^ ((r >> 2) & 3) for 64-k stages, c ^ ((r >> 1) & 7) for 128-k stages).
+template <bool THIN>
+struct F8Shape {
+  static constexpr int RA = THIN ? 64 : 128;          // A rows per stage
+  static constexpr int KS = THIN ? 128 : 64;          // k per stage
+  static constexpr int CH = KS / 16;                  // 16-byte chunks per A or B row
+  static constexpr int AC = RA * CH / kPassThreads;   // A chunks per thread per stage
+  static constexpr int BC = kTN * CH / kPassThreads;  // B chunks per thread per stage
+  static constexpr int ASTAGE = RA * KS;
+  static constexpr int BSTAGE = kTN * KS;
+  static constexpr int BUFS = THIN ? 1 : 2;
+  static constexpr int MW = THIN ? 1 : 2;             // 32-row MFMA tiles per wavefront
+  static constexpr int NBW = 2;                       // gate tile, up tile
+  static constexpr int DEPTH = THIN ? 2 : 1;
+  static_assert(BUFS * (ASTAGE + BSTAGE) <= kLdsBytes, "stage buffers exceed the LDS block");
+  static_assert(AC * kPassThreads == RA * CH && BC * kPassThreads == kTN * CH, "fetch map");
+  static __device__ __forceinline__ int arow0(int wm) { return (THIN ? 32 : 64) * wm; }
+  static __device__ __forceinline__ int brow(int wn, int nb) {
+    return nb == 0 ? 32 * wn : kTN / 2 + 32 * wn;
+  }
+  static __device__ __forceinline__ int swz(int r) { return CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+};
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8_t f8_operand(const uint8_t* row, int c0, int c1) {
+  const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * c0);
+  const uint4 b = *reinterpret_cast<const uint4*>(row + 16 * c1);
+  i32x8_t v;
+  v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
+  v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
+  return v;
+}
+
+template <int H, int I, bool THIN>
+__device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, const uint8_t* W,
+                                             const float* ss, const uint8_t* sx, const int* arow,
+                                             int valid, int r0, int n0, uint8_t* lds,
+                                             uint16_t* __restrict__ h) {
+  using S = F8Shape<THIN>;
+  constexpr int K = H, KS = S::KS, NS = K / KS, AC = S::AC, BC = S::BC, MW = S::MW,
+                NBW = S::NBW, CH = S::CH;
+  constexpr int NKB = K / kBK;
+  static_assert(K % KS == 0 && kBK % KS == 0, "stages must tile the scale blocks");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches only
+  const int wm = wave >> 2, wn = wave & 3;
+
+  // fetch map: chunk qq = tid + 512 i is row qq / CH, chunk qq % CH (A and B
+  // alike); moving qq by 512 moves the row by a multiple of 32, which leaves
+  // the swizzle alone (GU: tile rows 128 .. 255 are the up rows I + n0 ..)
+  const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(act, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(W, (uint32_t)(2 * I * K));
+  constexpr int RS = kPassThreads / CH;  // row step per chunk group
+  const int rt = tid / CH, ct = tid % CH;
+  const int dst0 = rt * KS + 16 * (ct ^ S::swz(rt));
+  uint32_t asrc[AC];
+#pragma unroll
+  for (int i = 0; i < AC; ++i) asrc[i] = (uint32_t)arow[rt + RS * i] * K + 16 * ct;
+  const uint32_t bsrc0 = (uint32_t)(n0 + rt) * K + 16 * ct;
+  auto brow_of = [](int i) -> int {
+    const int tr = RS * i;
+    return tr < kTN / 2 ? tr : I + tr - kTN / 2;
+  };
+  struct Regs {
+    uint4 a[AC], b[BC];
+  };
+  const float* bscale[BC];
+#pragma unroll
+  for (int i = 0; i < BC; ++i) bscale[i] = ss + (RS * i / kBK) * NKB;
+  auto fetch = [&](Regs& R, int st) {
+    st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never stored
+#pragma unroll
+    for (int i = 0; i < AC; ++i) R.a[i] = buffer_ld16(arsrc, asrc[i], (uint32_t)(st * KS));
+#pragma unroll
+    for (int i = 0; i < BC; ++i)
+      R.b[i] = buffer_ld16<THIN ? kBufNonTemporal : 0>(brsrc, bsrc0,
+                                                       (uint32_t)(brow_of(i) * K + st * KS));
+  };
+  auto put = [&](Regs& R, int buf, int st) {
+    uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
+    uint8_t* B = A + S::ASTAGE;
+    const int kb = st * KS / kBK;
+    bool zero = false;
+#pragma unroll
+    for (int i = 0; i < BC; ++i) zero |= bscale[i][kb] == 0.f;
+    if (zero) {  // rare: a zero block scale (uniform branch)
+#pragma unroll
+      for (int i = 0; i < BC; ++i)
+        if (bscale[i][kb] == 0.f) R.b[i] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + dst0 + RS * KS * i) = R.a[i];
+#pragma unroll
+    for (int i = 0; i < BC; ++i) *reinterpret_cast<uint4*>(B + dst0 + RS * KS * i) = R.b[i];
+  };
+
+  // fragments: A rows arow0 + 32 m + lane % 32, B rows brow(nb) + lane % 32;
+  // the row offsets are multiples of 32, so the swizzle depends on lane % 32
+  const int q = lane >> 5, l32 = lane & 31;
+  const int sw = S::swz(l32);
+  const int afr = (S::arow0(wm) + l32) * KS, bfr = l32 * KS;
+  const float* srow[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) srow[nb] = ss + (S::brow(wn, nb) / kBK) * NKB;
+  const uint8_t* sxr[MW];  // this lane's rows' activation exponents
+#pragma unroll
+  for (int m = 0; m < MW; ++m) sxr[m] = sx + (S::arow0(wm) + 32 * m + l32) * NKB;
+
+  f32x16_t acc[MW][NBW];
+#pragma unroll
+  for (int m = 0; m < MW; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[m][nb][v] = 0.f;
+  float unit[NBW], snext[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    unit[nb] = 0.f;
+    snext[nb] = srow[nb][0];
+  }
+  const bool idle = S::arow0(wm) >= valid;
+  auto compute = [&](int buf, int st) {
+    if (idle) return;
+    const int kb = st * KS / kBK;
+    if ((st * KS) % kBK == 0) {  // entering weight scale block kb (ratio form)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const float sn = snext[nb];
+        if (kb + 1 < NKB) snext[nb] = srow[nb][kb + 1];
+        const bool on = sn != 0.f;
+        const float r = on ? unit[nb] * __builtin_amdgcn_rcpf(sn) : 1.f;
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[m][nb][v] *= r;
+        unit[nb] = on ? sn : unit[nb];
+      }
+    }
+    int sc[MW];
+#pragma unroll
+    for (int m = 0; m < MW; ++m) sc[m] = sxr[m][kb];
+    const uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
+    const uint8_t* B = A + S::ASTAGE;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int p = 0; p < KS / 64; ++p) {
+      const int c0 = (4 * p + 2 * q) ^ sw, c1 = (4 * p + 2 * q + 1) ^ sw;
+      i32x8_t bf[NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) bf[nb] = f8_operand(B + S::brow(wn, nb) * KS + bfr, c0, c1);
+#pragma unroll
+      for (int m = 0; m < MW; ++m) {
+        const i32x8_t af = f8_operand(A + afr + 32 * m * KS, c0, c1);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+          acc[m][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[nb], acc[m][nb], 0, 0,
+                                                                      0, sc[m], 0, 127);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (S::DEPTH == 1) {
+    static_assert(NS % 2 == 0, "stages come in pairs");
+    Regs R;
+    fetch(R, 0);
+    put(R, 0, 0);
+    __syncthreads();
+    for (int st = 0; st < NS; st += 2) {
+      fetch(R, st + 1);
+      compute(0, st);
+      put(R, 1, st + 1);
+      __syncthreads();
+      fetch(R, st + 2);
+      compute(1, st + 1);
+      if (st + 2 < NS) put(R, 0, st + 2);
+      __syncthreads();
+    }
+  } else {
+    constexpr int D = S::DEPTH;
+    static_assert(NS % D == 0, "stage count must be a multiple of the prefetch depth");
+    Regs R[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {  // in stage order, as the loop issues them
+      fetch(R[j], j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int st0 = 0; st0 < NS; st0 += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int st = st0 + j;
+        put(R[j], 0, st);     // the previous stage's reads ended at the last barrier
+        fetch(R[j], st + D);  // set j is free once written
+        __syncthreads();
+        compute(0, st);
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue through LDS, as in the bf16 pass (gate/up: 128 fp16 columns)
+  constexpr int ORB = 128 * 2, OCH = ORB / 16;
+  static_assert(S::RA * ORB <= kLdsBytes, "output tile exceeds the LDS block");
+  auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
+  const bool odd = l32 & 1;
+  if (!idle) {
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const uint32_t a = f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
+        const uint32_t b =
+            f32_to_f16_sat(silu(acc[m][0][v + 1] * unit[0]) * (acc[m][1][v + 1] * unit[1]));
+        const uint32_t send = odd ? a : b;
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
+        const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3) + (odd ? 1 : 0);
+        const int col = S::brow(wn, 0) + l32 - (odd ? 1 : 0);
+        const uint32_t word = odd ? (recv | (b << 16)) : (a | (recv << 16));
+        *reinterpret_cast<uint32_t*>(lds + row * ORB + 16 * (((2 * col) >> 4) ^ oswz(row)) +
+                                     ((2 * col) & 15)) = word;
+      }
+  }
+  __syncthreads();
+  static_assert((S::RA * OCH) % kPassThreads == 0, "output chunks per thread");
+#pragma unroll
+  for (int i = 0; i < S::RA * OCH / kPassThreads; ++i) {
+    const int idx = tid + kPassThreads * i, r = idx / OCH, c = idx % OCH;
+    if (r >= valid) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
+    *reinterpret_cast<uint4*>(h + (size_t)(r0 + r) * I + n0 + 8 * c) = val;
+  }
+}
+
+template <int H, int I>
+__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void mfma_gate_up_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
+                     MfmaBank bk, const int32_t* __restrict__ meta,
+                     const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
+                     const int32_t* __restrict__ rtok, int E, uint16_t* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ int arow[kMfmaBM];
+  constexpr int NKB = H / kBK;
+  __shared__ float ss[2 * NKB];          // the tile's gate and up scale rows
+  __shared__ uint8_t sx[kMfmaBM * NKB];  // the tile rows' activation exponents
+  constexpr int NCB = I / 128;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;  // XCD-aware, as mfma_pass
+  const int tile = (j / NCB) * kXcds + xcd;
+  if (tile >= meta[1]) return;
+  const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
+  const int valid = min(kMfmaBM, offsets[g + 1] - r0);
+  const int tid = threadIdx.x;
+  const int n0 = (j % NCB) * 128;
+  const bool sh = g == E;
+  const uint8_t* W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
+  const float* Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
+  if (tid < kMfmaBM) arow[tid] = rtok[r0 + (tid < valid ? tid : valid - 1)];
+  if (tid >= 256 && tid < 256 + 2 * NKB) {
+    const int i = (tid - 256) / NKB, kb = (tid - 256) % NKB;
+    ss[i * NKB + kb] = Sc[(size_t)((i == 0 ? n0 : I + n0) / kBK) * NKB + kb];
+  }
+  __syncthreads();
+  for (int i = tid; i < kMfmaBM * NKB; i += kPassThreads)
+    sx[i] = exps[(size_t)arow[i / NKB] * NKB + i % NKB];
+  __syncthreads();
+  if (valid <= 64)
+    pass_tile_f8<H, I, true>(codes, W, ss, sx, arow, valid, r0, n0, lds, h);
+  else
+    pass_tile_f8<H, I, false>(codes, W, ss, sx, arow, valid, r0, n0, lds, h);
+}
+
+// ---------------------------------------------------------------------------
 template <int H, int I, int B>
 static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Work& w,
                      hipStream_t s, KernelEvents ev) {
@@ -572,12 +861,21 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
   const uint16_t* xa = reinterpret_cast<const uint16_t*>(x);
   const int32_t *meta = w.meta, *tiles = w.tiles, *offsets = w.offsets, *rtok = w.rtok,
                 *pair = w.pair;
-  if (ev.any())  // the events take the kernel's own start and end times
+  uint16_t* h = reinterpret_cast<uint16_t*>(w.h);
+  if (d.f8) {  // E4M3 activations, quantised after the router read x
+    if (ev.any())
+      hipExtLaunchKernelGGL(mfma_gate_up_f8<H, I>, grid, dim3(kPassThreads), 0, s, ev.begin,
+                            ev.end, 0, w.acodes, w.aexps, bk, meta, tiles, offsets, rtok, d.E, h);
+    else
+      mfma_gate_up_f8<H, I><<<grid, kPassThreads, 0, s>>>(w.acodes, w.aexps, bk, meta, tiles,
+                                                          offsets, rtok, d.E, h);
+  } else if (ev.any()) {  // the events take the kernel's own start and end times
     hipExtLaunchKernelGGL(mfma_pass<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin, ev.end,
                           0, xa, bk, meta, tiles, offsets, rtok, pair, d.E, w.h);
-  else
+  } else {
     mfma_pass<true, H, I><<<grid, kPassThreads, 0, s>>>(xa, bk, meta, tiles, offsets, rtok, pair,
                                                         d.E, w.h);
+  }
   mfma_pass<false, H, I><<<nt8 * (H / PassShape<false, H, I>::COLS), kPassThreads, 0, s>>>(
       reinterpret_cast<const uint16_t*>(w.h), bk, w.meta, w.tiles, w.offsets, w.rtok, w.pair, d.E,
       w.y);

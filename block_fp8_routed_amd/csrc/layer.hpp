@@ -23,6 +23,7 @@ struct Dims {
   int64_t P;     // rows of the permuted problem: T*k + S*T
   bool x_bf16, out_bf16;
   bool mfma;     // expert family: grouped bf16 MFMA (true) or wavefront GEMV
+  bool f8;       // grouped family with E4M3 activations in the gate/up contraction
 };
 
 // Router kernels and partial logits. The router writes partial logits per
@@ -89,6 +90,8 @@ struct Work {
   void* h;           // [P][I] fp16 SwiGLU output
   uint16_t* y;       // [P][H] fp16 expert outputs by slot (saturated at +-65504)
   int32_t* pblock;   // [2][16][E] per-block expert counts, then per-block bases
+  uint8_t* acodes;   // [T][H] E4M3 activations (FP8 gate/up only, else empty)
+  uint8_t* aexps;    // [T][H/128] their E8M0 exponents (FP8 gate/up only)
 };
 
 inline int64_t max_mfma_tiles(const Dims& d) {
@@ -133,5 +136,8 @@ hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_ba
 bool has_gemv_instance(const Dims& d);
 bool has_mfma_instance(const Dims& d);
 hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s);
+// x [T][H] bf16 -> E4M3 codes [T][H] and E8M0 exponents [T][H/128]
+hipError_t launch_quant_act(const void* x, int64_t T, int H, uint8_t* codes, uint8_t* exps,
+                            hipStream_t s);
 
 }  // namespace moe

@@ -14,7 +14,7 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 13;
+constexpr int kRegions = 15;
 
 static void region_sizes(const Dims& d, size_t* sz) {
   sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
@@ -30,6 +30,8 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[10] = (size_t)d.P * d.I * 2;         // h (fp16)
   sz[11] = (size_t)d.P * d.H * 2;         // y (fp16)
   sz[12] = (size_t)2 * kPermMaxBlocksHost * d.E * 4;  // permutation block counts and bases
+  sz[13] = d.f8 ? (size_t)d.T * d.H : 0;              // E4M3 activations
+  sz[14] = d.f8 ? (size_t)d.T * (d.H / 128) : 0;      // their exponents
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -62,6 +64,8 @@ Work carve(const Dims& d, void* base) {
   w.h = r[10];
   w.y = static_cast<uint16_t*>(r[11]);
   w.pblock = static_cast<int32_t*>(r[12]);
+  w.acodes = static_cast<uint8_t*>(r[13]);
+  w.aexps = static_cast<uint8_t*>(r[14]);
   return w;
 }
 
@@ -77,7 +81,8 @@ static moe_status basic_dims(const moe_config* c, Dims* d) {
   if ((c->x_dtype != MOE_F32 && c->x_dtype != MOE_BF16) ||
       (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16))
     return MOE_ERR_SHAPE;
-  if (c->path != MOE_PATH_AUTO && c->path != MOE_PATH_GEMV && c->path != MOE_PATH_MFMA)
+  if (c->path != MOE_PATH_AUTO && c->path != MOE_PATH_GEMV && c->path != MOE_PATH_MFMA &&
+      c->path != MOE_PATH_MFMA_FP8)
     return MOE_ERR_SHAPE;
   if (c->experts > kMaxExperts || c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (c->hidden % 16 != 0 || c->inter % 16 != 0) return MOE_ERR_UNSUPPORTED;
@@ -94,7 +99,8 @@ static moe_status basic_dims(const moe_config* c, Dims* d) {
   d->P = P;
   d->x_bf16 = c->x_dtype == MOE_BF16;
   d->out_bf16 = c->out_dtype == MOE_BF16;
-  d->mfma = c->path == MOE_PATH_MFMA ||
+  d->f8 = c->path == MOE_PATH_MFMA_FP8;
+  d->mfma = c->path == MOE_PATH_MFMA || d->f8 ||
             (c->path == MOE_PATH_AUTO && d->x_bf16 && c->tokens > kGemvMaxTokens);
   return MOE_OK;
 }
@@ -102,6 +108,8 @@ static moe_status basic_dims(const moe_config* c, Dims* d) {
 static moe_status expert_family_ok(const Dims& d) {
   if (d.mfma) {
     if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
+    if (d.f8 && (d.H % 128 != 0 || d.T * (int64_t)(d.H / 128) >= ((int64_t)1 << 32)))
+      return MOE_ERR_UNSUPPORTED;
     if (max_mfma_tiles(d) > 65535) return MOE_ERR_UNSUPPORTED;  // bounded tile list
     // the passes address activation and h rows with 32-bit byte offsets
     if ((uint64_t)d.T * d.H * 2 > 0xffffffffull || (uint64_t)d.P * d.I * 2 > 0xffffffffull)
@@ -180,6 +188,8 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
     if (launch_permute(d, w.topk, w, tile_rows, true, s) != hipSuccess) return MOE_ERR_HIP;
   }
   const moe_expert_bank* sh = d.S ? shared : nullptr;
+  if (d.f8 && launch_quant_act(x, d.T, d.H, w.acodes, w.aexps, s) != hipSuccess)
+    return MOE_ERR_HIP;
   const hipError_t e = d.mfma ? launch_experts_mfma(d, x, *experts, sh, w, s, ev_gate_up)
                               : launch_experts_gemv(d, x, *experts, sh, w, s, ev_gate_up);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -67,8 +67,17 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Expert-pass kernel family. AUTO picks the wavefront GEMV family when
  * tokens <= 16 or x is fp32, and the bf16-MFMA grouped family otherwise.
  * The forced values exist so both families can be exercised at any size;
- * MFMA requires bf16 activations. */
-typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_MFMA = 2 } moe_path;
+ * MFMA requires bf16 activations. MFMA_FP8 is the grouped family with the
+ * gate/up contraction in E4M3 on both sides: x is quantised as
+ * moe_quantize_act_e4m3 describes (the router still reads x itself), which
+ * changes the layer's numerics (about 2^-4 relative per activation); it
+ * requires bf16 x and H a multiple of 128, and is not chosen by AUTO. */
+typedef enum {
+  MOE_PATH_AUTO = 0,
+  MOE_PATH_GEMV = 1,
+  MOE_PATH_MFMA = 2,
+  MOE_PATH_MFMA_FP8 = 3
+} moe_path;
 
 typedef struct {
   int64_t tokens;      /* T: rows of x and out                                    */

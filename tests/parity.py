@@ -91,11 +91,11 @@ class DevLayer:
     def expert(self, e):
         return W.bank_expert(self.bank_host, e)
 
-    def oracle(self, routing=None, tokens=None):
+    def oracle(self, routing=None, tokens=None, act_block=None):
         sh = W.bank_expert(self.shared_host, 0) if self.shape.shared else None
         return oracle.moe_layer(self.x_host, self.router_host, self.bias_host, self.expert,
                                 self.shape.top_k, self.shape.inter, self.shape.block, shared=sh,
-                                routing=routing, tokens=tokens)
+                                routing=routing, tokens=tokens, act_block=act_block)
 
 
 def check_routing(layer: DevLayer, idx, gates, logits=None):

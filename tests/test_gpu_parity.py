@@ -352,6 +352,49 @@ def test_prefill_e512_full_size_sampled():
     check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 sampled")
 
 
+FP8_CASES = [  # (config, tokens, overrides): the E4M3-activation gate/up variant
+    ("c1", 37, {}),                              # thin tiles, ragged tails
+    ("c1", 300, {"experts": 16, "top_k": 4}),    # full and thin tiles, several per group
+    ("c2", None, {}),                            # the 512-token layer at full size
+    ("c3", 100, {}),                             # 4096 hidden, shared expert
+]
+
+
+@pytest.mark.parametrize("name,T,ov", FP8_CASES, ids=[fwd_id((n, t, "mfma_fp8", o)) for n, t, o in FP8_CASES])
+def test_forward_fp8_matches_oracle(name, T, ov):
+    """The grouped family with E4M3 activations in the gate/up contraction
+    against the oracle that quantises the experts' activations the same way
+    (reading R10, block 128); the router reads x itself on both sides."""
+    shape = C[name].with_(**ov) if ov else C[name]
+    layer = DevLayer(shape, tokens=T)
+    log(f"forward fp8 {name}: T={layer.T}")
+    idx, gates = layer.route()
+    accepted, ties = check_routing(layer, idx, gates)
+    out = layer.forward(path="mfma_fp8")
+    torch.cuda.synchronize()
+    ref = layer.oracle(routing=accepted, act_block=128)
+    check_output(out, ref["out"], what=f"{name} T={layer.T} mfma_fp8 ties={ties}")
+
+
+def test_prefill_e512_fp8_full_size_sampled():
+    """The E4M3-activation variant on the 512-expert prefill workload at full
+    size (4096 tokens), outputs on sampled tokens against the oracle."""
+    shape = C["c4"]
+    layer = DevLayer(shape)
+    idx, gates = layer.route()
+    accepted, ties = check_routing(layer, idx, gates)
+    out = layer.forward(path="mfma_fp8")
+    torch.cuda.synchronize()
+    counts = np.bincount(accepted.reshape(-1), minlength=shape.experts)
+    hot = set(np.argsort(-counts)[:16].tolist())
+    rng = np.random.default_rng(13)
+    sample = sorted(set(rng.choice(shape.tokens, 16, replace=False).tolist()) | {0, 4095})
+    n_hot = sum(1 for t in sample if hot & set(accepted[t].tolist()))
+    log(f"c4 fp8: oracle on {len(sample)} sampled tokens ({n_hot} touch a hot expert)")
+    ref = layer.oracle(routing=accepted, tokens=np.array(sample), act_block=128)
+    check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 mfma_fp8 sampled")
+
+
 WS_CASES = [("c1", 16, "auto"), ("c1", 4, "auto"), ("c0", 4, "auto"), ("c1", 16, "mfma"),
             ("c2", 512, "auto"), ("c3", 8, "auto")]
 
