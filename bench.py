@@ -45,6 +45,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 EV_EVERY = 21                  # default: timed steps per step that records the gate/up events
                                # (coprime with the input batches and bank copies: samples rotate)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 def log(msg):
@@ -124,8 +125,9 @@ def cpu_baseline(shape, host, x_batches, seconds):
 KERNEL_SOURCES = {
     "gemv": ["expert_gemv.hip", "device.hpp", "layer.hpp"],
     "mfma": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
+    "mfma_fp8": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
 }
-KERNEL_MATCH = {"gemv": "gemv_gate_up<", "mfma": "mfma_pass<true"}
+KERNEL_MATCH = {"gemv": "gemv_gate_up<", "mfma": "mfma_pass<true", "mfma_fp8": "mfma_gate_up_f8<"}
 COPY_MATCH = "MulFunctor"  # the copy kernel of --copy-calibration (dst = src * 1)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 512
@@ -215,8 +217,8 @@ def traffic_report(args):
     import workloads as W
     shape = W.CONFIGS[args.config]
     T = args.tokens if args.tokens is not None else shape.tokens
-    family = "mfma" if (args.path == "mfma" or (args.path == "auto" and shape.x_dtype == "bf16"
-                                                and T > 16)) else "gemv"
+    family = args.path if args.path in ("mfma", "mfma_fp8") else (
+        "mfma" if args.path == "auto" and shape.x_dtype == "bf16" and T > 16 else "gemv")
     f_kib, nf = counter_means(fetch_csv, KERNEL_MATCH[family])
     w_kib, nw = counter_means(write_csv, KERNEL_MATCH[family])
     cf_kib, _ = counter_means(copy_f_csv, COPY_MATCH)
@@ -261,7 +263,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--tokens", type=int, default=None, help="tokens per step (default: config)")
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma", "mfma_fp8"],
+                    help="expert family; mfma_fp8 runs the gate/up contraction on E4M3 "
+                         "activations (a numerics variant, never chosen by auto)")
     ap.add_argument("--batches", type=int, default=8, help="distinct input batches rotated")
     ap.add_argument("--copies", type=int, default=0, help="device copies of the bank (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -331,7 +335,9 @@ def main():
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    mfma = args.path == "mfma" or (args.path == "auto" and xdt == torch.bfloat16 and T > 16)
+    f8 = args.path == "mfma_fp8"
+    mfma = args.path in ("mfma", "mfma_fp8") or (args.path == "auto" and xdt == torch.bfloat16
+                                                 and T > 16)
 
     # routing of each batch: which experts a step touches (outside the timed region)
     uniq = []
@@ -418,12 +424,15 @@ def main():
     tflops = gu_flops / gu_s / 1e12
     # the gate/up kernel's bound: HBM unless its arithmetic intensity passes
     # the bf16 ridge point (peak FLOP/s over peak bytes/s)
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    family = "grouped bf16 MFMA" if mfma else "wavefront GEMV"
+    # (the fp8 ridge for the E4M3-activation variant, whose products are fp8)
+    peak = FP8_PEAK_TFLOPS if f8 else BF16_PEAK_TFLOPS
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    family = ("grouped FP8 MFMA, E4M3 activations" if f8 else
+              "grouped bf16 MFMA" if mfma else "wavefront GEMV")
     if gu_flops / gu_bytes > ridge:
         roof = {"bound": "mfma", "kernel": f"expert gate/up + SwiGLU ({family})",
-                "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": None,
                 "algorithmic_per_launch": gu_flops,
                 "hbm_GBps": round(gbps, 1)}
     else:
@@ -434,7 +443,8 @@ def main():
                 "mfma_TFLOPs": round(tflops, 2)}
     roof["avg_launch_us"] = round(gu_avg_ms * 1e3, 2)
     roof["launch_samples"] = len(sampled)
-    roof["traffic"] = recorded_traffic(args.config, T, "mfma" if mfma else "gemv")
+    roof["traffic"] = recorded_traffic(args.config, T,
+                                       "mfma_fp8" if f8 else "mfma" if mfma else "gemv")
 
     res = {
         "metric": "MoE-layer tokens/s; decode HBM GB/s vs peak, prefill MFMA util",
@@ -447,15 +457,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if mfma else "f32",  # arithmetic of the expert passes
+        # arithmetic of the expert passes (the fp8 variant: E4M3 x E4M3 gate/up
+        # products, fp16 down products, fp32 accumulation)
+        "dtype": "e4m3+f16" if f8 else "bf16" if mfma else "f32",
         "data": "synthetic",
         "config": {
             "workload": (f"{args.config} {shape.name}: hidden {H}, {E} experts top-{k}"
                          f"{' + 1 shared' if shape.shared else ''}, inter {I}, E4M3 weights "
                          f"with {B}x{B} fp32 block scales, {T} tokens per step, "
-                         f"{shape.x_dtype} activations, fp32 output"),
+                         f"{shape.x_dtype} activations"
+                         f"{' (E4M3, one power-of-two scale per 128 columns, in the gate/up contraction)' if f8 else ''}"
+                         ", fp32 output"),
             "tokens": T, "hidden": H, "experts": E, "top_k": k, "inter": I, "block": B,
-            "shared": shape.shared, "path": "mfma" if mfma else "gemv",
+            "shared": shape.shared,
+            "path": "mfma_fp8" if f8 else "mfma" if mfma else "gemv",
             "bank_copies": copies, "input_batches": len(xs),
         },
         "roofline": roof,

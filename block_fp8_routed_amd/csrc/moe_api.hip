@@ -108,7 +108,7 @@ static moe_status basic_dims(const moe_config* c, Dims* d) {
 static moe_status expert_family_ok(const Dims& d) {
   if (d.mfma) {
     if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
-    if (d.f8 && (d.H % 128 != 0 || d.T * (int64_t)(d.H / 128) >= ((int64_t)1 << 32)))
+    if (d.f8 && (d.H % 128 != 0 || d.T * (int64_t)(d.H / 128) >= ((int64_t)1 << 27)))
       return MOE_ERR_UNSUPPORTED;
     if (max_mfma_tiles(d) > 65535) return MOE_ERR_UNSUPPORTED;  // bounded tile list
     // the passes address activation and h rows with 32-bit byte offsets

@@ -18,9 +18,10 @@
 // E4M3's smallest subnormal (2^-10) and give a zero code either way, so
 // each code is decided exactly as an exact-arithmetic rounding would.
 //
-// One wavefront per block: lane L takes columns 2L and 2L + 1 (one dword of
-// bf16), the block's largest magnitude comes from a DPP maximum over the
-// lanes' fp32 bit patterns (non-negative floats order as unsigned integers).
+// Sixteen lanes per block (a DPP row): lane L of a row takes columns 8L ..
+// 8L + 7 with one 16-byte load, and the block's largest magnitude comes from
+// a four-step DPP maximum within the row over the lanes' fp32 bit patterns
+// (non-negative floats order as unsigned integers).
 #include "device.hpp"
 #include "layer.hpp"
 
@@ -57,28 +58,49 @@ __device__ __forceinline__ int act_exponent(float amax) {
   return (b & 0x7fffff) <= 0x600000u ? E - 8 : E - 7;
 }
 
-__global__ __launch_bounds__(256) void quant_act_kernel(const uint32_t* __restrict__ x,
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t k) {
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppXor1, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppXor2, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppHalfMirror, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kDppMirror, 0xF, 0xF, false));
+  return k;
+}
+
+// thread i of the grid takes 16-byte chunk i (columns 8 (i % 16) .. + 7 of
+// block i / 16); chunks past the end repeat the last one and store nothing
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint4* __restrict__ x,
                                                        int64_t nblocks,
-                                                       uint16_t* __restrict__ codes,
+                                                       uint2* __restrict__ codes,
                                                        uint8_t* __restrict__ exps) {
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nblocks) return;  // uniform over the wavefront
-  const int lane = threadIdx.x & 63;
-  const uint32_t w = x[blk * (kActBlock / 2) + lane];  // columns 2 lane, 2 lane + 1
-  const float v0 = bf16_lo(w), v1 = bf16_hi(w);
-  const uint32_t m = max(__float_as_uint(fabsf(v0)), __float_as_uint(fabsf(v1)));
-  const int e = act_exponent(__uint_as_float(wave_max_u32(m)));
-  const uint32_t c0 = e4m3_rne(__builtin_ldexpf(v0, -e));
-  const uint32_t c1 = e4m3_rne(__builtin_ldexpf(v1, -e));
-  codes[blk * (kActBlock / 2) + lane] = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) exps[blk] = (uint8_t)(e + 127);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = nblocks * (kActBlock / 8);
+  const uint4 w = x[i < n ? i : n - 1];
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bf16_lo(d[j]);
+    v[2 * j + 1] = bf16_hi(d[j]);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(fabsf(v[j])));
+  const int e = act_exponent(__uint_as_float(row16_max_u32(m)));
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = e4m3_rne(__builtin_ldexpf(v[j], -e));
+  if (i >= n) return;
+  codes[i] = make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                        c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+  if ((i & 15) == 0) exps[i >> 4] = (uint8_t)(e + 127);
 }
 
 hipError_t launch_quant_act(const void* x, int64_t T, int H, uint8_t* codes, uint8_t* exps,
                             hipStream_t s) {
   const int64_t nb = T * (H / kActBlock);
-  quant_act_kernel<<<(unsigned)((nb + 3) / 4), 256, 0, s>>>(
-      static_cast<const uint32_t*>(x), nb, reinterpret_cast<uint16_t*>(codes), exps);
+  const int64_t chunks = nb * (kActBlock / 8);
+  quant_act_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, s>>>(
+      static_cast<const uint4*>(x), nb, reinterpret_cast<uint2*>(codes), exps);
   return hipGetLastError();
 }
 
@@ -89,7 +111,8 @@ extern "C" moe_status moe_quantize_act_e4m3(const void* x, int64_t tokens, int32
   if (!x || !codes || !exps) return MOE_ERR_NULL;
   if (tokens < 0 || hidden <= 0) return MOE_ERR_SHAPE;
   if (hidden % moe::kActBlock != 0) return MOE_ERR_UNSUPPORTED;
-  if (tokens * (int64_t)(hidden / moe::kActBlock) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (tokens * (int64_t)(hidden / moe::kActBlock) >= ((int64_t)1 << 27))
+    return MOE_ERR_UNSUPPORTED;  // the grid's x dimension counts 16-byte chunks / 256
   if (tokens == 0) return MOE_OK;
   return moe::launch_quant_act(x, tokens, hidden, codes, exps, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
