@@ -727,15 +727,16 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
 #pragma unroll
     for (int p = 0; p < KS / 64; ++p) {
       const int c0 = (4 * p + 2 * q) ^ sw, c1 = (4 * p + 2 * q + 1) ^ sw;
-      i32x8_t bf[NBW];
+      // A fragments first, then one B fragment at a time: fewer live registers
+      i32x8_t af[MW];
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) bf[nb] = f8_operand(B + S::brow(wn, nb) * KS + bfr, c0, c1);
+      for (int m = 0; m < MW; ++m) af[m] = f8_operand(A + afr + 32 * m * KS, c0, c1);
 #pragma unroll
-      for (int m = 0; m < MW; ++m) {
-        const i32x8_t af = f8_operand(A + afr + 32 * m * KS, c0, c1);
+      for (int nb = 0; nb < NBW; ++nb) {
+        const i32x8_t bf = f8_operand(B + S::brow(wn, nb) * KS + bfr, c0, c1);
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-          acc[m][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[nb], acc[m][nb], 0, 0,
+        for (int m = 0; m < MW; ++m)
+          acc[m][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[m], bf, acc[m][nb], 0, 0,
                                                                       0, sc[m], 0, 127);
       }
     }
@@ -748,6 +749,7 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
     fetch(R, 0);
     put(R, 0, 0);
     __syncthreads();
+#pragma unroll 1
     for (int st = 0; st < NS; st += 2) {
       fetch(R, st + 1);
       compute(0, st);
@@ -767,6 +769,7 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
       fetch(R[j], j);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll 1  // a fully unrolled ring spills at 128 registers
     for (int st0 = 0; st0 < NS; st0 += D) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
