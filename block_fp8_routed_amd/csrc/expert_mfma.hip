@@ -29,6 +29,11 @@
 // MFMA operand layout (32x32x16): lane L supplies row L%32 of A and column
 // L%32 of B, each as 8 k of the 16 (k = 8*(L/32) .. +7); lane L of the result
 // holds column L%32, value v being row 8*(v/4) + 4*(L/32) + v%4.
+//
+// A third pass, mfma_gate_up_f8, is the gate/up contraction of the FP8
+// variant (both operands E4M3, the activations quantised beforehand with one
+// power-of-two scale per token and 128 columns); it is described where it is
+// defined, below the bf16 passes.
 #include <hip/hip_ext.h>
 
 #include "device.hpp"
