@@ -24,6 +24,9 @@ Prints one JSON line: MoE-layer tokens/s, plus
                 out) matches the current sources; null otherwise.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--tokens 16]
+                       [--path auto|gemv|mfma|mfma_fp8]
+       (mfma_fp8: the variant with E4M3 activations in the gate/up contraction;
+        its roofline takes the FP8 peak, 5.0 PFLOP/s, and its ridge)
        python bench.py --copy-calibration            (the copy kernel for the counters)
        python bench.py --gemm-calibration --config c4  (library bf16 GEMMs at the expert shapes)
        python bench.py --traffic-report FETCH.csv WRITE.csv COPYF.csv COPYW.csv --config c1
