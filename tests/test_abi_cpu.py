@@ -157,3 +157,20 @@ def test_quantize_act_validation():
     assert q(FAKE, 4, 0, FAKE, FAKE, None) == _lib.MOE_ERR_SHAPE
     assert q(FAKE, 4, 200, FAKE, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED
     assert q(FAKE, 0, 256, FAKE, FAKE, None) == _lib.MOE_OK  # nothing enqueued
+
+
+def test_fp8_path_validation_and_workspace():
+    """The E4M3-activation variant: bf16 activations only; its workspace adds
+    the activation codes (T*H bytes) and their exponents (T*H/128 bytes)."""
+    bf16 = _lib.torch.bfloat16
+    shape = dict(tokens=300, hidden=2048, experts=128, inter=768, top_k=8, block=128)
+    f32 = cfg(path="mfma_fp8", **shape)
+    assert forward(f32) == _lib.MOE_ERR_UNSUPPORTED  # fp32 activations
+    plain = cfg(path="mfma", x_dtype=bf16, **shape)
+    f8 = cfg(path="mfma_fp8", x_dtype=bf16, **shape)
+    extra = moe.workspace_bytes(f8) - moe.workspace_bytes(plain)
+    T, H = shape["tokens"], shape["hidden"]
+    assert T * H + T * H // 128 <= extra <= T * H + T * H // 128 + 2 * 256  # region alignment
+    auto = cfg(path="auto", x_dtype=bf16, **shape)
+    assert moe.workspace_bytes(auto) == moe.workspace_bytes(plain)  # AUTO never picks FP8
+    assert forward(f8, ws_bytes=moe.workspace_bytes(plain)) == _lib.MOE_ERR_WORKSPACE
