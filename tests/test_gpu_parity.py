@@ -357,6 +357,8 @@ FP8_CASES = [  # (config, tokens, overrides): the E4M3-activation gate/up varian
     ("c1", 300, {"experts": 16, "top_k": 4}),    # full and thin tiles, several per group
     ("c2", None, {}),                            # the 512-token layer at full size
     ("c3", 100, {}),                             # 4096 hidden, shared expert
+    ("c1", 5, {}),                               # decode sizes: one-workgroup selection
+    ("c3", None, {}),                            # 8 tokens, shared expert
 ]
 
 
