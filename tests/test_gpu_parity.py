@@ -398,7 +398,8 @@ def test_prefill_e512_fp8_full_size_sampled():
 
 
 WS_CASES = [("c1", 16, "auto"), ("c1", 4, "auto"), ("c0", 4, "auto"), ("c1", 16, "mfma"),
-            ("c2", 512, "auto"), ("c3", 8, "auto")]
+            ("c2", 512, "auto"), ("c3", 8, "auto"), ("c2", 512, "mfma_fp8"),
+            ("c1", 37, "mfma_fp8")]
 
 
 @pytest.mark.parametrize("name,T,path", WS_CASES, ids=[f"{n}-T{t}-{p}" for n, t, p in WS_CASES])
