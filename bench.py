@@ -460,12 +460,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # arithmetic of the expert passes: bf16 activations meet the (exact)
-        # bf16 form of the E4M3 weights in the gate/up products on both
-        # families, h meets fp16 weights in the down products, accumulation is
-        # fp32; fp32 activations (the tiny layer) take fp32 products. The fp8
-        # variant: E4M3 x E4M3 gate/up products.
-        "dtype": ("e4m3+f16" if f8 else "bf16+f16" if xdt == torch.bfloat16 else "f32+f16"),
+        # arithmetic of the dominant gate/up pass: bf16 activations meet the
+        # (exact) bf16 form of the E4M3 weights on both families, fp32
+        # activations (the tiny layer) take fp32 products, the fp8 variant
+        # E4M3 x E4M3 products; accumulation is fp32 throughout (the down
+        # products are fp16 x fp16 on every path)
+        "dtype": "fp8" if f8 else "bf16" if xdt == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {
             "workload": (f"{args.config} {shape.name}: hidden {H}, {E} experts top-{k}"
