@@ -12,6 +12,8 @@ from .moe_oracle import (  # noqa: F401
     e4m3fn_round,
     expert_matrices,
     gate_weights,
+    h_admissible_deviation,
+    h_band_width,
     moe_layer,
     permutation,
     quantise_activations,

@@ -43,8 +43,19 @@ silent (each restated at the function that uses it):
      (e = 0 for an all-zero block, never below -127), and each value becomes
      the nearest E4M3FN value of x * 2^-e (an exact tie goes to the even
      mantissa; the sign is kept, so negative values that round to zero give
-     -0). Power-of-two scales are the block-scale form of gfx950's FP8
-     matrix instructions. The router still reads the unquantised x.
+     -0). The down contraction reads the SwiGLU output h quantised the same
+     way (per expert row and block of `block` columns of h). Power-of-two
+     scales are the block-scale form of gfx950's FP8 matrix instructions.
+     The router still reads the unquantised x.
+  R11 h is a computed value, so the decisions that quantise it (the block
+     exponent from max|h|, then each code) are taken on h rounded to fp32,
+     the precision the kernels compute h in. A kernel's own fp32 h still
+     differs from that by its rounding error, so where h lies within that
+     error of a decision boundary either side of the boundary is a correct
+     result: h_admissible_deviation bounds how far the dequantised h can
+     move over every such choice, and moe_layer (given h_band) turns that
+     into a per-element bound on the output (the analogue of R9's tie band
+     for selections).
 Every function here is pinned by tests/test_oracle_pins.py; no function is
 parity-unpinned.
 """
@@ -235,17 +246,78 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
-    """y = (silu(xs Wg^T) * (xs Wu^T)) Wd^T for rows xs [n][H] (R6)."""
+def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
+                  h_block: Optional[int] = None, h_band: Optional[tuple] = None):
+    """y = (silu(xs Wg^T) * (xs Wu^T)) Wd^T for rows xs [n][H] (R6); with
+    h_block, h is rounded to fp32 and quantised to E4M3 in blocks of that many
+    columns first (R10, R11). With h_band = (acc_rel, eval_rel) as well,
+    returns (y, bound): bound [n][H] is the largest change of y that the
+    admissible quantisations of h can make (R11), from the band h_band_width
+    gives."""
     a = xs @ wg.T
     u = xs @ wu.T
-    return (silu(a) * u) @ wd.T
+    h = silu(a) * u
+    if h_block is None:
+        return h @ wd.T
+    h = h.astype(np.float32).astype(np.float64)
+    y = dequantise_activations(*quantise_activations(h, h_block), h_block) @ wd.T
+    if h_band is None:
+        return y
+    tau = h_band_width(xs, wg, wu, *h_band)
+    return y, h_admissible_deviation(h, tau, h_block) @ np.abs(wd).T
+
+
+def h_band_width(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, acc_rel: float,
+                 eval_rel: float) -> np.ndarray:
+    """Per element of h = silu(a) * u (a = xs Wg^T, u = xs Wu^T), a bound on
+    how far an fp32 evaluation can land from the exact value (R11): the sums
+    err by at most acc_rel times the sum of their terms' magnitudes, which
+    moves h by |silu'(a)| |u| da + |silu(a)| du to first order, and the
+    pointwise steps (scaling, exponential, division, product) by at most
+    eval_rel (8 + |a|) |h| (an exponential of a argument rounded to relative
+    e errs by about |a| e)."""
+    a = xs @ wg.T
+    u = xs @ wu.T
+    sa = np.abs(xs) @ np.abs(wg).T
+    su = np.abs(xs) @ np.abs(wu).T
+    sig = 1.0 / (1.0 + np.exp(-a))
+    dsilu = sig * (1.0 + a * (1.0 - sig))
+    h = a * sig * u
+    return acc_rel * (np.abs(dsilu * u) * sa + np.abs(a * sig) * su) + \
+        eval_rel * (8.0 + np.abs(a)) * np.abs(h)
+
+
+def h_admissible_deviation(h: np.ndarray, tau: np.ndarray, block: int) -> np.ndarray:
+    """For h [n][I] and a per-element band tau [n][I] (R11): the largest
+    |q(h') - q(h)| over every h' with |h' - h| <= tau elementwise, where q is
+    R10's quantise-then-dequantise in blocks of `block` columns. The block
+    exponent of such an h' lies between those of the smallest and largest
+    block maxima the band allows; under a fixed exponent the rounding is
+    monotone, so the extremes are taken at h - tau and h + tau (values past
+    448 under an exponent cannot occur with that exponent and are clipped)."""
+    n, I = h.shape
+    hb = np.asarray(h, np.float64).reshape(n, I // block, block)
+    tb = np.asarray(tau, np.float64).reshape(n, I // block, block)
+    codes, e = quantise_activations(h, block)
+    ref = dequantise_activations(codes, e, block).reshape(hb.shape)
+    e_lo = act_scale_exponent(np.maximum(np.abs(hb) - tb, 0.0).max(axis=2))
+    e_hi = act_scale_exponent((np.abs(hb) + tb).max(axis=2))
+    lo, hi = np.minimum(e_lo, e_hi), np.maximum(e_lo, e_hi)
+    dev = np.zeros_like(hb)
+    for step in range(int((hi - lo).max(initial=0)) + 1):
+        ec = np.minimum(lo + step, hi)[:, :, None]
+        for side in (-1.0, 0.0, 1.0):
+            v = np.clip((hb + side * tb) * np.ldexp(1.0, -ec), -448.0, 448.0)
+            q = e4m3fn_decode(e4m3fn_round(v)) * np.ldexp(1.0, ec)
+            dev = np.maximum(dev, np.abs(q - ref))
+    return dev.reshape(n, I)
 
 
 def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndarray],
               expert: Callable[[int], dict], top_k: int, inter: int, block: int,
               shared: Optional[dict] = None, routing: Optional[np.ndarray] = None,
-              tokens: Optional[np.ndarray] = None, act_block: Optional[int] = None):
+              tokens: Optional[np.ndarray] = None, act_block: Optional[int] = None,
+              h_band: Optional[tuple] = None):
     """The whole layer in fp64.
 
     expert(e) returns expert e's block-FP8 dict (w_gate_up, s_gate_up, w_down,
@@ -254,8 +326,12 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndar
     for a tie-flagged token); gates are then taken over those experts. With
     `tokens` given, only those rows of the output are computed (the logits of
     every token are still formed, since they are cheap). With `act_block`
-    given, the experts read the activations quantised to E4M3 in blocks of
-    that many columns (R10); the router reads x as it is.
+    given, both expert contractions read E4M3 operands in blocks of that many
+    columns (x for gate/up, h for down, R10); the router reads x as it is.
+    With h_band = (acc_rel, eval_rel) as well, the result also holds
+    "flip" [T'][H]: the bound on how far the admissible quantisations of h
+    (R11) can move each output element, summed over the token's experts with
+    their gates.
 
     Returns dict(out [T'][H], logits [T][E], topk_idx [T][k], gates [T][k],
     ties [T]) where T' = len(tokens) or T.
@@ -268,17 +344,30 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndar
     gates = gate_weights(logits, idx)
     rows = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
     out = np.zeros((len(rows), x.shape[1]), np.float64)
+    band = h_band if act_block is not None else None
+    flip = np.zeros_like(out) if band is not None else None
     sub_idx = idx[rows]
     for e in np.unique(sub_idx):
         wg, wu, wd = expert_matrices(expert(int(e)), inter, block)
         who, slot = np.nonzero(sub_idx == e)
-        y = swiglu_expert(xe[rows[who]], wg, wu, wd)
+        y = swiglu_expert(xe[rows[who]], wg, wu, wd, h_block=act_block, h_band=band)
+        if band is not None:
+            y, bound = y
         # each (token, slot) pair appears once; in fp64 the order of the k
         # terms of a token is immaterial at the tolerances this oracle serves
         for r, (i, j) in enumerate(zip(who, slot)):
             out[i] += gates[rows[i], j] * y[r]
+            if band is not None:
+                flip[i] += gates[rows[i], j] * bound[r]
     if shared is not None:
         wg, wu, wd = expert_matrices(shared, inter, block)
-        out += swiglu_expert(xe[rows], wg, wu, wd)
-    return {"out": out, "logits": logits, "topk_idx": idx, "gates": gates,
-            "ties": tie_flags(logits, top_k)}
+        y = swiglu_expert(xe[rows], wg, wu, wd, h_block=act_block, h_band=band)
+        if band is not None:
+            y, bound = y
+            flip += bound
+        out += y
+    res = {"out": out, "logits": logits, "topk_idx": idx, "gates": gates,
+           "ties": tie_flags(logits, top_k)}
+    if band is not None:
+        res["flip"] = flip
+    return res

@@ -324,9 +324,32 @@ def pin_act_quantise_blocks_bruteforce(O):
     assert np.array_equal(O.dequantise_activations(*O.quantise_activations(xh, B), B), xh)
 
 
+def torch_quantise_rows(v, B):
+    """Per row and block of B columns: scale exponent by counting up, E4M3 by
+    torch's cast, back to fp64."""
+    out = np.empty_like(v)
+    for t in range(v.shape[0]):
+        for b in range(v.shape[1] // B):
+            blk = v[t, b * B:(b + 1) * B]
+            e = scalar_exponent(float(np.abs(blk).max()))
+            out[t, b * B:(b + 1) * B] = lib_decode(lib_round(blk * 2.0 ** -e)) * 2.0 ** e
+    return out
+
+
+def torch_swiglu_q(x, expert, I, B):
+    """torch_swiglu with h quantised per row and B columns before the down
+    product (the FP8 variant's down contraction)."""
+    wgu = torch.from_numpy(lib_dequant(expert["w_gate_up"], expert["s_gate_up"], B))
+    wd = torch.from_numpy(lib_dequant(expert["w_down"], expert["s_down"], B))
+    xt = torch.from_numpy(np.asarray(x, np.float64))
+    h = (torch.nn.functional.silu(xt @ wgu[:I].T) * (xt @ wgu[I:].T)).float().double().numpy()
+    return (torch.from_numpy(torch_quantise_rows(h, B)) @ wd.T).numpy()
+
+
 def pin_act_layer_uses_quantised_experts_only(O):
-    """With act_block, the experts see the E4M3 activations and the router the
-    original ones: against a torch evaluation that quantises with torch's cast."""
+    """With act_block, the experts see E4M3 activations (x for gate/up, h for
+    down) and the router the original x: against a torch evaluation that
+    quantises with torch's cast."""
     rng = np.random.default_rng(12)
     H, I, B, E, k, T = 64, 32, 32, 4, 2, 5
     experts = [random_expert(rng, H, I, B) for _ in range(E)]
@@ -334,28 +357,177 @@ def pin_act_layer_uses_quantised_experts_only(O):
     x = rng.normal(0, 1, (T, H))
     wr = rng.normal(0, 0.3, (E, H))
     res = O.moe_layer(x, wr, None, lambda e: experts[e], k, I, B, shared=shared, act_block=B)
-    xh = np.empty_like(x)
-    for t in range(T):
-        for b in range(H // B):
-            blk = x[t, b * B:(b + 1) * B]
-            e = scalar_exponent(float(np.abs(blk).max()))
-            xh[t, b * B:(b + 1) * B] = lib_decode(lib_round(blk * 2.0 ** -e)) * 2.0 ** e
+    xh = torch_quantise_rows(x, B)
     logits = torch.from_numpy(x) @ torch.from_numpy(wr).T
     top = torch.topk(logits, k, dim=1).indices.numpy()
     assert np.array_equal(res["topk_idx"], top)
-    want = torch_swiglu(xh, shared, I, B)
+    want = torch_swiglu_q(xh, shared, I, B)
     for t in range(T):
         g = torch.softmax(logits[t, top[t]], 0).numpy()
         for j in range(k):
-            want[t] += g[j] * torch_swiglu(xh[t:t + 1], experts[top[t, j]], I, B)[0]
+            want[t] += g[j] * torch_swiglu_q(xh[t:t + 1], experts[top[t, j]], I, B)[0]
     assert np.allclose(res["out"], want, rtol=1e-9, atol=1e-12)
+
+
+# --------------------------- quantised h and its admissible flips (R11) ---
+def pin_h_decided_in_fp32(O):
+    """h = 1.0625 + 2^-30 (block maximum 448, exponent 0) is nearer 1.125 in
+    fp64 but rounds to the midpoint 1.0625 in fp32, where the tie goes to the
+    even code 1.0. silu(64) is exactly 64 in fp64, so h = 64 u exactly."""
+    v = 1.0625 + 2.0 ** -30
+    xs = np.array([[1.0]])
+    wg = np.array([[64.0], [64.0]])
+    wu = np.array([[7.0], [v / 64.0]])
+    wd = np.array([[0.0, 1.0], [1.0, 0.0]])
+    y = O.swiglu_expert(xs, wg, wu, wd, h_block=2)
+    assert y.tolist() == [[1.0, 448.0]]
+    assert lib_decode(lib_round(np.float32(v))) == 1.0  # the library's cast agrees
+
+
+def pin_h_deviation_closed_form(O):
+    """Hand-worked cases of the admissible deviation. Block [448, 1.0625,
+    1.03, 0.0052] with a band of 1e-9: the maximum may cross 448, so the
+    exponent may be 0 or 1; 1.0625 is a midpoint (1.0 by the even tie, 1.125
+    just above it); 1.03 gives 1.0 either way; 0.0052 is subnormal, 3 * 2^-9
+    under exponent 0 and 2 * 2^-9 under exponent 1. With a maximum of 300
+    the exponent is 0 across the band; with no band nothing moves."""
+    h = np.array([[448.0, 1.0625, 1.03, 0.0052, 300.0, 1.0625, 1.03, 0.0052]])
+    dev = O.h_admissible_deviation(h, np.full(h.shape, 1e-9), 4)
+    assert dev.tolist() == [[0.0, 0.125, 0.0, 2.0 ** -9, 0.0, 0.125, 0.0, 0.0]]
+    assert not O.h_admissible_deviation(h, np.zeros(h.shape), 4).any()
+    neg = O.h_admissible_deviation(-h, np.full(h.shape, 1e-9), 4)
+    assert np.array_equal(neg, dev)
+
+
+def pin_h_deviation_bruteforce(O):
+    """Soundness by brute force: every h' in the band, quantised by the
+    library's cast with the exponent its own block maximum gives, stays
+    within the deviation of q(h). The h values sit on code midpoints and
+    block maxima near 448 * 2^e, so flips of codes and of exponents occur."""
+    rng = np.random.default_rng(21)
+    B = 4
+    mags = lib_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (mags[:-1] + mags[1:]) / 2
+    n, I = 6, 8
+    e = rng.integers(-3, 3, (n, I // B))
+    h = rng.choice(mids[8:], (n, I)) * np.repeat(np.ldexp(1.0, e), B, axis=1)
+    h[:, ::B] = np.repeat(np.ldexp(448.0, e), 1, axis=1)  # block maxima on the boundary
+    h *= rng.choice([-1.0, 1.0], h.shape)
+    tau = np.abs(h) * 10.0 ** rng.uniform(-9, -3, h.shape)
+    dev = O.h_admissible_deviation(h, tau, B)
+    ref = torch_quantise_rows(h, B)
+    seen = np.zeros_like(h)
+    for blk in range(I // B):
+        cols = slice(blk * B, (blk + 1) * B)
+        for signs in itertools.product((-1.0, 0.0, 1.0), repeat=B):
+            hp = h[:, cols] + np.array(signs) * tau[:, cols]
+            seen[:, cols] = np.maximum(seen[:, cols], np.abs(torch_quantise_rows(hp, B) - ref[:, cols]))
+    for _ in range(200):
+        hp = h + rng.uniform(-1, 1, h.shape) * tau
+        seen = np.maximum(seen, np.abs(torch_quantise_rows(hp, B) - ref))
+    assert (seen <= dev).all()
+    assert (seen > 0).sum() >= 0.5 * (dev > 0).sum() and (dev > 0).any()
+
+
+def pin_h_band_covers_fp32(O):
+    """The band holds an fp32 evaluation of h: sums of 64 exact products
+    rounded to fp32 and accumulated in fp32, then silu and the product in
+    fp32 (numpy float32), against the fp64 value; with the band's
+    accumulation term scaled as for those sums (2 (K/64 + K/128 + 2) 2^-24)."""
+    rng = np.random.default_rng(22)
+    n, K, I = 24, 512, 64
+    xs = rng.normal(0, 1, (n, K))
+    wg = rng.normal(0, 0.05, (I, K))
+    wu = rng.normal(0, 0.05, (I, K))
+    wu[:, : K // 2] *= 4.0
+
+    def sum32(w):
+        acc = np.zeros((n, I), np.float32)
+        for c in range(0, K, 64):
+            acc = acc + (xs[:, c:c + 64] @ w[:, c:c + 64].T).astype(np.float32)
+        return acc
+
+    a32, u32 = sum32(wg), sum32(wu)
+    h32 = (a32 / (np.float32(1) + np.exp(-a32))) * u32
+    a, u = xs @ wg.T, xs @ wu.T
+    h = a / (1 + np.exp(-a)) * u
+    tau = O.h_band_width(xs, wg, wu, 2 * (K / 64 + K / 128 + 2) * 2.0 ** -24, 4 * 2.0 ** -24)
+    assert (np.abs(h32.astype(np.float64) - h) <= tau).all()
+    assert (tau <= 1e-3 * np.abs(h).max()).all()  # and it is a narrow band
+
+
+def pin_layer_flip_bound(O):
+    """The layer's flip bound is sound: perturbing each expert's h anywhere in
+    its band (fp32-rounded h, then re-quantised by the library's cast) moves
+    the torch evaluation of the layer by no more than "flip"; and with a band
+    of zero the bound vanishes."""
+    rng = np.random.default_rng(23)
+    H, I, B, E, k, T = 64, 32, 32, 4, 2, 5
+    experts = [random_expert(rng, H, I, B) for _ in range(E)]
+    shared = random_expert(rng, H, I, B)
+    x = rng.normal(0, 1, (T, H))
+    wr = rng.normal(0, 0.3, (E, H))
+    band = (3e-3, 1e-3)
+    res = O.moe_layer(x, wr, None, lambda e: experts[e], k, I, B, shared=shared, act_block=B,
+                      h_band=band)
+    zero = O.moe_layer(x, wr, None, lambda e: experts[e], k, I, B, shared=shared, act_block=B,
+                       h_band=(0.0, 0.0))
+    assert not zero["flip"].any() and np.array_equal(zero["out"], res["out"])
+    xh = torch_quantise_rows(x, B)
+    logits = torch.from_numpy(x) @ torch.from_numpy(wr).T
+    top = torch.topk(logits, k, dim=1).indices.numpy()
+
+    def h_tau_wd(ex, rows):
+        wgu = lib_dequant(ex["w_gate_up"], ex["s_gate_up"], B)
+        wd = lib_dequant(ex["w_down"], ex["s_down"], B)
+        xt = torch.from_numpy(rows)
+        h = (torch.nn.functional.silu(xt @ torch.from_numpy(wgu[:I]).T) *
+             (xt @ torch.from_numpy(wgu[I:]).T)).float().double().numpy()
+        a, u = rows @ wgu[:I].T, rows @ wgu[I:].T
+        sa, su = np.abs(rows) @ np.abs(wgu[:I]).T, np.abs(rows) @ np.abs(wgu[I:]).T
+        sig = 1 / (1 + np.exp(-a))
+        tau = band[0] * (np.abs(sig * (1 + a * (1 - sig)) * u) * sa + np.abs(a * sig) * su) + \
+            band[1] * (8 + np.abs(a)) * np.abs(a * sig * u)
+        return h, tau, wd
+
+    def perturbed(ex, rows, signs):
+        h, tau, wd = h_tau_wd(ex, rows)
+        return torch_quantise_rows(h + signs * tau, B) @ wd.T
+
+    def bound(ex, rows):  # the deviation (pinned above) through |Wd|
+        h, tau, wd = h_tau_wd(ex, rows)
+        return O.h_admissible_deviation(h, tau, B) @ np.abs(wd).T
+
+    want_flip = np.zeros((T, H))
+    for t in range(T):
+        g = torch.softmax(logits[t, top[t]], 0).numpy()
+        want_flip[t] = bound(shared, xh[t:t + 1])[0] + sum(
+            g[j] * bound(experts[top[t, j]], xh[t:t + 1])[0] for j in range(k))
+    assert np.allclose(res["flip"], want_flip, rtol=1e-9, atol=1e-15)
+    worst = 0.0
+    for trial in range(40):
+        want = np.zeros((T, H))
+        for t in range(T):
+            g = torch.softmax(logits[t, top[t]], 0).numpy()
+            want[t] += perturbed(shared, xh[t:t + 1], rng.uniform(-1, 1, (1, I)) if trial else 0)[0]
+            for j in range(k):
+                s = rng.choice([-1.0, 1.0], (1, I)) if trial % 2 else rng.uniform(-1, 1, (1, I))
+                want[t] += g[j] * perturbed(experts[top[t, j]], xh[t:t + 1], s if trial else 0)[0]
+        dev = np.abs(want - res["out"])
+        if trial == 0:
+            assert np.allclose(want, res["out"], rtol=1e-9, atol=1e-12)
+        assert (dev <= res["flip"] * (1 + 1e-9) + 1e-12).all()
+        worst = max(worst, float((dev / np.maximum(res["flip"], 1e-300)).max()))
+    assert worst > 0.05  # the bound is reached in part, not vacuous
 
 
 PINS = [pin_decode_matches_library, pin_decode_anchors, pin_dequant_bruteforce,
         pin_topk_bruteforce, pin_gates, pin_permutation, pin_single_expert_is_dense,
         pin_all_experts_equal_gates_is_dense_mean, pin_whole_layer_scalar, pin_tie_flags,
         pin_act_round_matches_library, pin_act_scale_closed_form,
-        pin_act_quantise_blocks_bruteforce, pin_act_layer_uses_quantised_experts_only]
+        pin_act_quantise_blocks_bruteforce, pin_act_layer_uses_quantised_experts_only,
+        pin_h_decided_in_fp32, pin_h_deviation_closed_form, pin_h_deviation_bruteforce,
+        pin_h_band_covers_fp32, pin_layer_flip_bound]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -377,8 +549,8 @@ MUTATIONS = {
                              'order = (len(logits[t]) - 1 - np.argsort(-logits[t][::-1], kind="stable"))'),
     "gates_not_renormalised": ("g[t] = sel / sel.sum()", "g[t] = sel"),
     "silu_sign": ("return z / (1.0 + np.exp(-z))", "return z / (1.0 + np.exp(z))"),
-    "down_not_transposed": ("return (silu(a) * u) @ wd.T", "return (silu(a) * u) @ wd.T[::-1]"),
-    "shared_dropped": ("out += swiglu_expert(xe[rows], wg, wu, wd)", "pass"),
+    "down_not_transposed": ("    return h @ wd.T", "    return h @ wd.T[::-1]"),
+    "shared_dropped": ("        out += y\n", "        pass\n"),
     "permutation_ties_by_descending_slot": ('order = np.argsort(flat, kind="stable")',
                                             "order = np.lexsort((-np.arange(flat.size), flat))"),
     "tie_band_relative": ("return (srt[:, k - 1] - srt[:, k]) < band",
@@ -389,8 +561,18 @@ MUTATIONS = {
     "act_scale_floor_clamp": ("e[nz] = np.maximum(est, -127)", "e[nz] = np.maximum(est, -126)"),
     "act_sign_dropped": ("return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)",
                          "return code"),
-    "experts_read_unquantised_x": ("y = swiglu_expert(xe[rows[who]], wg, wu, wd)",
-                                   "y = swiglu_expert(x[rows[who]], wg, wu, wd)"),
+    "experts_read_unquantised_x": ("y = swiglu_expert(xe[rows[who]], wg, wu, wd, h_block",
+                                   "y = swiglu_expert(x[rows[who]], wg, wu, wd, h_block"),
+    "h_not_quantised": ("y = dequantise_activations(*quantise_activations(h, h_block), h_block) @ wd.T",
+                        "y = h @ wd.T"),
+    "h_decided_in_fp64": ("    h = h.astype(np.float32).astype(np.float64)\n", ""),
+    "flip_ignores_exponent_ambiguity": ("lo, hi = np.minimum(e_lo, e_hi), np.maximum(e_lo, e_hi)",
+                                        "lo, hi = e, e"),
+    "flip_one_sided": ("for side in (-1.0, 0.0, 1.0):", "for side in (0.0, 1.0):"),
+    "band_drops_u_error": ("np.abs(dsilu * u) * sa + np.abs(a * sig) * su", "np.abs(dsilu * u) * sa"),
+    "band_drops_a_error": ("np.abs(dsilu * u) * sa + np.abs(a * sig) * su", "np.abs(a * sig) * su"),
+    "flip_gate_dropped": ("flip[i] += gates[rows[i], j] * bound[r]", "flip[i] += bound[r]"),
+    "flip_shared_dropped": ("            flip += bound\n", ""),
 }
 
 
