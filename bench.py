@@ -25,7 +25,7 @@ Prints one JSON line: MoE-layer tokens/s, plus
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--tokens 16]
                        [--path auto|gemv|mfma|mfma_fp8]
-       (mfma_fp8: the variant with E4M3 activations in the gate/up contraction;
+       (mfma_fp8: the variant with E4M3 operands in both expert contractions;
         its roofline takes the FP8 peak, 5.0 PFLOP/s, and its ridge)
        python bench.py --copy-calibration            (the copy kernel for the counters)
        python bench.py --gemm-calibration --config c4  (library bf16 GEMMs at the expert shapes)
@@ -130,7 +130,7 @@ KERNEL_SOURCES = {
     "mfma": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
     "mfma_fp8": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
 }
-KERNEL_MATCH = {"gemv": "gemv_gate_up<", "mfma": "mfma_pass<true", "mfma_fp8": "mfma_gate_up_f8<"}
+KERNEL_MATCH = {"gemv": "gemv_gate_up<", "mfma": "mfma_pass<true", "mfma_fp8": "mfma_pass_f8<true"}
 COPY_MATCH = "MulFunctor"  # the copy kernel of --copy-calibration (dst = src * 1)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 512
@@ -267,8 +267,8 @@ def main():
     ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--tokens", type=int, default=None, help="tokens per step (default: config)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma", "mfma_fp8"],
-                    help="expert family; mfma_fp8 runs the gate/up contraction on E4M3 "
-                         "activations (a numerics variant, never chosen by auto)")
+                    help="expert family; mfma_fp8 runs both expert contractions on E4M3 "
+                         "operands (a numerics variant, never chosen by auto)")
     ap.add_argument("--batches", type=int, default=8, help="distinct input batches rotated")
     ap.add_argument("--copies", type=int, default=0, help="device copies of the bank (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -427,10 +427,10 @@ def main():
     tflops = gu_flops / gu_s / 1e12
     # the gate/up kernel's bound: HBM unless its arithmetic intensity passes
     # the bf16 ridge point (peak FLOP/s over peak bytes/s)
-    # (the fp8 ridge for the E4M3-activation variant, whose products are fp8)
+    # (the fp8 ridge for the FP8 variant, whose products are fp8)
     peak = FP8_PEAK_TFLOPS if f8 else BF16_PEAK_TFLOPS
     ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
-    family = ("grouped FP8 MFMA, E4M3 activations" if f8 else
+    family = ("grouped FP8 MFMA, E4M3 x and h" if f8 else
               "grouped bf16 MFMA" if mfma else "wavefront GEMV")
     if gu_flops / gu_bytes > ridge:
         roof = {"bound": "mfma", "kernel": f"expert gate/up + SwiGLU ({family})",
@@ -463,8 +463,8 @@ def main():
         # arithmetic of the dominant gate/up pass: bf16 activations meet the
         # (exact) bf16 form of the E4M3 weights on both families, fp32
         # activations (the tiny layer) take fp32 products, the fp8 variant
-        # E4M3 x E4M3 products; accumulation is fp32 throughout (the down
-        # products are fp16 x fp16 on every path)
+        # E4M3 x E4M3 products (in both passes); accumulation is fp32
+        # throughout (the down products of the other paths are fp16 x fp16)
         "dtype": "fp8" if f8 else "bf16" if xdt == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {
@@ -472,7 +472,7 @@ def main():
                          f"{' + 1 shared' if shape.shared else ''}, inter {I}, E4M3 weights "
                          f"with {B}x{B} fp32 block scales, {T} tokens per step, "
                          f"{shape.x_dtype} activations"
-                         f"{' (E4M3, one power-of-two scale per 128 columns, in the gate/up contraction)' if f8 else ''}"
+                         f"{' (E4M3, one power-of-two scale per 128 columns, in both expert contractions, h likewise)' if f8 else ''}"
                          ", fp32 output"),
             "tokens": T, "hidden": H, "experts": E, "top_k": k, "inter": I, "block": B,
             "shared": shape.shared,

@@ -30,13 +30,15 @@
 // L%32 of B, each as 8 k of the 16 (k = 8*(L/32) .. +7); lane L of the result
 // holds column L%32, value v being row 8*(v/4) + 4*(L/32) + v%4.
 //
-// A third pass, mfma_gate_up_f8, is the gate/up contraction of the FP8
-// variant (both operands E4M3, the activations quantised beforehand with one
-// power-of-two scale per token and 128 columns); it is described where it is
-// defined, below the bf16 passes.
+// The FP8 variant's two passes, mfma_pass_f8 (both operands of both
+// contractions E4M3: the activations quantised beforehand with one
+// power-of-two scale per token and 128 columns, h quantised the same way in
+// the gate/up epilogue), are described where they are defined, below the
+// bf16 passes.
 #include <hip/hip_ext.h>
 
 #include "device.hpp"
+#include "e4m3_round.hpp"
 #include "layer.hpp"
 
 namespace moe {
@@ -567,24 +569,27 @@ void mfma_pass(const uint16_t* __restrict__ act,
 }
 
 // ---------------------------------------------------------------------------
-// FP8 gate/up: the variant that runs both operands of the gate/up contraction
-// in E4M3 (activations quantised by moe_quantize_act_e4m3: one power-of-two
-// scale per token and 128 columns), on v_mfma_scale_f32_32x32x64_f8f6f4.
+// FP8 passes: the variant that runs both expert contractions with E4M3 on
+// both sides, on v_mfma_scale_f32_32x32x64_f8f6f4. gate/up reads the
+// activations quantised by moe_quantize_act_e4m3 (one power-of-two scale per
+// token and 128 columns); its epilogue quantises h the same way (a tile's
+// 128 h columns are one block) into E4M3 codes and exponents, which the down
+// pass reads.
 //   Lane l supplies A row l % 32 and B column (weight row) l % 32, each as the
 //   32 bytes of K of its lane half (bytes 32 (l / 32) .. + 31 of the 64-k
 //   step: two 16-byte LDS chunks). A and B take K in the same order, so the
 //   contraction does not depend on the order in which the instruction walks K.
-//   The activation scale rides in the instruction: lane l's E8M0 byte scales A
-//   row l % 32 over its 32 K, all inside one 128-column block, so every lane
-//   of a row passes that block's exponent; B's scale byte is 127 (1). The
-//   weights' fp32 block scales are applied in the ratio form of the bf16 pass.
-// Tiles as in the bf16 pass with half the A bytes: full tiles (more than 64
-// rows) take 64-k stages through two LDS buffers (8 KiB of A, 16 KiB of B),
-// one stage fetched ahead; thin tiles take 128-k stages (one scale block)
-// through one 40 KiB buffer, two stages in flight in registers. A and B rows
-// are both KS bytes of E4M3 and share one swizzle (chunk c of row r at slot
+//   The A scale rides in the instruction: lane l's E8M0 byte scales A row
+//   l % 32 over its 32 K, all inside one 128-column block, so every lane of a
+//   row passes that block's exponent; B's scale byte is 127 (1). The weights'
+//   fp32 block scales are applied in the ratio form of the bf16 passes.
+// Tiles as in the bf16 passes with half the A bytes: full tiles (more than 64
+// rows) take 64-k stages through two LDS buffers (A 8 KiB, B 16 KiB), one
+// stage fetched ahead; thin tiles take 128-k stages (one scale block) through
+// one 40 KiB buffer, two stages in flight in registers. A and B rows are both
+// KS bytes of E4M3 and share one swizzle (chunk c of row r at slot
 // c ^ ((r >> 2) & 3) for 64-k stages, c ^ ((r >> 1) & 7) for 128-k stages).
-template <bool THIN>
+template <bool GU, bool THIN>
 struct F8Shape {
   static constexpr int RA = THIN ? 64 : 128;          // A rows per stage
   static constexpr int KS = THIN ? 128 : 64;          // k per stage
@@ -595,13 +600,15 @@ struct F8Shape {
   static constexpr int BSTAGE = kTN * KS;
   static constexpr int BUFS = THIN ? 1 : 2;
   static constexpr int MW = THIN ? 1 : 2;             // 32-row MFMA tiles per wavefront
-  static constexpr int NBW = 2;                       // gate tile, up tile
+  static constexpr int NBW = 2;                       // 32-column MFMA tiles per wavefront
   static constexpr int DEPTH = THIN ? 2 : 1;
   static_assert(BUFS * (ASTAGE + BSTAGE) <= kLdsBytes, "stage buffers exceed the LDS block");
   static_assert(AC * kPassThreads == RA * CH && BC * kPassThreads == kTN * CH, "fetch map");
   static __device__ __forceinline__ int arow0(int wm) { return (THIN ? 32 : 64) * wm; }
+  // gate/up: gate rows 32 wn .., then the matching up rows; down: 64 wn + 32 nb
   static __device__ __forceinline__ int brow(int wn, int nb) {
-    return nb == 0 ? 32 * wn : kTN / 2 + 32 * wn;
+    if (GU) return nb == 0 ? 32 * wn : kTN / 2 + 32 * wn;
+    return 64 * wn + 32 * nb;
   }
   static __device__ __forceinline__ int swz(int r) { return CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 };
@@ -617,13 +624,21 @@ __device__ __forceinline__ i32x8_t f8_operand(const uint8_t* row, int c0, int c1
   return v;
 }
 
-template <int H, int I, bool THIN>
+// Outputs of an FP8 pass: gate/up writes h as E4M3 codes [P][I] and E8M0
+// exponents [P][I/128]; down writes y (fp16, by slot).
+struct F8Out {
+  uint8_t* hcodes;
+  uint8_t* hexps;
+  uint16_t* y;
+};
+
+template <bool GU, int H, int I, bool THIN>
 __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, const uint8_t* W,
                                              const float* ss, const uint8_t* sx, const int* arow,
-                                             int valid, int r0, int n0, uint8_t* lds,
-                                             uint16_t* __restrict__ h) {
-  using S = F8Shape<THIN>;
-  constexpr int K = H, KS = S::KS, NS = K / KS, AC = S::AC, BC = S::BC, MW = S::MW,
+                                             const int* orow, int valid, int r0, int n0,
+                                             uint8_t* lds, F8Out out) {
+  using S = F8Shape<GU, THIN>;
+  constexpr int K = GU ? H : I, KS = S::KS, NS = K / KS, AC = S::AC, BC = S::BC, MW = S::MW,
                 NBW = S::NBW, CH = S::CH;
   constexpr int NKB = K / kBK;
   static_assert(K % KS == 0 && kBK % KS == 0, "stages must tile the scale blocks");
@@ -633,9 +648,9 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
 
   // fetch map: chunk qq = tid + 512 i is row qq / CH, chunk qq % CH (A and B
   // alike); moving qq by 512 moves the row by a multiple of 32, which leaves
-  // the swizzle alone (GU: tile rows 128 .. 255 are the up rows I + n0 ..)
+  // the swizzle alone (gate/up: tile rows 128 .. 255 are the up rows I + n0 ..)
   const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(act, 0xffffffffu);
-  const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(W, (uint32_t)(2 * I * K));
+  const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(W, (uint32_t)((GU ? 2 * I : H) * K));
   constexpr int RS = kPassThreads / CH;  // row step per chunk group
   const int rt = tid / CH, ct = tid % CH;
   const int dst0 = rt * KS + 16 * (ct ^ S::swz(rt));
@@ -645,7 +660,7 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
   const uint32_t bsrc0 = (uint32_t)(n0 + rt) * K + 16 * ct;
   auto brow_of = [](int i) -> int {
     const int tr = RS * i;
-    return tr < kTN / 2 ? tr : I + tr - kTN / 2;
+    return GU ? (tr < kTN / 2 ? tr : I + tr - kTN / 2) : tr;
   };
   struct Regs {
     uint4 a[AC], b[BC];
@@ -688,7 +703,7 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
   const float* srow[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) srow[nb] = ss + (S::brow(wn, nb) / kBK) * NKB;
-  const uint8_t* sxr[MW];  // this lane's rows' activation exponents
+  const uint8_t* sxr[MW];  // this lane's rows' A exponents
 #pragma unroll
   for (int m = 0; m < MW; ++m) sxr[m] = sx + (S::arow0(wm) + 32 * m + l32) * NKB;
 
@@ -788,74 +803,138 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
     }
   }
 
-  // epilogue through LDS, as in the bf16 pass (gate/up: 128 fp16 columns)
-  constexpr int ORB = 128 * 2, OCH = ORB / 16;
-  static_assert(S::RA * ORB <= kLdsBytes, "output tile exceeds the LDS block");
-  auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
-  const bool odd = l32 & 1;
-  if (!idle) {
+  // D layout (32x32): lane L holds column L % 32; value v is row
+  // 8 (v / 4) + 4 (L / 32) + v % 4
+  if (GU) {
+    // h through LDS as fp32 (512 bytes per tile row; 16-byte chunk c of row r
+    // at slot c ^ (((r >> 2) & 1) << 3), so the two row groups of one write
+    // use different banks), then quantised per row of the tile's 128 columns
+    // (one scale block): 16 lanes (a DPP row) per tile row, 8 values each
+    constexpr int HRB = 128 * 4;
+    static_assert(S::RA * HRB <= kLdsBytes, "h tile exceeds the LDS block");
+    auto hswz = [](int r) { return ((r >> 2) & 1) << 3; };
+    if (!idle) {
 #pragma unroll
-    for (int m = 0; m < MW; ++m)
+      for (int m = 0; m < MW; ++m)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const uint32_t a = f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
-        const uint32_t b =
-            f32_to_f16_sat(silu(acc[m][0][v + 1] * unit[0]) * (acc[m][1][v + 1] * unit[1]));
-        const uint32_t send = odd ? a : b;
-        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
-        const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3) + (odd ? 1 : 0);
-        const int col = S::brow(wn, 0) + l32 - (odd ? 1 : 0);
-        const uint32_t word = odd ? (recv | (b << 16)) : (a | (recv << 16));
-        *reinterpret_cast<uint32_t*>(lds + row * ORB + 16 * (((2 * col) >> 4) ^ oswz(row)) +
-                                     ((2 * col) & 15)) = word;
-      }
-  }
-  __syncthreads();
-  static_assert((S::RA * OCH) % kPassThreads == 0, "output chunks per thread");
+        for (int v = 0; v < 16; ++v) {
+          const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
+          const int col = S::brow(wn, 0) + l32;
+          *reinterpret_cast<float*>(lds + row * HRB + 16 * ((col >> 2) ^ hswz(row)) +
+                                    4 * (col & 3)) =
+              silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]);
+        }
+    }
+    __syncthreads();
+    static_assert((S::RA * 16) % kPassThreads == 0, "h rows per thread");
 #pragma unroll
-  for (int i = 0; i < S::RA * OCH / kPassThreads; ++i) {
-    const int idx = tid + kPassThreads * i, r = idx / OCH, c = idx % OCH;
-    if (r >= valid) continue;
-    const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
-    *reinterpret_cast<uint4*>(h + (size_t)(r0 + r) * I + n0 + 8 * c) = val;
+    for (int i = 0; i < S::RA * 16 / kPassThreads; ++i) {
+      const int idx = tid + kPassThreads * i, r = idx >> 4, k = idx & 15;
+      const uint4 a = *reinterpret_cast<const uint4*>(lds + r * HRB + 16 * ((2 * k) ^ hswz(r)));
+      const uint4 b = *reinterpret_cast<const uint4*>(lds + r * HRB + 16 * ((2 * k + 1) ^ hswz(r)));
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t mx = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, w[j] & 0x7fffffffu);
+      const int e = act_exponent(__uint_as_float(row16_max_u32(mx)));
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = e4m3_rne(__builtin_ldexpf(__uint_as_float(w[j]), -e));
+      if (r >= valid) continue;
+      *reinterpret_cast<uint2*>(out.hcodes + (size_t)(r0 + r) * I + n0 + 8 * k) =
+          make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                     c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+      if (k == 0) out.hexps[(size_t)(r0 + r) * (I / kBK) + n0 / kBK] = (uint8_t)(e + 127);
+    }
+  } else {
+    // y (fp16) through LDS as in the bf16 down pass, stored by slot
+    constexpr int ORB = 256 * 2, OCH = ORB / 16;
+    static_assert(S::RA * ORB <= kLdsBytes, "output tile exceeds the LDS block");
+    auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
+    const bool odd = l32 & 1;
+    if (!idle) {
+#pragma unroll
+      for (int m = 0; m < MW; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2)
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) {
+            const uint32_t a = f32_to_f16_sat(acc[m][nb][v] * unit[nb]);
+            const uint32_t b = f32_to_f16_sat(acc[m][nb][v + 1] * unit[nb]);
+            const uint32_t send = odd ? a : b;
+            const uint32_t recv =
+                (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
+            const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3) + (odd ? 1 : 0);
+            const int col = S::brow(wn, nb) + l32 - (odd ? 1 : 0);
+            const uint32_t word = odd ? (recv | (b << 16)) : (a | (recv << 16));
+            *reinterpret_cast<uint32_t*>(lds + row * ORB + 16 * (((2 * col) >> 4) ^ oswz(row)) +
+                                         ((2 * col) & 15)) = word;
+          }
+    }
+    __syncthreads();
+    static_assert((S::RA * OCH) % kPassThreads == 0, "output chunks per thread");
+#pragma unroll
+    for (int i = 0; i < S::RA * OCH / kPassThreads; ++i) {
+      const int idx = tid + kPassThreads * i, r = idx / OCH, c = idx % OCH;
+      if (r >= valid) continue;
+      const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
+      *reinterpret_cast<uint4*>(out.y + (size_t)orow[r] * H + n0 + 8 * c) = val;
+    }
   }
 }
 
-template <int H, int I>
+template <bool GU, int H, int I>
 __global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void mfma_gate_up_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
-                     MfmaBank bk, const int32_t* __restrict__ meta,
-                     const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
-                     const int32_t* __restrict__ rtok, int E, uint16_t* __restrict__ h) {
+void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
+                  MfmaBank bk, const int32_t* __restrict__ meta,
+                  const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
+                  const int32_t* __restrict__ rtok, const int32_t* __restrict__ pair, int E,
+                  F8Out out) {
+  constexpr int K = GU ? H : I, NKB = K / kBK;
+  constexpr int COLS = GU ? 128 : 256, NCB = (GU ? I : H) / COLS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ int arow[kMfmaBM];
-  constexpr int NKB = H / kBK;
-  __shared__ float ss[2 * NKB];          // the tile's gate and up scale rows
-  __shared__ uint8_t sx[kMfmaBM * NKB];  // the tile rows' activation exponents
-  constexpr int NCB = I / 128;
+  __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
+  __shared__ float ss[2 * NKB];           // the tile's two weight scale rows
+  __shared__ uint8_t sx[kMfmaBM * NKB];   // the tile rows' A exponents
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;  // XCD-aware, as mfma_pass
   const int tile = (j / NCB) * kXcds + xcd;
   if (tile >= meta[1]) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
   const int tid = threadIdx.x;
-  const int n0 = (j % NCB) * 128;
+  const int n0 = (j % NCB) * COLS;
   const bool sh = g == E;
-  const uint8_t* W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
-  const float* Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
-  if (tid < kMfmaBM) arow[tid] = rtok[r0 + (tid < valid ? tid : valid - 1)];
+  const uint8_t* W;
+  const float* Sc;
+  if (GU) {
+    W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
+    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
+  } else {
+    W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
+    Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / kBK) * (I / kBK);
+  }
+  // source row of each tile row (gate/up: the token; down: the h row)
+  if (tid < kMfmaBM) {
+    const int rr = tid < valid ? tid : valid - 1;
+    arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
+    if (!GU) orow[tid] = pair[r0 + rr];
+  }
+  // weight scale rows: gate/up: the gate block of rows n0 .. n0 + 127 and the
+  // matching up block; down: rows n0 .. + 127, then n0 + 128 .. + 255
   if (tid >= 256 && tid < 256 + 2 * NKB) {
     const int i = (tid - 256) / NKB, kb = (tid - 256) % NKB;
-    ss[i * NKB + kb] = Sc[(size_t)((i == 0 ? n0 : I + n0) / kBK) * NKB + kb];
+    const int wrow = GU ? (i == 0 ? n0 : I + n0) : n0 + 128 * i;
+    ss[i * NKB + kb] = Sc[(size_t)(wrow / kBK) * NKB + kb];
   }
   __syncthreads();
   for (int i = tid; i < kMfmaBM * NKB; i += kPassThreads)
     sx[i] = exps[(size_t)arow[i / NKB] * NKB + i % NKB];
   __syncthreads();
   if (valid <= 64)
-    pass_tile_f8<H, I, true>(codes, W, ss, sx, arow, valid, r0, n0, lds, h);
+    pass_tile_f8<GU, H, I, true>(codes, W, ss, sx, arow, orow, valid, r0, n0, lds, out);
   else
-    pass_tile_f8<H, I, false>(codes, W, ss, sx, arow, valid, r0, n0, lds, h);
+    pass_tile_f8<GU, H, I, false>(codes, W, ss, sx, arow, orow, valid, r0, n0, lds, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -869,14 +948,20 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
   const uint16_t* xa = reinterpret_cast<const uint16_t*>(x);
   const int32_t *meta = w.meta, *tiles = w.tiles, *offsets = w.offsets, *rtok = w.rtok,
                 *pair = w.pair;
-  uint16_t* h = reinterpret_cast<uint16_t*>(w.h);
-  if (d.f8) {  // E4M3 activations, quantised after the router read x
+  if (d.f8) {  // both contractions on E4M3 operands; h goes between them as E4M3
+    const F8Out hout{static_cast<uint8_t*>(w.h), w.hexps, nullptr};
+    const F8Out yout{nullptr, nullptr, w.y};
     if (ev.any())
-      hipExtLaunchKernelGGL(mfma_gate_up_f8<H, I>, grid, dim3(kPassThreads), 0, s, ev.begin,
-                            ev.end, 0, w.acodes, w.aexps, bk, meta, tiles, offsets, rtok, d.E, h);
+      hipExtLaunchKernelGGL(mfma_pass_f8<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin,
+                            ev.end, 0, w.acodes, w.aexps, bk, meta, tiles, offsets, rtok, pair,
+                            d.E, hout);
     else
-      mfma_gate_up_f8<H, I><<<grid, kPassThreads, 0, s>>>(w.acodes, w.aexps, bk, meta, tiles,
-                                                          offsets, rtok, d.E, h);
+      mfma_pass_f8<true, H, I><<<grid, kPassThreads, 0, s>>>(w.acodes, w.aexps, bk, meta, tiles,
+                                                             offsets, rtok, pair, d.E, hout);
+    mfma_pass_f8<false, H, I><<<nt8 * (H / PassShape<false, H, I>::COLS), kPassThreads, 0, s>>>(
+        static_cast<const uint8_t*>(w.h), w.hexps, bk, meta, tiles, offsets, rtok, pair, d.E,
+        yout);
+    return;
   } else if (ev.any()) {  // the events take the kernel's own start and end times
     hipExtLaunchKernelGGL(mfma_pass<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin, ev.end,
                           0, xa, bk, meta, tiles, offsets, rtok, pair, d.E, w.h);

@@ -23,7 +23,7 @@ struct Dims {
   int64_t P;     // rows of the permuted problem: T*k + S*T
   bool x_bf16, out_bf16;
   bool mfma;     // expert family: grouped bf16 MFMA (true) or wavefront GEMV
-  bool f8;       // grouped family with E4M3 activations in the gate/up contraction
+  bool f8;       // grouped family with E4M3 operands in both expert contractions
 };
 
 // Router kernels and partial logits. The router writes partial logits per
@@ -87,11 +87,12 @@ struct Work {
   int32_t* pair;     // [P] row -> slot
   int32_t* inv;      // [P] slot -> row
   int32_t* tiles;    // [max_tiles][2] (group, first row) of each MFMA row tile
-  void* h;           // [P][I] fp16 SwiGLU output
+  void* h;           // [P][I] fp16 SwiGLU output (FP8 variant: E4M3 codes)
   uint16_t* y;       // [P][H] fp16 expert outputs by slot (saturated at +-65504)
   int32_t* pblock;   // [2][16][E] per-block expert counts, then per-block bases
-  uint8_t* acodes;   // [T][H] E4M3 activations (FP8 gate/up only, else empty)
-  uint8_t* aexps;    // [T][H/128] their E8M0 exponents (FP8 gate/up only)
+  uint8_t* acodes;   // [T][H] E4M3 activations (FP8 variant only, else empty)
+  uint8_t* aexps;    // [T][H/128] their E8M0 exponents (FP8 variant only)
+  uint8_t* hexps;    // [P][I/128] E8M0 exponents of h (FP8 only; the codes live in h)
 };
 
 inline int64_t max_mfma_tiles(const Dims& d) {

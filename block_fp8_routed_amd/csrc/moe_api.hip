@@ -14,7 +14,7 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 15;
+constexpr int kRegions = 16;
 
 static void region_sizes(const Dims& d, size_t* sz) {
   sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
@@ -32,6 +32,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[12] = (size_t)2 * kPermMaxBlocksHost * d.E * 4;  // permutation block counts and bases
   sz[13] = d.f8 ? (size_t)d.T * d.H : 0;              // E4M3 activations
   sz[14] = d.f8 ? (size_t)d.T * (d.H / 128) : 0;      // their exponents
+  sz[15] = d.f8 ? (size_t)d.P * (d.I / 128) : 0;      // exponents of h
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -66,6 +67,7 @@ Work carve(const Dims& d, void* base) {
   w.pblock = static_cast<int32_t*>(r[12]);
   w.acodes = static_cast<uint8_t*>(r[13]);
   w.aexps = static_cast<uint8_t*>(r[14]);
+  w.hexps = static_cast<uint8_t*>(r[15]);
   return w;
 }
 
@@ -108,7 +110,8 @@ static moe_status basic_dims(const moe_config* c, Dims* d) {
 static moe_status expert_family_ok(const Dims& d) {
   if (d.mfma) {
     if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
-    if (d.f8 && (d.H % 128 != 0 || d.T * (int64_t)(d.H / 128) >= ((int64_t)1 << 27)))
+    if (d.f8 && (d.H % 128 != 0 || d.I % 128 != 0 ||
+                 d.T * (int64_t)(d.H / 128) >= ((int64_t)1 << 27)))
       return MOE_ERR_UNSUPPORTED;
     if (max_mfma_tiles(d) > 65535) return MOE_ERR_UNSUPPORTED;  // bounded tile list
     // the passes address activation and h rows with 32-bit byte offsets

@@ -67,11 +67,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Expert-pass kernel family. AUTO picks the wavefront GEMV family when
  * tokens <= 16 or x is fp32, and the bf16-MFMA grouped family otherwise.
  * The forced values exist so both families can be exercised at any size;
- * MFMA requires bf16 activations. MFMA_FP8 is the grouped family with the
- * gate/up contraction in E4M3 on both sides: x is quantised as
- * moe_quantize_act_e4m3 describes (the router still reads x itself), which
- * changes the layer's numerics (about 2^-4 relative per activation); it
- * requires bf16 x and H a multiple of 128, and is not chosen by AUTO. */
+ * MFMA requires bf16 activations. MFMA_FP8 is the grouped family with both
+ * expert contractions in E4M3 on both sides: x is quantised as
+ * moe_quantize_act_e4m3 describes (the router still reads x itself), and
+ * the SwiGLU output h, computed in fp32, is quantised by the same rule (per
+ * expert row and 128 columns) before the down contraction. This changes the
+ * layer's numerics (about 2^-4 relative per operand value); it requires bf16
+ * x and H and I multiples of 128, and is not chosen by AUTO. */
 typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_GEMV = 1,
@@ -186,8 +188,8 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t* offsets, int32_t* pair,
 moe_status moe_dequant_e4m3(const uint8_t* w, const float* scales, int64_t rows, int32_t cols,
                             int32_t block, float* out, void* stream);
 
-/* E4M3 activations for the variant that runs both operands of the gate/up
- * contraction in FP8 (a reading of this project: the pages describe E4M3
+/* E4M3 activations for the variant that runs both operands of both expert
+ * contractions in FP8 (a reading of this project: the pages describe E4M3
  * weights only, colizig page, "What this project is trying to prove").
  * Each token's row of x is cut into blocks of 128 columns; block b of token t
  * gets the scale 2^e, e the smallest integer with max|x| <= 448 * 2^e over the

@@ -160,8 +160,10 @@ def test_quantize_act_validation():
 
 
 def test_fp8_path_validation_and_workspace():
-    """The E4M3-activation variant: bf16 activations only; its workspace adds
-    the activation codes (T*H bytes) and their exponents (T*H/128 bytes)."""
+    """The FP8 variant: bf16 activations only; its
+    workspace adds the activation codes (T*H bytes), their exponents (T*H/128
+    bytes) and the exponents of h (P*I/128 bytes; h's codes take the fp16 h
+    region)."""
     bf16 = _lib.torch.bfloat16
     shape = dict(tokens=300, hidden=2048, experts=128, inter=768, top_k=8, block=128)
     f32 = cfg(path="mfma_fp8", **shape)
@@ -169,8 +171,10 @@ def test_fp8_path_validation_and_workspace():
     plain = cfg(path="mfma", x_dtype=bf16, **shape)
     f8 = cfg(path="mfma_fp8", x_dtype=bf16, **shape)
     extra = moe.workspace_bytes(f8) - moe.workspace_bytes(plain)
-    T, H = shape["tokens"], shape["hidden"]
-    assert T * H + T * H // 128 <= extra <= T * H + T * H // 128 + 2 * 256  # region alignment
+    T, H, I = shape["tokens"], shape["hidden"], shape["inter"]
+    P = T * shape["top_k"] + (T if f8.has_shared else 0)
+    want = T * H + T * H // 128 + P * I // 128
+    assert want <= extra <= want + 3 * 256  # region alignment
     auto = cfg(path="auto", x_dtype=bf16, **shape)
     assert moe.workspace_bytes(auto) == moe.workspace_bytes(plain)  # AUTO never picks FP8
     assert forward(f8, ws_bytes=moe.workspace_bytes(plain)) == _lib.MOE_ERR_WORKSPACE

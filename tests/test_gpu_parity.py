@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import DevLayer, check_output, check_routing, host_bank, log
+from parity import DevLayer, check_output, check_routing, fp8_h_band, host_bank, log
 
 pytestmark = pytest.mark.gpu
 
@@ -352,7 +352,7 @@ def test_prefill_e512_full_size_sampled():
     check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 sampled")
 
 
-FP8_CASES = [  # (config, tokens, overrides): the E4M3-activation gate/up variant
+FP8_CASES = [  # (config, tokens, overrides): the FP8 variant (E4M3 x and h)
     ("c1", 37, {}),                              # thin tiles, ragged tails
     ("c1", 300, {"experts": 16, "top_k": 4}),    # full and thin tiles, several per group
     ("c2", None, {}),                            # the 512-token layer at full size
@@ -364,9 +364,10 @@ FP8_CASES = [  # (config, tokens, overrides): the E4M3-activation gate/up varian
 
 @pytest.mark.parametrize("name,T,ov", FP8_CASES, ids=[fwd_id((n, t, "mfma_fp8", o)) for n, t, o in FP8_CASES])
 def test_forward_fp8_matches_oracle(name, T, ov):
-    """The grouped family with E4M3 activations in the gate/up contraction
-    against the oracle that quantises the experts' activations the same way
-    (reading R10, block 128); the router reads x itself on both sides."""
+    """The grouped family with E4M3 operands in both expert contractions
+    against the oracle that quantises x and h the same way (readings R10 and
+    R11, block 128), with R11's allowance for admissible h codes; the router
+    reads x itself on both sides."""
     shape = C[name].with_(**ov) if ov else C[name]
     layer = DevLayer(shape, tokens=T)
     log(f"forward fp8 {name}: T={layer.T}")
@@ -374,13 +375,14 @@ def test_forward_fp8_matches_oracle(name, T, ov):
     accepted, ties = check_routing(layer, idx, gates)
     out = layer.forward(path="mfma_fp8")
     torch.cuda.synchronize()
-    ref = layer.oracle(routing=accepted, act_block=128)
-    check_output(out, ref["out"], what=f"{name} T={layer.T} mfma_fp8 ties={ties}")
+    ref = layer.oracle(routing=accepted, act_block=128, h_band=fp8_h_band(shape.hidden))
+    check_output(out, ref["out"], what=f"{name} T={layer.T} mfma_fp8 ties={ties}",
+                 flip=ref["flip"])
 
 
 def test_prefill_e512_fp8_full_size_sampled():
-    """The E4M3-activation variant on the 512-expert prefill workload at full
-    size (4096 tokens), outputs on sampled tokens against the oracle."""
+    """The FP8 variant on the 512-expert prefill workload at full size (4096
+    tokens), outputs on sampled tokens against the oracle."""
     shape = C["c4"]
     layer = DevLayer(shape)
     idx, gates = layer.route()
@@ -393,8 +395,10 @@ def test_prefill_e512_fp8_full_size_sampled():
     sample = sorted(set(rng.choice(shape.tokens, 16, replace=False).tolist()) | {0, 4095})
     n_hot = sum(1 for t in sample if hot & set(accepted[t].tolist()))
     log(f"c4 fp8: oracle on {len(sample)} sampled tokens ({n_hot} touch a hot expert)")
-    ref = layer.oracle(routing=accepted, tokens=np.array(sample), act_block=128)
-    check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 mfma_fp8 sampled")
+    ref = layer.oracle(routing=accepted, tokens=np.array(sample), act_block=128,
+                       h_band=fp8_h_band(shape.hidden))
+    check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 mfma_fp8 sampled",
+                 flip=ref["flip"])
 
 
 WS_CASES = [("c1", 16, "auto"), ("c1", 4, "auto"), ("c0", 4, "auto"), ("c1", 16, "mfma"),
