@@ -380,6 +380,36 @@ def test_forward_fp8_matches_oracle(name, T, ov):
                  flip=ref["flip"])
 
 
+@pytest.mark.parametrize("path", ["mfma_fp8", "mfma"])
+def test_forward_scaled_and_zero_rows(path):
+    """Rows at scales 2^-4 .. 2^3 of the usual activations (so the E4M3
+    exponents of x and h vary from token to token), rows whose first 128
+    columns are zero (an all-zero activation block: exponent 0, zero codes),
+    and all-zero rows (h is zero too; the output row is exactly zero), on
+    both grouped families against the oracle."""
+    shape = C["c1"]
+    T = 48
+    x = W.gen_x(shape, T, 5).astype(np.float64)
+    x *= (2.0 ** (np.arange(T) % 8 - 4))[:, None]
+    x[1::6, :128] = 0.0
+    zero = np.array([5, 23, 47])
+    x[zero] = 0.0
+    layer = DevLayer(shape, x=x.astype(np.float32))
+    log(f"scaled and zero rows {path}: T={T}")
+    idx, gates = layer.route()
+    accepted, ties = check_routing(layer, idx, gates)
+    out = layer.forward(path=path)
+    torch.cuda.synchronize()
+    f8 = path == "mfma_fp8"
+    ref = layer.oracle(routing=accepted, act_block=128 if f8 else None,
+                       h_band=fp8_h_band(shape.hidden) if f8 else None)
+    got = out.float().cpu().numpy()
+    assert not got[zero].any() and not ref["out"][zero].any()
+    rest = np.setdiff1d(np.arange(T), zero)
+    check_output(out, ref["out"][rest], tokens=rest, what=f"scaled rows {path} ties={ties}",
+                 flip=ref["flip"][rest] if f8 else None)
+
+
 def test_prefill_e512_fp8_full_size_sampled():
     """The FP8 variant on the 512-expert prefill workload at full size (4096
     tokens), outputs on sampled tokens against the oracle."""
