@@ -411,7 +411,7 @@ def pin_h_deviation_bruteforce(O):
     n, I = 6, 8
     e = rng.integers(-3, 3, (n, I // B))
     h = rng.choice(mids[8:], (n, I)) * np.repeat(np.ldexp(1.0, e), B, axis=1)
-    h[:, ::B] = np.repeat(np.ldexp(448.0, e), 1, axis=1)  # block maxima on the boundary
+    h[:, ::B] = np.ldexp(448.0, e)  # each block's maximum on the exponent boundary
     h *= rng.choice([-1.0, 1.0], h.shape)
     tau = np.abs(h) * 10.0 ** rng.uniform(-9, -3, h.shape)
     dev = O.h_admissible_deviation(h, tau, B)
