@@ -165,6 +165,8 @@ FWD_CASES = [  # (config, tokens, path, overrides)
     ("c1", 5, "mfma", {}),
     ("c1", 37, "mfma", {}),
     ("c1", 300, "mfma", {"experts": 16, "top_k": 4}),
+    ("c1", 70, "mfma", {"experts": 8, "top_k": 8}),
+    ("c1", 130, "mfma", {"experts": 4, "top_k": 1}),
     ("c2", None, "auto", {}),
     ("c3", 100, "mfma", {}),
     # the limits: top-16 (the most a token may choose) of 512 experts through the
@@ -359,6 +361,9 @@ FP8_CASES = [  # (config, tokens, overrides): the FP8 variant (E4M3 x and h)
     ("c3", 100, {}),                             # 4096 hidden, shared expert
     ("c1", 5, {}),                               # decode sizes: one-workgroup selection
     ("c3", None, {}),                            # 8 tokens, shared expert
+    ("c1", 70, {"experts": 8, "top_k": 8}),      # every token in every group (k = E)
+    ("c1", 130, {"experts": 4, "top_k": 1}),     # one expert per token, large groups
+    ("c1", 200, {"experts": 16, "top_k": 16, "shared": True}),  # top-16 with a shared expert
 ]
 
 
