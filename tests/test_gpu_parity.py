@@ -364,6 +364,7 @@ FP8_CASES = [  # (config, tokens, overrides): the FP8 variant (E4M3 x and h)
     ("c1", 70, {"experts": 8, "top_k": 8}),      # every token in every group (k = E)
     ("c1", 130, {"experts": 4, "top_k": 1}),     # one expert per token, large groups
     ("c1", 200, {"experts": 16, "top_k": 16, "shared": True}),  # top-16 with a shared expert
+    ("c1", 10000, {}),                           # > 512 row tiles: tiles dealt to XCDs in chunks
 ]
 
 
