@@ -507,6 +507,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   }
 }
 
+constexpr int kChunkTiles = 512;  // tile lists at least this long are dealt in chunks
+
 template <bool GU, int H, int I>
 __global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void mfma_pass(const uint16_t* __restrict__ act,
@@ -529,9 +531,14 @@ void mfma_pass(const uint16_t* __restrict__ act,
   // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
   // tile's activation rows are fetched into one L2 and reused from it.
   constexpr int NCB = P::NOUT / P::COLS;
-  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int tile = (j / NCB) * kXcds + xcd;
-  if (tile >= meta[1]) return;
+  // XCD-aware (workgroups go round-robin over the XCDs): on long tile lists
+  // XCD x takes a contiguous chunk of tiles, so the row tiles of a hot expert
+  // share few L2s; on short ones it takes tiles x, x + 8, ...
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds, nt = meta[1];
+  const int chunk = (nt + kXcds - 1) / kXcds;
+  const bool chunked = nt >= kChunkTiles;
+  const int tile = chunked ? xcd * chunk + j / NCB : (j / NCB) * kXcds + xcd;
+  if ((chunked && j / NCB >= chunk) || tile >= nt) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
   const int tid = threadIdx.x;
@@ -883,8 +890,6 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
   }
 }
 
-constexpr int kF8ChunkTiles = 512;  // tile lists at least this long are dealt in chunks
-
 template <bool GU, int H, int I>
 __global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
@@ -899,12 +904,10 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
   __shared__ float ss[2 * NKB];           // the tile's two weight scale rows
   __shared__ uint8_t sx[kMfmaBM * NKB];   // the tile rows' A exponents
-  // XCD-aware (workgroups go round-robin over the XCDs): on long tile lists
-  // XCD x takes a contiguous chunk of tiles, so the row tiles of a hot expert
-  // share few L2s; on short ones it takes tiles x, x + 8, ... as mfma_pass
+  // XCD-aware, as mfma_pass
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds, nt = meta[1];
   const int chunk = (nt + kXcds - 1) / kXcds;
-  const bool chunked = nt >= kF8ChunkTiles;
+  const bool chunked = nt >= kChunkTiles;
   const int tile = chunked ? xcd * chunk + j / NCB : (j / NCB) * kXcds + xcd;
   if ((chunked && j / NCB >= chunk) || tile >= nt) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];

@@ -167,6 +167,7 @@ FWD_CASES = [  # (config, tokens, path, overrides)
     ("c1", 300, "mfma", {"experts": 16, "top_k": 4}),
     ("c1", 70, "mfma", {"experts": 8, "top_k": 8}),
     ("c1", 130, "mfma", {"experts": 4, "top_k": 1}),
+    ("c1", 10000, "mfma", {}),  # > 512 row tiles: tiles dealt to XCDs in chunks
     ("c2", None, "auto", {}),
     ("c3", 100, "mfma", {}),
     # the limits: top-16 (the most a token may choose) of 512 experts through the
