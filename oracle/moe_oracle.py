@@ -75,15 +75,17 @@ def e4m3fn_decode(codes) -> np.ndarray:
     """Value of each OCP E4M3FN byte, by the closed form (R1):
     sign s = b >> 7, exponent e = (b >> 3) & 15, mantissa m = b & 7;
     e == 0: (-1)^s * m * 2^-9 (subnormal); e == 15 and m == 7: NaN;
-    otherwise (-1)^s * 2^(e - 7) * (1 + m / 8)."""
-    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    otherwise (-1)^s * 2^(e - 7) * (1 + m / 8).
+    The closed form is evaluated once for each of the 256 byte values and the
+    codes index that table."""
+    b = np.arange(256, dtype=np.int64)
     s = b >> 7
     e = (b >> 3) & 15
     m = b & 7
     mag = np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
     val = np.where(s == 1, -mag, mag)
-    val = np.where((e == 15) & (m == 7), np.nan, val)
-    return val.astype(np.float64)
+    val = np.where((e == 15) & (m == 7), np.nan, val).astype(np.float64)
+    return val[np.asarray(codes, dtype=np.uint8)]
 
 
 def dequantise(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
