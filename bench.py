@@ -9,13 +9,16 @@ expert bank, so that repeated calls cannot be served from the 256 MB MALL.
 Prints one JSON line: MoE-layer tokens/s, plus
   roofline:     the dominant kernel (gate/up expert pass) timed with HIP events
                 attached to its own dispatch (the library launches it with
-                hipExtLaunchKernel when the caller passes them) on every 21st
-                timed step; recording them costs the stream about 1 us, so the
-                other steps run without; algorithmic bytes = the bytes of the experts the
-                step's routing touches (E4M3 weights + fp32 scales), or
-                algorithmic FLOPs for MFMA-bound workloads;
+                hipExtLaunchKernel when the caller passes them): on every timed
+                step of a prefill-sized workload, on every 21st step of a
+                decode-sized one (recording them costs the stream about 1 us,
+                which a ~20-80 us decode step would feel), and always on at
+                least the last timed step; algorithmic bytes = the bytes of the
+                experts the step's routing touches (E4M3 weights + fp32
+                scales), or algorithmic FLOPs for MFMA-bound workloads;
   cpu_baseline: the CPU oracle (fp64 NumPy) timed on a bounded sample of the
-                same workload on this host.
+                same workload on this host (consecutive token chunks of the
+                input batches, for about --cpu-seconds);
   roofline.traffic: HBM bytes per launch of that kernel, from rocprofv3 PMC
                 runs (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by
                 the bytes a plain copy kernel of known size moves per KiB the
@@ -23,7 +26,13 @@ Prints one JSON line: MoE-layer tokens/s, plus
                 recorded hash of the kernel code (comments and whitespace left
                 out) matches the current sources; null otherwise.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--tokens 16]
+The default workload is the 512-expert, 4096-token prefill layer (hidden 4096,
+top-10 + 1 shared expert, skewed routing): the largest one-GPU configuration.
+After the W warm-up steps, further untimed steps run until --settle-seconds
+have passed, so that the K timed steps see the steady clock the chip settles
+at under load rather than the first steps' ramp.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4] [--tokens T]
                        [--path auto|gemv|mfma|mfma_fp8]
        (mfma_fp8: the variant with E4M3 operands in both expert contractions;
         its roofline takes the FP8 peak, 5.0 PFLOP/s, and its ridge)
@@ -45,8 +54,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-EV_EVERY = 21                  # default: timed steps per step that records the gate/up events
-                               # (coprime with the input batches and bank copies: samples rotate)
+EV_EVERY = 21                  # decode default: timed steps per step that records the gate/up
+                               # events (coprime with the input batches and bank copies)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
@@ -85,8 +94,9 @@ def expert_bytes(shape):
     return shape.expert_bytes()
 
 
-def cpu_baseline(shape, host, x_batches, seconds):
-    """Time the CPU oracle on successive input batches for about `seconds`."""
+def cpu_baseline(shape, host, x_batches, seconds, chunk=64):
+    """Time the CPU oracle on consecutive chunks of at most `chunk` tokens of
+    the input batches (in order) for about `seconds` (at least one chunk)."""
     import numpy as np
     import oracle
     import workloads as W
@@ -97,9 +107,10 @@ def cpu_baseline(shape, host, x_batches, seconds):
     bank, shared = host
     sh = W.bank_expert(shared, 0) if shape.shared else None
     wr, b = W.gen_router(shape), W.gen_bias(shape)
+    chunks = [xb[lo:lo + chunk] for xb in x_batches for lo in range(0, len(xb), chunk)]
     done, t0, i = 0, time.perf_counter(), 0
     while True:
-        x = x_batches[i % len(x_batches)]
+        x = chunks[i % len(chunks)]
         oracle.moe_layer(x, wr, b, lambda e: W.bank_expert(bank, e), shape.top_k, shape.inter,
                          shape.block, shared=sh)
         done += len(x)
@@ -117,8 +128,9 @@ def cpu_baseline(shape, host, x_batches, seconds):
         pass
     return {
         "value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": (f"{i} oracle forwards of {len(x_batches[0])} tokens ({done} tokens, "
-                   f"{el:.1f} s) on the first input batches of the same workload; fp64 NumPy, "
+        "sample": (f"{i} oracle forwards of {len(chunks[0])} tokens ({done} tokens, "
+                   f"{el:.1f} s): consecutive chunks of the timed workload's input batches, "
+                   f"same bank and router; fp64 NumPy, "
                    f"BLAS may use {cores} threads, decode and dequantisation single-threaded; "
                    f"host CPU: {model}"),
     }
@@ -264,7 +276,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--config", default="c4", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--tokens", type=int, default=None, help="tokens per step (default: config)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma", "mfma_fp8"],
                     help="expert family; mfma_fp8 runs both expert contractions on E4M3 "
@@ -272,9 +284,14 @@ def main():
     ap.add_argument("--batches", type=int, default=8, help="distinct input batches rotated")
     ap.add_argument("--copies", type=int, default=0, help="device copies of the bank (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--event-every", type=int, default=EV_EVERY,
+    ap.add_argument("--cpu-chunk", type=int, default=64,
+                    help="tokens per oracle call in the cpu_baseline sample")
+    ap.add_argument("--settle-seconds", type=float, default=2.0,
+                    help="untimed steps after the warm-up until this much time has passed")
+    ap.add_argument("--event-every", type=int, default=None,
                     help="record the gate/up kernel events on every N-th timed step "
-                         "(0: none, no roofline figure)")
+                         "(default: 1 above 16 tokens per step, else 21; always at least the "
+                         "last timed step; 0: none, no roofline figure)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the copy kernel the PMC counters are calibrated on")
@@ -367,9 +384,11 @@ def main():
     # stream about a microsecond, so recording on every step would slow the
     # steps being timed
     K, Wm = args.steps, args.warmup
-    # (the first sample is step EV_EVERY-1: the first timed step follows the
-    # warm-up's synchronize and can run at a lower clock)
-    sampled = list(range(args.event_every - 1, K, args.event_every)) if args.event_every > 0 else []
+    every = args.event_every if args.event_every is not None else (1 if T > 16 else EV_EVERY)
+    every = min(every, K)
+    # (with every > 1 the first sample is step every-1: the first timed step
+    # follows the settling phase's synchronize and can start at a lower clock)
+    sampled = list(range(every - 1, K, every)) if every > 0 else []
     ev_pairs = [(hip.event(), hip.event()) for _ in sampled]
     ev_structs = {}
     for i, (a, b) in zip(sampled, ev_pairs):
@@ -383,10 +402,20 @@ def main():
     for i in range(Wm):
         call(i)
     torch.cuda.synchronize()
-    log(f"timing {K} steps")
+    # settle: untimed steps until the clock has had settle_seconds under load
+    settle, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(8):
+            call(Wm + settle)
+            settle += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
+    # keep the timed steps on the same rotation of batches and bank copies
+    Wm_eff = Wm + settle
+    log(f"settled for {settle} untimed steps ({settle_s:.1f} s); timing {K} steps")
     hip.record(start, sp)
     for i in range(K):
-        call(Wm + i, ev_structs.get(i))
+        call(Wm_eff + i, ev_structs.get(i))
     hip.record(stop, sp)
     torch.cuda.synchronize()
     total_ms = hip.elapsed_ms(start, stop)
@@ -397,8 +426,8 @@ def main():
         return
     gu_avg_ms = sum(gu_ms) / len(gu_ms)
     # the bytes of the sampled steps (for the kernel) and of all steps (for the layer)
-    gu_bytes = sum(uniq[(Wm + i) % len(xs)] for i in sampled) / len(sampled) * gu_bytes_per_expert
-    mean_uniq = sum(uniq[(Wm + i) % len(xs)] for i in range(K)) / K
+    gu_bytes = sum(uniq[(Wm_eff + i) % len(xs)] for i in sampled) / len(sampled) * gu_bytes_per_expert
+    mean_uniq = sum(uniq[(Wm_eff + i) % len(xs)] for i in range(K)) / K
     layer_bytes = mean_uniq * all_bytes_per_expert
 
     # phase breakdown (outside the timed region): all phase events on a few
@@ -456,6 +485,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
+        "settle": {"untimed_steps": settle, "seconds": round(settle_s, 2)},
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -492,7 +522,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
-        res["cpu_baseline"] = cpu_baseline(shape, (bank_h, shared_h), x_host, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(shape, (bank_h, shared_h), x_host, args.cpu_seconds,
+                                           args.cpu_chunk)
     print(json.dumps(res), flush=True)
 
 

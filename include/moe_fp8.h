@@ -141,6 +141,13 @@ typedef struct {
 size_t moe_workspace_bytes(const moe_config* cfg);
 
 /* Whole layer (router, top-k, permutation, SwiGLU experts, combine).
+ * Source: colizig page, "What this project is trying to prove" (model table:
+ * top-8 of 128 experts; top-10 of 512 plus one always-on shared expert;
+ * natively block-FP8 checkpoints), "Features" (E4M3 weights dequantised inside
+ * the dot products; per-expert work fanned out, bit-identical to the serial
+ * path) and "Architecture & how it works" (a small resident router in front of
+ * the experts, which hold most of the parameters). The formulas are the
+ * readings in this file's header.
  *   x           [T][H] of cfg->x_dtype
  *   router_w    [E][H] fp32
  *   router_bias [E] fp32 added to the logits (affects selection and gates),
@@ -158,6 +165,11 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
                        const moe_phase_events* events, void* stream);
 
 /* Router and selection only (the first two steps of moe_forward).
+ * Source: colizig page, "Architecture & how it works" (the router is small and
+ * always resident) and "What this project is trying to prove" (top-8 / top-10
+ * expert counts); the routing function (softmax, top-k with ties to the lower
+ * expert index, gates renormalised over the chosen experts) is this file's
+ * reading, the pages do not write it out.
  *   topk_idx [T][k] int32 expert ids, descending logit, ties to lower id
  *   gates    [T][k] fp32 renormalised softmax weights (sum to 1 per token)
  *   logits   [T][E] fp32 router logits, or NULL to keep them in the workspace */
@@ -167,7 +179,11 @@ moe_status moe_route(const void* x, const float* router_w, const float* router_b
                      void* stream);
 
 /* Token→expert permutation only (the third step of moe_forward), from a
- * given topk_idx [T][k]. Slot s = t·k + j is the j-th choice of token t;
+ * given topk_idx [T][k]. Source: colizig page, "Features" (routed experts
+ * evaluated per expert, the work fanned out over workers with results
+ * bit-identical to the serial order): grouping every token's choices by
+ * expert, stable in token order, is what lets each expert's weights stream
+ * once for all of its tokens. Slot s = t·k + j is the j-th choice of token t;
  * when cfg->has_shared, slots T·k + t (t = 0..T-1) are the shared expert's.
  *   offsets [E+2] int32: rows of routed expert e are offsets[e] .. offsets[e+1]-1;
  *           the shared group is offsets[E] .. offsets[E+1]-1 (empty without one)
