@@ -25,7 +25,10 @@ PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA,
  MOE_EV_END, MOE_EV_COUNT) = range(7)
 
 EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_route", "moe_permute",
-           "moe_dequant_e4m3", "moe_quantize_act_e4m3", "moe_status_string", "moe_version")
+           "moe_dequant_e4m3", "moe_quantize_act_e4m3", "moe_workspace_region",
+           "moe_status_string", "moe_version")
+(MOE_WS_TOPK, MOE_WS_GATES, MOE_WS_OFFSETS, MOE_WS_PAIR, MOE_WS_INV, MOE_WS_H, MOE_WS_H_EXPS,
+ MOE_WS_Y, MOE_WS_Y_EXPS, MOE_WS_COUNT) = range(10)
 
 
 class MoeConfig(ctypes.Structure):
@@ -90,6 +93,9 @@ def load() -> ctypes.CDLL:
     lib.moe_dequant_e4m3.restype = ctypes.c_int
     lib.moe_quantize_act_e4m3.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P]
     lib.moe_quantize_act_e4m3.restype = ctypes.c_int
+    lib.moe_workspace_region.argtypes = [cfgp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t),
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_workspace_region.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_version.argtypes = []
@@ -122,6 +128,23 @@ def make_config(tokens: int, hidden: int, experts: int, inter: int, top_k: int, 
 
 def workspace_bytes(cfg: MoeConfig) -> int:
     return int(load().moe_workspace_bytes(ctypes.byref(cfg)))
+
+
+def workspace_region(cfg: MoeConfig, region: int):
+    """(offset, bytes) of one intermediate result in the workspace of `cfg`."""
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    st = load().moe_workspace_region(ctypes.byref(cfg), int(region), ctypes.byref(off),
+                                     ctypes.byref(n))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_workspace_region")
+    return off.value, n.value
+
+
+def workspace_view(workspace: torch.Tensor, cfg: MoeConfig, region: int,
+                   dtype=torch.uint8) -> torch.Tensor:
+    """A flat view of one region of a workspace tensor, as `dtype`."""
+    off, n = workspace_region(cfg, region)
+    return workspace[off:off + n].view(dtype)
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -4,19 +4,25 @@
 // expert with weight 1 (colizig page, model table: "top-10 + 1 shared").
 // Summed in fp32 in a fixed order (slots j = 0..k-1, then the shared expert),
 // so the result does not depend on how the expert passes were scheduled; one
-// rounding to the output dtype at the end. y rows are fp16, stored by slot
-// (the down passes write row r's output to y row pair[r]), so a token's
-// outputs are rows t*k .. t*k + k - 1 (and T*k + t for the shared expert).
+// rounding to the output dtype at the end. y rows are stored by slot (the
+// down passes write row r's output to y row pair[r]), so a token's outputs
+// are rows t*k .. t*k + k - 1 (and T*k + t for the shared expert). The
+// decode (GEMV) passes leave y in fp32; the grouped passes leave it as fp16
+// with one power-of-two exponent byte per row and 128 columns (value =
+// fp16 * 2^(byte - 127)).
 #include "device.hpp"
 #include "layer.hpp"
 
 namespace moe {
 
+constexpr int kYBlock = 128;  // columns per exponent byte of a scaled fp16 y row
+
 // Thread i of a workgroup sums 8 consecutive outputs of one token (16-byte
-// fp16 loads of y, fp32 accumulation). y is read once and out written once,
-// so both go through non-temporal accesses.
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+// fp16 loads, or two 16-byte fp32 loads, of y; fp32 accumulation). y is read
+// once and out written once, so both go through non-temporal accesses.
+template <bool OUT_BF16, bool Y_F32>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yv,
+                                                     const uint8_t* __restrict__ yexp,
                                                      const float* __restrict__ gates, int64_t T,
                                                      int H, int k, int S, void* __restrict__ out) {
   const int64_t t = blockIdx.x;
@@ -25,27 +31,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float a[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[i] = 0.f;
-  auto add = [&](const uint4 v, float g) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // value v of y row `row`, columns n .. n + 7, times g (g = 1: plain add)
+  auto add = [&](int64_t row, float g, bool gated) {
+    float v[8];
+    if (Y_F32) {
+      const float* yr = static_cast<const float*>(yv) + row * H + n;
+      const uint4 p = ld16_nt(yr), q = ld16_nt(yr + 4);
+      const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x2_t p = __builtin_bit_cast(f16x2_t, w[i]);
-      a[2 * i] = fmaf(g, (float)p[0], a[2 * i]);
-      a[2 * i + 1] = fmaf(g, (float)p[1], a[2 * i + 1]);
+      for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+    } else {
+      const uint4 p = ld16_nt(static_cast<const uint16_t*>(yv) + row * H + n);
+      const uint32_t eb = yexp[row * (H / kYBlock) + n / kYBlock];
+      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x2_t h2 = __builtin_bit_cast(f16x2_t, w[i]);
+        v[2 * i] = f16_scaled_value(h2[0], eb);
+        v[2 * i + 1] = f16_scaled_value(h2[1], eb);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = gated ? fmaf(g, v[i], a[i]) : a[i] + v[i];
   };
-  for (int j = 0; j < k; ++j)
-    add(ld16_nt(y + (size_t)(t * k + j) * H + n), gates[t * k + j]);
-  if (S) {
-    const uint4 v = ld16_nt(y + (size_t)(T * k + t) * H + n);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x2_t p = __builtin_bit_cast(f16x2_t, w[i]);
-      a[2 * i] += (float)p[0];
-      a[2 * i + 1] += (float)p[1];
-    }
-  }
+  for (int j = 0; j < k; ++j) add(t * k + j, gates[t * k + j], true);
+  if (S) add(T * k + t, 1.f, false);
   if (OUT_BF16) {
     uint4 o;
     o.x = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
@@ -65,10 +75,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s) {
   const dim3 grid((unsigned)d.T, (d.H + 2047) / 2048);
-  if (d.out_bf16)
-    combine_kernel<true><<<grid, 256, 0, s>>>(w.y, w.gates, d.T, d.H, d.k, d.S, out);
-  else
-    combine_kernel<false><<<grid, 256, 0, s>>>(w.y, w.gates, d.T, d.H, d.k, d.S, out);
+#define MOE_COMBINE(OB, YF)                                                               \
+  combine_kernel<OB, YF><<<grid, 256, 0, s>>>(w.y, w.yexps, w.gates, d.T, d.H, d.k, d.S, \
+                                              out)
+  if (d.mfma) {
+    if (d.out_bf16) MOE_COMBINE(true, false);
+    else MOE_COMBINE(false, false);
+  } else {
+    if (d.out_bf16) MOE_COMBINE(true, true);
+    else MOE_COMBINE(false, true);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

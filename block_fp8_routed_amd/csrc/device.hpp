@@ -51,10 +51,28 @@ __device__ __forceinline__ float dot2_f16(f16x2_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2_t, b), c, false);
 }
 
-// fp32 -> fp16 bits, round to nearest even, saturated to the finite range.
-__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
-  v = fminf(fmaxf(v, -65504.f), 65504.f);
+// fp32 -> fp16 bits, round to nearest even (callers keep |v| below 2^15).
+__device__ __forceinline__ uint16_t f32_to_f16(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Scaled fp16 storage of the intermediates h and y. A row block of values
+// whose largest magnitude is amax is stored as fp16(v * 2^-e) with one
+// exponent byte e + 127 beside it, e = (binary exponent of amax) - 15, so the
+// block's largest value lands in [2^14, 2^15): rounding cannot carry it past
+// 2^15 < 65504, every value at least 2^-28 of amax keeps fp16's full 11-bit
+// significand, and any finite fp32 range fits. e = 0 for an all-zero block;
+// e is clamped to [-127, 127] (below -127 only blocks smaller than 2^-112
+// lose range, and fp32 itself ends at 2^128).
+constexpr int kF16ExpBias = 127;
+__device__ __forceinline__ int f16_block_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 15;  // amax = f 2^p, f in [0.5, 1)
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// value of one stored fp16 element under its block's exponent byte
+__device__ __forceinline__ float f16_scaled_value(_Float16 v, uint32_t ebyte) {
+  return __builtin_ldexpf((float)v, (int)ebyte - kF16ExpBias);
 }
 
 // bf16 halves of a dword to fp32 (exact).

@@ -22,12 +22,16 @@
 //            h = silu(a) * u is applied in the segment's last lane. bf16
 //            activations meet exact bf16 weight pairs (v_cvt_scalef32_pk_
 //            bf16_fp8 with unit scale) in v_dot2c_f32_bf16; fp32 activations
-//            use fp32 FMA. h is written as fp16 (saturated at +-65504), row-
-//            major [P][I] in permuted row order, the form the MFMA family uses.
-//   down:    y[row][n] = sum_i h[row][i] * Wd[n][i]: exact fp16 weight pairs
-//            meet h in v_dot2c_f32_f16; y is written as fp16 [P][H] (saturated
-//            at +-65504) by slot (row r's output to y row pair[r]), the form
-//            the combine reads.
+//            use fp32 FMA. h is written as fp32, row-major [P][I] in permuted
+//            row order (decode groups are small, so h is too).
+//   down:    y[row][n] = sum_i h[row][i] * Wd[n][i]. Each workgroup stages
+//            its group's h rows in LDS as fp16 scaled by one power of two
+//            per row (its largest value lands in [2^14, 2^15): no overflow
+//            at any fp32 magnitude, full fp16 precision down to 2^-28 of the
+//            row's largest value), so exact fp16 weight pairs meet h in
+//            v_dot2c_f32_f16 and the row's power of two is applied to the
+//            fp32 sum; y is written as fp32 [P][H] by slot (row r's output to
+//            y row pair[r]), the form the combine reads.
 // Tokens of a group are taken NT at a time; a larger group takes several
 // passes over the weights already held in registers.
 #include <hip/hip_ext.h>
@@ -101,14 +105,19 @@ struct RowStage {
   static constexpr bool UNIFORM = CPR % 256 == 0;
   static_assert((L * ELEM) % 16 == 0, "rows must be whole 16-byte chunks");
   uint4 v[N];
+  // row t and chunk c of register j (entries past the NT rows repeat the last chunk)
+  static __device__ __forceinline__ void at(int j, int& t, int& c) {
+    int i = threadIdx.x + 256 * j;
+    if (i >= NT * CPR) i = NT * CPR - 1;
+    t = UNIFORM ? (256 * j) / CPR : i / CPR;
+    c = i - t * CPR;
+  }
   template <class RowOf>
   __device__ __forceinline__ void load(const void* src, RowOf row_of) {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      int i = threadIdx.x + 256 * j;
-      if (i >= NT * CPR) i = NT * CPR - 1;
-      const int t = UNIFORM ? (256 * j) / CPR : i / CPR;
-      const int c = i - t * CPR;
+      int t, c;
+      at(j, t, c);
       v[j] = ld16(reinterpret_cast<const uint8_t*>(src) + ((size_t)row_of(t) * CPR + c) * 16);
     }
   }
@@ -120,6 +129,45 @@ struct RowStage {
   }
 };
 
+// A pass's fp32 h rows (held in registers by a RowStage<I, 4, NT>) into LDS
+// as fp16, row t scaled by 2^-hexp[t] (f16_block_exponent of the row's
+// largest magnitude, found with LDS atomic maxima on the magnitudes' bits:
+// non-negative floats order as their bit patterns, and a maximum does not
+// depend on the order of the atomics). hs row t starts at element t * I.
+// Ends with a barrier; the caller's previous reads of hs and hexp must have
+// ended (a barrier) before the call.
+template <int I, int NT>
+__device__ __forceinline__ void put_scaled_rows(const RowStage<I, 4, NT>& st, uint16_t* hs,
+                                                uint32_t* hmax, int* hexp) {
+  using RS = RowStage<I, 4, NT>;
+  if (threadIdx.x < NT) hmax[threadIdx.x] = 0u;
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < RS::N; ++j) {
+    int t, c;
+    RS::at(j, t, c);
+    const uint4 w = st.v[j];
+    const uint32_t m = max(max(w.x & 0x7fffffffu, w.y & 0x7fffffffu),
+                           max(w.z & 0x7fffffffu, w.w & 0x7fffffffu));
+    atomicMax(&hmax[t], m);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < RS::N; ++j) {
+    int t, c;
+    RS::at(j, t, c);
+    const int e = f16_block_exponent(__uint_as_float(hmax[t]));
+    const uint4 w = st.v[j];
+    const uint32_t lo = f32_to_f16(__builtin_ldexpf(__uint_as_float(w.x), -e)) |
+                        ((uint32_t)f32_to_f16(__builtin_ldexpf(__uint_as_float(w.y), -e)) << 16);
+    const uint32_t hi = f32_to_f16(__builtin_ldexpf(__uint_as_float(w.z), -e)) |
+                        ((uint32_t)f32_to_f16(__builtin_ldexpf(__uint_as_float(w.w), -e)) << 16);
+    *reinterpret_cast<uint2*>(hs + (size_t)t * I + 4 * c) = make_uint2(lo, hi);
+  }
+  if (threadIdx.x < NT) hexp[threadIdx.x] = f16_block_exponent(__uint_as_float(hmax[threadIdx.x]));
+  lds_barrier();
+}
+
 // ------------------------------------------------------------- gate/up ---
 // grid: (slabs of PPW row pairs, 4 per workgroup; group slots). Slots past
 // the last group exit at once.
@@ -127,7 +175,7 @@ template <int H, int I, int B, int NT, int M, bool XBF16>
 __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, BankPtrs bk,
                                                    const int4* __restrict__ gdesc,
                                                    const int32_t* __restrict__ rtok, int E,
-                                                   uint16_t* __restrict__ h) {
+                                                   float* __restrict__ h) {
   using G = GateUpMap<H, M>;
   constexpr int LPP = G::LPP, PPW = G::PPW, SPG = I / PPW;
   static_assert(I % PPW == 0, "row pairs must split evenly into slabs");
@@ -239,7 +287,7 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
         if (t >= nv) continue;
         const float a = seg_sum<LPP>(ag[t]);
         const float u = seg_sum<LPP>(au[t]);
-        if (sub == LPP - 1) h[(size_t)(r0 + t0 + t) * I + i] = f32_to_f16_sat(silu(a) * u);
+        if (sub == LPP - 1) h[(size_t)(r0 + t0 + t) * I + i] = silu(a) * u;
       }
     }
     t0 += NT;
@@ -256,13 +304,15 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
 // ---------------------------------------------------------------- down ---
 template <int H, int I, int B, int NT>
 __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __restrict__ gdesc,
-                                                int E, const uint16_t* __restrict__ h,
+                                                int E, const float* __restrict__ h,
                                                 const int32_t* __restrict__ pair,
-                                                uint16_t* __restrict__ y) {
+                                                float* __restrict__ y) {
   using D = DownMap<I>;
   constexpr int LPR = D::LPR, MD = D::MD, RW = D::RW, SPG = H / RW;
   static_assert(H % RW == 0, "rows must split evenly into slabs");
-  __shared__ __attribute__((aligned(16))) uint16_t hs[RowStage<I, 2, NT>::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[NT * I];  // scaled fp16 h rows
+  __shared__ uint32_t hmax[NT];
+  __shared__ int hexp[NT];
   const int4 gd = gdesc[blockIdx.y];
   const int g = gd.x;
   if (g < 0) return;  // uniform over the workgroup
@@ -277,10 +327,10 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
   const float* Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / B) * (I / B);
 
   // the group's h rows are contiguous (rows r0 .. r0 + n - 1); the first
-  // pass's rows are requested before the weights and scales, so storing them
-  // to LDS does not wait for the weights. No load is conditional, as in
+  // pass's rows are requested before the weights and scales, so staging them
+  // in LDS does not wait for the weights. No load is conditional, as in
   // gemv_gate_up.
-  RowStage<I, 2, NT> st;
+  RowStage<I, 4, NT> st;
   int nv = n < NT ? n : NT;  // tokens in this pass (uniform)
   const auto seq_row = [&](int t) { return t < nv ? t : nv - 1; };
   st.load(h + (size_t)r0 * I, seq_row);
@@ -292,8 +342,7 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
 #pragma unroll
   for (int m = 0; m < MD; ++m) sd[m] = Sc[(row / B) * (I / B) + (16 * (m * LPR + sub)) / B];
   __builtin_amdgcn_sched_barrier(0);
-  st.store(hs);
-  lds_barrier();
+  put_scaled_rows(st, hs, hmax, hexp);
   for (int t0 = 0;;) {
     // y is stored by slot (row r's output goes to y row pair[r]), so the
     // combine reads a token's outputs without the inverse permutation
@@ -331,7 +380,7 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
       for (int t = 0; t < NT; ++t) {
         if (t >= nv) continue;
         const float v = seg_sum<LPR>(acc[t]);
-        if (sub == LPR - 1) y[(size_t)oslot[t] * H + row] = f32_to_f16_sat(v);
+        if (sub == LPR - 1) y[(size_t)oslot[t] * H + row] = __builtin_ldexpf(v, hexp[t]);
       }
     }
     t0 += NT;
@@ -339,8 +388,7 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
     nv = n - t0 < NT ? n - t0 : NT;
     st.load(h + (size_t)(r0 + t0) * I, seq_row);
     lds_barrier();  // every wavefront is done with the previous pass
-    st.store(hs);
-    lds_barrier();
+    put_scaled_rows(st, hs, hmax, hexp);
   }
 }
 
@@ -361,14 +409,14 @@ static void run_gemv(const Dims& d, const void* x, const BankPtrs& bk, const Wor
   const int4* gdesc = reinterpret_cast<const int4*>(w.gdesc);
   const int groups = (int)std::min<int64_t>(d.E, d.T * d.k) + d.S;
   const dim3 grid((SPG1 + 3) / 4, groups);
-  uint16_t* h = reinterpret_cast<uint16_t*>(w.h);
+  float* h = static_cast<float*>(w.h);
   if (ev.any())  // the events take the kernel's own start and end times
     hipExtLaunchKernelGGL(gemv_gate_up<H, I, B, NT, M, XBF16>, grid, dim3(256), 0, s, ev.begin,
                           ev.end, 0, x, bk, gdesc, static_cast<const int32_t*>(w.rtok), d.E, h);
   else
     gemv_gate_up<H, I, B, NT, M, XBF16><<<grid, 256, 0, s>>>(x, bk, gdesc, w.rtok, d.E, h);
   gemv_down<H, I, B, NT><<<dim3((SPG2 + 3) / 4, groups), 256, 0, s>>>(
-      bk, gdesc, d.E, reinterpret_cast<const uint16_t*>(w.h), w.pair, w.y);
+      bk, gdesc, d.E, h, w.pair, static_cast<float*>(w.y));
 }
 
 template <int H, int I, int B>

@@ -18,13 +18,20 @@
 //
 // gate/up runs bf16 MFMA: activations are bf16 and the weights exact in bf16,
 // so nothing is rounded on the way in; SwiGLU is applied to the accumulator
-// registers and h is written as fp16 [P][I] (11-bit significand, saturated at
-// +-65504). down runs fp16 MFMA on h (the weights are exact in fp16 as well)
-// and writes y as fp16 [P][H] by slot (row r's output to y row pair[r]),
-// saturated the same way. h and y are the two
-// intermediates rounded below fp32: fp16 keeps their relative error at 2^-11,
-// which leaves the layer's output well inside its tolerance (max error <=
-// 1e-2 x RMS); bf16 would use up most of it.
+// registers and h is written as scaled fp16 [P][I]: each row's 128 columns
+// (one tile's output) share one power of two, chosen so that the block's
+// largest value lands in [2^14, 2^15) (f16_block_exponent), with the
+// exponent byte in hexps [P][I/128]. down runs fp16 MFMA on h (the weights
+// are exact in fp16 as well): a tile first brings each of its h rows to one
+// common power of two (the largest of the row's block exponents; the other
+// blocks are multiplied by 2^-d in fp16, exact unless a block is more than
+// 2^14 below the row's largest), and applies it to the fp32 result; y is
+// written as scaled fp16 [P][H] by slot (row r's output to y row pair[r]),
+// one exponent byte per row and 128 columns in yexps. h and y are the two
+// intermediates rounded below fp32: fp16 keeps their relative error at
+// 2^-11, which leaves the layer's output well inside its tolerance (max
+// error <= 1e-2 x RMS; bf16 would use up most of it), and the exponents keep
+// any fp32 magnitude representable.
 //
 // MFMA operand layout (32x32x16): lane L supplies row L%32 of A and column
 // L%32 of B, each as 8 k of the 16 (k = 8*(L/32) .. +7); lane L of the result
@@ -58,6 +65,7 @@ struct MfmaBank {
 };
 
 constexpr int kBK = 128;            // K per scale block (the block edge)
+constexpr int kPassThreadsDecl = 512;  // threads of a grouped pass workgroup
 
 // 8 E4M3 bytes (two dwords) to 8 bf16 (exact).
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
@@ -90,6 +98,77 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
   r[7] = d[1];
   return r;
 }
+
+// ---- epilogue helpers: an fp32 output tile of 128 columns through LDS ----
+// Tile row r at byte r * 512, 16-byte chunk c at slot c ^ f32_swz(r), so the
+// two row groups of one accumulator write land on different banks.
+__device__ __forceinline__ int f32_swz(int r) { return ((r >> 2) & 1) << 3; }
+__device__ __forceinline__ void put_f32(uint8_t* lds, int row, int col, float v) {
+  *reinterpret_cast<float*>(lds + row * 512 + 16 * ((col >> 2) ^ f32_swz(row)) + 4 * (col & 3)) = v;
+}
+// Rows [0, valid) of an RA-row fp32 tile in LDS (as put_f32 leaves it) stored
+// as scaled fp16: 16 lanes (one DPP row) per tile row take 8 values each, a
+// DPP maximum gives the row's largest magnitude and f16_block_exponent its
+// power of two; dst(r) is the row's first fp16 element in global memory,
+// ebyte(r) where its exponent byte goes. `wave` is the (uniform) wavefront
+// index: the thread index is rebuilt from it and the lane id, which keeps
+// the loop before the epilogue from holding the thread index in a register.
+template <int RA, class Dst, class Eb>
+__device__ __forceinline__ void store_f16_rows(const uint8_t* lds, int valid, int wave, Dst dst,
+                                               Eb ebyte) {
+  static_assert((RA * 16) % kPassThreadsDecl == 0, "tile rows per thread");
+  const int tid = 64 * wave + (int)__lane_id();
+#pragma unroll
+  for (int i = 0; i < RA * 16 / kPassThreadsDecl; ++i) {
+    const int idx = tid + kPassThreadsDecl * i, r = idx >> 4, k = idx & 15;
+    const uint4 a = *reinterpret_cast<const uint4*>(lds + r * 512 + 16 * ((2 * k) ^ f32_swz(r)));
+    const uint4 b = *reinterpret_cast<const uint4*>(lds + r * 512 + 16 * ((2 * k + 1) ^ f32_swz(r)));
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = max(mx, w[j] & 0x7fffffffu);
+    const int e = f16_block_exponent(__uint_as_float(row16_max_u32(mx)));
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = f32_to_f16(__builtin_ldexpf(__uint_as_float(w[2 * j]), -e)) |
+             ((uint32_t)f32_to_f16(__builtin_ldexpf(__uint_as_float(w[2 * j + 1]), -e)) << 16);
+    if (r >= valid) continue;
+    *reinterpret_cast<uint4*>(dst(r) + 8 * k) = make_uint4(o[0], o[1], o[2], o[3]);
+    if (k == 0) *ebyte(r) = (uint8_t)(e + kF16ExpBias);
+  }
+}
+
+// fp16 factors that bring an h block to its row's common power of two:
+// 2^d (d <= 0) as two fp16 multipliers 2^a and 2^b (a = max(d, -24), b =
+// max(d - a, -24)), since fp16 holds powers of two down to 2^-24 only; the
+// two fp16 bit patterns in one word (low: a).
+__device__ __forceinline__ uint32_t f16_pow2_bits(int a) {  // a in [-24, 0]
+  return a >= -14 ? (uint32_t)(a + 15) << 10 : 1u << (a + 24);
+}
+__device__ __forceinline__ uint32_t rescale_word(int d) {
+  const int a = d > -24 ? d : -24;
+  const int b = d - a > -24 ? d - a : -24;
+  return f16_pow2_bits(a) | (f16_pow2_bits(b) << 16);
+}
+// 8 fp16 values (a 16-byte chunk) times the two multipliers of a rescale word
+__device__ __forceinline__ uint4 rescale_f16x8(uint4 v, uint32_t word) {
+  const f16x2_t fa = __builtin_bit_cast(f16x2_t, (word & 0xffffu) * 0x10001u);
+  const f16x2_t fb = __builtin_bit_cast(f16x2_t, (word >> 16) * 0x10001u);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, w[j]) * fa * fb);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Outputs of a bf16 pass: gate/up writes h (scaled fp16 [P][I]) and its
+// exponent bytes; down reads h's exponent bytes and writes y (scaled fp16
+// [P][H], by slot) and its exponent bytes.
+struct PassIO {
+  void* out;
+  uint8_t* oexps;
+  const uint8_t* hexps;
+};
 
 // Grouped pass, one template for both projections.
 //
@@ -148,7 +227,7 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
 // as whole 16-byte chunks.
 constexpr int kTN = 256;            // weight rows per tile
 constexpr int kXcds = 8;            // accelerator complex dies (one L2 each)
-constexpr int kPassThreads = 512;
+constexpr int kPassThreads = kPassThreadsDecl;
 constexpr int kLdsBytes = 65536;    // stage buffers of one workgroup
 static_assert(kMfmaBM == 128, "tile geometry assumes 128-row tiles");
 
@@ -218,8 +297,8 @@ struct TileShape {
 template <bool GU, int H, int I, bool THIN>
 __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, const uint8_t* W,
                                           const float* ss, const int* arow, const int* orow,
-                                          int valid, int r0, int n0, uint8_t* lds,
-                                          void* __restrict__ out) {
+                                          const uint32_t* hfac, const int* herow, int valid,
+                                          int r0, int n0, uint8_t* lds, PassIO io) {
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
   using S = TileShape<GU, THIN>;
@@ -287,6 +366,10 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
 #pragma unroll
       for (int i = 0; i < BC; ++i)
         if (bscale[i][kb] == 0.f) R.b[i] = make_uint4(0, 0, 0, 0);
+    }
+    if (!GU) {  // h rows to their row's common power of two
+#pragma unroll
+      for (int i = 0; i < AC; ++i) R.a[i] = rescale_f16x8(R.a[i], hfac[(ar0 + ARS * i) * NKB + kb]);
     }
 #pragma unroll
     for (int i = 0; i < AC; ++i) *reinterpret_cast<uint4*>(A + adst0 + ARS * (KS * 2) * i) = R.a[i];
@@ -452,58 +535,55 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     }
   }
 
-  // Epilogue through LDS (free after the loop's last barrier): each wavefront
-  // writes its fp16 results into a row-major tile, then every output row is
-  // stored as 16-byte chunks. D layout (32x32): lane L holds column L % 32;
-  // value v is row 8 (v / 4) + 4 (L / 32) + v % 4. Lanes exchange one value
-  // with their neighbour (DPP quad_perm 1,0,3,2) so that each writes one
-  // dword: an even lane two columns of row R (value v), an odd lane two
-  // columns of row R + 1 (value v + 1). The 64-byte row pieces of one write
-  // (rows R, R + 1, R + 4, R + 5) are spread over the banks by XOR-ing the
-  // chunk index with (row & 1 | (row >> 2 & 1) << 1) << 2.
-  constexpr int OC = GU ? 128 : 256;  // output columns of the tile
-  constexpr int ORB = OC * 2;         // bytes per tile row in LDS
-  constexpr int OCH = ORB / 16;       // 16-byte chunks per row
-  static_assert(S::RA * ORB <= kLdsBytes, "output tile exceeds the LDS block");
-  auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
-  const bool odd = l32 & 1;
-  auto wput = [&](int m, int col0, uint32_t a, uint32_t b, int v) {
-    const uint32_t send = odd ? a : b;
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
-    const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3) + (odd ? 1 : 0);
-    const int col = col0 + l32 - (odd ? 1 : 0);
-    const uint32_t word = odd ? (recv | (b << 16)) : (a | (recv << 16));
-    *reinterpret_cast<uint32_t*>(lds + row * ORB + 16 * (((2 * col) >> 4) ^ oswz(row)) +
-                                 ((2 * col) & 15)) = word;
-  };
-  if (!idle) {
+  // Epilogue through LDS (free after the loop's last barrier) as fp32 tiles
+  // of 128 columns, stored as scaled fp16 rows (store_f16_rows). D layout
+  // (32x32): lane L holds column L % 32; value v is row 8 (v / 4) + 4 (L / 32)
+  // + v % 4. gate/up: the tile's 128 h columns in one round; down: 256
+  // output columns in two rounds of 128 (wavefronts wn = 0, 1, then 2, 3),
+  // the h row's common power of two applied to the fp32 results.
+  static_assert(S::RA * 512 <= kLdsBytes, "output tile exceeds the LDS block");
+  // the lane's position, rebuilt here rather than kept live through the loop
+  const int eln = (int)__lane_id(), eq = eln >> 5, el32 = eln & 31;
+  if (GU) {
+    if (!idle) {
 #pragma unroll
-    for (int m = 0; m < MW; ++m)
+      for (int m = 0; m < MW; ++m)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        if (GU) {
-          const uint32_t a = f32_to_f16_sat(silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
-          const uint32_t b =
-              f32_to_f16_sat(silu(acc[m][0][v + 1] * unit[0]) * (acc[m][1][v + 1] * unit[1]));
-          wput(m, S::brow(wn, 0), a, b, v);
-        } else {
-#pragma unroll
-          for (int nb = 0; nb < NBW; ++nb)
-            wput(m, S::brow(wn, nb), f32_to_f16_sat(acc[m][nb][v] * unit[nb]),
-                 f32_to_f16_sat(acc[m][nb][v + 1] * unit[nb]), v);
+        for (int v = 0; v < 16; ++v) {
+          const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * eq + (v & 3);
+          put_f32(lds, row, S::brow(wn, 0) + el32,
+                  silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
         }
-      }
-  }
-  __syncthreads();
-  static_assert((S::RA * OCH) % kPassThreads == 0, "output chunks per thread");
+    }
+    __syncthreads();
+    uint16_t* h = static_cast<uint16_t*>(io.out);
+    store_f16_rows<S::RA>(
+        lds, valid, wave, [&](int r) { return h + (size_t)(r0 + r) * I + n0; },
+        [&](int r) { return io.oexps + (size_t)(r0 + r) * (I / kBK) + n0 / kBK; });
+  } else {
+    uint16_t* y = static_cast<uint16_t*>(io.out);
 #pragma unroll
-  for (int i = 0; i < S::RA * OCH / kPassThreads; ++i) {
-    const int idx = tid + kPassThreads * i, r = idx / OCH, c = idx % OCH;
-    if (r >= valid) continue;
-    const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
-    uint16_t* dst = GU ? reinterpret_cast<uint16_t*>(out) + (size_t)(r0 + r) * I + n0 + 8 * c
-                       : reinterpret_cast<uint16_t*>(out) + (size_t)orow[r] * H + n0 + 8 * c;
-    *reinterpret_cast<uint4*>(dst) = val;
+    for (int rho = 0; rho < 2; ++rho) {
+      if (rho) __syncthreads();  // the first round's reads are done
+      if (!idle && (wn >> 1) == rho) {
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * eq + (v & 3);
+            const int e = herow[row];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+              put_f32(lds, row, S::brow(wn, nb) - 128 * rho + el32,
+                      __builtin_ldexpf(acc[m][nb][v] * unit[nb], e));
+          }
+      }
+      __syncthreads();
+      const int c0 = n0 + 128 * rho;
+      store_f16_rows<S::RA>(
+          lds, valid, wave, [&](int r) { return y + (size_t)orow[r] * H + c0; },
+          [&](int r) { return io.oexps + (size_t)orow[r] * (H / kBK) + c0 / kBK; });
+    }
   }
 }
 
@@ -518,7 +598,7 @@ void mfma_pass(const uint16_t* __restrict__ act,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ rtok,
                                                         const int32_t* __restrict__ pair, int E,
-                                                        void* __restrict__ out) {
+                                                        PassIO io) {
   using P = PassShape<GU, H, I>;
   static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
@@ -526,6 +606,9 @@ void mfma_pass(const uint16_t* __restrict__ act,
   __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
   constexpr int NKB = P::K / kBK;  // scale blocks along K
   __shared__ float ss[2 * NKB];    // the tile's two scale rows
+  // down: the tile's h rows' rescale words per block, and their common exponents
+  __shared__ uint32_t hfac[GU ? 1 : kMfmaBM * NKB];
+  __shared__ int herow[GU ? 1 : kMfmaBM];
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
   // (each with its own L2), so workgroup L runs on XCD L % 8. XCD x takes row
   // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
@@ -569,10 +652,26 @@ void mfma_pass(const uint16_t* __restrict__ act,
     ss[i * NKB + kb] = Sc[(size_t)(wrow / kBK) * NKB + kb];
   }
   __syncthreads();
+  if (!GU && tid < kMfmaBM) {
+    // each h row's common power of two: the largest of its block exponents;
+    // its blocks are brought to it by rescale words (exact unless a block
+    // lies more than 2^14 below the row's largest block)
+    const uint8_t* eb = io.hexps + (size_t)arow[tid] * NKB;
+    int b[NKB], emax = 0;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      b[kb] = eb[kb];
+      emax = max(emax, b[kb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) hfac[tid * NKB + kb] = rescale_word(b[kb] - emax);
+    herow[tid] = emax - kF16ExpBias;
+  }
+  if (!GU) __syncthreads();
   if (valid <= 64)
-    pass_tile<GU, H, I, true>(act, W, ss, arow, orow, valid, r0, n0, lds, out);
+    pass_tile<GU, H, I, true>(act, W, ss, arow, orow, hfac, herow, valid, r0, n0, lds, io);
   else
-    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, valid, r0, n0, lds, out);
+    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, hfac, herow, valid, r0, n0, lds, io);
 }
 
 // ---------------------------------------------------------------------------
@@ -637,6 +736,7 @@ struct F8Out {
   uint8_t* hcodes;
   uint8_t* hexps;
   uint16_t* y;
+  uint8_t* yexps;
 };
 
 template <bool GU, int H, int I, bool THIN>
@@ -854,38 +954,27 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
       if (k == 0) out.hexps[(size_t)(r0 + r) * (I / kBK) + n0 / kBK] = (uint8_t)(e + 127);
     }
   } else {
-    // y (fp16) through LDS as in the bf16 down pass, stored by slot
-    constexpr int ORB = 256 * 2, OCH = ORB / 16;
-    static_assert(S::RA * ORB <= kLdsBytes, "output tile exceeds the LDS block");
-    auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
-    const bool odd = l32 & 1;
-    if (!idle) {
+    // y as scaled fp16 by slot, through LDS as in the bf16 down pass
+    static_assert(S::RA * 512 <= kLdsBytes, "output tile exceeds the LDS block");
 #pragma unroll
-      for (int m = 0; m < MW; ++m)
+    for (int rho = 0; rho < 2; ++rho) {
+      if (rho) __syncthreads();  // the first round's reads are done
+      if (!idle && (wn >> 1) == rho) {
 #pragma unroll
-        for (int v = 0; v < 16; v += 2)
+        for (int m = 0; m < MW; ++m)
 #pragma unroll
-          for (int nb = 0; nb < NBW; ++nb) {
-            const uint32_t a = f32_to_f16_sat(acc[m][nb][v] * unit[nb]);
-            const uint32_t b = f32_to_f16_sat(acc[m][nb][v + 1] * unit[nb]);
-            const uint32_t send = odd ? a : b;
-            const uint32_t recv =
-                (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
-            const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3) + (odd ? 1 : 0);
-            const int col = S::brow(wn, nb) + l32 - (odd ? 1 : 0);
-            const uint32_t word = odd ? (recv | (b << 16)) : (a | (recv << 16));
-            *reinterpret_cast<uint32_t*>(lds + row * ORB + 16 * (((2 * col) >> 4) ^ oswz(row)) +
-                                         ((2 * col) & 15)) = word;
+          for (int v = 0; v < 16; ++v) {
+            const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+              put_f32(lds, row, S::brow(wn, nb) - 128 * rho + l32, acc[m][nb][v] * unit[nb]);
           }
-    }
-    __syncthreads();
-    static_assert((S::RA * OCH) % kPassThreads == 0, "output chunks per thread");
-#pragma unroll
-    for (int i = 0; i < S::RA * OCH / kPassThreads; ++i) {
-      const int idx = tid + kPassThreads * i, r = idx / OCH, c = idx % OCH;
-      if (r >= valid) continue;
-      const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
-      *reinterpret_cast<uint4*>(out.y + (size_t)orow[r] * H + n0 + 8 * c) = val;
+      }
+      __syncthreads();
+      const int c0 = n0 + 128 * rho;
+      store_f16_rows<S::RA>(
+          lds, valid, wave, [&](int r) { return out.y + (size_t)orow[r] * H + c0; },
+          [&](int r) { return out.yexps + (size_t)orow[r] * (H / kBK) + c0 / kBK; });
     }
   }
 }
@@ -959,8 +1048,8 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
   const int32_t *meta = w.meta, *tiles = w.tiles, *offsets = w.offsets, *rtok = w.rtok,
                 *pair = w.pair;
   if (d.f8) {  // both contractions on E4M3 operands; h goes between them as E4M3
-    const F8Out hout{static_cast<uint8_t*>(w.h), w.hexps, nullptr};
-    const F8Out yout{nullptr, nullptr, w.y};
+    const F8Out hout{static_cast<uint8_t*>(w.h), w.hexps, nullptr, nullptr};
+    const F8Out yout{nullptr, nullptr, static_cast<uint16_t*>(w.y), w.yexps};
     if (ev.any())
       hipExtLaunchKernelGGL(mfma_pass_f8<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin,
                             ev.end, 0, w.acodes, w.aexps, bk, meta, tiles, offsets, rtok, pair,
@@ -972,16 +1061,19 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
         static_cast<const uint8_t*>(w.h), w.hexps, bk, meta, tiles, offsets, rtok, pair, d.E,
         yout);
     return;
-  } else if (ev.any()) {  // the events take the kernel's own start and end times
+  }
+  const PassIO hio{w.h, w.hexps, nullptr};
+  const PassIO yio{w.y, w.yexps, w.hexps};
+  if (ev.any()) {  // the events take the kernel's own start and end times
     hipExtLaunchKernelGGL(mfma_pass<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin, ev.end,
-                          0, xa, bk, meta, tiles, offsets, rtok, pair, d.E, w.h);
+                          0, xa, bk, meta, tiles, offsets, rtok, pair, d.E, hio);
   } else {
     mfma_pass<true, H, I><<<grid, kPassThreads, 0, s>>>(xa, bk, meta, tiles, offsets, rtok, pair,
-                                                        d.E, w.h);
+                                                        d.E, hio);
   }
   mfma_pass<false, H, I><<<nt8 * (H / PassShape<false, H, I>::COLS), kPassThreads, 0, s>>>(
       reinterpret_cast<const uint16_t*>(w.h), bk, w.meta, w.tiles, w.offsets, w.rtok, w.pair, d.E,
-      w.y);
+      yio);
 }
 
 #define MOE_MFMA_SHAPES(X) \

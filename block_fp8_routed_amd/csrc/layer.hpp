@@ -87,12 +87,16 @@ struct Work {
   int32_t* pair;     // [P] row -> slot
   int32_t* inv;      // [P] slot -> row
   int32_t* tiles;    // [max_tiles][2] (group, first row) of each MFMA row tile
-  void* h;           // [P][I] fp16 SwiGLU output (FP8 variant: E4M3 codes)
-  uint16_t* y;       // [P][H] fp16 expert outputs by slot (saturated at +-65504)
+  void* h;           // [P][I] SwiGLU output in permuted row order: fp32 (GEMV
+                     // family), fp16 scaled per 128 columns by hexps (bf16 MFMA),
+                     // E4M3 codes scaled by hexps (FP8 variant)
+  void* y;           // [P][H] expert outputs by slot: fp32 (GEMV family), fp16
+                     // scaled per 128 columns by yexps (grouped families)
   int32_t* pblock;   // [2][16][E] per-block expert counts, then per-block bases
   uint8_t* acodes;   // [T][H] E4M3 activations (FP8 variant only, else empty)
   uint8_t* aexps;    // [T][H/128] their E8M0 exponents (FP8 variant only)
-  uint8_t* hexps;    // [P][I/128] E8M0 exponents of h (FP8 only; the codes live in h)
+  uint8_t* hexps;    // [P][I/128] exponent bytes of h (grouped families)
+  uint8_t* yexps;    // [P][H/128] exponent bytes of y (grouped families)
 };
 
 inline int64_t max_mfma_tiles(const Dims& d) {

@@ -14,7 +14,7 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 16;
+constexpr int kRegions = 17;
 
 static void region_sizes(const Dims& d, size_t* sz) {
   sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
@@ -27,12 +27,15 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[7] = (size_t)d.P * 4;                // pair
   sz[8] = (size_t)d.P * 4;                // inv
   sz[9] = (size_t)max_mfma_tiles(d) * 8;  // tiles
-  sz[10] = (size_t)d.P * d.I * 2;         // h (fp16)
-  sz[11] = (size_t)d.P * d.H * 2;         // y (fp16)
+  // h and y: fp32 on the decode (GEMV) family; fp16 (h of the FP8 variant:
+  // E4M3 bytes) with exponent bytes per 128 columns on the grouped families
+  sz[10] = (size_t)d.P * d.I * (d.mfma ? (d.f8 ? 1 : 2) : 4);  // h
+  sz[11] = (size_t)d.P * d.H * (d.mfma ? 2 : 4);               // y
   sz[12] = (size_t)2 * kPermMaxBlocksHost * d.E * 4;  // permutation block counts and bases
   sz[13] = d.f8 ? (size_t)d.T * d.H : 0;              // E4M3 activations
   sz[14] = d.f8 ? (size_t)d.T * (d.H / 128) : 0;      // their exponents
-  sz[15] = d.f8 ? (size_t)d.P * (d.I / 128) : 0;      // exponents of h
+  sz[15] = d.mfma ? (size_t)d.P * (d.I / 128) : 0;    // exponents of h
+  sz[16] = d.mfma ? (size_t)d.P * (d.H / 128) : 0;    // exponents of y
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -63,11 +66,12 @@ Work carve(const Dims& d, void* base) {
   w.inv = static_cast<int32_t*>(r[8]);
   w.tiles = static_cast<int32_t*>(r[9]);
   w.h = r[10];
-  w.y = static_cast<uint16_t*>(r[11]);
+  w.y = r[11];
   w.pblock = static_cast<int32_t*>(r[12]);
   w.acodes = static_cast<uint8_t*>(r[13]);
   w.aexps = static_cast<uint8_t*>(r[14]);
   w.hexps = static_cast<uint8_t*>(r[15]);
+  w.yexps = static_cast<uint8_t*>(r[16]);
   return w;
 }
 
@@ -236,6 +240,24 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t* offsets, int32_t* pair,
   w.inv = inv;
   if (launch_permute(d, topk_idx, w, 0, false, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_region(const moe_config* cfg, int32_t region, size_t* offset,
+                                size_t* bytes) {
+  if (!offset || !bytes) return MOE_ERR_NULL;
+  Dims d;
+  moe_status st = basic_dims(cfg, &d);
+  if (st != MOE_OK) return st;
+  // carve-order index of each exported region
+  static const int kIndex[MOE_WS_COUNT] = {1, 2, 3, 7, 8, 10, 15, 11, 16};
+  if (region < 0 || region >= MOE_WS_COUNT) return MOE_ERR_SHAPE;
+  size_t sz[kRegions], off = 0;
+  region_sizes(d, sz);
+  const int idx = kIndex[region];
+  for (int i = 0; i < idx; ++i) off += al(sz[i]);
+  *offset = off;
+  *bytes = sz[idx];
   return MOE_OK;
 }
 

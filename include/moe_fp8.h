@@ -220,6 +220,44 @@ moe_status moe_dequant_e4m3(const uint8_t* w, const float* scales, int64_t rows,
 moe_status moe_quantize_act_e4m3(const void* x, int64_t tokens, int32_t hidden, uint8_t* codes,
                                  uint8_t* exps, void* stream);
 
+/* Intermediate results of moe_forward, readable from its workspace once the
+ * call's stream work has completed (the workspace is the caller's memory).
+ * moe_workspace_region reports where one of them lies for `cfg`:
+ *   *offset  byte offset from the workspace base (a multiple of 256)
+ *   *bytes   its size in bytes (0 when the configuration does not use it)
+ * Regions (P = T·k + T·has_shared rows; "row" = a row of the permuted
+ * problem, whose order moe_permute defines; "slot" s = t·k + j, or T·k + t
+ * for the shared expert):
+ *   TOPK     int32 [T][k]   selected experts (as moe_route returns them)
+ *   GATES    fp32  [T][k]   their gates
+ *   OFFSETS  int32 [E+2]    group offsets (as moe_permute returns them)
+ *   PAIR     int32 [P]      row -> slot
+ *   INV      int32 [P]      slot -> row
+ *   H        [P][I] SwiGLU output by row: fp32 (GEMV family); fp16 scaled by
+ *            H_EXPS (MFMA family); E4M3 codes scaled by H_EXPS (MFMA_FP8)
+ *   H_EXPS   uint8 [P][I/128] exponent bytes of H (MFMA families): element
+ *            (r, c) of H is value(H[r][c]) * 2^(H_EXPS[r][c/128] - 127)
+ *   Y        [P][H] expert outputs by slot: fp32 (GEMV family), fp16
+ *            scaled by Y_EXPS (MFMA families)
+ *   Y_EXPS   uint8 [P][H/128] exponent bytes of Y (MFMA families)
+ * Returns MOE_ERR_NULL for a NULL pointer, MOE_ERR_SHAPE for an invalid cfg
+ * or region. This call touches no device memory. It is what lets tests
+ * compare each step's result with an independent evaluation. */
+typedef enum {
+  MOE_WS_TOPK = 0,
+  MOE_WS_GATES = 1,
+  MOE_WS_OFFSETS = 2,
+  MOE_WS_PAIR = 3,
+  MOE_WS_INV = 4,
+  MOE_WS_H = 5,
+  MOE_WS_H_EXPS = 6,
+  MOE_WS_Y = 7,
+  MOE_WS_Y_EXPS = 8,
+  MOE_WS_COUNT = 9
+} moe_ws_region;
+moe_status moe_workspace_region(const moe_config* cfg, int32_t region, size_t* offset,
+                                size_t* bytes);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

@@ -74,6 +74,9 @@ def test_workspace_bytes():
               has_shared=True)
     P = 4096 * 11
     assert moe.workspace_bytes(big) >= P * 4096 * 2 + P * 1024 * 2  # y and h fp16
+    small = cfg(tokens=16, hidden=4096, experts=512, inter=1024, top_k=10, block=128,
+                has_shared=True)
+    assert moe.workspace_bytes(small) >= 16 * 11 * (4096 + 1024) * 4  # y and h fp32
     assert moe.workspace_bytes(cfg(top_k=9)) == 0  # invalid config
 
 
@@ -160,10 +163,10 @@ def test_quantize_act_validation():
 
 
 def test_fp8_path_validation_and_workspace():
-    """The FP8 variant: bf16 activations only; its
-    workspace adds the activation codes (T*H bytes), their exponents (T*H/128
-    bytes) and the exponents of h (P*I/128 bytes; h's codes take the fp16 h
-    region)."""
+    """The FP8 variant: bf16 activations only; against the bf16 grouped path
+    its workspace adds the activation codes (T*H bytes) and their exponents
+    (T*H/128 bytes), and holds h as one-byte codes instead of fp16 (P*I bytes
+    fewer); both keep exponent bytes for h and y."""
     bf16 = _lib.torch.bfloat16
     shape = dict(tokens=300, hidden=2048, experts=128, inter=768, top_k=8, block=128)
     f32 = cfg(path="mfma_fp8", **shape)
@@ -173,8 +176,48 @@ def test_fp8_path_validation_and_workspace():
     extra = moe.workspace_bytes(f8) - moe.workspace_bytes(plain)
     T, H, I = shape["tokens"], shape["hidden"], shape["inter"]
     P = T * shape["top_k"] + (T if f8.has_shared else 0)
-    want = T * H + T * H // 128 + P * I // 128
-    assert want <= extra <= want + 3 * 256  # region alignment
+    want = T * H + T * H // 128 - P * I
+    assert want - 3 * 256 <= extra <= want + 3 * 256  # region alignment
     auto = cfg(path="auto", x_dtype=bf16, **shape)
     assert moe.workspace_bytes(auto) == moe.workspace_bytes(plain)  # AUTO never picks FP8
-    assert forward(f8, ws_bytes=moe.workspace_bytes(plain)) == _lib.MOE_ERR_WORKSPACE
+    assert forward(f8, ws_bytes=moe.workspace_bytes(f8) - 256) == _lib.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("path,tokens", [("gemv", 16), ("auto", 8), ("mfma", 300),
+                                         ("mfma_fp8", 300)])
+def test_workspace_regions(path, tokens):
+    """moe_workspace_region: every exported region is 256-byte aligned, lies
+    inside moe_workspace_bytes and overlaps no other, and has the size its
+    declaration gives for the path's kernel family (h and y in fp32 on the
+    GEMV family; fp16 or E4M3 bytes plus exponent bytes per 128 columns on
+    the grouped families)."""
+    bf16 = _lib.torch.bfloat16
+    T, H, E, I, k = tokens, 4096, 512, 1024, 10
+    c = cfg(tokens=T, hidden=H, experts=E, inter=I, top_k=k, block=128, has_shared=True,
+            x_dtype=bf16, path=path)
+    total = moe.workspace_bytes(c)
+    P = T * (k + 1)
+    grouped = path in ("mfma", "mfma_fp8")
+    h_elem = (1 if path == "mfma_fp8" else 2) if grouped else 4
+    want = {moe.MOE_WS_TOPK: T * k * 4, moe.MOE_WS_GATES: T * k * 4,
+            moe.MOE_WS_OFFSETS: (E + 2) * 4, moe.MOE_WS_PAIR: P * 4, moe.MOE_WS_INV: P * 4,
+            moe.MOE_WS_H: P * I * h_elem, moe.MOE_WS_H_EXPS: P * I // 128 if grouped else 0,
+            moe.MOE_WS_Y: P * H * (2 if grouped else 4),
+            moe.MOE_WS_Y_EXPS: P * H // 128 if grouped else 0}
+    spans = []
+    for region, n in want.items():
+        off, got = moe.workspace_region(c, region)
+        assert got == n, (region, got, n)
+        assert off % 256 == 0 and off + got <= total
+        spans.append((off, off + got))
+    spans.sort()
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0, "regions overlap"
+    lib = moe.load()
+    o, n = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_workspace_region(ctypes.byref(c), 9,
+                                    ctypes.byref(o), ctypes.byref(n)) == _lib.MOE_ERR_SHAPE
+    assert lib.moe_workspace_region(ctypes.byref(c), -1, ctypes.byref(o),
+                                    ctypes.byref(n)) == _lib.MOE_ERR_SHAPE
+    assert lib.moe_workspace_region(ctypes.byref(c), 0, None, ctypes.byref(n)) == _lib.MOE_ERR_NULL
+    assert lib.moe_workspace_region(None, 0, ctypes.byref(o), ctypes.byref(n)) == _lib.MOE_ERR_NULL

@@ -326,11 +326,11 @@ def test_expert_relabelling_invariance():
     assert torch.equal(out, out2)
 
 
-def test_prefill_e512_full_size_sampled():
+def test_prefill_e512_full_size():
     """The 512-expert prefill workload at full size (4096 tokens, 16 hot
     experts) in the launch configuration the benchmark uses: routing of every
-    token and the whole permutation against the oracle; outputs on a sample of
-    tokens (hot-expert, cold-expert and shared rows) computed one by one."""
+    token and the whole permutation against the oracle, and every one of the
+    4096 x 4096 outputs against the oracle."""
     import block_fp8_routed_amd as moe
     shape = C["c4"]
     layer = DevLayer(shape)
@@ -346,13 +346,26 @@ def test_prefill_e512_full_size_sampled():
     out = layer.forward()
     torch.cuda.synchronize()
     counts = np.bincount(accepted.reshape(-1), minlength=shape.experts)
-    hot = set(np.argsort(-counts)[:16].tolist())
-    rng = np.random.default_rng(11)
-    sample = sorted(set(rng.choice(shape.tokens, 24, replace=False).tolist()) | {0, 4095})
-    n_hot = sum(1 for t in sample if hot & set(accepted[t].tolist()))
-    log(f"c4: oracle on {len(sample)} sampled tokens ({n_hot} touch a hot expert), ties={ties}")
-    ref = layer.oracle(routing=accepted, tokens=np.array(sample))
-    check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 sampled")
+    log(f"c4: oracle on all {shape.tokens} tokens ({int((counts > 0).sum())} routed experts "
+        f"+ shared), ties={ties}")
+    ref = layer.oracle(routing=accepted)
+    check_output(out, ref["out"], what="c4 T=4096 full")
+
+
+def tile_boundary_tokens(accepted, experts, shared, tile_rows=128):
+    """Tokens holding the first and the last row of every row tile of every
+    group of the permutation (the grouped passes' tiles): comparing their
+    outputs touches every tile, including each group's partial last tile."""
+    T, k = accepted.shape
+    off, pair, _ = oracle.permutation(accepted, experts, shared)
+    toks = set()
+    for g in range(experts + (1 if shared else 0)):
+        lo, hi = int(off[g]), int(off[g + 1])
+        for r0 in range(lo, hi, tile_rows):
+            for row in (r0, min(r0 + tile_rows, hi) - 1):
+                slot = int(pair[row])
+                toks.add(slot // k if slot < T * k else slot - T * k)
+    return np.array(sorted(toks))
 
 
 FP8_CASES = [  # (config, tokens, overrides): the FP8 variant (E4M3 x and h)
@@ -417,25 +430,119 @@ def test_forward_scaled_and_zero_rows(path):
                  flip=ref["flip"][rest] if f8 else None)
 
 
-def test_prefill_e512_fp8_full_size_sampled():
+def test_prefill_e512_fp8_full_size_tiles():
     """The FP8 variant on the 512-expert prefill workload at full size (4096
-    tokens), outputs on sampled tokens against the oracle."""
+    tokens): outputs of the tokens that hold the first and the last row of
+    every row tile of every group (so every tile of both passes is compared)
+    against the oracle."""
     shape = C["c4"]
     layer = DevLayer(shape)
     idx, gates = layer.route()
     accepted, ties = check_routing(layer, idx, gates)
     out = layer.forward(path="mfma_fp8")
     torch.cuda.synchronize()
-    counts = np.bincount(accepted.reshape(-1), minlength=shape.experts)
-    hot = set(np.argsort(-counts)[:16].tolist())
-    rng = np.random.default_rng(13)
-    sample = sorted(set(rng.choice(shape.tokens, 16, replace=False).tolist()) | {0, 4095})
-    n_hot = sum(1 for t in sample if hot & set(accepted[t].tolist()))
-    log(f"c4 fp8: oracle on {len(sample)} sampled tokens ({n_hot} touch a hot expert)")
-    ref = layer.oracle(routing=accepted, tokens=np.array(sample), act_block=128,
+    sample = tile_boundary_tokens(accepted, shape.experts, True)
+    log(f"c4 fp8: oracle on {len(sample)} tokens covering every row tile")
+    ref = layer.oracle(routing=accepted, tokens=sample, act_block=128,
                        h_band=fp8_h_band(shape.hidden))
-    check_output(out, ref["out"], tokens=np.array(sample), what="c4 T=4096 mfma_fp8 sampled",
+    check_output(out, ref["out"], tokens=sample, what="c4 T=4096 mfma_fp8 tile rows",
                  flip=ref["flip"])
+
+
+RANGE_CASES = [("gemv", 16), ("mfma", 48), ("mfma_fp8", 48)]
+
+
+@pytest.mark.parametrize("scale", ["large", "tiny", "mixed"])
+@pytest.mark.parametrize("path,T", RANGE_CASES, ids=[f"{p}-T{t}" for p, t in RANGE_CASES])
+def test_forward_far_outside_fp16_range(path, T, scale):
+    """h and y are stored below fp32 between the passes; their power-of-two
+    exponents must keep any magnitude. Activations scaled by 2^9 drive h and y
+    far past fp16's largest value (65504), by 2^-14 far below its smallest
+    normal (6.1e-5), and a mixed batch puts rows of both kinds (and 2^0) in the
+    same expert groups; outputs against the oracle at the layer tolerance,
+    whose per-token cosine sees each row at its own scale. The router weights
+    take the inverse power of two (of the largest scale), so that the logits
+    stay in the range whose absolute tolerances the routing check states:
+    with a uniform scale they are exactly those of the unscaled rows."""
+    shape = C["c1"]
+    x = W.gen_x(shape, T, 7).astype(np.float64)
+    if scale == "large":
+        x *= 2.0 ** 9
+        r = 2.0 ** -9
+    elif scale == "tiny":
+        x *= 2.0 ** -14
+        r = 2.0 ** 14
+    else:
+        x *= (2.0 ** np.array([9, -14, 0])[np.arange(T) % 3])[:, None]
+        r = 2.0 ** -9
+    layer = DevLayer(shape, x=x.astype(np.float32))
+    layer.router_host = (layer.router_host * np.float32(r)).astype(np.float32)
+    layer.router_w = torch.from_numpy(layer.router_host).cuda()
+    idx, gates = layer.route()
+    accepted, ties = check_routing(layer, idx, gates)
+    out = layer.forward(path=path)
+    torch.cuda.synchronize()
+    f8 = path == "mfma_fp8"
+    ref = layer.oracle(routing=accepted, act_block=128 if f8 else None,
+                       h_band=fp8_h_band(shape.hidden) if f8 else None)
+    if scale == "large":
+        log(f"max |h| drives: output rms {np.sqrt(np.mean(ref['out'] ** 2)):.3e}")
+    check_output(out, ref["out"], what=f"{path} T={T} {scale} rows ties={ties}",
+                 flip=ref["flip"] if f8 else None)
+
+
+DECODE_PERM_CASES = [  # (config, tokens, overrides): the fused decode selection + permutation
+    ("c1", 1, {}), ("c1", 4, {}), ("c1", 16, {}), ("c3", None, {}), ("c3", 3, {}),
+    ("c0", 16, {"experts": 512, "top_k": 16}), ("c0", 9, {"experts": 100, "top_k": 3,
+                                                          "shared": True}),
+]
+
+
+@pytest.mark.parametrize("name,T,ov", DECODE_PERM_CASES,
+                         ids=[fwd_id((n, t, "auto", o)) for n, t, o in DECODE_PERM_CASES])
+def test_decode_permutation_in_the_workspace(name, T, ov):
+    """At decode sizes one kernel selects every token's experts and builds the
+    permutation; after moe_forward its results are read from the workspace
+    (moe_workspace_region) and compared bit-exactly with the oracle's
+    selection and permutation, and the fp32 SwiGLU output h of every
+    permuted row with the oracle's h of that (token, expert) pair."""
+    import block_fp8_routed_amd as moe
+    shape = C[name].with_(**ov) if ov else C[name]
+    layer = DevLayer(shape, tokens=T)
+    s = layer.shape
+    T = layer.T
+    cfg = moe.make_config(T, s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
+                          layer.x.dtype, torch.float32, "auto")
+    ws = moe.make_workspace(cfg, "cuda")
+    layer.forward(workspace=ws, cfg=cfg)
+    torch.cuda.synchronize()
+
+    def view(region, dtype):
+        return moe.workspace_view(ws, cfg, region, dtype).cpu().numpy()
+    topk = view(moe.MOE_WS_TOPK, torch.int32).reshape(T, s.top_k)
+    gates = torch.from_numpy(view(moe.MOE_WS_GATES, torch.float32).reshape(T, s.top_k))
+    accepted, ties = check_routing(layer, torch.from_numpy(topk), gates)
+    r_off, r_pair, r_inv = oracle.permutation(accepted, s.experts, s.shared)
+    assert np.array_equal(view(moe.MOE_WS_OFFSETS, torch.int32), r_off)
+    assert np.array_equal(view(moe.MOE_WS_PAIR, torch.int32), r_pair)
+    assert np.array_equal(view(moe.MOE_WS_INV, torch.int32), r_inv)
+    # S4 alone: h of each permuted row (fp32 on this family)
+    h = view(moe.MOE_WS_H, torch.float32).reshape(len(r_pair), s.inter).astype(np.float64)
+    x = layer.x_host.astype(np.float64)
+    worst = 0.0
+    for row, slot in enumerate(r_pair):
+        if slot < T * s.top_k:
+            t, e = slot // s.top_k, int(accepted[slot // s.top_k, slot % s.top_k])
+            wg, wu, _ = oracle.expert_matrices(layer.expert(e), s.inter, s.block)
+        else:
+            t = slot - T * s.top_k
+            wg, wu, _ = oracle.expert_matrices(W.bank_expert(layer.shared_host, 0), s.inter,
+                                               s.block)
+        ref_h = oracle.silu(x[t] @ wg.T) * (x[t] @ wu.T)
+        scale = np.abs(ref_h).max()
+        worst = max(worst, float(np.abs(h[row] - ref_h).max() / scale))
+    log(f"decode {name} T={T}: permutation bit-exact, h max rel err {worst:.2e}, ties={ties}")
+    assert worst <= 1e-4, f"h error {worst:.2e} of the row's largest value"
 
 
 WS_CASES = [("c1", 16, "auto"), ("c1", 4, "auto"), ("c0", 4, "auto"), ("c1", 16, "mfma"),
