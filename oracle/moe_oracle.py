@@ -55,7 +55,10 @@ silent (each restated at the function that uses it):
      result: h_admissible_deviation bounds how far the dequantised h can
      move over every such choice, and moe_layer (given h_band) turns that
      into a per-element bound on the output (the analogue of R9's tie band
-     for selections).
+     for selections). Given a kernel's own codes for h, h_admissible_codes
+     decides element by element whether they are such a correct result, and
+     moe_layer (given h_codes) evaluates the down contraction on them, as
+     R9 re-runs the layer on an accepted selection.
 Every function here is pinned by tests/test_oracle_pins.py; no function is
 parity-unpinned.
 """
@@ -315,11 +318,38 @@ def h_admissible_deviation(h: np.ndarray, tau: np.ndarray, block: int) -> np.nda
     return dev.reshape(n, I)
 
 
+def h_admissible_codes(h: np.ndarray, tau: np.ndarray, codes: np.ndarray, exps: np.ndarray,
+                       block: int) -> np.ndarray:
+    """For h [n][I], a per-element band tau [n][I] and a candidate
+    quantisation of h (E4M3 codes [n][I], block exponents [n][I/block]):
+    True where element (r, c) is one that an evaluation of h landing within
+    tau of it produces under R10 (R11). The block's exponent must lie between
+    those of the smallest and the largest block maximum the band allows
+    (the exponent rule is monotone in the maximum), and under that exponent
+    the element's value must lie between the values h - tau and h + tau
+    round to (rounding is monotone, so every value between is reached).
+    Values are compared, so +0 and -0 are the same result."""
+    n, I = h.shape
+    hb = np.asarray(h, np.float64).reshape(n, I // block, block)
+    tb = np.asarray(tau, np.float64).reshape(n, I // block, block)
+    ex = np.asarray(exps, np.int64).reshape(n, I // block)
+    e_lo = act_scale_exponent(np.maximum(np.abs(hb) - tb, 0.0).max(axis=2))
+    e_hi = act_scale_exponent((np.abs(hb) + tb).max(axis=2))
+    ok_e = (ex >= np.minimum(e_lo, e_hi)) & (ex <= np.maximum(e_lo, e_hi))
+    down = np.ldexp(1.0, -ex)[:, :, None]
+    lo = e4m3fn_decode(e4m3fn_round(np.clip((hb - tb) * down, -448.0, 448.0)))
+    hi = e4m3fn_decode(e4m3fn_round(np.clip((hb + tb) * down, -448.0, 448.0)))
+    v = e4m3fn_decode(np.asarray(codes, np.uint8)).reshape(hb.shape)
+    with np.errstate(invalid="ignore"):  # a NaN code compares false: not admissible
+        ok = ok_e[:, :, None] & (v >= lo) & (v <= hi)
+    return ok.reshape(n, I)
+
+
 def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndarray],
               expert: Callable[[int], dict], top_k: int, inter: int, block: int,
               shared: Optional[dict] = None, routing: Optional[np.ndarray] = None,
               tokens: Optional[np.ndarray] = None, act_block: Optional[int] = None,
-              h_band: Optional[tuple] = None):
+              h_band: Optional[tuple] = None, h_codes: Optional[Callable] = None):
     """The whole layer in fp64.
 
     expert(e) returns expert e's block-FP8 dict (w_gate_up, s_gate_up, w_down,
@@ -333,7 +363,15 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndar
     With h_band = (acc_rel, eval_rel) as well, the result also holds
     "flip" [T'][H]: the bound on how far the admissible quantisations of h
     (R11) can move each output element, summed over the token's experts with
-    their gates.
+    their gates. With h_codes as well (a kernel's quantisation of h:
+    h_codes(e, tokens, slots) returns (codes [n][I], block exponents) for
+    expert e's rows of those tokens and slots j, and h_codes(None, tokens,
+    None) for the shared expert's), the down contraction reads those codes
+    instead of the oracle's own, "h_check" counts the elements whose codes
+    are not admissible under R11 (h_admissible_codes, with the band h_band
+    gives) and those whose value differs from the oracle's own, and no flip
+    bound is formed: the output is the layer evaluated on the kernel's
+    accepted codes, as R9 evaluates it on an accepted selection.
 
     Returns dict(out [T'][H], logits [T][E], topk_idx [T][k], gates [T][k],
     ties [T]) where T' = len(tokens) or T.
@@ -347,29 +385,51 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, router_bias: Optional[np.ndar
     rows = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
     out = np.zeros((len(rows), x.shape[1]), np.float64)
     band = h_band if act_block is not None else None
-    flip = np.zeros_like(out) if band is not None else None
+    given = h_codes is not None and band is not None
+    flip = np.zeros_like(out) if band is not None and not given else None
+    check = {"inadmissible": 0, "flips": 0, "elements": 0}
+
+    def expert_out(xs, wg, wu, wd, codes):
+        if not given:
+            return swiglu_expert(xs, wg, wu, wd, h_block=act_block, h_band=band)
+        # R11: the kernel's codes, once each is admissible, feed the down contraction
+        a, u = xs @ wg.T, xs @ wu.T
+        h32 = (silu(a) * u).astype(np.float32).astype(np.float64)
+        c, ex = codes
+        ok = h_admissible_codes(h32, h_band_width(xs, wg, wu, *band), c, ex, act_block)
+        hq = dequantise_activations(c, ex, act_block)
+        own = dequantise_activations(*quantise_activations(h32, act_block), act_block)
+        check["inadmissible"] += int((~ok).sum())
+        check["flips"] += int(np.count_nonzero(hq != own))
+        check["elements"] += hq.size
+        return hq @ wd.T
+
     sub_idx = idx[rows]
     for e in np.unique(sub_idx):
         wg, wu, wd = expert_matrices(expert(int(e)), inter, block)
         who, slot = np.nonzero(sub_idx == e)
-        y = swiglu_expert(xe[rows[who]], wg, wu, wd, h_block=act_block, h_band=band)
-        if band is not None:
+        codes = h_codes(int(e), rows[who], slot) if given else None
+        y = expert_out(xe[rows[who]], wg, wu, wd, codes)
+        if flip is not None:
             y, bound = y
         # each (token, slot) pair appears once; in fp64 the order of the k
         # terms of a token is immaterial at the tolerances this oracle serves
         for r, (i, j) in enumerate(zip(who, slot)):
             out[i] += gates[rows[i], j] * y[r]
-            if band is not None:
+            if flip is not None:
                 flip[i] += gates[rows[i], j] * bound[r]
     if shared is not None:
         wg, wu, wd = expert_matrices(shared, inter, block)
-        y = swiglu_expert(xe[rows], wg, wu, wd, h_block=act_block, h_band=band)
-        if band is not None:
+        codes = h_codes(None, rows, None) if given else None
+        y = expert_out(xe[rows], wg, wu, wd, codes)
+        if flip is not None:
             y, bound = y
             flip += bound
         out += y
     res = {"out": out, "logits": logits, "topk_idx": idx, "gates": gates,
            "ties": tie_flags(logits, top_k)}
-    if band is not None:
+    if flip is not None:
         res["flip"] = flip
+    if given:
+        res["h_check"] = check
     return res

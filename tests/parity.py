@@ -15,9 +15,12 @@ Tolerances this project derives itself (the pages state none for them):
     the error well inside the 1e-5 tie band.
   * gates: |gpu - ref| <= 5e-6 (a logit error d moves a gate by about 2 d g).
   * bf16 output: the fp32 tolerance plus the output rounding, 2^-8 |ref|.
-  * FP8 variant (E4M3 h in the down contraction): the output tolerance plus
-    the oracle's bound on what the admissible quantisations of h can move
-    (reading R11), from the band fp8_h_band derives.
+  * FP8 variant (E4M3 h in the down contraction): every E4M3 code and block
+    exponent of h the kernel wrote (read from its workspace) must be one of
+    the admissible quantisations of h under reading R11 (within the band
+    fp8_h_band derives); the outputs are then held to the layer tolerance
+    against the oracle evaluated on the kernel's accepted codes, as tie-
+    flagged selections are.
 """
 from __future__ import annotations
 
@@ -94,12 +97,46 @@ class DevLayer:
     def expert(self, e):
         return W.bank_expert(self.bank_host, e)
 
-    def oracle(self, routing=None, tokens=None, act_block=None, h_band=None):
+    def oracle(self, routing=None, tokens=None, act_block=None, h_band=None, h_codes=None):
         sh = W.bank_expert(self.shared_host, 0) if self.shape.shared else None
         return oracle.moe_layer(self.x_host, self.router_host, self.bias_host, self.expert,
                                 self.shape.top_k, self.shape.inter, self.shape.block, shared=sh,
                                 routing=routing, tokens=tokens, act_block=act_block,
-                                h_band=h_band)
+                                h_band=h_band, h_codes=h_codes)
+
+    def forward_fp8_checked(self, tokens=None, what=""):
+        """The FP8 variant through moe_forward, then the check of its h codes
+        and of its outputs against the oracle on those codes (see the module
+        docstring). Returns (max error / RMS, min cosine, h_check)."""
+        moe = self.moe
+        s = self.shape
+        idx, gates = self.route()
+        accepted, ties = check_routing(self, idx, gates)
+        cfg = moe.make_config(self.T, s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
+                              self.x.dtype, torch.float32, "mfma_fp8")
+        ws = moe.make_workspace(cfg, self.x.device)
+        out = self.forward(path="mfma_fp8", workspace=ws, cfg=cfg)
+        torch.cuda.synchronize()
+        P = self.T * (s.top_k + int(s.shared))
+        codes = moe.workspace_view(ws, cfg, moe.MOE_WS_H).cpu().numpy()[:P * s.inter]
+        codes = codes.reshape(P, s.inter)
+        exps = moe.workspace_view(ws, cfg, moe.MOE_WS_H_EXPS).cpu().numpy()[:P * (s.inter // 128)]
+        exps = exps.reshape(P, s.inter // 128).astype(np.int64) - 127
+        inv = moe.workspace_view(ws, cfg, moe.MOE_WS_INV, torch.int32).cpu().numpy()[:P]
+        k, T = s.top_k, self.T
+
+        def h_codes(e, toks, js):
+            slots = T * k + toks if e is None else toks * k + js
+            rows = inv[slots]
+            return codes[rows], exps[rows]
+
+        ref = self.oracle(routing=accepted, tokens=tokens, act_block=128,
+                          h_band=fp8_h_band(s.hidden), h_codes=h_codes)
+        chk = ref["h_check"]
+        log(f"{what}: h codes: {chk['inadmissible']} inadmissible, {chk['flips']} admissible "
+            f"flips of {chk['elements']} ({chk['flips'] / max(chk['elements'], 1):.2e})")
+        assert chk["inadmissible"] == 0, f"{what}: {chk['inadmissible']} inadmissible h codes"
+        return (*check_output(out, ref["out"], tokens=tokens, what=f"{what} ties={ties}"), chk)
 
 
 def fp8_h_band(hidden):

@@ -429,6 +429,110 @@ def pin_h_deviation_bruteforce(O):
     assert (seen > 0).sum() >= 0.5 * (dev > 0).sum() and (dev > 0).any()
 
 
+def pin_h_admissible_codes_closed_form(O):
+    """Hand-worked cases of the admissible codes, block [448, 1.0625, 1.03,
+    0.0052] with a band of 1e-9 (as the deviation pin): the exponent may be 0
+    or 1, not 2. Under exponent 0: 448 only as 448, 1.0625 (a midpoint) as
+    1.0 or 1.125 but not 1.25, 1.03 only as 1.0, 0.0052 only as 3 * 2^-9.
+    Under exponent 1 (values halved): 224, 0.5 or 0.5625 (0.53125 is a
+    midpoint), 0.5, 1 * 2^-9. A block of maximum 300 takes exponent 0 only.
+    With no band only the oracle's own codes pass (the tie goes to 1.0)."""
+    h = np.array([[448.0, 1.0625, 1.03, 0.0052, 300.0, 1.0625, 1.03, 0.0052]])
+    tau = np.full(h.shape, 1e-9)
+
+    def ok(vals, e0, e1, t=tau):
+        codes = lib_round(np.array([vals], np.float64))
+        return O.h_admissible_codes(h, t, codes, np.array([[e0, e1]]), 4)[0].tolist()
+
+    assert ok([448, 1.0, 1.0, 3 * 2.0 ** -9, 300, 1.0, 1.0, 3 * 2.0 ** -9], 0, 0) == [True] * 8
+    assert ok([448, 1.125, 1.125, 2 * 2.0 ** -9, 320, 1.125, 1.125, 2 * 2.0 ** -9], 0, 0) == \
+        [True, True, False, False, False, True, False, False]
+    assert ok([416, 1.25, 0.875, 4 * 2.0 ** -9, 300, 1.25, 0.875, 3 * 2.0 ** -9], 0, 0) == \
+        [False, False, False, False, True, False, False, True]
+    assert ok([224, 0.5, 0.5, 2.0 ** -9, 300, 1.0, 1.0, 3 * 2.0 ** -9], 1, 0) == [True] * 8
+    assert ok([224, 0.5625, 0.5625, 2 * 2.0 ** -9, 150, 0.5, 0.5, 2.0 ** -9], 1, 1) == \
+        [True, True, False, False, False, False, False, False]
+    # exponent 2 is outside the band: not even values that round alike pass
+    assert ok([112, 0.25, 0.25, 2.0 ** -9, 300, 1.0, 1.0, 3 * 2.0 ** -9], 2, 0) == \
+        [False] * 4 + [True] * 4
+    zero = np.zeros(h.shape)
+    assert ok([448, 1.0, 1.0, 3 * 2.0 ** -9, 300, 1.0, 1.0, 3 * 2.0 ** -9], 0, 0, zero) == [True] * 8
+    assert ok([448, 1.125, 1.0, 3 * 2.0 ** -9, 300, 1.125, 1.0, 3 * 2.0 ** -9], 0, 0, zero) == \
+        [True, False, True, True, True, False, True, True]
+    assert ok([224, 0.5, 0.5, 2.0 ** -9, 300, 1.0, 1.0, 3 * 2.0 ** -9], 1, 0, zero)[:4] == [False] * 4
+    # the sign is part of the value; -0 and +0 are one value
+    neg = -h
+    codes = lib_round(-np.array([[448, 1.0, 1.0, 3 * 2.0 ** -9, 300, 1.125, 1.0, 3 * 2.0 ** -9]]))
+    assert O.h_admissible_codes(neg, tau, codes, np.array([[0, 0]]), 4).all()
+    assert not O.h_admissible_codes(neg, tau, lib_round(np.abs(lib_decode(codes))),
+                                    np.array([[0, 0]]), 4).any()
+    tiny = np.array([[448.0, 2.0 ** -11, -2.0 ** -11, 0.0]])
+    z = lib_round(np.array([[448.0, 0.0, -0.0, -0.0]]))
+    assert O.h_admissible_codes(tiny, np.zeros(tiny.shape), z, np.array([[0]]), 4).all()
+
+
+def pin_h_admissible_codes_bruteforce(O):
+    """Against brute force: the codes and exponents reached by quantising
+    (the library's cast, the exponent by counting up from each block's own
+    maximum) points of the band, its corners and a dense sweep of each
+    element at every exponent the band allows, are admissible; and at a
+    fixed exponent every admissible value of an element is reached by the
+    sweep (so the check is exact, not merely permissive). h sits on code
+    midpoints and block maxima on exponent boundaries."""
+    rng = np.random.default_rng(24)
+    B, n, I = 4, 5, 8
+    mags = lib_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (mags[:-1] + mags[1:]) / 2
+    e = rng.integers(-3, 3, (n, I // B))
+    h = rng.choice(mids[8:], (n, I)) * np.repeat(np.ldexp(1.0, e), B, axis=1)
+    h[:, ::B] = np.ldexp(448.0, e)
+    h *= rng.choice([-1.0, 1.0], h.shape)
+    tau = np.abs(h) * 10.0 ** rng.uniform(-3, -1.3, h.shape)
+
+    def quantise(hp):  # codes and exponents by counting up (independent of the oracle)
+        codes = np.empty(hp.shape, np.uint8)
+        ex = np.empty((hp.shape[0], hp.shape[1] // B), np.int64)
+        for t in range(hp.shape[0]):
+            for b in range(hp.shape[1] // B):
+                blk = hp[t, b * B:(b + 1) * B]
+                ex[t, b] = scalar_exponent(float(np.abs(blk).max()))
+                codes[t, b * B:(b + 1) * B] = lib_round(blk * 2.0 ** -ex[t, b])
+        return codes, ex
+
+    for signs in itertools.product((-1.0, 1.0), repeat=B):
+        hp = h + np.tile(np.array(signs), I // B) * tau
+        assert O.h_admissible_codes(h, tau, *quantise(hp), B).all()
+    for _ in range(100):
+        hp = h + rng.uniform(-1, 1, h.shape) * tau
+        assert O.h_admissible_codes(h, tau, *quantise(hp), B).all()
+    # per element and exponent: the swept values are exactly the admissible ones
+    sweep = np.linspace(-1.0, 1.0, 4001)
+    for t in range(n):
+        for b in range(I // B):
+            blk = np.abs(h[t, b * B:(b + 1) * B])
+            lo = scalar_exponent(float(np.maximum(blk - tau[t, b * B:(b + 1) * B], 0).max()))
+            hi = scalar_exponent(float((blk + tau[t, b * B:(b + 1) * B]).max()))
+            for ex in range(lo, hi + 1):
+                for c in range(b * B, (b + 1) * B):
+                    vals = h[t, c] + sweep * tau[t, c]
+                    vals = np.clip(vals * 2.0 ** -ex, -448, 448)
+                    reached = set(lib_decode(lib_round(vals)).tolist())
+                    cand = np.arange(256, dtype=np.uint8)
+                    cand = cand[(cand & 0x7F) != 0x7F]
+                    hh = np.repeat(h[t:t + 1, b * B:(b + 1) * B], len(cand), axis=0)
+                    tt = np.repeat(tau[t:t + 1, b * B:(b + 1) * B], len(cand), axis=0)
+                    cc = np.tile(lib_round(hh[:1] * 2.0 ** -ex), (len(cand), 1))
+                    cc[:, c - b * B] = cand
+                    okc = O.h_admissible_codes(hh, tt, cc, np.full((len(cand), 1), ex), B)
+                    adm = set(lib_decode(cand[okc[:, c - b * B]]).tolist())
+                    assert adm == reached, (t, c, ex, sorted(adm), sorted(reached))
+            # exponents outside the band's range are refused
+            cc = lib_round(h[t:t + 1, b * B:(b + 1) * B] * 2.0 ** -(hi + 1))
+            assert not O.h_admissible_codes(h[t:t + 1, b * B:(b + 1) * B],
+                                            tau[t:t + 1, b * B:(b + 1) * B], cc,
+                                            np.array([[hi + 1]]), B).any()
+
+
 def pin_h_band_covers_fp32(O):
     """The band holds an fp32 evaluation of h: sums of 64 exact products
     rounded to fp32 and accumulated in fp32, then silu and the product in
@@ -521,13 +625,98 @@ def pin_layer_flip_bound(O):
     assert worst > 0.05  # the bound is reached in part, not vacuous
 
 
+def pin_layer_on_given_h_codes(O):
+    """With h_codes the layer's down contraction reads the given codes: a
+    torch evaluation of the layer on the same codes (routing and gates by
+    torch, x quantised by the library's cast, h codes decoded by the
+    library) matches; codes that are the quantisation of a point inside the
+    band count as admissible, with their flips counted; a code off by a
+    factor of two (the largest element's, halved) counts as inadmissible; the
+    shared expert's codes are asked for with expert None."""
+    rng = np.random.default_rng(25)
+    H, I, B, E, k, T = 64, 32, 32, 4, 2, 6
+    experts = [random_expert(rng, H, I, B) for _ in range(E)]
+    shared = random_expert(rng, H, I, B)
+    x = rng.normal(0, 1, (T, H))
+    wr = rng.normal(0, 0.3, (E, H))
+    band = (3e-3, 1e-3)
+    xh = torch_quantise_rows(x, B)
+
+    def h_of(ex, rows):
+        wgu = lib_dequant(ex["w_gate_up"], ex["s_gate_up"], B)
+        a = torch.from_numpy(xh[rows]) @ torch.from_numpy(wgu[:I]).T
+        u = torch.from_numpy(xh[rows]) @ torch.from_numpy(wgu[I:]).T
+        return (torch.nn.functional.silu(a) * u).numpy().astype(np.float32).astype(np.float64)
+
+    def codes_of(hp):
+        codes = np.empty(hp.shape, np.uint8)
+        ex = np.empty((hp.shape[0], hp.shape[1] // B), np.int64)
+        for t in range(hp.shape[0]):
+            for b in range(hp.shape[1] // B):
+                blk = hp[t, b * B:(b + 1) * B]
+                ex[t, b] = scalar_exponent(float(np.abs(blk).max()))
+                codes[t, b * B:(b + 1) * B] = lib_round(blk * 2.0 ** -ex[t, b])
+        return codes, ex
+
+    asked = []
+    given = {}
+
+    def h_codes_for(perturb, spoil):
+        def cb(e, toks, js):
+            ex = shared if e is None else experts[e]
+            asked.append(e)
+            h = h_of(ex, toks)
+            wgu = lib_dequant(ex["w_gate_up"], ex["s_gate_up"], B)
+            tau = O.h_band_width(xh[toks], wgu[:I], wgu[I:], *band)
+            c, exps = codes_of(h + perturb * rng.uniform(-1, 1, h.shape) * tau)
+            if spoil and e is not None:
+                big = np.unravel_index(np.argmax(np.abs(h)), h.shape)
+                c[big] = lib_round(0.5 * lib_decode(c[big[0]:big[0] + 1, big[1]:big[1] + 1]))[0, 0]
+            given[(e, tuple(toks), None if js is None else tuple(js))] = (c, exps)
+            return c, exps
+        return cb
+
+    for perturb, spoil in ((0.0, False), (1.0, False), (0.0, True)):
+        asked.clear()
+        given.clear()
+        res = O.moe_layer(x, wr, None, lambda e: experts[e], k, I, B, shared=shared,
+                          act_block=B, h_band=band, h_codes=h_codes_for(perturb, spoil))
+        assert None in asked and "flip" not in res
+        chk = res["h_check"]
+        assert chk["elements"] == (T * k + T) * I
+        if spoil:
+            assert chk["inadmissible"] >= 1
+        else:
+            assert chk["inadmissible"] == 0
+        if perturb == 0.0 and not spoil:
+            assert chk["flips"] == 0
+        logits = torch.from_numpy(x) @ torch.from_numpy(wr).T
+        top = torch.topk(logits, k, dim=1).indices.numpy()
+        want = np.zeros((T, H))
+        for (e, toks, js), (c, exps) in given.items():
+            ex = shared if e is None else experts[e]
+            wd = lib_dequant(ex["w_down"], ex["s_down"], B)
+            hq = lib_decode(c) * np.repeat(np.ldexp(1.0, exps), B, axis=1)
+            y = (torch.from_numpy(hq) @ torch.from_numpy(wd).T).numpy()
+            for r, t in enumerate(toks):
+                if e is None:
+                    want[t] += y[r]
+                else:
+                    j = js[r]
+                    assert top[t, j] == e
+                    g = torch.softmax(logits[t, top[t]], 0).numpy()
+                    want[t] += g[j] * y[r]
+        assert np.allclose(res["out"], want, rtol=1e-9, atol=1e-12)
+
+
 PINS = [pin_decode_matches_library, pin_decode_anchors, pin_dequant_bruteforce,
         pin_topk_bruteforce, pin_gates, pin_permutation, pin_single_expert_is_dense,
         pin_all_experts_equal_gates_is_dense_mean, pin_whole_layer_scalar, pin_tie_flags,
         pin_act_round_matches_library, pin_act_scale_closed_form,
         pin_act_quantise_blocks_bruteforce, pin_act_layer_uses_quantised_experts_only,
         pin_h_decided_in_fp32, pin_h_deviation_closed_form, pin_h_deviation_bruteforce,
-        pin_h_band_covers_fp32, pin_layer_flip_bound]
+        pin_h_band_covers_fp32, pin_layer_flip_bound, pin_h_admissible_codes_closed_form,
+        pin_h_admissible_codes_bruteforce, pin_layer_on_given_h_codes]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -561,8 +750,8 @@ MUTATIONS = {
     "act_scale_floor_clamp": ("e[nz] = np.maximum(est, -127)", "e[nz] = np.maximum(est, -126)"),
     "act_sign_dropped": ("return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)",
                          "return code"),
-    "experts_read_unquantised_x": ("y = swiglu_expert(xe[rows[who]], wg, wu, wd, h_block",
-                                   "y = swiglu_expert(x[rows[who]], wg, wu, wd, h_block"),
+    "experts_read_unquantised_x": ("y = expert_out(xe[rows[who]], wg, wu, wd, codes)",
+                                   "y = expert_out(x[rows[who]], wg, wu, wd, codes)"),
     "h_not_quantised": ("y = dequantise_activations(*quantise_activations(h, h_block), h_block) @ wd.T",
                         "y = h @ wd.T"),
     "h_decided_in_fp64": ("    h = h.astype(np.float32).astype(np.float64)\n", ""),
@@ -573,6 +762,15 @@ MUTATIONS = {
     "band_drops_a_error": ("np.abs(dsilu * u) * sa + np.abs(a * sig) * su", "np.abs(a * sig) * su"),
     "flip_gate_dropped": ("flip[i] += gates[rows[i], j] * bound[r]", "flip[i] += bound[r]"),
     "flip_shared_dropped": ("            flip += bound\n", ""),
+    "admissible_any_exponent": ("ok = ok_e[:, :, None] & (v >= lo) & (v <= hi)",
+                                "ok = (v >= lo) & (v <= hi)"),
+    "admissible_one_sided": ("hi = e4m3fn_decode(e4m3fn_round(np.clip((hb + tb) * down",
+                             "hi = e4m3fn_decode(e4m3fn_round(np.clip((hb + 0 * tb) * down"),
+    "admissible_exponent_range_too_narrow": (
+        "e_hi = act_scale_exponent((np.abs(hb) + tb).max(axis=2))\n    ok_e",
+        "e_hi = act_scale_exponent(np.abs(hb).max(axis=2))\n    ok_e"),
+    "given_codes_ignored": ("        return hq @ wd.T\n", "        return own @ wd.T\n"),
+    "given_codes_unchecked": ('        check["inadmissible"] += int((~ok).sum())\n', ""),
 }
 
 
