@@ -36,6 +36,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4] [--toke
                        [--path auto|gemv|mfma|mfma_fp8]
        (mfma_fp8: the variant with E4M3 operands in both expert contractions;
         its roofline takes the FP8 peak, 5.0 PFLOP/s, and its ridge)
+       python bench.py --stream-slots N [--config c3]  (routed experts streamed from pinned
+                                      host memory through an LRU cache of N device slots)
        python bench.py --copy-calibration            (the copy kernel for the counters)
        python bench.py --gemm-calibration --config c4  (library bf16 GEMMs at the expert shapes)
        python bench.py --traffic-report FETCH.csv WRITE.csv COPYF.csv COPYW.csv --config c1
@@ -271,6 +273,89 @@ def recorded_traffic(config, tokens, family):
     return entry["traffic_bytes_per_launch"]
 
 
+def stream_main(args):
+    """moe_forward_streamed on the workload: every step routes a new input
+    batch (batches rotate), brings its missing experts from pinned host
+    memory into the least recently used device slots, and runs the layer.
+    Each call returns once its work is done, so steps are timed on the host
+    clock. Reports tokens/s, the cache's hit rate and the host-to-device
+    expert rate."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import block_fp8_routed_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    moe.load()
+    dev = torch.device("cuda:0")
+    shape = W.CONFIGS[args.config]
+    T = args.tokens if args.tokens is not None else shape.tokens
+    H, E, I, B, k = shape.hidden, shape.experts, shape.inter, shape.block, shape.top_k
+    xdt = torch.bfloat16 if shape.x_dtype == "bf16" else torch.float32
+    log(f"generating {args.config} bank (E={E}) into pinned host memory")
+    bank_h = W.gen_bank(shape)
+    host = moe.Bank.pinned_from_numpy(bank_h)
+    del bank_h
+    shared = moe.Bank.from_numpy(W.gen_bank(shape, shared=True), dev) if shape.shared else None
+    slots = args.stream_slots
+    cache = moe.ExpertCache(slots)
+    slot_bank = moe.Bank.empty_slots(slots, H, I, B, dev)
+    router = torch.from_numpy(W.gen_router(shape)).to(dev)
+    bias_h = W.gen_bias(shape)
+    bias = None if bias_h is None else torch.from_numpy(bias_h).to(dev)
+    xs = [torch.from_numpy(W.gen_x(shape, T, batch=r)).to(xdt).to(dev) for r in range(args.batches)]
+    cfg = moe.make_config(T, H, E, I, k, B, shape.shared, xdt, torch.float32, args.path)
+    ws = moe.make_workspace(cfg, dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def call(i):
+        moe.moe_forward_streamed(xs[i % len(xs)], router, host, slot_bank, cache, k, B,
+                                 shared=shared, router_bias=bias, path=args.path, out=out,
+                                 workspace=ws)
+
+    log(f"warmup {args.warmup} streamed steps (T={T}, slots={slots})")
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    h0, m0, b0 = cache.hits, cache.misses, cache.bytes_in
+    rounds = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(args.warmup + i)
+        rounds.append(cache.rounds_last)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    hits, misses, bytes_in = cache.hits - h0, cache.misses - m0, cache.bytes_in - b0
+    res = {
+        "metric": "MoE-layer tokens/s, routed experts streamed host->HBM through an LRU cache",
+        "value": round(T * args.steps / el, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(el / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if args.path == "mfma_fp8" else "bf16" if xdt == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config} {shape.name}: hidden {H}, {E} experts top-{k}"
+                               f"{' + 1 shared (resident)' if shape.shared else ''}, inter {I}, "
+                               f"{T} tokens per step, routed experts in pinned host memory, "
+                               f"{slots} device expert slots (LRU)",
+                   "tokens": T, "slots": slots, "input_batches": len(xs), "path": args.path},
+        "stream": {
+            "hit_rate": round(hits / max(hits + misses, 1), 4),
+            "experts_needed_per_step": round((hits + misses) / args.steps, 2),
+            "experts_copied_per_step": round(misses / args.steps, 2),
+            "bytes_in_per_step": round(bytes_in / args.steps),
+            "host_to_device_GBps": round(bytes_in / el / 1e9, 2),
+            "rounds_per_step": round(sum(rounds) / len(rounds), 2),
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +378,9 @@ def main():
                          "(default: 1 above 16 tokens per step, else 21; always at least the "
                          "last timed step; 0: none, no roofline figure)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-slots", type=int, default=0,
+                    help="run moe_forward_streamed: routed experts in pinned host memory, "
+                         "an LRU cache of this many device expert slots")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the copy kernel the PMC counters are calibrated on")
     ap.add_argument("--gemm-calibration", action="store_true",
@@ -310,6 +398,12 @@ def main():
     if args.gemm_calibration:
         import workloads as W
         gemm_calibration(W.CONFIGS[args.config])
+        return
+    if args.stream_slots:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        stream_main(args)
         return
 
     if args.gpus != 1:

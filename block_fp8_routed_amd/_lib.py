@@ -24,7 +24,8 @@ PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA,
 (MOE_EV_START, MOE_EV_ROUTED, MOE_EV_PERMUTED, MOE_EV_GATE_UP, MOE_EV_DOWN,
  MOE_EV_END, MOE_EV_COUNT) = range(7)
 
-EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_route", "moe_permute",
+EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_forward_streamed", "moe_route",
+           "moe_permute",
            "moe_dequant_e4m3", "moe_quantize_act_e4m3", "moe_workspace_region",
            "moe_status_string", "moe_version")
 (MOE_WS_TOPK, MOE_WS_GATES, MOE_WS_OFFSETS, MOE_WS_PAIR, MOE_WS_INV, MOE_WS_H, MOE_WS_H_EXPS,
@@ -52,6 +53,19 @@ class MoeExpertBank(ctypes.Structure):
         ("w_down", ctypes.c_void_p),
         ("s_gate_up", ctypes.c_void_p),
         ("s_down", ctypes.c_void_p),
+    ]
+
+
+class MoeExpertCache(ctypes.Structure):
+    _fields_ = [
+        ("slots", ctypes.c_int32),
+        ("slot_expert", ctypes.POINTER(ctypes.c_int32)),
+        ("slot_used", ctypes.POINTER(ctypes.c_int64)),
+        ("calls", ctypes.c_int64),
+        ("hits", ctypes.c_int64),
+        ("misses", ctypes.c_int64),
+        ("bytes_in", ctypes.c_int64),
+        ("rounds_last", ctypes.c_int32),
     ]
 
 
@@ -85,6 +99,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [P, P, P, bankp, bankp, ctypes.c_int32, P, cfgp, P,
                                 ctypes.c_size_t, ctypes.POINTER(MoePhaseEvents), P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_streamed.argtypes = [P, P, P, bankp, bankp, ctypes.POINTER(MoeExpertCache),
+                                         bankp, ctypes.c_int32, P, cfgp, P, ctypes.c_size_t, P]
+    lib.moe_forward_streamed.restype = ctypes.c_int
     lib.moe_route.argtypes = [P, P, P, P, P, P, cfgp, P, ctypes.c_size_t, P]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_permute.argtypes = [P, P, P, P, cfgp, P, ctypes.c_size_t, P]
@@ -168,11 +185,17 @@ def make_workspace(cfg: MoeConfig, device) -> torch.Tensor:
 
 
 class Bank:
-    """A block-FP8 expert bank on the device: n experts, layout of moe_expert_bank."""
+    """A block-FP8 expert bank: n experts, layout of moe_expert_bank; on the
+    device, or (host=True) in pinned host memory for moe_forward_streamed."""
 
     def __init__(self, w_gate_up: torch.Tensor, s_gate_up: torch.Tensor,
-                 w_down: torch.Tensor, s_down: torch.Tensor):
-        _dev(w_gate_up, s_gate_up, w_down, s_down)
+                 w_down: torch.Tensor, s_down: torch.Tensor, host: bool = False):
+        if host:
+            for t in (w_gate_up, s_gate_up, w_down, s_down):
+                if t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+                    raise ValueError("a host bank needs contiguous pinned CPU tensors")
+        else:
+            _dev(w_gate_up, s_gate_up, w_down, s_down)
         if w_gate_up.dtype != torch.uint8 or w_down.dtype != torch.uint8:
             raise ValueError("E4M3 weights must be uint8 tensors")
         if s_gate_up.dtype != torch.float32 or s_down.dtype != torch.float32:
@@ -186,6 +209,20 @@ class Bank:
     def from_numpy(cls, bank: dict, device="cuda"):
         t = {k: torch.from_numpy(v).to(device) for k, v in bank.items()}
         return cls(t["w_gate_up"], t["s_gate_up"], t["w_down"], t["s_down"])
+
+    @classmethod
+    def pinned_from_numpy(cls, bank: dict):
+        """A host bank in newly allocated pinned memory."""
+        t = {k: torch.from_numpy(v).pin_memory() for k, v in bank.items()}
+        return cls(t["w_gate_up"], t["s_gate_up"], t["w_down"], t["s_down"], host=True)
+
+    @classmethod
+    def empty_slots(cls, slots: int, H: int, I: int, B: int, device="cuda"):
+        """A device bank of `slots` expert slots (the streamed cache)."""
+        return cls(torch.empty((slots, 2 * I, H), dtype=torch.uint8, device=device),
+                   torch.empty((slots, 2 * I // B, H // B), dtype=torch.float32, device=device),
+                   torch.empty((slots, H, I), dtype=torch.uint8, device=device),
+                   torch.empty((slots, H // B, I // B), dtype=torch.float32, device=device))
 
     @property
     def experts(self) -> int:
@@ -233,6 +270,57 @@ def moe_forward(x: torch.Tensor, router_w: torch.Tensor, bank: Bank, top_k: int,
                          ctypes.byref(evs) if evs is not None else None, _stream(stream))
     if st != MOE_OK:
         raise MoeError(st, "moe_forward")
+    return out
+
+
+class ExpertCache:
+    """Host-side state of a streamed expert cache of `slots` slots
+    (moe_expert_cache), with the counters moe_forward_streamed keeps."""
+
+    def __init__(self, slots: int):
+        import numpy as np
+        self.slot_expert = np.full(slots, -1, np.int32)
+        self.slot_used = np.zeros(slots, np.int64)
+        self.c = MoeExpertCache(slots, self.slot_expert.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                self.slot_used.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                0, 0, 0, 0, 0)
+
+    def __getattr__(self, name):
+        if name in ("slots", "calls", "hits", "misses", "bytes_in", "rounds_last"):
+            return getattr(self.c, name)
+        raise AttributeError(name)
+
+
+def moe_forward_streamed(x: torch.Tensor, router_w: torch.Tensor, host_bank: Bank,
+                         slot_bank: Bank, cache: ExpertCache, top_k: int, block: int,
+                         shared: Optional[Bank] = None, router_bias: Optional[torch.Tensor] = None,
+                         out_dtype=torch.float32, path: str = "auto",
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The whole layer through moe_forward_streamed: routed experts in pinned
+    host memory (host_bank), streamed into the device slots of slot_bank."""
+    lib = load()
+    T, H = x.shape
+    E = router_w.shape[0]
+    I = host_bank.w_gate_up.shape[1] // 2
+    cfg = make_config(T, H, E, I, top_k, block, shared is not None, x.dtype, out_dtype, path)
+    _dev(x, router_w, router_bias)
+    host_bank.check(E, H, I, block)
+    slot_bank.check(cache.slots, H, I, block)
+    if shared is not None:
+        shared.check(1, H, I, block)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = make_workspace(cfg, x.device)
+    st = lib.moe_forward_streamed(_ptr(x), _ptr(router_w), _ptr(router_bias),
+                                  ctypes.byref(host_bank.c), ctypes.byref(slot_bank.c),
+                                  ctypes.byref(cache.c),
+                                  ctypes.byref(shared.c) if shared is not None else None,
+                                  int(top_k), _ptr(out), ctypes.byref(cfg), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_forward_streamed")
     return out
 
 

@@ -52,6 +52,10 @@ struct BankPtrs {
   const uint8_t* sh_wd;
   const float* sh_sgu;
   const float* sh_sd;
+  // streamed banks: the slot holding each routed expert (-1: not in this
+  // round), entry E = 0 when the shared group runs in this round; null: the
+  // routed bank holds every expert at its own index
+  const int32_t* slot;
 };
 
 // gate/up lane map: C chunks of 16 bytes per row, M per lane, LPP lanes per
@@ -133,7 +137,11 @@ struct RowStage {
 // as fp16, row t scaled by 2^-hexp[t] (f16_block_exponent of the row's
 // largest magnitude, found with LDS atomic maxima on the magnitudes' bits:
 // non-negative floats order as their bit patterns, and a maximum does not
-// depend on the order of the atomics). hs row t starts at element t * I.
+// depend on the order of the atomics). When a row spans whole multiples of
+// 64 chunks every wavefront's chunks lie in one row, so the wavefront takes
+// its maximum by DPP and one lane does the atomic: 64 atomics on one LDS
+// word serialise (measured: the 4096-hidden down pass at 138 us instead of
+// 54). hs row t starts at element t * I.
 // Ends with a barrier; the caller's previous reads of hs and hexp must have
 // ended (a barrier) before the call.
 template <int I, int NT>
@@ -149,7 +157,12 @@ __device__ __forceinline__ void put_scaled_rows(const RowStage<I, 4, NT>& st, ui
     const uint4 w = st.v[j];
     const uint32_t m = max(max(w.x & 0x7fffffffu, w.y & 0x7fffffffu),
                            max(w.z & 0x7fffffffu, w.w & 0x7fffffffu));
-    atomicMax(&hmax[t], m);
+    if (RS::CPR % 64 == 0) {
+      const uint32_t wm = wave_max_u32(m);
+      if ((threadIdx.x & 63) == 0) atomicMax(&hmax[t], wm);
+    } else {
+      atomicMax(&hmax[t], m);
+    }
   }
   lds_barrier();
 #pragma unroll
@@ -191,8 +204,10 @@ __global__ __launch_bounds__(256) void gemv_gate_up(const void* __restrict__ x, 
   const int sub = lane % LPP;
   const int i = (live ? slab : 0) * PPW + lane / LPP;  // gate row; up row is I + i
   const bool sh = g == E;
-  const uint8_t* W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
-  const float* Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / B) * (H / B);
+  if (bk.slot && bk.slot[g] < 0) return;  // a streamed expert outside this round
+  const int gs = bk.slot && !sh ? bk.slot[g] : g;
+  const uint8_t* W = sh ? bk.sh_wgu : bk.wgu + (size_t)gs * 2 * I * H;
+  const float* Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)gs * (2 * I / B) * (H / B);
 
   // Issue order: the first pass's token ids (a vector load: lane u < NT
   // fetches id u), then the weights and scales, then the token rows, which
@@ -323,8 +338,10 @@ __global__ __launch_bounds__(256) void gemv_down(BankPtrs bk, const int4* __rest
   const int sub = lane % LPR;
   const int row = (live ? slab : 0) * RW + lane / LPR;
   const bool sh = g == E;
-  const uint8_t* W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
-  const float* Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / B) * (I / B);
+  if (bk.slot && bk.slot[g] < 0) return;  // a streamed expert outside this round
+  const int gs = bk.slot && !sh ? bk.slot[g] : g;
+  const uint8_t* W = sh ? bk.sh_wd : bk.wd + (size_t)gs * H * I;
+  const float* Sc = sh ? bk.sh_sd : bk.sd + (size_t)gs * (H / B) * (I / B);
 
   // the group's h rows are contiguous (rows r0 .. r0 + n - 1); the first
   // pass's rows are requested before the weights and scales, so staging them
@@ -451,10 +468,10 @@ bool has_gemv_instance(const Dims& d) {
 
 hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               KernelEvents gate_up_events) {
+                               KernelEvents gate_up_events, const int32_t* slot) {
   BankPtrs bk{routed.w_gate_up, routed.w_down, routed.s_gate_up, routed.s_down,
               shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
-              shared ? shared->s_gate_up : nullptr, shared ? shared->s_down : nullptr};
+              shared ? shared->s_gate_up : nullptr, shared ? shared->s_down : nullptr, slot};
 #define X(h, i, b)                                       \
   if (d.H == h && d.I == i && d.B == b) {                \
     run_gemv_nt<h, i, b>(d, x, bk, w, s, gate_up_events); \

@@ -62,7 +62,11 @@ struct MfmaBank {
   const uint8_t* sh_wd;
   const float* sh_sgu;
   const float* sh_sd;
+  const int32_t* slot;  // streamed banks: the slot of each routed expert (-1: skip), entry E
+                        // for the shared group (null: every expert at its own index)
 };
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 128;            // K per scale block (the block edge)
 constexpr int kPassThreadsDecl = 512;  // threads of a grouped pass workgroup
@@ -161,6 +165,91 @@ __device__ __forceinline__ uint4 rescale_f16x8(uint4 v, uint32_t word) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// ---- the down passes' y: scaled fp16 with an exponent known in advance ----
+// A down tile's 256 output columns are two blocks of 128, and each block's
+// weights share one scale per 128 K (the scale grid's 128 x 128 blocks), so
+// with |A| <= amax_a(row) elementwise the output obeys
+//   |y| <= amax_a(row) * 448 * 128 * S(b),  S(b) = sum over K blocks of s(b, kb)
+// (|code| <= 448). With 2^g(row) >= amax_a(row) / 2^15 (bf16 pass: the h
+// row's common power of two, h' < 2^15; FP8 pass: the largest of the row's h
+// block exponents, codes <= 448 folded into q) and 2^q(b) > 448 * 128 * S(b)
+// (* 448 / 2^15 for the FP8 pass), y is stored as fp16(y * 2^-ey) with
+// ey = g(row) + q(b), below 2^15 by construction: no maximum has to be found
+// across the tile. The bound is loose by the usual cancellation of a sum
+// (typically 2^8 - 2^10), which still leaves every y value down to 2^-20 or
+// so of its block's largest with the full fp16 significand; the exponent
+// byte is ey + 127, clamped to [0, 254] (only beyond fp32's own range).
+__device__ __forceinline__ int y_block_q(const float* srow, int nkb, float coef) {
+  float sum = 0.f;
+  for (int kb = 0; kb < nkb; ++kb) sum += srow[kb];
+  // 2^q > coef * sum: q = binary exponent (frexp) of the product, 0 for 0
+  const float b = coef * sum;
+  return b > 0.f ? __builtin_amdgcn_frexp_expf(b) : 0;
+}
+__device__ __forceinline__ int clamp_exp(int e) { return e < -127 ? -127 : (e > 127 ? 127 : e); }
+
+// The down tile's fp16 y through LDS (a row-major tile of 256 fp16 columns,
+// 16-byte chunk c of row r at slot c ^ oswz(r)), every row then stored as
+// whole 16-byte chunks by slot (orow), with the exponent bytes. acc holds
+// the wavefront's MW x 2 MFMA tiles; value (row, block b) is stored as
+// acc * unit[nb] * 2^(G(row) - ey), ey = clamp(g(row) + q(b)), where G is
+// the power of two acc is expressed in (the bf16 pass: g; FP8: 0).
+template <int RA, int MW, int H, bool GISG>
+__device__ __forceinline__ void store_y_tile(const f32x16_t (&acc)[MW][2], const float* unit,
+                                             const int* rowg, const int* yq, int arow0, int wn,
+                                             bool idle, int valid, int n0, const int* orow,
+                                             int wave, uint8_t* lds, uint16_t* y,
+                                             uint8_t* yexps) {
+  constexpr int ORB = 256 * 2, OCH = ORB / 16;
+  static_assert(RA * ORB <= 65536, "output tile exceeds the LDS block");
+  auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
+  const int ln = (int)__lane_id(), q = ln >> 5, l32 = ln & 31;
+  const bool odd = l32 & 1;
+  if (!idle) {
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const int row = arow0 + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
+        const int g0 = rowg[row], g1 = rowg[row + 1];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col0 = 64 * wn + 32 * nb, b = col0 >> 7;
+          const int s0 = (GISG ? g0 : 0) - clamp_exp(g0 + yq[b]);
+          const int s1 = (GISG ? g1 : 0) - clamp_exp(g1 + yq[b]);
+          const uint32_t a = f32_to_f16(__builtin_ldexpf(acc[m][nb][v] * unit[nb], s0));
+          const uint32_t c = f32_to_f16(__builtin_ldexpf(acc[m][nb][v + 1] * unit[nb], s1));
+          // lanes exchange one value with their neighbour (DPP quad_perm
+          // 1,0,3,2): an even lane writes two columns of row R, an odd lane
+          // two columns of row R + 1
+          const uint32_t send = odd ? a : c;
+          const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
+          const int r = row + (odd ? 1 : 0);
+          const int col = col0 + l32 - (odd ? 1 : 0);
+          const uint32_t word = odd ? (recv | (c << 16)) : (a | (recv << 16));
+          *reinterpret_cast<uint32_t*>(lds + r * ORB + 16 * (((2 * col) >> 4) ^ oswz(r)) +
+                                       ((2 * col) & 15)) = word;
+        }
+      }
+  }
+  __syncthreads();
+  const int tid = 64 * wave + ln;
+  static_assert((RA * OCH) % kPassThreadsDecl == 0, "output chunks per thread");
+#pragma unroll
+  for (int i = 0; i < RA * OCH / kPassThreadsDecl; ++i) {
+    const int idx = tid + kPassThreadsDecl * i, r = idx / OCH, c = idx % OCH;
+    if (r >= valid) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
+    *reinterpret_cast<uint4*>(y + (size_t)orow[r] * H + n0 + 8 * c) = val;
+  }
+  if (tid < 2 * RA) {
+    const int r = tid % RA, b = tid / RA;
+    if (r < valid)
+      yexps[(size_t)orow[r] * (H / 128) + n0 / 128 + b] =
+          (uint8_t)(clamp_exp(rowg[r] + yq[b]) + kF16ExpBias);
+  }
+}
+
 // Outputs of a bf16 pass: gate/up writes h (scaled fp16 [P][I]) and its
 // exponent bytes; down reads h's exponent bytes and writes y (scaled fp16
 // [P][H], by slot) and its exponent bytes.
@@ -238,7 +327,6 @@ struct PassShape {
   static constexpr int NOUT = GU ? I : H;      // output row length
 };
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // 8 E4M3 bytes to the MFMA operand type (bf16 for GU, fp16 for down) and the
 // 32x32x16 MFMA of that type
@@ -297,8 +385,8 @@ struct TileShape {
 template <bool GU, int H, int I, bool THIN>
 __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, const uint8_t* W,
                                           const float* ss, const int* arow, const int* orow,
-                                          const uint32_t* hfac, const int* herow, int valid,
-                                          int r0, int n0, uint8_t* lds, PassIO io) {
+                                          const uint32_t* hfac, const int* herow, const int* yq,
+                                          int valid, int r0, int n0, uint8_t* lds, PassIO io) {
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
   using S = TileShape<GU, THIN>;
@@ -561,29 +649,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         lds, valid, wave, [&](int r) { return h + (size_t)(r0 + r) * I + n0; },
         [&](int r) { return io.oexps + (size_t)(r0 + r) * (I / kBK) + n0 / kBK; });
   } else {
-    uint16_t* y = static_cast<uint16_t*>(io.out);
-#pragma unroll
-    for (int rho = 0; rho < 2; ++rho) {
-      if (rho) __syncthreads();  // the first round's reads are done
-      if (!idle && (wn >> 1) == rho) {
-#pragma unroll
-        for (int m = 0; m < MW; ++m)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * eq + (v & 3);
-            const int e = herow[row];
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-              put_f32(lds, row, S::brow(wn, nb) - 128 * rho + el32,
-                      __builtin_ldexpf(acc[m][nb][v] * unit[nb], e));
-          }
-      }
-      __syncthreads();
-      const int c0 = n0 + 128 * rho;
-      store_f16_rows<S::RA>(
-          lds, valid, wave, [&](int r) { return y + (size_t)orow[r] * H + c0; },
-          [&](int r) { return io.oexps + (size_t)orow[r] * (H / kBK) + c0 / kBK; });
-    }
+    store_y_tile<S::RA, MW, H, true>(acc, unit, herow, yq, S::arow0(wm), wn, idle, valid, n0,
+                                     orow, wave, lds, static_cast<uint16_t*>(io.out), io.oexps);
   }
 }
 
@@ -609,6 +676,7 @@ void mfma_pass(const uint16_t* __restrict__ act,
   // down: the tile's h rows' rescale words per block, and their common exponents
   __shared__ uint32_t hfac[GU ? 1 : kMfmaBM * NKB];
   __shared__ int herow[GU ? 1 : kMfmaBM];
+  __shared__ int yq[2];  // down: the two output column blocks' bound exponents
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
   // (each with its own L2), so workgroup L runs on XCD L % 8. XCD x takes row
   // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
@@ -627,22 +695,41 @@ void mfma_pass(const uint16_t* __restrict__ act,
   const int tid = threadIdx.x;
   const int n0 = (j % NCB) * P::COLS;
   const bool sh = g == E;
+  if (bk.slot && bk.slot[g] < 0) return;  // a streamed expert outside this round
+  const int gs = bk.slot && !sh ? bk.slot[g] : g;
   const uint8_t* W;
   const float* Sc;
   if (GU) {
-    W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
-    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
+    W = sh ? bk.sh_wgu : bk.wgu + (size_t)gs * 2 * I * H;
+    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)gs * (2 * I / kBK) * (H / kBK);
   } else {
-    W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
-    Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / kBK) * (I / kBK);
+    W = sh ? bk.sh_wd : bk.wd + (size_t)gs * H * I;
+    Sc = sh ? bk.sh_sd : bk.sd + (size_t)gs * (H / kBK) * (I / kBK);
   }
+  // Everything the tile needs before its first stage, loaded in one round
+  // (no load below depends on another):
   // source row of each tile row (GU: the token; down: the h row)
   if (tid < kMfmaBM) {
     const int rr = tid < valid ? tid : valid - 1;
     arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
-    // y is stored by slot (row r's output goes to y row pair[r]), so the
-    // combine reads a token's outputs without the inverse permutation
-    if (!GU) orow[tid] = pair[r0 + rr];
+    if (!GU) {
+      // y is stored by slot (row r's output goes to y row pair[r]), so the
+      // combine reads a token's outputs without the inverse permutation
+      orow[tid] = pair[r0 + rr];
+      // the h row's common power of two: the largest of its block
+      // exponents; its blocks are brought to it by rescale words (exact
+      // unless a block lies more than 2^14 below the row's largest block)
+      const uint8_t* eb = io.hexps + (size_t)(r0 + rr) * NKB;
+      int b[NKB], emax = 0;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        b[kb] = eb[kb];
+        emax = max(emax, b[kb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) hfac[tid * NKB + kb] = rescale_word(b[kb] - emax);
+      herow[tid] = emax - kF16ExpBias;
+    }
   }
   // scale rows of the tile's weight rows: GU: the gate block of rows n0 ..
   // n0 + 127 and the matching up block; down: rows n0 .. and n0 + 128 ..
@@ -651,27 +738,16 @@ void mfma_pass(const uint16_t* __restrict__ act,
     const int wrow = GU ? (i == 0 ? n0 : I + n0) : n0 + 128 * i;
     ss[i * NKB + kb] = Sc[(size_t)(wrow / kBK) * NKB + kb];
   }
+  // down: the output column blocks' bound exponents (|h'| <= 2^15 and
+  // |code| <= 448: 2^q > 448 * 128 * S(b), the 2^15 of h' cancelling)
+  if (!GU && tid >= 320 && tid < 322)
+    yq[tid - 320] = y_block_q(Sc + (size_t)((n0 + 128 * (tid - 320)) / kBK) * NKB, NKB,
+                              448.f * 128.f);
   __syncthreads();
-  if (!GU && tid < kMfmaBM) {
-    // each h row's common power of two: the largest of its block exponents;
-    // its blocks are brought to it by rescale words (exact unless a block
-    // lies more than 2^14 below the row's largest block)
-    const uint8_t* eb = io.hexps + (size_t)arow[tid] * NKB;
-    int b[NKB], emax = 0;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      b[kb] = eb[kb];
-      emax = max(emax, b[kb]);
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) hfac[tid * NKB + kb] = rescale_word(b[kb] - emax);
-    herow[tid] = emax - kF16ExpBias;
-  }
-  if (!GU) __syncthreads();
   if (valid <= 64)
-    pass_tile<GU, H, I, true>(act, W, ss, arow, orow, hfac, herow, valid, r0, n0, lds, io);
+    pass_tile<GU, H, I, true>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, io);
   else
-    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, hfac, herow, valid, r0, n0, lds, io);
+    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, io);
 }
 
 // ---------------------------------------------------------------------------
@@ -742,8 +818,8 @@ struct F8Out {
 template <bool GU, int H, int I, bool THIN>
 __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, const uint8_t* W,
                                              const float* ss, const uint8_t* sx, const int* arow,
-                                             const int* orow, int valid, int r0, int n0,
-                                             uint8_t* lds, F8Out out) {
+                                             const int* orow, const int* rowg, const int* yq,
+                                             int valid, int r0, int n0, uint8_t* lds, F8Out out) {
   using S = F8Shape<GU, THIN>;
   constexpr int K = GU ? H : I, KS = S::KS, NS = K / KS, AC = S::AC, BC = S::BC, MW = S::MW,
                 NBW = S::NBW, CH = S::CH;
@@ -954,28 +1030,10 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
       if (k == 0) out.hexps[(size_t)(r0 + r) * (I / kBK) + n0 / kBK] = (uint8_t)(e + 127);
     }
   } else {
-    // y as scaled fp16 by slot, through LDS as in the bf16 down pass
-    static_assert(S::RA * 512 <= kLdsBytes, "output tile exceeds the LDS block");
-#pragma unroll
-    for (int rho = 0; rho < 2; ++rho) {
-      if (rho) __syncthreads();  // the first round's reads are done
-      if (!idle && (wn >> 1) == rho) {
-#pragma unroll
-        for (int m = 0; m < MW; ++m)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = S::arow0(wm) + 32 * m + 8 * (v >> 2) + 4 * q + (v & 3);
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-              put_f32(lds, row, S::brow(wn, nb) - 128 * rho + l32, acc[m][nb][v] * unit[nb]);
-          }
-      }
-      __syncthreads();
-      const int c0 = n0 + 128 * rho;
-      store_f16_rows<S::RA>(
-          lds, valid, wave, [&](int r) { return out.y + (size_t)orow[r] * H + c0; },
-          [&](int r) { return out.yexps + (size_t)orow[r] * (H / kBK) + c0 / kBK; });
-    }
+    // y as scaled fp16 by slot (acc is y itself: the h exponents ride in the
+    // instruction), as in the bf16 down pass
+    store_y_tile<S::RA, MW, H, false>(acc, unit, rowg, yq, S::arow0(wm), wn, idle, valid, n0,
+                                      orow, wave, lds, out.y, out.yexps);
   }
 }
 
@@ -993,6 +1051,8 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
   __shared__ float ss[2 * NKB];           // the tile's two weight scale rows
   __shared__ uint8_t sx[kMfmaBM * NKB];   // the tile rows' A exponents
+  __shared__ int rowg[GU ? 1 : kMfmaBM];  // down: each row's largest h exponent
+  __shared__ int yq[2];                   // down: the output column blocks' bound exponents
   // XCD-aware, as mfma_pass
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds, nt = meta[1];
   const int chunk = (nt + kXcds - 1) / kXcds;
@@ -1004,20 +1064,32 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   const int tid = threadIdx.x;
   const int n0 = (j % NCB) * COLS;
   const bool sh = g == E;
+  if (bk.slot && bk.slot[g] < 0) return;  // a streamed expert outside this round
+  const int gs = bk.slot && !sh ? bk.slot[g] : g;
   const uint8_t* W;
   const float* Sc;
   if (GU) {
-    W = sh ? bk.sh_wgu : bk.wgu + (size_t)g * 2 * I * H;
-    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)g * (2 * I / kBK) * (H / kBK);
+    W = sh ? bk.sh_wgu : bk.wgu + (size_t)gs * 2 * I * H;
+    Sc = sh ? bk.sh_sgu : bk.sgu + (size_t)gs * (2 * I / kBK) * (H / kBK);
   } else {
-    W = sh ? bk.sh_wd : bk.wd + (size_t)g * H * I;
-    Sc = sh ? bk.sh_sd : bk.sd + (size_t)g * (H / kBK) * (I / kBK);
+    W = sh ? bk.sh_wd : bk.wd + (size_t)gs * H * I;
+    Sc = sh ? bk.sh_sd : bk.sd + (size_t)gs * (H / kBK) * (I / kBK);
   }
-  // source row of each tile row (gate/up: the token; down: the h row)
+  // source row of each tile row (gate/up: the token; down: the h row); the
+  // down pass also takes its rows' h exponents in the same round of loads
   if (tid < kMfmaBM) {
     const int rr = tid < valid ? tid : valid - 1;
     arow[tid] = GU ? rtok[r0 + rr] : r0 + rr;
-    if (!GU) orow[tid] = pair[r0 + rr];
+    if (!GU) {
+      orow[tid] = pair[r0 + rr];
+      int emax = 0;
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int b = exps[(size_t)(r0 + rr) * NKB + kb];
+        sx[tid * NKB + kb] = (uint8_t)b;
+        emax = max(emax, b);
+      }
+      rowg[tid] = emax - 127;
+    }
   }
   // weight scale rows: gate/up: the gate block of rows n0 .. n0 + 127 and the
   // matching up block; down: rows n0 .. + 127, then n0 + 128 .. + 255
@@ -1026,14 +1098,20 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
     const int wrow = GU ? (i == 0 ? n0 : I + n0) : n0 + 128 * i;
     ss[i * NKB + kb] = Sc[(size_t)(wrow / kBK) * NKB + kb];
   }
+  // down: |h| <= 448 * 2^g and |code| <= 448: 2^(q + 15) > 448 * 448 * 128 * S(b)
+  if (!GU && tid >= 320 && tid < 322)
+    yq[tid - 320] = y_block_q(Sc + (size_t)((n0 + 128 * (tid - 320)) / kBK) * NKB, NKB,
+                              448.f * 448.f * 128.f) - 15;
   __syncthreads();
-  for (int i = tid; i < kMfmaBM * NKB; i += kPassThreads)
-    sx[i] = exps[(size_t)arow[i / NKB] * NKB + i % NKB];
-  __syncthreads();
+  if (GU) {  // gate/up: the activation exponents of each row's token
+    for (int i = tid; i < kMfmaBM * NKB; i += kPassThreads)
+      sx[i] = exps[(size_t)arow[i / NKB] * NKB + i % NKB];
+    __syncthreads();
+  }
   if (valid <= 64)
-    pass_tile_f8<GU, H, I, true>(codes, W, ss, sx, arow, orow, valid, r0, n0, lds, out);
+    pass_tile_f8<GU, H, I, true>(codes, W, ss, sx, arow, orow, rowg, yq, valid, r0, n0, lds, out);
   else
-    pass_tile_f8<GU, H, I, false>(codes, W, ss, sx, arow, orow, valid, r0, n0, lds, out);
+    pass_tile_f8<GU, H, I, false>(codes, W, ss, sx, arow, orow, rowg, yq, valid, r0, n0, lds, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1090,10 +1168,10 @@ bool has_mfma_instance(const Dims& d) {
 
 hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               KernelEvents gate_up_events) {
+                               KernelEvents gate_up_events, const int32_t* slot) {
   MfmaBank bk{routed.w_gate_up, routed.w_down, routed.s_gate_up, routed.s_down,
               shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
-              shared ? shared->s_gate_up : nullptr, shared ? shared->s_down : nullptr};
+              shared ? shared->s_gate_up : nullptr, shared ? shared->s_down : nullptr, slot};
 #define X(hh, ii, bb)                                    \
   if (d.H == hh && d.I == ii && d.B == bb) {             \
     run_mfma<hh, ii, bb>(d, x, bk, w, s, gate_up_events); \

@@ -97,11 +97,23 @@ struct Work {
   uint8_t* aexps;    // [T][H/128] their E8M0 exponents (FP8 variant only)
   uint8_t* hexps;    // [P][I/128] exponent bytes of h (grouped families)
   uint8_t* yexps;    // [P][H/128] exponent bytes of y (grouped families)
+  int32_t* slotmap;  // [E+1] slot map of a streamed bank (moe_forward_streamed)
 };
 
 inline int64_t max_mfma_tiles(const Dims& d) {
   return d.P / kMfmaBM + d.E + d.S + 1;
 }
+
+// Validation shared by the entry points (host only, no HIP call).
+moe_status basic_dims(const moe_config* c, Dims* d);
+moe_status expert_family_ok(const Dims& d);
+bool bank_ok(const moe_expert_bank* b);
+moe_status check_workspace(const Dims& d, void* ws, size_t bytes);
+// Router, selection and permutation (and the FP8 variant's activation
+// quantiser) for one call, with the optional phase events START and ROUTED.
+moe_status enqueue_routing(const Dims& d, const void* x, const float* router_w,
+                           const float* router_bias, const struct Work& w,
+                           const moe_phase_events* events, hipStream_t s);
 
 // Sum of region sizes; carve() lays them out in this order.
 size_t workspace_bytes(const Dims& d);
@@ -132,12 +144,15 @@ struct KernelEvents {
   bool any() const { return begin != nullptr || end != nullptr; }
 };
 // expert passes; returns hipErrorInvalidValue if no instantiation matches
+// slot (device, may be null): for a streamed bank, the slot of each routed
+// expert in `routed` (-1: skipped in this launch) and entry E: 0 when the
+// shared group runs in this launch, -1 when it is skipped
 hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               KernelEvents gate_up_events);
+                               KernelEvents gate_up_events, const int32_t* slot = nullptr);
 hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               KernelEvents gate_up_events);
+                               KernelEvents gate_up_events, const int32_t* slot = nullptr);
 bool has_gemv_instance(const Dims& d);
 bool has_mfma_instance(const Dims& d);
 hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s);

@@ -14,7 +14,7 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 17;
+constexpr int kRegions = 18;
 
 static void region_sizes(const Dims& d, size_t* sz) {
   sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
@@ -36,6 +36,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[14] = d.f8 ? (size_t)d.T * (d.H / 128) : 0;      // their exponents
   sz[15] = d.mfma ? (size_t)d.P * (d.I / 128) : 0;    // exponents of h
   sz[16] = d.mfma ? (size_t)d.P * (d.H / 128) : 0;    // exponents of y
+  sz[17] = (size_t)(d.E + 1) * 4;                     // slot map of a streamed bank
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -72,11 +73,12 @@ Work carve(const Dims& d, void* base) {
   w.aexps = static_cast<uint8_t*>(r[14]);
   w.hexps = static_cast<uint8_t*>(r[15]);
   w.yexps = static_cast<uint8_t*>(r[16]);
+  w.slotmap = static_cast<int32_t*>(r[17]);
   return w;
 }
 
 // Shape checks shared by every entry point (no HIP call).
-static moe_status basic_dims(const moe_config* c, Dims* d) {
+moe_status basic_dims(const moe_config* c, Dims* d) {
   if (!c) return MOE_ERR_NULL;
   if (c->tokens < 0 || c->hidden <= 0 || c->experts <= 0 || c->inter <= 0 || c->top_k <= 0 ||
       c->block <= 0)
@@ -111,7 +113,7 @@ static moe_status basic_dims(const moe_config* c, Dims* d) {
   return MOE_OK;
 }
 
-static moe_status expert_family_ok(const Dims& d) {
+moe_status expert_family_ok(const Dims& d) {
   if (d.mfma) {
     if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
     if (d.f8 && (d.H % 128 != 0 || d.I % 128 != 0 ||
@@ -126,11 +128,11 @@ static moe_status expert_family_ok(const Dims& d) {
   return has_gemv_instance(d) ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 
-static bool bank_ok(const moe_expert_bank* b) {
+bool bank_ok(const moe_expert_bank* b) {
   return b && b->w_gate_up && b->w_down && b->s_gate_up && b->s_down;
 }
 
-static moe_status check_workspace(const Dims& d, void* ws, size_t bytes) {
+moe_status check_workspace(const Dims& d, void* ws, size_t bytes) {
   if (!ws) return MOE_ERR_NULL;
   if (bytes < workspace_bytes(d) || reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
     return MOE_ERR_WORKSPACE;
@@ -140,6 +142,30 @@ static moe_status check_workspace(const Dims& d, void* ws, size_t bytes) {
 static bool rec(const moe_phase_events* ev, moe_phase p, hipStream_t s) {
   if (!ev || !ev->ev[p]) return true;
   return hipEventRecord(static_cast<hipEvent_t>(ev->ev[p]), s) == hipSuccess;
+}
+
+moe_status enqueue_routing(const Dims& d, const void* x, const float* router_w,
+                           const float* router_bias, const Work& w, const moe_phase_events* events,
+                           hipStream_t s) {
+  if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
+  if (launch_router(d, x, router_w, w, s) != hipSuccess) return MOE_ERR_HIP;
+  const int tile_rows = d.mfma ? kMfmaBM : 0;
+  if (small_select_permute(d)) {
+    // decode sizes: selection and permutation share one launch, so ROUTED
+    // marks the end of the router logits here
+    if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
+    if (launch_select_permute_small(d, w.logits, router_bias, w, tile_rows, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    if (launch_topk(d, w.logits, router_bias, w.topk, w.gates, nullptr,
+                    w.meta + kMetaPermCounter, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
+    if (launch_permute(d, w.topk, w, tile_rows, true, s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (d.f8 && launch_quant_act(x, d.T, d.H, w.acodes, w.aexps, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 }  // namespace moe
@@ -177,26 +203,9 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
   const KernelEvents ev_gate_up{
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_PERMUTED]) : nullptr,
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr};
-  if (!rec(events, MOE_EV_START, s)) return MOE_ERR_HIP;
-  const bool small = small_select_permute(d);
-  if (launch_router(d, x, router_w, w, s) != hipSuccess) return MOE_ERR_HIP;
-  const int tile_rows = d.mfma ? kMfmaBM : 0;
-  if (small) {
-    // decode sizes: selection and permutation share one launch, so ROUTED
-    // marks the end of the router logits here
-    if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
-    if (launch_select_permute_small(d, w.logits, router_bias, w, tile_rows, s) != hipSuccess)
-      return MOE_ERR_HIP;
-  } else {
-    if (launch_topk(d, w.logits, router_bias, w.topk, w.gates, nullptr,
-                    w.meta + kMetaPermCounter, s) != hipSuccess)
-      return MOE_ERR_HIP;
-    if (!rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
-    if (launch_permute(d, w.topk, w, tile_rows, true, s) != hipSuccess) return MOE_ERR_HIP;
-  }
+  st = enqueue_routing(d, x, router_w, router_bias, w, events, s);
+  if (st != MOE_OK) return st;
   const moe_expert_bank* sh = d.S ? shared : nullptr;
-  if (d.f8 && launch_quant_act(x, d.T, d.H, w.acodes, w.aexps, s) != hipSuccess)
-    return MOE_ERR_HIP;
   const hipError_t e = d.mfma ? launch_experts_mfma(d, x, *experts, sh, w, s, ev_gate_up)
                               : launch_experts_gemv(d, x, *experts, sh, w, s, ev_gate_up);
   if (e != hipSuccess) return MOE_ERR_HIP;

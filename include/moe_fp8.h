@@ -164,6 +164,52 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
                        void* workspace, size_t workspace_bytes,
                        const moe_phase_events* events, void* stream);
 
+/* ---- Routed experts streamed from host memory through an HBM cache ----
+ * State of a bounded cache of expert slots in device memory, kept by the
+ * caller in HOST memory and updated by moe_forward_streamed. Before the first
+ * call: slot_expert[i] = -1 and slot_used[i] = 0 for every slot, counters 0.
+ */
+typedef struct {
+  int32_t slots;         /* expert slots of the device bank (>= 1)                   */
+  int32_t* slot_expert;  /* [slots] routed expert held by each slot, -1 = empty      */
+  int64_t* slot_used;    /* [slots] value of `calls` when the slot was last used     */
+  int64_t calls;         /* calls made with this cache                                */
+  int64_t hits;          /* needed experts found resident, summed over calls         */
+  int64_t misses;        /* needed experts copied in, summed over calls              */
+  int64_t bytes_in;      /* expert bytes copied host -> device, summed over calls    */
+  int32_t rounds_last;   /* expert-pass rounds of the last call                       */
+} moe_expert_cache;
+
+/* moe_forward with the routed experts kept in HOST memory and streamed on
+ * demand into a bounded cache of device expert slots, least recently used
+ * out first. Source: colizig page, "Features" (memory-tiered streaming with
+ * a bounded LRU expert cache; the GPU backend's LRU VRAM weight cache) and
+ * "What this project is trying to prove" (most of a 512-expert model is cold
+ * at any instant, so its experts stream across memory tiers instead of all
+ * being resident).
+ *   host_experts  routed bank (n = E) in pinned host memory (hipHostMalloc or
+ *                 equivalent), layout as moe_expert_bank
+ *   slot_bank     device bank of n = cache->slots experts, the cache itself
+ *   cache         host-memory state (above); read and updated by the call
+ *   shared        the shared expert's bank in DEVICE memory (always resident)
+ * Everything else as moe_forward (no phase events). The call routes on the
+ * device, brings the group offsets back to name the experts it needs (it
+ * waits for them), then runs the expert passes in rounds of at most `slots`
+ * experts: experts already resident first, the missing ones copied into the
+ * least recently used slots that the round does not use. A call needing
+ * more experts than there are slots takes several rounds. The call returns
+ * once its work has completed on `stream`. Outputs are bit-identical to
+ * moe_forward's on the same inputs (the same kernels compute each group
+ * once). The workspace is moe_forward's (moe_workspace_bytes). Errors: as
+ * moe_forward; MOE_ERR_SHAPE also for slots < 1 or a slot_expert entry that
+ * is not -1 or a distinct routed expert; MOE_ERR_NULL for NULL cache arrays. */
+moe_status moe_forward_streamed(const void* x, const float* router_w, const float* router_bias,
+                                const moe_expert_bank* host_experts,
+                                const moe_expert_bank* slot_bank, moe_expert_cache* cache,
+                                const moe_expert_bank* shared, int32_t top_k, void* out,
+                                const moe_config* cfg, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Router and selection only (the first two steps of moe_forward).
  * Source: colizig page, "Architecture & how it works" (the router is small and
  * always resident) and "What this project is trying to prove" (top-8 / top-10

@@ -221,3 +221,37 @@ def test_workspace_regions(path, tokens):
                                     ctypes.byref(n)) == _lib.MOE_ERR_SHAPE
     assert lib.moe_workspace_region(ctypes.byref(c), 0, None, ctypes.byref(n)) == _lib.MOE_ERR_NULL
     assert lib.moe_workspace_region(None, 0, ctypes.byref(o), ctypes.byref(n)) == _lib.MOE_ERR_NULL
+
+
+def test_streamed_forward_validation():
+    """moe_forward_streamed refuses a missing cache, an empty cache, cache
+    arrays that are NULL, and slot contents that do not name distinct routed
+    experts, before anything is enqueued."""
+    import numpy as np
+    lib = moe.load()
+    c = cfg()
+    hb, sb = bank(), bank()
+    n = moe.workspace_bytes(c)
+
+    def call(cache):
+        return lib.moe_forward_streamed(FAKE, FAKE, None, ctypes.byref(hb), ctypes.byref(sb),
+                                        ctypes.byref(cache.c) if cache is not None else None,
+                                        None, c.top_k, FAKE, ctypes.byref(c), FAKE, n, None)
+
+    assert call(None) == _lib.MOE_ERR_NULL
+    empty = moe.ExpertCache(1)
+    empty.c.slots = 0
+    assert call(empty) == _lib.MOE_ERR_SHAPE
+    nulls = moe.ExpertCache(2)
+    nulls.c.slot_used = ctypes.POINTER(ctypes.c_int64)()
+    assert call(nulls) == _lib.MOE_ERR_NULL
+    for bad in ([3, 3], [8, -1], [-2, 0]):  # duplicate, past E = 8, not -1
+        ch = moe.ExpertCache(2)
+        ch.slot_expert[:] = np.array(bad, np.int32)
+        assert call(ch) == _lib.MOE_ERR_SHAPE, bad
+    ok = moe.ExpertCache(2)
+    ok.slot_expert[:] = np.array([5, -1], np.int32)
+    null_bank = bank(null=True)
+    assert lib.moe_forward_streamed(FAKE, FAKE, None, ctypes.byref(null_bank), ctypes.byref(sb),
+                                    ctypes.byref(ok.c), None, c.top_k, FAKE, ctypes.byref(c),
+                                    FAKE, n, None) == _lib.MOE_ERR_NULL
