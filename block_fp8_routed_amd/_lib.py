@@ -16,7 +16,9 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_fp8.so")
 
-MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+(MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
+ MOE_ERR_TOO_LARGE) = range(7)
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA_FP8 = 0, 1, 2, 3
 PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA,
@@ -24,7 +26,7 @@ PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA,
 (MOE_EV_START, MOE_EV_ROUTED, MOE_EV_PERMUTED, MOE_EV_GATE_UP, MOE_EV_DOWN,
  MOE_EV_END, MOE_EV_COUNT) = range(7)
 
-EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_forward_streamed", "moe_route",
+EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_forward_static", "moe_forward_streamed", "moe_route",
            "moe_permute",
            "moe_dequant_e4m3", "moe_quantize_act_e4m3", "moe_workspace_region",
            "moe_status_string", "moe_version")
@@ -99,6 +101,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [P, P, P, bankp, bankp, ctypes.c_int32, P, cfgp, P,
                                 ctypes.c_size_t, ctypes.POINTER(MoePhaseEvents), P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_static.argtypes = [P, P, P, bankp, bankp, ctypes.c_int32, P, cfgp,
+                                       ctypes.POINTER(MoePhaseEvents), P]
+    lib.moe_forward_static.restype = ctypes.c_int
     lib.moe_forward_streamed.argtypes = [P, P, P, bankp, bankp, ctypes.POINTER(MoeExpertCache),
                                          bankp, ctypes.c_int32, P, cfgp, P, ctypes.c_size_t, P]
     lib.moe_forward_streamed.restype = ctypes.c_int
@@ -321,6 +326,33 @@ def moe_forward_streamed(x: torch.Tensor, router_w: torch.Tensor, host_bank: Ban
                                   workspace.numel(), _stream(stream))
     if st != MOE_OK:
         raise MoeError(st, "moe_forward_streamed")
+    return out
+
+
+def moe_forward_static(x: torch.Tensor, router_w: torch.Tensor, bank: Bank, top_k: int,
+                       block: int, shared: Optional[Bank] = None,
+                       router_bias: Optional[torch.Tensor] = None, out_dtype=torch.float32,
+                       path: str = "auto", out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """The whole layer through moe_forward_static (scratch in the library's
+    static device array: no workspace is allocated). `out` may be given to
+    avoid torch's own allocation of the result."""
+    lib = load()
+    T, H = x.shape
+    E = router_w.shape[0]
+    I = bank.w_gate_up.shape[1] // 2
+    cfg = make_config(T, H, E, I, top_k, block, shared is not None, x.dtype, out_dtype, path)
+    _dev(x, router_w, router_bias)
+    bank.check(E, H, I, block)
+    if shared is not None:
+        shared.check(1, H, I, block)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    st = lib.moe_forward_static(_ptr(x), _ptr(router_w), _ptr(router_bias), ctypes.byref(bank.c),
+                                ctypes.byref(shared.c) if shared is not None else None,
+                                int(top_k), _ptr(out), ctypes.byref(cfg), None, _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_forward_static")
     return out
 
 

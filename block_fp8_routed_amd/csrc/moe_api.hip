@@ -278,6 +278,7 @@ const char* moe_status_string(moe_status status) {
     case MOE_ERR_UNSUPPORTED: return "no kernel for this shape, dtype or path";
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_TOO_LARGE: return "the call needs more scratch than the static scratch holds";
   }
   return "unknown status";
 }

@@ -59,7 +59,9 @@ typedef enum {
                            /* dtype, path) combination                              */
   MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_bytes()          */
                            /* or not 256-byte aligned                               */
-  MOE_ERR_HIP = 5          /* a HIP launch or event call failed                     */
+  MOE_ERR_HIP = 5,         /* a HIP launch or event call failed                     */
+  MOE_ERR_TOO_LARGE = 6    /* moe_forward_static: the call needs more scratch than  */
+                           /* MOE_STATIC_SCRATCH_BYTES                              */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -163,6 +165,25 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
                        int32_t top_k, void* out, const moe_config* cfg,
                        void* workspace, size_t workspace_bytes,
                        const moe_phase_events* events, void* stream);
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Its scratch is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES inside the library (each GPU it runs on holds one
+ * copy until the process ends); the call allocates nothing, and everything
+ * else (arguments, results, events, stream, errors) is as moe_forward.
+ * Calls whose moe_workspace_bytes(cfg) exceeds MOE_STATIC_SCRATCH_BYTES
+ * return MOE_ERR_TOO_LARGE before anything is enqueued (64 MiB hold the
+ * decode layers and prefill batches of several hundred tokens). All calls on
+ * one GPU share its array: calls that may overlap on one GPU (several
+ * streams or host threads) race and must be serialised by the caller. The
+ * first call on a device looks up the array's device address with that
+ * device current (MOE_ERR_HIP if that fails). */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_static(const void* x, const float* router_w, const float* router_bias,
+                              const moe_expert_bank* experts, const moe_expert_bank* shared,
+                              int32_t top_k, void* out, const moe_config* cfg,
+                              const moe_phase_events* events, void* stream);
 
 /* ---- Routed experts streamed from host memory through an HBM cache ----
  * State of a bounded cache of expert slots in device memory, kept by the

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for st in range(6):
+    for st in range(7):
         s = moe.status_string(st)
         assert isinstance(s, str) and s
     assert moe.status_string(99) == "unknown status"
@@ -255,3 +255,20 @@ def test_streamed_forward_validation():
     assert lib.moe_forward_streamed(FAKE, FAKE, None, ctypes.byref(null_bank), ctypes.byref(sb),
                                     ctypes.byref(ok.c), None, c.top_k, FAKE, ctypes.byref(c),
                                     FAKE, n, None) == _lib.MOE_ERR_NULL
+
+
+def test_static_scratch_entry_refuses_oversized_calls():
+    """moe_forward_static (scratch in the library's static device array)
+    refuses a call whose workspace would exceed MOE_STATIC_SCRATCH_BYTES with
+    MOE_ERR_TOO_LARGE before touching the device, and a NULL config with
+    MOE_ERR_NULL."""
+    lib = moe.load()
+    big = cfg(tokens=4096, hidden=4096, experts=512, inter=1024, top_k=10, block=128,
+              has_shared=True, x_dtype=_lib.torch.bfloat16)
+    assert moe.workspace_bytes(big) > moe.MOE_STATIC_SCRATCH_BYTES
+    b = bank()
+    assert lib.moe_forward_static(FAKE, FAKE, None, ctypes.byref(b), ctypes.byref(b), big.top_k,
+                                  FAKE, ctypes.byref(big), None, None) == moe.MOE_ERR_TOO_LARGE
+    assert lib.moe_forward_static(FAKE, FAKE, None, ctypes.byref(b), None, 2, FAKE, None, None,
+                                  None) == _lib.MOE_ERR_NULL
+    assert moe.status_string(moe.MOE_ERR_TOO_LARGE) != "unknown status"
