@@ -140,11 +140,14 @@ def cpu_baseline(shape, host, x_batches, seconds, chunk=64):
 
 # sources that define each dominant kernel (its traffic is void once they change)
 KERNEL_SOURCES = {
-    "gemv": ["expert_gemv.hip", "device.hpp", "layer.hpp"],
+    "gemv": ["expert_gemv.hip", "gemv_body.hpp", "device.hpp", "layer.hpp"],
+    "gemv_fused": ["decode_fused.hip", "gemv_body.hpp", "router_decode.hpp", "select.hpp",
+                   "permute.hpp", "device.hpp", "layer.hpp"],
     "mfma": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
     "mfma_fp8": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
 }
-KERNEL_MATCH = {"gemv": "gemv_gate_up<", "mfma": "mfma_pass<true", "mfma_fp8": "mfma_pass_f8<true"}
+KERNEL_MATCH = {"gemv": "gemv_gate_up<", "gemv_fused": "decode_fused<", "mfma": "mfma_pass<true",
+                "mfma_fp8": "mfma_pass_f8<true"}
 COPY_MATCH = "MulFunctor"  # the copy kernel of --copy-calibration (dst = src * 1)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 512
@@ -236,6 +239,14 @@ def traffic_report(args):
     T = args.tokens if args.tokens is not None else shape.tokens
     family = args.path if args.path in ("mfma", "mfma_fp8") else (
         "mfma" if args.path == "auto" and shape.x_dtype == "bf16" and T > 16 else "gemv")
+    if family == "gemv":  # the single-launch decode layer where the library takes it
+        import torch
+        import block_fp8_routed_amd as moe
+        xdt = torch.bfloat16 if shape.x_dtype == "bf16" else torch.float32
+        cfg = moe.make_config(T, shape.hidden, shape.experts, shape.inter, shape.top_k,
+                              shape.block, shape.shared, xdt, torch.float32, args.path)
+        if moe.workspace_region(cfg, moe.MOE_WS_STATUS)[1] > 0:
+            family = "gemv_fused"
     f_kib, nf = counter_means(fetch_csv, KERNEL_MATCH[family])
     w_kib, nw = counter_means(write_csv, KERNEL_MATCH[family])
     cf_kib, _ = counter_means(copy_f_csv, COPY_MATCH)
@@ -363,9 +374,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c4", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--tokens", type=int, default=None, help="tokens per step (default: config)")
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma", "mfma_fp8"],
+    ap.add_argument("--path", default="auto",
+                    choices=["auto", "gemv", "gemv_fused", "mfma", "mfma_fp8"],
                     help="expert family; mfma_fp8 runs both expert contractions on E4M3 "
-                         "operands (a numerics variant, never chosen by auto)")
+                         "operands (a numerics variant, never chosen by auto); gemv_fused "
+                         "the whole decode layer in one launch (never chosen by auto)")
     ap.add_argument("--batches", type=int, default=8, help="distinct input batches rotated")
     ap.add_argument("--copies", type=int, default=0, help="device copies of the bank (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -452,6 +465,9 @@ def main():
     f8 = args.path == "mfma_fp8"
     mfma = args.path in ("mfma", "mfma_fp8") or (args.path == "auto" and xdt == torch.bfloat16
                                                  and T > 16)
+    # the single-launch decode layer has a status region; the other paths none
+    fused = moe.workspace_region(cfg, moe.MOE_WS_STATUS)[1] > 0
+    family_key = "mfma_fp8" if f8 else "mfma" if mfma else "gemv_fused" if fused else "gemv"
 
     # routing of each batch: which experts a step touches (outside the timed region)
     uniq = []
@@ -492,7 +508,7 @@ def main():
         ev_structs[i] = s
     start, stop = hip.event(), hip.event()
 
-    log(f"warmup {Wm} steps (T={T}, copies={copies}, batches={len(xs)}, path={'mfma' if mfma else 'gemv'})")
+    log(f"warmup {Wm} steps (T={T}, copies={copies}, batches={len(xs)}, path={family_key})")
     for i in range(Wm):
         call(i)
     torch.cuda.synchronize()
@@ -530,7 +546,7 @@ def main():
     # (ROUTED marker -> gate/up kernel start) carries that overhead; the
     # rocprofv3 kernel traces give the per-kernel times.
     phase = {n: [] for n in ("route", "permute", "gate_up", "down", "combine")}
-    for i in range(min(20, K)):
+    for i in range(0 if fused else min(20, K)):  # one kernel: no phases to split
         evs = [hip.event() for _ in range(moe.MOE_EV_COUNT)]
         s = moe.MoePhaseEvents()
         for j, e in enumerate(evs):
@@ -539,12 +555,15 @@ def main():
         torch.cuda.synchronize()
         for j, n in enumerate(phase):
             phase[n].append(hip.elapsed_ms(evs[j], evs[j + 1]) * 1e3)
-    phases_us = {n: round(sorted(v)[len(v) // 2], 2) for n, v in phase.items()}
+    phases_us = {n: round(sorted(v)[len(v) // 2], 2) for n, v in phase.items() if v}
 
     tokens_per_s = T / (ms / 1e3)
     rows = T * k + T * int(shape.shared)
     flops = rows * 6 * H * I
     gu_flops = rows * 4 * H * I
+    if fused:  # the timed kernel is the whole layer: all expert bytes and products
+        gu_bytes = gu_bytes / gu_bytes_per_expert * all_bytes_per_expert
+        gu_flops = flops
     gu_s = gu_avg_ms / 1e3
     gbps = gu_bytes / gu_s / 1e9
     tflops = gu_flops / gu_s / 1e12
@@ -555,22 +574,24 @@ def main():
     ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     family = ("grouped FP8 MFMA, E4M3 x and h" if f8 else
               "grouped bf16 MFMA" if mfma else "wavefront GEMV")
+    what = ("the whole decode layer in one launch (router, selection, permutation, gate/up + "
+            "SwiGLU, down, combine; wavefront GEMV)" if fused else
+            f"expert gate/up + SwiGLU ({family})")
     if gu_flops / gu_bytes > ridge:
-        roof = {"bound": "mfma", "kernel": f"expert gate/up + SwiGLU ({family})",
+        roof = {"bound": "mfma", "kernel": what,
                 "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4), "traffic": None,
                 "algorithmic_per_launch": gu_flops,
                 "hbm_GBps": round(gbps, 1)}
     else:
-        roof = {"bound": "hbm", "kernel": f"expert gate/up + SwiGLU ({family})",
+        roof = {"bound": "hbm", "kernel": what,
                 "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_per_launch": round(gu_bytes),
                 "mfma_TFLOPs": round(tflops, 2)}
     roof["avg_launch_us"] = round(gu_avg_ms * 1e3, 2)
     roof["launch_samples"] = len(sampled)
-    roof["traffic"] = recorded_traffic(args.config, T,
-                                       "mfma_fp8" if f8 else "mfma" if mfma else "gemv")
+    roof["traffic"] = recorded_traffic(args.config, T, family_key)
 
     res = {
         "metric": "MoE-layer tokens/s; decode HBM GB/s vs peak, prefill MFMA util",
@@ -600,7 +621,7 @@ def main():
                          ", fp32 output"),
             "tokens": T, "hidden": H, "experts": E, "top_k": k, "inter": I, "block": B,
             "shared": shape.shared,
-            "path": "mfma_fp8" if f8 else "mfma" if mfma else "gemv",
+            "path": family_key,
             "bank_copies": copies, "input_batches": len(xs),
         },
         "roofline": roof,

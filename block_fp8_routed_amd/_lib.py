@@ -20,9 +20,9 @@ LIB_PATH = os.path.join(HERE, "libmoe_fp8.so")
  MOE_ERR_TOO_LARGE) = range(7)
 MOE_STATIC_SCRATCH_BYTES = 64 << 20
 MOE_F32, MOE_BF16 = 0, 1
-MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA_FP8 = 0, 1, 2, 3
+MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA_FP8, MOE_PATH_GEMV_FUSED = range(5)
 PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA,
-         "mfma_fp8": MOE_PATH_MFMA_FP8}
+         "mfma_fp8": MOE_PATH_MFMA_FP8, "gemv_fused": MOE_PATH_GEMV_FUSED}
 (MOE_EV_START, MOE_EV_ROUTED, MOE_EV_PERMUTED, MOE_EV_GATE_UP, MOE_EV_DOWN,
  MOE_EV_END, MOE_EV_COUNT) = range(7)
 
@@ -31,7 +31,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_forward_static", "moe_forw
            "moe_dequant_e4m3", "moe_quantize_act_e4m3", "moe_workspace_region",
            "moe_status_string", "moe_version")
 (MOE_WS_TOPK, MOE_WS_GATES, MOE_WS_OFFSETS, MOE_WS_PAIR, MOE_WS_INV, MOE_WS_H, MOE_WS_H_EXPS,
- MOE_WS_Y, MOE_WS_Y_EXPS, MOE_WS_COUNT) = range(10)
+ MOE_WS_Y, MOE_WS_Y_EXPS, MOE_WS_STATUS, MOE_WS_COUNT) = range(11)
 
 
 class MoeConfig(ctypes.Structure):

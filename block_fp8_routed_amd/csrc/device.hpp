@@ -229,6 +229,25 @@ __device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 constexpr int kBufNonTemporal = 2;
 
+// Loads and stores at the device's point of coherence (agent-scope relaxed
+// atomics, sc1): data that one workgroup hands to another inside a kernel
+// goes through these, so neither side needs a cache write-back or
+// invalidation (the producer waits for its stores to complete before it
+// signals; the consumer reads after it has seen the signal).
+template <class T>
+__device__ __forceinline__ T ld_coherent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ void st_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint4 ld16_coherent(const void* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = ld_coherent(q), b = ld_coherent(q + 1);
+  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads still in
 // flight (streamed weights) stay in flight across it, where __syncthreads()
 // would first wait for every outstanding load of the wavefront.

@@ -24,6 +24,7 @@ struct Dims {
   bool x_bf16, out_bf16;
   bool mfma;     // expert family: grouped bf16 MFMA (true) or wavefront GEMV
   bool f8;       // grouped family with E4M3 operands in both expert contractions
+  bool fused;    // GEMV family with the whole layer in one launch (decode_fused.hip)
 };
 
 // Router kernels and partial logits. The router writes partial logits per
@@ -98,6 +99,8 @@ struct Work {
   uint8_t* hexps;    // [P][I/128] exponent bytes of h (grouped families)
   uint8_t* yexps;    // [P][H/128] exponent bytes of y (grouped families)
   int32_t* slotmap;  // [E+1] slot map of a streamed bank (moe_forward_streamed)
+  void* sync;        // single-launch decode layer: flags and counters (decode_fused.hip)
+  uint32_t* status;  // single-launch decode layer: error bits of its waits (0: none)
 };
 
 inline int64_t max_mfma_tiles(const Dims& d) {
@@ -154,6 +157,16 @@ hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_ba
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
                                KernelEvents gate_up_events, const int32_t* slot = nullptr);
 bool has_gemv_instance(const Dims& d);
+// The single-launch decode layer (decode_fused.hip): whether it covers d
+// (GEMV family, 1 <= T <= 16, decode router, E <= 512, a GEMV instance), the
+// bytes of its sync region (0 when it does not), and its launch. PERMUTED and
+// GATE_UP events, when given, take the kernel's start and end.
+bool fused_decode_ok(const Dims& d);
+size_t fused_sync_bytes(const Dims& d);
+hipError_t launch_decode_fused(const Dims& d, const void* x, const float* router_w,
+                               const float* router_bias, const moe_expert_bank& routed,
+                               const moe_expert_bank* shared, const Work& w, void* out,
+                               hipStream_t s, KernelEvents ev);
 bool has_mfma_instance(const Dims& d);
 hipError_t launch_combine(const Dims& d, const Work& w, void* out, hipStream_t s);
 // x [T][H] bf16 -> E4M3 codes [T][H] and E8M0 exponents [T][H/128]

@@ -14,7 +14,7 @@ namespace moe {
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Region sizes in carve order.
-constexpr int kRegions = 18;
+constexpr int kRegions = 20;
 
 static void region_sizes(const Dims& d, size_t* sz) {
   sz[0] = (size_t)router_slices(d) * d.T * d.E * 4;  // partial router logits
@@ -37,6 +37,8 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[15] = d.mfma ? (size_t)d.P * (d.I / 128) : 0;    // exponents of h
   sz[16] = d.mfma ? (size_t)d.P * (d.H / 128) : 0;    // exponents of y
   sz[17] = (size_t)(d.E + 1) * 4;                     // slot map of a streamed bank
+  sz[18] = d.fused ? fused_sync_bytes(d) : 0;         // single-launch decode: flags, counters
+  sz[19] = d.fused ? 16 : 0;  // single-launch decode: status word, then the give-up tag
 }
 
 size_t workspace_bytes(const Dims& d) {
@@ -74,6 +76,8 @@ Work carve(const Dims& d, void* base) {
   w.hexps = static_cast<uint8_t*>(r[15]);
   w.yexps = static_cast<uint8_t*>(r[16]);
   w.slotmap = static_cast<int32_t*>(r[17]);
+  w.sync = r[18];
+  w.status = static_cast<uint32_t*>(r[19]);
   return w;
 }
 
@@ -90,7 +94,7 @@ moe_status basic_dims(const moe_config* c, Dims* d) {
       (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16))
     return MOE_ERR_SHAPE;
   if (c->path != MOE_PATH_AUTO && c->path != MOE_PATH_GEMV && c->path != MOE_PATH_MFMA &&
-      c->path != MOE_PATH_MFMA_FP8)
+      c->path != MOE_PATH_MFMA_FP8 && c->path != MOE_PATH_GEMV_FUSED)
     return MOE_ERR_SHAPE;
   if (c->experts > kMaxExperts || c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (c->hidden % 16 != 0 || c->inter % 16 != 0) return MOE_ERR_UNSUPPORTED;
@@ -110,10 +114,14 @@ moe_status basic_dims(const moe_config* c, Dims* d) {
   d->f8 = c->path == MOE_PATH_MFMA_FP8;
   d->mfma = c->path == MOE_PATH_MFMA || d->f8 ||
             (c->path == MOE_PATH_AUTO && d->x_bf16 && c->tokens > kGemvMaxTokens);
+  // the single-launch decode layer only when asked for: the five-launch
+  // GEMV path measures faster on MI355X at every decode size
+  d->fused = c->path == MOE_PATH_GEMV_FUSED && fused_decode_ok(*d);
   return MOE_OK;
 }
 
 moe_status expert_family_ok(const Dims& d) {
+  if (d.fused) return MOE_OK;
   if (d.mfma) {
     if (!d.x_bf16) return MOE_ERR_UNSUPPORTED;
     if (d.f8 && (d.H % 128 != 0 || d.I % 128 != 0 ||
@@ -193,6 +201,7 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
   st = expert_family_ok(d);
   if (st != MOE_OK) return st;
   if (d.T == 0) return MOE_OK;
+  if (cfg->path == MOE_PATH_GEMV_FUSED && !d.fused) return MOE_ERR_UNSUPPORTED;
   st = check_workspace(d, workspace, workspace_bytes_);
   if (st != MOE_OK) return st;
 
@@ -203,6 +212,16 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
   const KernelEvents ev_gate_up{
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_PERMUTED]) : nullptr,
       events ? static_cast<hipEvent_t>(events->ev[MOE_EV_GATE_UP]) : nullptr};
+  if (d.fused) {
+    // one kernel: START and ROUTED before it, PERMUTED and GATE_UP on its
+    // dispatch, DOWN and END after it
+    if (!rec(events, MOE_EV_START, s) || !rec(events, MOE_EV_ROUTED, s)) return MOE_ERR_HIP;
+    if (launch_decode_fused(d, x, router_w, router_bias, *experts, d.S ? shared : nullptr, w,
+                            out, s, ev_gate_up) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (!rec(events, MOE_EV_DOWN, s) || !rec(events, MOE_EV_END, s)) return MOE_ERR_HIP;
+    return MOE_OK;
+  }
   st = enqueue_routing(d, x, router_w, router_bias, w, events, s);
   if (st != MOE_OK) return st;
   const moe_expert_bank* sh = d.S ? shared : nullptr;
@@ -259,14 +278,15 @@ moe_status moe_workspace_region(const moe_config* cfg, int32_t region, size_t* o
   moe_status st = basic_dims(cfg, &d);
   if (st != MOE_OK) return st;
   // carve-order index of each exported region
-  static const int kIndex[MOE_WS_COUNT] = {1, 2, 3, 7, 8, 10, 15, 11, 16};
+  static const int kIndex[MOE_WS_COUNT] = {1, 2, 3, 7, 8, 10, 15, 11, 16, 19};
   if (region < 0 || region >= MOE_WS_COUNT) return MOE_ERR_SHAPE;
   size_t sz[kRegions], off = 0;
   region_sizes(d, sz);
   const int idx = kIndex[region];
   for (int i = 0; i < idx; ++i) off += al(sz[i]);
   *offset = off;
-  *bytes = sz[idx];
+  // STATUS: the status word only (the region also holds an internal give-up tag)
+  *bytes = region == MOE_WS_STATUS ? std::min<size_t>(sz[idx], 4) : sz[idx];
   return MOE_OK;
 }
 

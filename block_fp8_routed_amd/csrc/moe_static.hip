@@ -10,7 +10,9 @@
 // and kept; kernels are given that address, never the name. Every call on
 // one device shares the array: calls that overlap on one GPU (other streams,
 // other host threads) race on it. The layer reads no scratch byte it has not
-// written in the same call, so nothing needs clearing between calls.
+// written in the same call (the single-launch decode layer's flags excepted:
+// they only pass a wait when they hold that call's epoch), so nothing needs
+// clearing between calls.
 #include <mutex>
 
 #include "layer.hpp"

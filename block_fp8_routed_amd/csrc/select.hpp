@@ -21,7 +21,11 @@
 
 namespace moe {
 
-template <int NV>
+// UNROLL: partial logits per expert requested together (more slices are added
+// one at a time, in the same slice order).
+// COHERENT: the partial logits are read at the point of coherence (written
+// by other workgroups of the same kernel).
+template <int NV, int UNROLL = (NV <= 2 ? 16 : 8), bool COHERENT = false>
 __device__ __forceinline__ int select_token(const float* __restrict__ plog, int slices,
                                             const float* __restrict__ bias, int64_t T, int64_t t,
                                             int E, int k, int32_t* topk_out, float* gates_out,
@@ -32,7 +36,7 @@ __device__ __forceinline__ int select_token(const float* __restrict__ plog, int 
   // requested before any is used: the addresses are clamped into range
   // instead of branched around, so the loads go out together and the token
   // pays one memory latency, not one per expert.
-  constexpr int kMaxUnrolled = NV <= 2 ? 16 : 8;
+  constexpr int kMaxUnrolled = UNROLL;
   float part[NV][kMaxUnrolled];
   float bv[NV];
 #pragma unroll
@@ -41,7 +45,8 @@ __device__ __forceinline__ int select_token(const float* __restrict__ plog, int 
 #pragma unroll
     for (int s = 0; s < kMaxUnrolled; ++s) {
       const int sc = s < slices ? s : slices - 1;
-      part[i][s] = plog[((size_t)sc * T + t) * E + e];
+      const float* src = plog + ((size_t)sc * T + t) * E + e;
+      part[i][s] = COHERENT ? ld_coherent(src) : *src;
     }
   }
 #pragma unroll
@@ -63,7 +68,10 @@ __device__ __forceinline__ int select_token(const float* __restrict__ plog, int 
       if (s < slices) val += part[i][s];
     key[i] = 0u;
     if (e < E) {
-      for (int s = kMaxUnrolled; s < slices; ++s) val += plog[((size_t)s * T + t) * E + e];
+      for (int s = kMaxUnrolled; s < slices; ++s) {
+        const float* src = plog + ((size_t)s * T + t) * E + e;
+        val += COHERENT ? ld_coherent(src) : *src;
+      }
       if (bias) val += bv[i];
       if (logits_out) logits_out[t * E + e] = val;
       if (val != val) val = -INFINITY;

@@ -75,12 +75,27 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * the SwiGLU output h, computed in fp32, is quantised by the same rule (per
  * expert row and 128 columns) before the down contraction. This changes the
  * layer's numerics (about 2^-4 relative per operand value); it requires bf16
- * x and H and I multiples of 128, and is not chosen by AUTO. */
+ * x and H and I multiples of 128, and is not chosen by AUTO.
+ * GEMV_FUSED runs the GEMV family's whole layer (router, selection,
+ * permutation, gate/up, down, combine) as one kernel launch whose workgroups
+ * hand results to each other through the workspace (flags holding a per-call
+ * epoch, counters), instead of five launches: the fixed per-step operation
+ * graph of decode that the ferrite page describes, without the kernel
+ * boundaries. Same arithmetic as GEMV (the router's partial sums and the
+ * combine's order included), so the two give identical outputs. It covers
+ * 1 <= tokens <= 16, experts <= 512 and hidden < 512 or a multiple of 512,
+ * on the GEMV shapes. AUTO does not take it: on MI355X its in-kernel
+ * hand-offs cost more than the four kernel boundaries they replace. Its
+ * workers wait for one another, so it expects the device to itself (they
+ * are sized to fit on it at once); every wait is bounded, and the
+ * workspace's STATUS region (moe_workspace_region) reports one that gave up
+ * (the output is then not valid). */
 typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_GEMV = 1,
   MOE_PATH_MFMA = 2,
-  MOE_PATH_MFMA_FP8 = 3
+  MOE_PATH_MFMA_FP8 = 3,
+  MOE_PATH_GEMV_FUSED = 4
 } moe_path;
 
 typedef struct {
@@ -307,6 +322,11 @@ moe_status moe_quantize_act_e4m3(const void* x, int64_t tokens, int32_t hidden, 
  *   Y        [P][H] expert outputs by slot: fp32 (GEMV family), fp16
  *            scaled by Y_EXPS (MFMA families)
  *   Y_EXPS   uint8 [P][H/128] exponent bytes of Y (MFMA families)
+ *   STATUS   uint32 (single-launch decode layer only, else 0 bytes): error
+ *            bits of the call's in-kernel waits, 0 when every wait ended
+ *            normally (1: router results, 2: the permutation, 4: gate/up
+ *            results not seen within the bounded wait; the output is then
+ *            not valid)
  * Returns MOE_ERR_NULL for a NULL pointer, MOE_ERR_SHAPE for an invalid cfg
  * or region. This call touches no device memory. It is what lets tests
  * compare each step's result with an independent evaluation. */
@@ -320,7 +340,8 @@ typedef enum {
   MOE_WS_H_EXPS = 6,
   MOE_WS_Y = 7,
   MOE_WS_Y_EXPS = 8,
-  MOE_WS_COUNT = 9
+  MOE_WS_STATUS = 9,
+  MOE_WS_COUNT = 10
 } moe_ws_region;
 moe_status moe_workspace_region(const moe_config* cfg, int32_t region, size_t* offset,
                                 size_t* bytes);

@@ -91,6 +91,9 @@ def test_workspace_bytes():
     (dict(experts=64, top_k=17), _lib.MOE_ERR_UNSUPPORTED),
     (dict(hidden=128, inter=64), _lib.MOE_ERR_UNSUPPORTED),  # no kernel for this shape
     (dict(path="mfma"), _lib.MOE_ERR_UNSUPPORTED),  # MFMA needs bf16 activations
+    # the single-launch decode layer: at most 16 tokens, at most 512 experts
+    (dict(path="gemv_fused", tokens=17), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(path="gemv_fused", experts=513, top_k=2), _lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_forward_rejects_bad_configs(kw, status):
     assert forward(cfg(**kw)) == status
@@ -102,6 +105,9 @@ def test_forward_rejects_bad_enums():
     assert forward(c) == _lib.MOE_ERR_SHAPE
     c = cfg()
     c.path = 5
+    assert forward(c) == _lib.MOE_ERR_SHAPE
+    c = cfg()
+    c.path = -1
     assert forward(c) == _lib.MOE_ERR_SHAPE
     c = cfg()
     c.has_shared = 2
@@ -184,7 +190,7 @@ def test_fp8_path_validation_and_workspace():
 
 
 @pytest.mark.parametrize("path,tokens", [("gemv", 16), ("auto", 8), ("mfma", 300),
-                                         ("mfma_fp8", 300)])
+                                         ("mfma_fp8", 300), ("gemv_fused", 16)])
 def test_workspace_regions(path, tokens):
     """moe_workspace_region: every exported region is 256-byte aligned, lies
     inside moe_workspace_bytes and overlaps no other, and has the size its
@@ -203,7 +209,9 @@ def test_workspace_regions(path, tokens):
             moe.MOE_WS_OFFSETS: (E + 2) * 4, moe.MOE_WS_PAIR: P * 4, moe.MOE_WS_INV: P * 4,
             moe.MOE_WS_H: P * I * h_elem, moe.MOE_WS_H_EXPS: P * I // 128 if grouped else 0,
             moe.MOE_WS_Y: P * H * (2 if grouped else 4),
-            moe.MOE_WS_Y_EXPS: P * H // 128 if grouped else 0}
+            moe.MOE_WS_Y_EXPS: P * H // 128 if grouped else 0,
+            # the single-launch decode layer's status word
+            moe.MOE_WS_STATUS: 4 if path == "gemv_fused" else 0}
     spans = []
     for region, n in want.items():
         off, got = moe.workspace_region(c, region)
@@ -215,7 +223,7 @@ def test_workspace_regions(path, tokens):
         assert a1 <= b0, "regions overlap"
     lib = moe.load()
     o, n = ctypes.c_size_t(), ctypes.c_size_t()
-    assert lib.moe_workspace_region(ctypes.byref(c), 9,
+    assert lib.moe_workspace_region(ctypes.byref(c), moe.MOE_WS_COUNT,
                                     ctypes.byref(o), ctypes.byref(n)) == _lib.MOE_ERR_SHAPE
     assert lib.moe_workspace_region(ctypes.byref(c), -1, ctypes.byref(o),
                                     ctypes.byref(n)) == _lib.MOE_ERR_SHAPE

@@ -29,7 +29,7 @@ def test_traffic_report_scales_counters_by_the_copy_kernel(tmp_path, monkeypatch
     copy_f = _csv(tmp_path / "cf.csv", [("MulFunctor<float>", mib / 2048)] * 3)
     copy_w = _csv(tmp_path / "cw.csv", [("FillFunctor<float>", 1.0), ("MulFunctor<float>", mib / 1024)])
     args = types.SimpleNamespace(traffic_report=[fetch, write, copy_f, copy_w], config="c1",
-                                 tokens=None, path="auto")
+                                 tokens=None, path="gemv")
     bench.traffic_report(args)
 
     entry = json.load(open(tmp_path / "traffic.json"))["c1:T16:gemv"]
@@ -77,3 +77,21 @@ def test_traffic_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.sources_sha("gemv") == h0
     (src / "k.hip").write_text("// header\n__global__ void k(int* p) { p[0] = 2; }\n")
     assert bench.sources_sha("gemv") != h0
+
+
+def test_traffic_report_picks_the_single_launch_layer(tmp_path, monkeypatch):
+    """The single-launch decode layer runs as one kernel (decode_fused): its
+    dispatches are the ones counted."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    k = "void moe::decode_fused<2048, 768, 128, 4, 4, true, false>(moe::FusedArgs)"
+    fetch = _csv(tmp_path / "f.csv", [(k, 500.0), ("void moe::gemv_gate_up<...>", 9.0)])
+    write = _csv(tmp_path / "w.csv", [(k, 4.0)])
+    mib = bench.COPY_MIB * 2 ** 20
+    copy_f = _csv(tmp_path / "cf.csv", [("MulFunctor<float>", mib / 1024)])
+    copy_w = _csv(tmp_path / "cw.csv", [("MulFunctor<float>", mib / 1024)])
+    args = types.SimpleNamespace(traffic_report=[fetch, write, copy_f, copy_w], config="c1",
+                                 tokens=None, path="gemv_fused")
+    bench.traffic_report(args)
+    entry = json.load(open(tmp_path / "traffic.json"))["c1:T16:gemv_fused"]
+    assert entry["kernel"] == "decode_fused<"
+    assert entry["traffic_bytes_per_launch"] == 504 * 1024

@@ -183,6 +183,12 @@ FWD_CASES = [  # (config, tokens, path, overrides)
     ("c0", 9, "gemv", {"experts": 100, "top_k": 3, "shared": True}),
     ("c0", 16, "auto", {"experts": 200, "top_k": 5}),
     ("c1", 17, "auto", {}),
+    # the single-launch decode layer
+    ("c1", 1, "gemv_fused", {}),
+    ("c1", 16, "gemv_fused", {}),
+    ("c3", None, "gemv_fused", {}),
+    ("c0", 16, "gemv_fused", {"experts": 512, "top_k": 16}),
+    ("c0", 9, "gemv_fused", {"experts": 100, "top_k": 3, "shared": True}),
 ]
 
 
@@ -536,7 +542,9 @@ def test_decode_permutation_in_the_workspace(name, T, ov):
 
 WS_CASES = [("c1", 16, "auto"), ("c1", 4, "auto"), ("c0", 4, "auto"), ("c1", 16, "mfma"),
             ("c2", 512, "auto"), ("c3", 8, "auto"), ("c2", 512, "mfma_fp8"),
-            ("c1", 37, "mfma_fp8")]
+            ("c1", 37, "mfma_fp8"),
+            # the single-launch decode layer: arbitrary flag words never pass a wait
+            ("c1", 16, "gemv_fused"), ("c3", 8, "gemv_fused")]
 
 
 @pytest.mark.parametrize("name,T,path", WS_CASES, ids=[f"{n}-T{t}-{p}" for n, t, p in WS_CASES])
