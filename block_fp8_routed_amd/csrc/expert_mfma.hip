@@ -103,6 +103,40 @@ __device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// unit / s for the ratio form of the block scales: the accumulators, held in
+// units of the last block's scale, move to the units of the next block's
+// scale s (nonzero). Mantissas and exponents are taken apart (frexp reads
+// subnormal scales exactly, where the reciprocal of a subnormal overflows),
+// so the ratio is finite whenever unit / s is within fp32 range; for normal
+// scales it equals unit * rcp(s), the power-of-two factors being exact.
+// unit 0 (nothing accumulated yet): 1.
+__device__ __forceinline__ float scale_ratio(float unit, float s) {
+  if (unit == 0.f) return 1.f;
+  const float mu = __builtin_amdgcn_frexp_mantf(unit), ms = __builtin_amdgcn_frexp_mantf(s);
+  const int e = __builtin_amdgcn_frexp_expf(unit) - __builtin_amdgcn_frexp_expf(s);
+  return __builtin_ldexpf(mu * __builtin_amdgcn_rcpf(ms), e);
+}
+
+// A tile's scale rows, before its stages: a block whose scale lies more
+// than 2^48 below its row's running scale (the last kept nonzero scale
+// before it along K) is dropped (its scale read as 0). Entering it, the
+// ratio form would multiply accumulators held in units of the running scale
+// by up to 2^127 and overflow; the block adds less than 2^-48 of what a
+// block at the running scale can. Magnitudes are compared (a scale may be
+// negative).
+constexpr float kScaleDropRatio = 0x1p-48f;
+__device__ __forceinline__ void drop_far_blocks(float* row, int nkb) {
+  float unit = 0.f;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const float s = row[kb];
+    if (s == 0.f) continue;
+    if (unit != 0.f && fabsf(s) < fabsf(unit) * kScaleDropRatio)
+      row[kb] = 0.f;
+    else
+      unit = s;
+  }
+}
+
 // ---- epilogue helpers: an fp32 output tile of 128 columns through LDS ----
 // Tile row r at byte r * 512, 16-byte chunk c at slot c ^ f32_swz(r), so the
 // two row groups of one accumulator write land on different banks.
@@ -515,7 +549,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         const bool on = sn != 0.f;
         // unit 0 (nothing added yet): the accumulators are 0 and stay 0; a
         // block of scale 0 (codes zeroed in LDS) leaves the unit as it is
-        const float r = on ? unit[nb] * __builtin_amdgcn_rcpf(sn) : 1.f;
+        const float r = on ? scale_ratio(unit[nb], sn) : 1.f;
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
@@ -744,6 +778,8 @@ void mfma_pass(const uint16_t* __restrict__ act,
     yq[tid - 320] = y_block_q(Sc + (size_t)((n0 + 128 * (tid - 320)) / kBK) * NKB, NKB,
                               448.f * 128.f);
   __syncthreads();
+  if (tid < 2) drop_far_blocks(ss + tid * NKB, NKB);
+  __syncthreads();
   if (valid <= 64)
     pass_tile<GU, H, I, true>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, io);
   else
@@ -913,7 +949,7 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
         const float sn = snext[nb];
         if (kb + 1 < NKB) snext[nb] = srow[nb][kb + 1];
         const bool on = sn != 0.f;
-        const float r = on ? unit[nb] * __builtin_amdgcn_rcpf(sn) : 1.f;
+        const float r = on ? scale_ratio(unit[nb], sn) : 1.f;
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
@@ -1102,6 +1138,8 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   if (!GU && tid >= 320 && tid < 322)
     yq[tid - 320] = y_block_q(Sc + (size_t)((n0 + 128 * (tid - 320)) / kBK) * NKB, NKB,
                               448.f * 448.f * 128.f) - 15;
+  __syncthreads();
+  if (tid < 2) drop_far_blocks(ss + tid * NKB, NKB);
   __syncthreads();
   if (GU) {  // gate/up: the activation exponents of each row's token
     for (int i = tid; i < kMfmaBM * NKB; i += kPassThreads)

@@ -264,6 +264,38 @@ def test_forward_tile_edges_and_zero_scales(path):
     check_output(out, ref["out"], what=f"constructed routing, zero scales, {path}")
 
 
+@pytest.mark.parametrize("case", ["subnormal", "far_apart"])
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_forward_subnormal_and_far_apart_block_scales(path, case):
+    """Block scales that are subnormal fp32 numbers (first block of a row,
+    mid-row, the smallest one), or a down row whose consecutive blocks differ
+    by 10^30 (each case alone, so that its outputs are not hidden under the
+    other's RMS): the grouped passes keep their accumulators in units of the
+    current block's scale and move between blocks by the ratio of the scales,
+    which must stay finite and exact in exponent (a reciprocal of a
+    subnormal overflows)."""
+    import block_fp8_routed_amd as moe
+    shape, x, wr, bank = _constructed_routing_layer()
+    k = shape.top_k
+    if case == "subnormal":
+        bank["s_gate_up"][0, 0, 0] = np.float32(1e-39)   # first block of its rows
+        bank["s_gate_up"][1, 1, 2] = np.float32(3e-40)   # mid-row
+        bank["s_gate_up"][4, 7, 9] = np.float32(2e-45)   # the smallest subnormal
+        bank["s_down"][3, 5, 2] = np.float32(5e-39)
+        assert bank["s_gate_up"][4, 7, 9] > 0
+    else:
+        far = np.array([1e-20, 1e10, 1e-20, 1e10, 1e-20, 1e10], np.float32)
+        bank["s_down"][2, 3, :] = far[: bank["s_down"].shape[2]]
+        bank["s_gate_up"][0, 2, :] = np.resize(far, bank["s_gate_up"].shape[2])
+    out = moe.moe_forward(torch.from_numpy(x).to(torch.bfloat16).cuda(), torch.from_numpy(wr).cuda(),
+                          moe.Bank.from_numpy(bank), k, shape.block, path=path)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+    ref = oracle.moe_layer(x, wr, None, lambda e: W.bank_expert(bank, e), k, shape.inter,
+                           shape.block)
+    check_output(out, ref["out"], what=f"{case} block scales, {path}")
+
+
 @pytest.mark.parametrize("T,path", [(16, "gemv"), (5, "mfma"), (40, "gemv")])
 def test_exact_ties_go_to_the_lower_index(T, path):
     """A router of zeros, its odd rows -0, makes every logit exactly +0 or -0
