@@ -70,7 +70,6 @@ constexpr uint32_t kStatusRouter = 1u, kStatusExpertFlag = 2u, kStatusGateUp = 4
 // channels): polls of one must not queue behind another's updates.
 constexpr int kFlagStride = 8;  // uint64 words: 64 bytes
 constexpr int kGuStride = 64;   // int32 words: 256 bytes
-constexpr int kCmbStride = 16;  // int32 words: 64 bytes
 constexpr int kMaxSlices = 8;   // router slices (H <= 4096 on the GEMV shapes)
 
 struct FusedArgs {
@@ -358,7 +357,6 @@ __global__ __launch_bounds__(256) void decode_fused(const FusedArgs a) {
   int* marked = hexp + NT;                // tokens whose row block this item completes
   int* nmarked = marked + kGemvMaxTokens;
   const int dn_items = nact * DS::ITEMS;
-  const int need = a.k + a.S;
   for (int j = w; j < dn_items; j += a.nw) {
     const int gi = j / DS::ITEMS, bx = j - gi * DS::ITEMS;
     const int4 gd = a.gdesc[gi];
@@ -368,36 +366,8 @@ __global__ __launch_bounds__(256) void decode_fused(const FusedArgs a) {
         wt.fail(kStatusGateUp);
       __syncthreads();
     });
-    if (tid == 0) *nmarked = 0;
-    __builtin_amdgcn_s_waitcnt(0);  // this item's y stores are complete
-    __syncthreads();
-    for (int r = tid; r < gd.z; r += 256) {
-      const int t = a.rtok[gd.y + r];
-      const int old = __hip_atomic_fetch_add(a.cmb + (size_t)(t * DS::ITEMS + bx) * kCmbStride,
-                                             1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == need - 1) marked[atomicAdd(nmarked, 1)] = t;
-    }
-    __syncthreads();
-    const int nm = *nmarked;
-    if (nm > 0) {
-      // out[t][rows] = sum_j g[t][j] y[t k + j][rows] (+ y[T k + t][rows]),
-      // in slot order then the shared expert, as the combine kernel sums
-      const int row0 = bx * DS::ROWS;
-      const int nrows = std::min(DS::ROWS, H - row0);
-      for (int q = tid; q < nm * nrows; q += 256) {
-        const int t = marked[q / nrows], row = row0 + q % nrows;
-        float acc = 0.f;
-        for (int jj = 0; jj < a.k; ++jj)
-          acc = fmaf(a.gates[t * a.k + jj], ld_coherent(a.y + (size_t)(t * a.k + jj) * H + row),
-                     acc);
-        if (a.S) acc = acc + ld_coherent(a.y + (size_t)(a.T * a.k + t) * H + row);
-        if (OUT_BF16)
-          reinterpret_cast<uint16_t*>(a.out)[(size_t)t * H + row] = (uint16_t)f32_to_bf16_bits(acc);
-        else
-          reinterpret_cast<float*>(a.out)[(size_t)t * H + row] = acc;
-      }
-    }
-    __syncthreads();  // LDS (h rows, marks) free for the next item
+    complete_rows<H, DS::ROWS, DS::ITEMS, OUT_BF16>(gd, bx, a.rtok, a.cmb, a.gates, a.y, a.T,
+                                                    a.k, a.S, a.out, marked, nmarked);
   }
 }
 

@@ -315,8 +315,10 @@ __device__ __forceinline__ void gate_up_item(const void* __restrict__ x, const B
 // HANDOFF (h produced by other workgroups of the same kernel): the weights
 // and scales are requested first and wait_h() is called before the group's
 // h rows are read (the caller waits there for h, with the weights in
-// flight); h is read and y stored at the point of coherence. Otherwise the
-// first pass's h rows are requested first and wait_h is not called.
+// flight); h is read at the point of coherence. Otherwise the first pass's
+// h rows are requested first and wait_h is not called. Y_COHERENT: y is
+// stored at the point of coherence (read by other workgroups of the same
+// kernel: the combine of complete_rows).
 template <int H, int I>
 struct DownShape {
   static constexpr int SPG = H / DownMap<I>::RW;  // slabs per group
@@ -328,7 +330,8 @@ struct NoWait {
   __device__ void operator()() const {}
 };
 
-template <int H, int I, int B, int NT, bool HANDOFF = false, class WaitH = NoWait>
+template <int H, int I, int B, int NT, bool HANDOFF = false, bool Y_COHERENT = HANDOFF,
+          class WaitH = NoWait>
 __device__ __forceinline__ void down_item(const BankPtrs& bk, const int4 gd, const int bx, int E,
                                           const float* __restrict__ h,
                                           const int32_t* __restrict__ pair,
@@ -411,7 +414,7 @@ __device__ __forceinline__ void down_item(const BankPtrs& bk, const int4 gd, con
         const float v = seg_sum<LPR>(acc[t]);
         if (sub == LPR - 1) {
           float* dst = y + (size_t)oslot[t] * H + row;
-          if (HANDOFF)
+          if (Y_COHERENT)
             st_coherent(dst, __builtin_ldexpf(v, hexp[t]));
           else
             *dst = __builtin_ldexpf(v, hexp[t]);
@@ -425,6 +428,59 @@ __device__ __forceinline__ void down_item(const BankPtrs& bk, const int4 gd, con
     lds_barrier();  // every wavefront is done with the previous pass
     put_scaled_rows(st, hs, hmax, hexp);
   }
+}
+
+// ---------------------------------------------------------- combine ---
+// The combine done by the down items themselves. After a down item (group
+// descriptor gd, slab group bx) has stored its y rows coherently, it adds
+// one to the count of (token, row block bx) for each of its tokens; the item
+// whose addition completes a count (k routed experts plus the shared one)
+// sums that token's rows of the block, in the combine kernel's order (slots
+// 0 .. k-1 by gate, then the shared expert with weight 1), and writes them
+// to out. No float atomics: every output is summed by one thread in a fixed
+// order, so results are the combine kernel's, bit for bit. The counts
+// (cmb, stride kCmbStride) must be zero before the first item adds to them.
+// Called by the whole workgroup; marked / nmarked: LDS of kGemvMaxTokens + 1
+// ints (free again when it returns).
+constexpr int kCmbStride = 16;  // int32 words between counters: 64 bytes
+
+template <int H, int ROWS, int ITEMS, bool OUT_BF16>
+__device__ __forceinline__ void complete_rows(const int4 gd, const int bx,
+                                              const int32_t* __restrict__ rtok,
+                                              int32_t* __restrict__ cmb,
+                                              const float* __restrict__ gates,
+                                              const float* __restrict__ y, int T, int k, int S,
+                                              void* __restrict__ out, int* marked,
+                                              int* nmarked) {
+  const int tid = threadIdx.x;
+  if (tid == 0) *nmarked = 0;
+  __builtin_amdgcn_s_waitcnt(0);  // this item's y stores are complete
+  __syncthreads();
+  const int need = k + S;
+  for (int r = tid; r < gd.z; r += blockDim.x) {
+    const int t = rtok[gd.y + r];
+    const int old = __hip_atomic_fetch_add(cmb + (size_t)(t * ITEMS + bx) * kCmbStride, 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == need - 1) marked[atomicAdd(nmarked, 1)] = t;
+  }
+  __syncthreads();
+  const int nm = *nmarked;
+  if (nm > 0) {
+    const int row0 = bx * ROWS;
+    const int nrows = H - row0 < ROWS ? H - row0 : ROWS;
+    for (int q = tid; q < nm * nrows; q += blockDim.x) {
+      const int t = marked[q / nrows], row = row0 + q % nrows;
+      float acc = 0.f;
+      for (int j = 0; j < k; ++j)
+        acc = fmaf(gates[t * k + j], ld_coherent(y + (size_t)(t * k + j) * H + row), acc);
+      if (S) acc = acc + ld_coherent(y + (size_t)(T * k + t) * H + row);
+      if (OUT_BF16)
+        reinterpret_cast<uint16_t*>(out)[(size_t)t * H + row] = (uint16_t)f32_to_bf16_bits(acc);
+      else
+        reinterpret_cast<float*>(out)[(size_t)t * H + row] = acc;
+    }
+  }
+  __syncthreads();
 }
 
 }  // namespace moe

@@ -25,6 +25,7 @@ struct Dims {
   bool mfma;     // expert family: grouped bf16 MFMA (true) or wavefront GEMV
   bool f8;       // grouped family with E4M3 operands in both expert contractions
   bool fused;    // GEMV family with the whole layer in one launch (decode_fused.hip)
+  bool fold_combine;  // decode GEMV path: the combine runs inside the down kernel
 };
 
 // Router kernels and partial logits. The router writes partial logits per
@@ -99,7 +100,8 @@ struct Work {
   uint8_t* hexps;    // [P][I/128] exponent bytes of h (grouped families)
   uint8_t* yexps;    // [P][H/128] exponent bytes of y (grouped families)
   int32_t* slotmap;  // [E+1] slot map of a streamed bank (moe_forward_streamed)
-  void* sync;        // single-launch decode layer: flags and counters (decode_fused.hip)
+  void* sync;        // single-launch decode layer: flags and counters (decode_fused.hip);
+                     // decode GEMV path: the combine's (token, row block) counters
   uint32_t* status;  // single-launch decode layer: error bits of its waits (0: none)
 };
 
@@ -150,13 +152,20 @@ struct KernelEvents {
 // slot (device, may be null): for a streamed bank, the slot of each routed
 // expert in `routed` (-1: skipped in this launch) and entry E: 0 when the
 // shared group runs in this launch, -1 when it is skipped
+// out (may be null): with d.fold_combine, the down kernel also combines into
+// out (no combine launch follows); null runs the down kernel alone.
 hipError_t launch_experts_gemv(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
-                               KernelEvents gate_up_events, const int32_t* slot = nullptr);
+                               KernelEvents gate_up_events, const int32_t* slot = nullptr,
+                               void* out = nullptr);
 hipError_t launch_experts_mfma(const Dims& d, const void* x, const moe_expert_bank& routed,
                                const moe_expert_bank* shared, const Work& w, hipStream_t s,
                                KernelEvents gate_up_events, const int32_t* slot = nullptr);
 bool has_gemv_instance(const Dims& d);
+// Decode GEMV path with the combine inside the down kernel: its (token, row
+// block) counters, zeroed by the selection kernel (bytes, 0 when unused).
+size_t fold_combine_bytes(const Dims& d);
+int gemv_down_items(const Dims& d);
 // The single-launch decode layer (decode_fused.hip): whether it covers d
 // (GEMV family, 1 <= T <= 16, decode router, E <= 512, a GEMV instance), the
 // bytes of its sync region (0 when it does not), and its launch. PERMUTED and

@@ -37,7 +37,7 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[15] = d.mfma ? (size_t)d.P * (d.I / 128) : 0;    // exponents of h
   sz[16] = d.mfma ? (size_t)d.P * (d.H / 128) : 0;    // exponents of y
   sz[17] = (size_t)(d.E + 1) * 4;                     // slot map of a streamed bank
-  sz[18] = d.fused ? fused_sync_bytes(d) : 0;         // single-launch decode: flags, counters
+  sz[18] = d.fused ? fused_sync_bytes(d) : fold_combine_bytes(d);  // flags and counters
   sz[19] = d.fused ? 16 : 0;  // single-launch decode: status word, then the give-up tag
 }
 
@@ -117,6 +117,14 @@ moe_status basic_dims(const moe_config* c, Dims* d) {
   // the single-launch decode layer only when asked for: the five-launch
   // GEMV path measures faster on MI355X at every decode size
   d->fused = c->path == MOE_PATH_GEMV_FUSED && fused_decode_ok(*d);
+  // the combine inside the down kernel: each item waits for its coherent y
+  // stores and counts its tokens, which lengthens every down workgroup by a
+  // few microseconds; that pays for the combine launch only while the down
+  // grid is one round of workgroups (measured: one token -1.0 us per step;
+  // c1 at 4 and 16 tokens +1.0 and +2.3 us, c3 at 8 tokens +6.4 us)
+  d->fold_combine = !d->mfma && !d->fused && d->T >= 1 && small_select_permute(*d) &&
+                    has_gemv_instance(*d) &&
+                    (std::min<int64_t>(d->E, d->T * d->k) + d->S) * gemv_down_items(*d) <= 1024;
   return MOE_OK;
 }
 
@@ -225,11 +233,14 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
   st = enqueue_routing(d, x, router_w, router_bias, w, events, s);
   if (st != MOE_OK) return st;
   const moe_expert_bank* sh = d.S ? shared : nullptr;
-  const hipError_t e = d.mfma ? launch_experts_mfma(d, x, *experts, sh, w, s, ev_gate_up)
-                              : launch_experts_gemv(d, x, *experts, sh, w, s, ev_gate_up);
+  const hipError_t e =
+      d.mfma ? launch_experts_mfma(d, x, *experts, sh, w, s, ev_gate_up)
+             : launch_experts_gemv(d, x, *experts, sh, w, s, ev_gate_up, nullptr,
+                                   d.fold_combine ? out : nullptr);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (!rec(events, MOE_EV_DOWN, s)) return MOE_ERR_HIP;
-  if (launch_combine(d, w, out, s) != hipSuccess) return MOE_ERR_HIP;
+  // (decode GEMV path: the down kernel has combined already)
+  if (!d.fold_combine && launch_combine(d, w, out, s) != hipSuccess) return MOE_ERR_HIP;
   if (!rec(events, MOE_EV_END, s)) return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -3,6 +3,7 @@
 // selects every token's experts and then permutes them.
 #include "layer.hpp"
 #include "permute.hpp"
+#include "gemv_body.hpp"
 #include "select.hpp"
 
 namespace moe {
@@ -28,8 +29,10 @@ __global__ __launch_bounds__(64 * kGemvMaxTokens) void select_permute_small(
     int E, int S, int32_t* __restrict__ topk, float* __restrict__ gates,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
     int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
-    int32_t* __restrict__ tiles, int tile_rows) {
+    int32_t* __restrict__ tiles, int tile_rows, int32_t* __restrict__ cmb, int ncmb) {
   static_assert(kGemvMaxTokens <= 32, "a token mask is one 32-bit word");
+  // the down kernel's combine counters (when it combines): zero for this call
+  for (int i = threadIdx.x; i < ncmb; i += blockDim.x) cmb[(size_t)i * kCmbStride] = 0;
   __shared__ uint32_t tmask[64 * NV];  // bit t: token t chose the expert
   __shared__ int32_t first[64 * NV];   // first row of each expert's group
   __shared__ int32_t routed_rows;
@@ -113,11 +116,13 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
   const int ns = router_slices(d);
   const int nv = (d.E + 63) / 64;
   const unsigned threads = (unsigned)(64 * d.T);
+  int32_t* cmb = d.fold_combine ? static_cast<int32_t*>(w.sync) : nullptr;
+  const int ncmb = d.fold_combine ? (int)d.T * gemv_down_items(d) : 0;
 #define MOE_SP(NV)                                                                             \
   select_permute_small<NV><<<1, threads, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk,  \
                                                  w.gates, w.offsets, w.pair, w.inv, w.rtok,   \
                                                  w.meta, reinterpret_cast<int4*>(w.gdesc),    \
-                                                 w.tiles, tile_rows)
+                                                 w.tiles, tile_rows, cmb, ncmb)
   if (nv <= 1)
     MOE_SP(1);
   else if (nv <= 2)
