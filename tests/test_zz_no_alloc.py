@@ -2,7 +2,9 @@
 a static device array inside the library): through the C ABI, on two calls in
 a row (the second with a smaller input), its outputs equal moe_forward's with
 a caller workspace bit for bit, on the decode (GEMV) and grouped (MFMA)
-families; a call too large for the array is refused before any launch."""
+families and the single-launch decode layer (whose flags, in the static
+array, must be left cleared by each call); a call too large for the array is
+refused before any launch."""
 import ctypes
 
 import numpy as np
@@ -24,7 +26,8 @@ def _static(layer, path):
 
 @pytest.mark.parametrize("name,tokens,path", [("c1", (16, 3), "auto"), ("c3", (8, 2), "auto"),
                                               ("c2", (512, 100), "mfma"),
-                                              ("c2", (300, 40), "mfma_fp8")])
+                                              ("c2", (300, 40), "mfma_fp8"),
+                                              ("c1", (16, 1), "gemv_fused")])
 def test_static_scratch_matches_workspace_path(name, tokens, path):
     import block_fp8_routed_amd as moe
     moe.load()
