@@ -22,8 +22,10 @@ namespace moe {
 //      per group: a group has at most 16 < tile_rows rows).
 //   3. the slot of token t's j-th choice e goes to row first[e] + (tokens
 //      below t in e's mask): rows keep ascending token order (stable).
-// Same results as topk_softmax + the multi-block permutation.
-template <int NV>
+// Same results as topk_softmax + the multi-block permutation. U: partial
+// logits requested together per expert (the slice count when it is 1, 4 or
+// 8, so that no request repeats a clamped slice).
+template <int NV, int U>
 __global__ __launch_bounds__(64 * kGemvMaxTokens) void select_permute_small(
     const float* __restrict__ plog, int slices, const float* __restrict__ bias, int64_t T, int k,
     int E, int S, int32_t* __restrict__ topk, float* __restrict__ gates,
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(64 * kGemvMaxTokens) void select_permute_small(
   const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;  // blockDim.x = 64 T
   for (int e = threadIdx.x; e < 64 * NV; e += blockDim.x) tmask[e] = 0u;
   __syncthreads();
-  const int my_e = select_token<NV>(plog, slices, bias, T, t, E, k, topk, gates, nullptr);
+  const int my_e = select_token<NV, U>(plog, slices, bias, T, t, E, k, topk, gates, nullptr);
   if (lane < k) atomicOr(&tmask[my_e], 1u << t);
   __syncthreads();
   if (t == 0) {
@@ -118,20 +120,32 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
   const unsigned threads = (unsigned)(64 * d.T);
   int32_t* cmb = d.fold_combine ? static_cast<int32_t*>(w.sync) : nullptr;
   const int ncmb = d.fold_combine ? (int)d.T * gemv_down_items(d) : 0;
-#define MOE_SP(NV)                                                                             \
-  select_permute_small<NV><<<1, threads, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S, w.topk,  \
-                                                 w.gates, w.offsets, w.pair, w.inv, w.rtok,   \
-                                                 w.meta, reinterpret_cast<int4*>(w.gdesc),    \
-                                                 w.tiles, tile_rows, cmb, ncmb)
-  if (nv <= 1)
+#define MOE_SPU(NV, U)                                                                        \
+  select_permute_small<NV, U><<<1, threads, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S,       \
+                                                    w.topk, w.gates, w.offsets, w.pair, w.inv, \
+                                                    w.rtok, w.meta,                            \
+                                                    reinterpret_cast<int4*>(w.gdesc), w.tiles, \
+                                                    tile_rows, cmb, ncmb)
+#define MOE_SP(NV)            \
+  if (ns == 1)                \
+    MOE_SPU(NV, 1);           \
+  else if (ns == 4)           \
+    MOE_SPU(NV, 4);           \
+  else if (ns == 8)           \
+    MOE_SPU(NV, 8);           \
+  else                        \
+    MOE_SPU(NV, NV <= 2 ? 16 : 8)
+  if (nv <= 1) {
     MOE_SP(1);
-  else if (nv <= 2)
+  } else if (nv <= 2) {
     MOE_SP(2);
-  else if (nv <= 4)
+  } else if (nv <= 4) {
     MOE_SP(4);
-  else
+  } else {
     MOE_SP(8);
+  }
 #undef MOE_SP
+#undef MOE_SPU
   return hipGetLastError();
 }
 
