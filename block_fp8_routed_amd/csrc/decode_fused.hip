@@ -32,9 +32,9 @@
 // the select workgroup and for other workers' gate/up items, so the host
 // sizes NW to fit on the device beside the select workgroup (from the
 // kernel's occupancy), and the routers, which exit without waiting, free
-// their slots for workers dispatched after them. Every wait is also bounded (kSpinLimit polls): past it the workgroup records an error
-// bit in the status word and goes on, so every wavefront exits whatever
-// happens. Flags hold a 64-bit epoch given by the host per call (never 0),
+// their slots for workers dispatched after them. Every wait is also bounded
+// (kSpinLimit polls): past it the workgroup records an error bit in the
+// status word and goes on, so every wavefront exits whatever happens. Flags hold a 64-bit epoch given by the host per call (never 0),
 // so stale or arbitrary workspace contents never satisfy a wait; every flag
 // is reset to 0 by its consumer within the call, so a captured launch
 // replayed with the same epoch also starts from cleared flags. Counters are
@@ -55,6 +55,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 
 #include "gemv_body.hpp"
 #include "permute.hpp"
@@ -372,7 +373,11 @@ __global__ __launch_bounds__(256) void decode_fused(const FusedArgs a) {
 }
 
 // ---------------------------------------------------------------- host ---
-static std::atomic<uint64_t> g_epoch{0};
+// Per-call epochs: a process-wide counter started from the clock, so that
+// flag words left by another process in reused device memory are not this
+// call's epoch either.
+static std::atomic<uint64_t> g_epoch{
+    (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
 
 template <int H, int I, int B>
 struct FusedItems {
