@@ -141,26 +141,30 @@ __device__ __forceinline__ void drop_far_blocks(float* row, int nkb) {
 // Tile row r at byte r * 512, 16-byte chunk c at slot c ^ f32_swz(r), so the
 // two row groups of one accumulator write land on different banks.
 __device__ __forceinline__ int f32_swz(int r) { return ((r >> 2) & 1) << 3; }
-__device__ __forceinline__ void put_f32(uint8_t* lds, int row, int col, float v) {
-  *reinterpret_cast<float*>(lds + row * 512 + 16 * ((col >> 2) ^ f32_swz(row)) + 4 * (col & 3)) = v;
+// (rp: the 512 bytes of tile row `row`)
+__device__ __forceinline__ void put_f32_row(uint8_t* rp, int row, int col, float v) {
+  *reinterpret_cast<float*>(rp + 16 * ((col >> 2) ^ f32_swz(row)) + 4 * (col & 3)) = v;
 }
-// Rows [0, valid) of an RA-row fp32 tile in LDS (as put_f32 leaves it) stored
-// as scaled fp16: 16 lanes (one DPP row) per tile row take 8 values each, a
+__device__ __forceinline__ void put_f32(uint8_t* lds, int row, int col, float v) {
+  put_f32_row(lds + row * 512, row, col, v);
+}
+// Rows [0, valid) of an RA-row fp32 tile in LDS (as put_f32 leaves it; row r
+// at rows(r)) stored as scaled fp16: 16 lanes (one DPP row) per tile row take 8 values each, a
 // DPP maximum gives the row's largest magnitude and f16_block_exponent its
 // power of two; dst(r) is the row's first fp16 element in global memory,
 // ebyte(r) where its exponent byte goes. `wave` is the (uniform) wavefront
 // index: the thread index is rebuilt from it and the lane id, which keeps
 // the loop before the epilogue from holding the thread index in a register.
-template <int RA, class Dst, class Eb>
-__device__ __forceinline__ void store_f16_rows(const uint8_t* lds, int valid, int wave, Dst dst,
-                                               Eb ebyte) {
+template <int RA, class Rows, class Dst, class Eb>
+__device__ __forceinline__ void store_f16_rows(Rows rows, int valid, int wave, Dst dst, Eb ebyte) {
   static_assert((RA * 16) % kPassThreadsDecl == 0, "tile rows per thread");
   const int tid = 64 * wave + (int)__lane_id();
 #pragma unroll
   for (int i = 0; i < RA * 16 / kPassThreadsDecl; ++i) {
     const int idx = tid + kPassThreadsDecl * i, r = idx >> 4, k = idx & 15;
-    const uint4 a = *reinterpret_cast<const uint4*>(lds + r * 512 + 16 * ((2 * k) ^ f32_swz(r)));
-    const uint4 b = *reinterpret_cast<const uint4*>(lds + r * 512 + 16 * ((2 * k + 1) ^ f32_swz(r)));
+    const uint8_t* rp = rows(r);
+    const uint4 a = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * k) ^ f32_swz(r)));
+    const uint4 b = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * k + 1) ^ f32_swz(r)));
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t mx = 0;
 #pragma unroll
@@ -308,10 +312,14 @@ struct PassIO {
 //     64 of them. A = fp16 h rows (a group's rows are contiguous); fp16 MFMA.
 // Two tile shapes, chosen per tile:
 //   full (more than 64 rows): wavefront (wm, wn) takes rows 64 wm .. + 63
-//     (two 32-row MFMA tiles). K runs in stages of 64 (half a scale block):
-//     a stage's A tile (128 rows) and B tile (256 x 64 bytes) are fetched
-//     global -> registers one stage ahead and written into the other of two
-//     LDS buffers after the current stage's MFMAs; one barrier per stage.
+//     (two 32-row MFMA tiles). K runs in stages of 64 (half a scale block),
+//     a stage's A tile (128 rows) and B tile (256 x 64 bytes) going through
+//     one of two LDS buffers, one stage ahead, one barrier per stage.
+//     gate/up (pass_tile_gu_dma) loads them straight from global memory
+//     into LDS (buffer_load ... lds), with no register round trip; down
+//     fetches them into registers and writes them to LDS after the current
+//     stage's MFMAs, bringing each h block to its row's common power of two
+//     on the way.
 //   thin (at most 64 rows, where the pass streams weights): rows 32 wm ..
 //     + 31 (one MFMA tile); the A tile has 64 rows. gate/up: K runs in
 //     stages of 128 (one scale block), so every weight row is read 128
@@ -420,10 +428,17 @@ template <bool GU, int H, int I, bool THIN>
 __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, const uint8_t* W,
                                           const float* ss, const int* arow, const int* orow,
                                           const uint32_t* hfac, const int* herow, const int* yq,
-                                          int valid, int r0, int n0, uint8_t* lds, PassIO io) {
+                                          int valid, int r0, int n0, uint8_t* lds, uint8_t* ldsb,
+                                          PassIO io) {
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
   using S = TileShape<GU, THIN>;
+  // full gate/up tiles take pass_tile_gu_dma; the thin gate/up stage's B
+  // tile goes to ldsb (its A tile to lds), the down pass's buffers are one
+  // block at lds
+  static_assert(!GU || THIN, "full gate/up tiles load through LDS-DMA");
+  static_assert(!GU || (S::ASTAGE <= kLdsBytes / 2 && S::BSTAGE <= kLdsBytes / 2 &&
+                        S::RA * 512 <= kLdsBytes / 2), "gate/up LDS halves");
   constexpr int K = P::K, KS = S::KS, NS = K / KS, AC = S::AC, BC = S::BC, MW = S::MW,
                 NBW = S::NBW, CA = S::CA, CB = S::CB;
   constexpr int NKB = K / kBK;
@@ -479,7 +494,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   };
   auto put = [&](Regs& R, int buf, int st) {
     uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
-    uint8_t* B = A + S::ASTAGE;
+    uint8_t* B = GU ? ldsb : A + S::ASTAGE;
     const int kb = st * KS / kBK;
     bool zero = false;
 #pragma unroll
@@ -558,7 +573,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
       }
     }
     const uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
-    const uint8_t* B = A + S::ASTAGE;
+    const uint8_t* B = GU ? ldsb : A + S::ASTAGE;
     // the stage's MFMAs run at raised wave priority, so that a wavefront
     // ready to compute issues ahead of those waiting on loads and barriers
     __builtin_amdgcn_s_setprio(1);
@@ -680,7 +695,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     __syncthreads();
     uint16_t* h = static_cast<uint16_t*>(io.out);
     store_f16_rows<S::RA>(
-        lds, valid, wave, [&](int r) { return h + (size_t)(r0 + r) * I + n0; },
+        [&](int r) { return lds + r * 512; }, valid, wave,
+        [&](int r) { return h + (size_t)(r0 + r) * I + n0; },
         [&](int r) { return io.oexps + (size_t)(r0 + r) * (I / kBK) + n0 / kBK; });
   } else {
     store_y_tile<S::RA, MW, H, true>(acc, unit, herow, yq, S::arow0(wm), wn, idle, valid, n0,
@@ -688,7 +704,187 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   }
 }
 
+// A full gate/up tile (more than 64 rows; shape and K order as pass_tile's
+// full tiles) whose stages go from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds): lane l of a wavefront's load writes its 16
+// bytes at the wavefront's LDS base + 16 l, so a load fills 1 KiB of LDS in
+// lane order and the swizzle is applied on the source side (the lane at
+// slot s of row r fetches chunk s ^ swz(r)). Stage st (64 k) goes to buffer
+// st % 2: its A tile (128 rows x 128 bytes) at offset 0, its B tile (256 rows
+// x 64 bytes: gate rows n0 .., then the matching up rows) at 16 KiB; each
+// wavefront issues two 1 KiB loads of each. The two buffers are separate
+// LDS objects, so the compiler sees that loads into one do not touch the
+// other while its fragments are read. Stage st + 1 is issued before stage
+// st's MFMAs; each wavefront waits for its own loads (vmcnt 0) before the
+// barrier that ends the stage, after which the whole stage is in LDS and
+// the buffer just read is free. A block of scale 0 has its B fragments
+// zeroed as they are read. The epilogue goes through the two buffers as one
+// fp32 tile (rows 0 .. 63 in the first).
+template <int H, int I>
+__device__ __forceinline__ void pass_tile_gu_dma(const uint16_t* __restrict__ act,
+                                                 const uint8_t* W, const float* ss,
+                                                 const int* arow, int valid, int r0, int n0,
+                                                 uint8_t* lds0, uint8_t* lds1, PassIO io) {
+  using O = Op<true>;
+  constexpr int K = H, KS = 64, NS = K / KS, NKB = K / kBK;
+  constexpr int ABYTES = kMfmaBM * KS * 2, BBYTES = kTN * KS;
+  static_assert(NS % 2 == 0 && kBK % KS == 0, "stages come in pairs and tile the scale blocks");
+  static_assert(ABYTES + BBYTES <= kLdsBytes / 2 && kMfmaBM * 512 <= kLdsBytes,
+                "stage and output tile fit the two LDS halves");
+  static_assert(ABYTES == 2 * 16 * kPassThreads && BBYTES == 2 * 16 * kPassThreads,
+                "two 16-byte loads per lane and tile");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+  const int wm = wave >> 2, wn = wave & 3;
+  const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(act, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(W, (uint32_t)(2 * I * K));
+  // load i of this lane fills LDS slot qq = tid + 512 i of the tile: A row
+  // qq / 8 (slot qq % 8), B tile row qq / 4 (slot qq % 4); tile B rows
+  // 0 .. 127 are gate rows n0 .., rows 128 .. 255 the up rows I + n0 ..
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int qq = tid + kPassThreads * i;
+    const int r = qq >> 3, c = (qq & 7) ^ ((r >> 1) & 7);
+    aoff[i] = (uint32_t)arow[r] * (K * 2) + 16 * c;
+    const int rb = qq >> 2, cb = (qq & 3) ^ ((rb >> 2) & 3);
+    const int wrow = rb < kTN / 2 ? n0 + rb : I + n0 + rb - kTN / 2;
+    boff[i] = (uint32_t)wrow * K + 16 * cb;
+  }
+  // load i of wavefront w fills bytes 16 (512 i + 64 w) .. + 1023 of its tile
+  constexpr int kLoadBytes = 16 * kPassThreads;  // LDS bytes of one load over the workgroup
+  auto issue = [&](uint8_t* buf, int st) {
+    st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never read
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, buf + kLoadBytes * i + 1024 * wave, 16,
+                                               aoff[i], (uint32_t)(st * KS * 2), 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, buf + ABYTES + kLoadBytes * i + 1024 * wave,
+                                               16, boff[i], (uint32_t)(st * KS), 0, 0);
+  };
+  // fragments (as pass_tile): A rows 64 wm + 32 m + lane % 32, B tile rows
+  // brow(nb) + lane % 32; row offsets are multiples of 32, so the swizzle of
+  // a fragment read depends on lane % 32 only
+  const int q = lane >> 5, l32 = lane & 31;
+  const int afr = (64 * wm + l32) * (KS * 2), asw = (l32 >> 1) & 7;
+  const int bfr = ABYTES + l32 * KS, bsw = (l32 >> 2) & 3;
+  auto brow = [&](int nb) { return nb == 0 ? 32 * wn : kTN / 2 + 32 * wn; };
+  const float* srow[2] = {ss, ss + NKB};  // gate block, up block
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[m][nb][v] = 0.f;
+  float unit[2] = {0.f, 0.f};  // scale the accumulators are expressed in
+  bool on[2] = {true, true};   // the current block's scale is not 0
+  auto compute = [&](const uint8_t* buf, int st) {
+    if ((st * KS) % kBK == 0) {  // entering scale block kb (as pass_tile)
+      const int kb = st * KS / kBK;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float sn = srow[nb][kb];
+        on[nb] = sn != 0.f;
+        const float r = on[nb] ? scale_ratio(unit[nb], sn) : 1.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[m][nb][v] *= r;
+        unit[nb] = on[nb] ? sn : unit[nb];
+      }
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int p = 0; p < KS / 32; ++p) {
+      uint4 braw[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        braw[nb] = *reinterpret_cast<const uint4*>(buf + bfr + brow(nb) * KS +
+                                                   16 * ((2 * p + q) ^ bsw));
+        if (!on[nb]) braw[nb] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        typename O::T bf[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          bf[nb] = hh ? O::cvt(braw[nb].z, braw[nb].w) : O::cvt(braw[nb].x, braw[nb].y);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint4 af = *reinterpret_cast<const uint4*>(buf + afr + 32 * m * (KS * 2) +
+                                                           16 * ((4 * p + 2 * q + hh) ^ asw));
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) acc[m][nb] = O::mma(af, bf[nb], acc[m][nb]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0) (lgkm and exp counts not waited on)
+  issue(lds0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < NS; st += 2) {
+    issue(lds1, st + 1);
+    compute(lds0, st);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    issue(lds0, st + 2);
+    compute(lds1, st + 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+  // epilogue (as pass_tile's): the fp32 tile, rows 0 .. 63 in lds0 and
+  // 64 .. 127 in lds1, then scaled fp16 rows
+  const int eln = (int)__lane_id(), eq = eln >> 5, el32 = eln & 31;
+  auto rows = [&](int r) { return (r < 64 ? lds0 : lds1) + (r & 63) * 512; };
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 64 * wm + 32 * m + 8 * (v >> 2) + 4 * eq + (v & 3);
+      put_f32_row(rows(row), row, brow(0) + el32,
+                  silu(acc[m][0][v] * unit[0]) * (acc[m][1][v] * unit[1]));
+    }
+  __syncthreads();
+  uint16_t* h = static_cast<uint16_t*>(io.out);
+  store_f16_rows<kMfmaBM>(
+      rows, valid, wave, [&](int r) { return h + (size_t)(r0 + r) * I + n0; },
+      [&](int r) { return io.oexps + (size_t)(r0 + r) * (I / kBK) + n0 / kBK; });
+}
+
 constexpr int kChunkTiles = 512;  // tile lists at least this long are dealt in chunks
+static_assert(kXcds == kXcdCount, "one XCD count");
+
+// The row tile of this workgroup (its column block is j % NCB), or -1 for a
+// slot without one. XCD-aware: workgroups are dispatched round-robin over
+// the XCDs (each with its own L2), so workgroup L runs on XCD L % 8, and XCD
+// x takes, for each of its tiles, all NCB column blocks in a row, so that a
+// tile's activation rows are fetched into one L2 and reused from it. On
+// long tile lists XCD x takes a contiguous chunk of tiles, so the row tiles
+// of a hot expert share few L2s; the permutation cuts the chunks at equal
+// cost (tile_cost), so every XCD gets a like share of the work. On short
+// ones it takes tiles x, x + 8, ... The launch gives every XCD
+// mfma_chunk_tiles slots (long lists can occur) or a round-robin share.
+template <int NCB>
+__device__ __forceinline__ int pass_tile_of(const int32_t* __restrict__ meta, int& j) {
+  const int xcd = blockIdx.x % kXcds;
+  j = blockIdx.x / kXcds;
+  // loaded together (clamped indices): no load waits for another
+  const int nt = meta[1];
+  const int lo = meta[kMetaXcdBounds + (xcd > 0 ? xcd - 1 : 0)];
+  const int hi = meta[kMetaXcdBounds + (xcd < kXcds - 1 ? xcd : 0)];
+  if (nt >= kChunkTiles) {
+    const int t = (xcd > 0 ? lo : 0) + j / NCB;
+    return t < (xcd < kXcds - 1 ? hi : nt) ? t : -1;
+  }
+  const int t = (j / NCB) * kXcds + xcd;
+  return t < nt ? t : -1;
+}
 
 template <bool GU, int H, int I>
 __global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
@@ -702,7 +898,9 @@ void mfma_pass(const uint16_t* __restrict__ act,
                                                         PassIO io) {
   using P = PassShape<GU, H, I>;
   static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  // stage buffers: gate/up two separate halves (pass_tile_gu_dma), down one block
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GU ? kLdsBytes / 2 : kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb[GU ? kLdsBytes / 2 : 16];
   __shared__ int arow[kMfmaBM];
   __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
   constexpr int NKB = P::K / kBK;  // scale blocks along K
@@ -711,19 +909,10 @@ void mfma_pass(const uint16_t* __restrict__ act,
   __shared__ uint32_t hfac[GU ? 1 : kMfmaBM * NKB];
   __shared__ int herow[GU ? 1 : kMfmaBM];
   __shared__ int yq[2];  // down: the two output column blocks' bound exponents
-  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
-  // (each with its own L2), so workgroup L runs on XCD L % 8. XCD x takes row
-  // tiles x, x + 8, ... and, for each, all NCB column blocks in a row, so a
-  // tile's activation rows are fetched into one L2 and reused from it.
   constexpr int NCB = P::NOUT / P::COLS;
-  // XCD-aware (workgroups go round-robin over the XCDs): on long tile lists
-  // XCD x takes a contiguous chunk of tiles, so the row tiles of a hot expert
-  // share few L2s; on short ones it takes tiles x, x + 8, ...
-  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds, nt = meta[1];
-  const int chunk = (nt + kXcds - 1) / kXcds;
-  const bool chunked = nt >= kChunkTiles;
-  const int tile = chunked ? xcd * chunk + j / NCB : (j / NCB) * kXcds + xcd;
-  if ((chunked && j / NCB >= chunk) || tile >= nt) return;
+  int j;
+  const int tile = pass_tile_of<NCB>(meta, j);
+  if (tile < 0) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
   const int tid = threadIdx.x;
@@ -781,9 +970,13 @@ void mfma_pass(const uint16_t* __restrict__ act,
   if (tid < 2) drop_far_blocks(ss + tid * NKB, NKB);
   __syncthreads();
   if (valid <= 64)
-    pass_tile<GU, H, I, true>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, io);
+    pass_tile<GU, H, I, true>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, ldsb,
+                              io);
+  else if constexpr (GU)
+    pass_tile_gu_dma<H, I>(act, W, ss, arow, valid, r0, n0, lds, ldsb, io);
   else
-    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, io);
+    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, ldsb,
+                               io);
 }
 
 // ---------------------------------------------------------------------------
@@ -1089,12 +1282,9 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   __shared__ uint8_t sx[kMfmaBM * NKB];   // the tile rows' A exponents
   __shared__ int rowg[GU ? 1 : kMfmaBM];  // down: each row's largest h exponent
   __shared__ int yq[2];                   // down: the output column blocks' bound exponents
-  // XCD-aware, as mfma_pass
-  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds, nt = meta[1];
-  const int chunk = (nt + kXcds - 1) / kXcds;
-  const bool chunked = nt >= kChunkTiles;
-  const int tile = chunked ? xcd * chunk + j / NCB : (j / NCB) * kXcds + xcd;
-  if ((chunked && j / NCB >= chunk) || tile >= nt) return;
+  int j;  // XCD-aware, as mfma_pass
+  const int tile = pass_tile_of<NCB>(meta, j);
+  if (tile < 0) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
   const int tid = threadIdx.x;
@@ -1157,8 +1347,11 @@ template <int H, int I, int B>
 static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Work& w,
                      hipStream_t s, KernelEvents ev) {
   static_assert(B == kBK, "MFMA passes take 128 x 128 scale blocks");
-  // tile slots rounded up to whole rounds of the XCDs (extra slots exit)
-  const unsigned nt8 = (unsigned)((max_mfma_tiles(d) + kXcds - 1) / kXcds * kXcds);
+  // tile slots: every XCD gets the longest chunk it can be dealt (long tile
+  // lists) or its round-robin share; slots without a tile exit
+  const int64_t mt = max_mfma_tiles(d);
+  const unsigned nt8 =
+      (unsigned)(kXcds * (mt >= kChunkTiles ? mfma_chunk_tiles(d) : (mt + kXcds - 1) / kXcds));
   const dim3 grid(nt8 * (I / PassShape<true, H, I>::COLS));
   const uint16_t* xa = reinterpret_cast<const uint16_t*>(x);
   const int32_t *meta = w.meta, *tiles = w.tiles, *offsets = w.offsets, *rtok = w.rtok,

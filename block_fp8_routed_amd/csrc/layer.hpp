@@ -73,6 +73,20 @@ inline int router_slices(const Dims& d) {
 }
 
 constexpr int kMetaPermCounter = 9;    // multi-block permutation's completion counter
+// meta[kMetaXcdBounds + x - 1], x = 1 .. kXcdCount - 1: first MFMA row tile of
+// XCD x's contiguous range when the tile list is dealt in chunks (XCD 0
+// starts at tile 0, the last range ends at meta[1])
+constexpr int kMetaXcdBounds = 2;
+constexpr int kXcdCount = 8;           // accelerator complex dies (one L2 each)
+static_assert(kMetaXcdBounds + kXcdCount - 1 <= kMetaPermCounter, "meta layout");
+// Relative cost of a row tile when the chunks are cut: a thin tile (at most
+// kMfmaBM / 2 rows) reads the same weights as a full one with half its MFMA
+// work. Every range then holds less than C / (8 kTileCostThin) + 1 tiles, C
+// the list's total cost (mfma_chunk_tiles).
+constexpr int kTileCostFull = 3, kTileCostThin = 2;
+__host__ __device__ constexpr int tile_cost(int rows) {
+  return rows > kMfmaBM / 2 ? kTileCostFull : kTileCostThin;
+}
 constexpr int kPermMaxBlocksHost = 16; // blocks of the multi-block permutation (at most)
 
 // Carved workspace. Every region is kAlign-aligned.
@@ -107,6 +121,12 @@ struct Work {
 
 inline int64_t max_mfma_tiles(const Dims& d) {
   return d.P / kMfmaBM + d.E + d.S + 1;
+}
+// tile slots per XCD that cover the longest cost-balanced chunk of any tile
+// list of this problem (at most max_mfma_tiles tiles, each of cost at most
+// kTileCostFull and at least kTileCostThin)
+inline int64_t mfma_chunk_tiles(const Dims& d) {
+  return max_mfma_tiles(d) * kTileCostFull / (kXcdCount * kTileCostThin) + 1;
 }
 
 // Validation shared by the entry points (host only, no HIP call).

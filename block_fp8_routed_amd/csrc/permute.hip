@@ -87,6 +87,9 @@ __global__ __launch_bounds__(64 * kGemvMaxTokens) void select_permute_small(
       }
       meta[0] = nact + S;
       meta[1] = tile_rows > 0 ? nact + S : 0;
+      // XCD chunks of the tile list (every tile here is thin: equal counts)
+      const int ntl = tile_rows > 0 ? nact + S : 0;
+      for (int x = 1; x < kXcdCount; ++x) meta[kMetaXcdBounds + x - 1] = x * ntl / kXcdCount;
       routed_rows = total;
     }
     for (int y = nact + S + lane; y < E + 2; y += 64) gdesc[y] = make_int4(-1, 0, 0, 0);
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(1024) void perm_count(
     int32_t* __restrict__ meta, int4* __restrict__ gdesc, int32_t* __restrict__ tiles,
     int tile_rows) {
   __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t tmp[3 * 64];
+  __shared__ int32_t tmp[4 * 64];
   __shared__ int last;
   const int tid = threadIdx.x;
   const int64_t TK = T * k;
@@ -235,10 +238,12 @@ __global__ __launch_bounds__(1024) void perm_count(
   // non-empty groups and MFMA row tiles, ascending expert, shared last
   const int nf = (e < E && c > 0) ? 1 : 0;
   const int nt = (e < E && tile_rows > 0) ? (c + tile_rows - 1) / tile_rows : 0;
-  const int sv[3] = {c, nf, nt};
-  int sx[3], st[3];
-  block_excl_scan<16, 3>(sv, sx, st, tmp);
-  const int off = sx[0], apos = sx[1], tpos = sx[2];
+  // the tiles' cost (all but the last are full)
+  const int cost = nt > 0 ? (nt - 1) * kTileCostFull + tile_cost(c - (nt - 1) * tile_rows) : 0;
+  const int sv[4] = {c, nf, nt, cost};
+  int sx[4], st[4];
+  block_excl_scan<16, 4>(sv, sx, st, tmp);
+  const int off = sx[0], apos = sx[1], tpos = sx[2], pcost = sx[3];
   const int total = st[0], nact = st[1], ntile = st[2];
   if (e < E) {
     offsets[e] = off;
@@ -262,6 +267,33 @@ __global__ __launch_bounds__(1024) void perm_count(
       tiles[2 * (ntile + i)] = E;
       tiles[2 * (ntile + i) + 1] = (int)(total + (int64_t)i * tile_rows);
     }
+  }
+  // Cost-balanced chunks of the tile list, one per XCD: chunk x starts at
+  // the first tile t with 8 * (cost of the tiles before t) >= x * C. The
+  // prefix cost is a step function of the tile index; the target of chunk x
+  // lies in exactly one group's cost interval (8 pc, 8 (pc + cost)] (the
+  // shared group's last), and that group's thread (thread 0 for the shared
+  // group) places the start among its tiles.
+  const int64_t shared_cost =
+      nshared_tiles > 0 ? (int64_t)(nshared_tiles - 1) * kTileCostFull +
+                              tile_cost((int)(T - (int64_t)(nshared_tiles - 1) * tile_rows))
+                        : 0;
+  const int64_t C = (int64_t)st[3] + shared_cost;
+  auto place = [&](int64_t X, int64_t pc, int64_t cst, int n, int first, int x) {
+    // X = x * C in (8 pc, 8 (pc + cst)]: smallest m in [1, n] with
+    // 8 (cost of the group's first m tiles) >= X
+    if (X <= 8 * pc || X > 8 * (pc + cst)) return;
+    int64_t m = (X - 8 * pc + 8 * kTileCostFull - 1) / (8 * kTileCostFull);
+    if (m > n) m = n;
+    meta[kMetaXcdBounds + x - 1] = first + (int)m;
+  };
+  for (int x = 1; x < kXcdCount; ++x) {
+    if (C == 0) {
+      if (tid == 0) meta[kMetaXcdBounds + x - 1] = 0;
+      continue;
+    }
+    place((int64_t)x * C, pcost, cost, nt, tpos, x);
+    if (tid == 0) place((int64_t)x * C, st[3], shared_cost, nshared_tiles, ntile, x);
   }
   if (tid == 0) {
     if (S) gdesc[nact] = make_int4(E, total, (int)T, 0);
