@@ -226,20 +226,19 @@ __device__ __forceinline__ int y_block_q(const float* srow, int nkb, float coef)
 }
 __device__ __forceinline__ int clamp_exp(int e) { return e < -127 ? -127 : (e > 127 ? 127 : e); }
 
-// The down tile's fp16 y through LDS (a row-major tile of 256 fp16 columns,
-// 16-byte chunk c of row r at slot c ^ oswz(r)), every row then stored as
+// The down tile's fp16 y through LDS (a tile of 256 fp16 columns, row r at
+// rows(r), 16-byte chunk c at slot c ^ oswz(r)), every row then stored as
 // whole 16-byte chunks by slot (orow), with the exponent bytes. acc holds
 // the wavefront's MW x 2 MFMA tiles; value (row, block b) is stored as
 // acc * unit[nb] * 2^(G(row) - ey), ey = clamp(g(row) + q(b)), where G is
 // the power of two acc is expressed in (the bf16 pass: g; FP8: 0).
-template <int RA, int MW, int H, bool GISG>
+template <int RA, int MW, int H, bool GISG, class Rows>
 __device__ __forceinline__ void store_y_tile(const f32x16_t (&acc)[MW][2], const float* unit,
                                              const int* rowg, const int* yq, int arow0, int wn,
                                              bool idle, int valid, int n0, const int* orow,
-                                             int wave, uint8_t* lds, uint16_t* y,
+                                             int wave, Rows rows, uint16_t* y,
                                              uint8_t* yexps) {
   constexpr int ORB = 256 * 2, OCH = ORB / 16;
-  static_assert(RA * ORB <= 65536, "output tile exceeds the LDS block");
   auto oswz = [](int r) { return ((r & 1) | (((r >> 2) & 1) << 1)) << 2; };
   const int ln = (int)__lane_id(), q = ln >> 5, l32 = ln & 31;
   const bool odd = l32 & 1;
@@ -265,7 +264,7 @@ __device__ __forceinline__ void store_y_tile(const f32x16_t (&acc)[MW][2], const
           const int r = row + (odd ? 1 : 0);
           const int col = col0 + l32 - (odd ? 1 : 0);
           const uint32_t word = odd ? (recv | (c << 16)) : (a | (recv << 16));
-          *reinterpret_cast<uint32_t*>(lds + r * ORB + 16 * (((2 * col) >> 4) ^ oswz(r)) +
+          *reinterpret_cast<uint32_t*>(rows(r) + 16 * (((2 * col) >> 4) ^ oswz(r)) +
                                        ((2 * col) & 15)) = word;
         }
       }
@@ -277,7 +276,7 @@ __device__ __forceinline__ void store_y_tile(const f32x16_t (&acc)[MW][2], const
   for (int i = 0; i < RA * OCH / kPassThreadsDecl; ++i) {
     const int idx = tid + kPassThreadsDecl * i, r = idx / OCH, c = idx % OCH;
     if (r >= valid) continue;
-    const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ORB + 16 * (c ^ oswz(r)));
+    const uint4 val = *reinterpret_cast<const uint4*>(rows(r) + 16 * (c ^ oswz(r)));
     *reinterpret_cast<uint4*>(y + (size_t)orow[r] * H + n0 + 8 * c) = val;
   }
   if (tid < 2 * RA) {
@@ -433,12 +432,16 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
   using P = PassShape<GU, H, I>;
   using O = Op<GU>;
   using S = TileShape<GU, THIN>;
-  // full gate/up tiles take pass_tile_gu_dma; the thin gate/up stage's B
-  // tile goes to ldsb (its A tile to lds), the down pass's buffers are one
-  // block at lds
-  static_assert(!GU || THIN, "full gate/up tiles load through LDS-DMA");
-  static_assert(!GU || (S::ASTAGE <= kLdsBytes / 2 && S::BSTAGE <= kLdsBytes / 2 &&
-                        S::RA * 512 <= kLdsBytes / 2), "gate/up LDS halves");
+  // LDS: two separate halves, lds and ldsb. Full tiles take
+  // pass_tile_gu_dma / pass_tile_down_dma; the thin gate/up stage (one
+  // buffer) has its A tile in lds and its B tile in ldsb; the thin down
+  // pass's stage buffer b is lds (b = 0) or ldsb (b = 1), A then B.
+  static_assert(THIN, "full tiles load their B tiles through LDS-DMA");
+  static_assert(GU ? (S::ASTAGE <= kLdsBytes / 2 && S::BSTAGE <= kLdsBytes / 2)
+                   : S::ASTAGE + S::BSTAGE <= kLdsBytes / 2, "stage buffers fit the LDS halves");
+  static_assert(S::RA * 512 <= kLdsBytes / 2, "output tile fits one LDS half");
+  auto abuf = [&](int buf) -> uint8_t* { return GU || buf == 0 ? lds : ldsb; };
+  auto bbuf = [&](int buf) -> uint8_t* { return GU ? ldsb : abuf(buf) + S::ASTAGE; };
   constexpr int K = P::K, KS = S::KS, NS = K / KS, AC = S::AC, BC = S::BC, MW = S::MW,
                 NBW = S::NBW, CA = S::CA, CB = S::CB;
   constexpr int NKB = K / kBK;
@@ -493,8 +496,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
                                                           (uint32_t)(brow_of(i) * K + st * KS));
   };
   auto put = [&](Regs& R, int buf, int st) {
-    uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
-    uint8_t* B = GU ? ldsb : A + S::ASTAGE;
+    uint8_t* A = abuf(buf);
+    uint8_t* B = bbuf(buf);
     const int kb = st * KS / kBK;
     bool zero = false;
 #pragma unroll
@@ -572,8 +575,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         unit[nb] = on ? sn : unit[nb];
       }
     }
-    const uint8_t* A = lds + buf * (S::ASTAGE + S::BSTAGE);
-    const uint8_t* B = GU ? ldsb : A + S::ASTAGE;
+    const uint8_t* A = abuf(buf);
+    const uint8_t* B = bbuf(buf);
     // the stage's MFMAs run at raised wave priority, so that a wavefront
     // ready to compute issues ahead of those waiting on loads and barriers
     __builtin_amdgcn_s_setprio(1);
@@ -602,24 +605,7 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
     __builtin_amdgcn_s_setprio(0);
   };
 
-  if (S::DEPTH == 1) {
-    // two LDS buffers, one stage fetched ahead, one barrier per stage
-    static_assert(NS % 2 == 0, "stages come in pairs");
-    Regs R;
-    fetch(R, 0);
-    put(R, 0, 0);
-    __syncthreads();
-    for (int st = 0; st < NS; st += 2) {
-      fetch(R, st + 1);
-      compute(0, st);
-      put(R, 1, st + 1);
-      __syncthreads();
-      fetch(R, st + 2);
-      compute(1, st + 1);
-      if (st + 2 < NS) put(R, 0, st + 2);
-      __syncthreads();
-    }
-  } else if (S::BUFS == 2) {
+  if (S::BUFS == 2) {
     // two LDS buffers and a ring of DEPTH register sets: while stage st is
     // computed, stages st + 1 .. st + DEPTH are in flight (stage s lives in
     // set s % DEPTH); the loop is unrolled by DEPTH so the sets are fixed
@@ -700,7 +686,8 @@ __device__ __forceinline__ void pass_tile(const uint16_t* __restrict__ act, cons
         [&](int r) { return io.oexps + (size_t)(r0 + r) * (I / kBK) + n0 / kBK; });
   } else {
     store_y_tile<S::RA, MW, H, true>(acc, unit, herow, yq, S::arow0(wm), wn, idle, valid, n0,
-                                     orow, wave, lds, static_cast<uint16_t*>(io.out), io.oexps);
+                                     orow, wave, [&](int r) { return lds + r * 512; },
+                                     static_cast<uint16_t*>(io.out), io.oexps);
   }
 }
 
@@ -857,6 +844,149 @@ __device__ __forceinline__ void pass_tile_gu_dma(const uint16_t* __restrict__ ac
       [&](int r) { return io.oexps + (size_t)(r0 + r) * (I / kBK) + n0 / kBK; });
 }
 
+// A full down tile (more than 64 rows; shape and K order as pass_tile's full
+// tiles, K = I): B tiles (256 weight rows x 64 bytes per stage) go straight
+// into LDS as in pass_tile_gu_dma; A tiles (h rows, fp16) go through
+// registers, where each h block is brought to its row's common power of two
+// (rescale words in hfac) before it is written to LDS. Stage st uses buffer
+// st % 2 (lds or ldsb: A at offset 0, B at 16 KiB). A block of scale 0 has
+// its B fragments zeroed as they are read.
+template <int H, int I>
+__device__ __forceinline__ void pass_tile_down_dma(const uint16_t* __restrict__ act,
+                                                   const uint8_t* W, const float* ss,
+                                                   const int* arow, const int* orow,
+                                                   const uint32_t* hfac, const int* herow,
+                                                   const int* yq, int valid, int r0, int n0,
+                                                   uint8_t* lds0, uint8_t* lds1, PassIO io) {
+  using O = Op<false>;
+  constexpr int K = I, KS = 64, NS = K / KS, NKB = K / kBK;
+  constexpr int ABYTES = kMfmaBM * KS * 2, BBYTES = kTN * KS;
+  static_assert(NS % 2 == 0 && kBK % KS == 0, "stages come in pairs and tile the scale blocks");
+  static_assert(ABYTES + BBYTES <= kLdsBytes / 2 && kMfmaBM * 512 <= kLdsBytes,
+                "stage and output tile fit the two LDS halves");
+  static_assert(ABYTES == 2 * 16 * kPassThreads && BBYTES == 2 * 16 * kPassThreads,
+                "two 16-byte chunks per lane and tile");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+  const int wm = wave >> 2, wn = wave & 3;
+  const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(act, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(W, (uint32_t)(H * K));
+  // A: chunk i of this thread is tile row ar0 + 64 i (8 chunks of 16 bytes
+  // per row and stage), written at its swizzled slot; moving the row by 64
+  // leaves the swizzle alone. B: load i fills tile slot qq = tid + 512 i
+  // (weight row n0 + qq / 4, slot qq % 4), as pass_tile_gu_dma.
+  const int ar0 = tid >> 3, ac0 = tid & 7;
+  const int adst0 = ar0 * (KS * 2) + 16 * (ac0 ^ ((ar0 >> 1) & 7));
+  uint32_t asrc[2], boff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    asrc[i] = (uint32_t)arow[ar0 + 64 * i] * (K * 2) + 16 * ac0;
+    const int qq = tid + kPassThreads * i;
+    const int rb = qq >> 2, cb = (qq & 3) ^ ((rb >> 2) & 3);
+    boff[i] = (uint32_t)(n0 + rb) * K + 16 * cb;
+  }
+  constexpr int kLoadBytes = 16 * kPassThreads;  // LDS bytes of one load over the workgroup
+  uint4 ra[2];
+  auto fetch = [&](uint8_t* buf, int st) {  // A into registers, B into buf
+    st = st < NS ? st : NS - 1;  // past the end: a harmless repeat, never read
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ra[i] = buffer_ld16(arsrc, asrc[i], (uint32_t)(st * KS * 2));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, buf + ABYTES + kLoadBytes * i + 1024 * wave,
+                                               16, boff[i], (uint32_t)(st * KS), 0, 0);
+  };
+  auto put = [&](uint8_t* buf, int st) {  // A to LDS, each h block to its row's power of two
+    st = st < NS ? st : NS - 1;  // as fetch
+    const int kb = st * KS / kBK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(buf + adst0 + 64 * (KS * 2) * i) =
+          rescale_f16x8(ra[i], hfac[(ar0 + 64 * i) * NKB + kb]);
+  };
+  const int q = lane >> 5, l32 = lane & 31;
+  const int afr = (64 * wm + l32) * (KS * 2), asw = (l32 >> 1) & 7;
+  const int bfr = ABYTES + l32 * KS, bsw = (l32 >> 2) & 3;
+  auto brow = [&](int nb) { return 64 * wn + 32 * nb; };
+  const float* srow[2] = {ss + (brow(0) / kBK) * NKB, ss + (brow(1) / kBK) * NKB};
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[m][nb][v] = 0.f;
+  float unit[2] = {0.f, 0.f};
+  bool on[2] = {true, true};
+  auto compute = [&](const uint8_t* buf, int st) {
+    if ((st * KS) % kBK == 0) {  // entering scale block kb (as pass_tile)
+      const int kb = st * KS / kBK;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float sn = srow[nb][kb];
+        on[nb] = sn != 0.f;
+        const float r = on[nb] ? scale_ratio(unit[nb], sn) : 1.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[m][nb][v] *= r;
+        unit[nb] = on[nb] ? sn : unit[nb];
+      }
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int p = 0; p < KS / 32; ++p) {
+      uint4 braw[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        braw[nb] = *reinterpret_cast<const uint4*>(buf + bfr + brow(nb) * KS +
+                                                   16 * ((2 * p + q) ^ bsw));
+        if (!on[nb]) braw[nb] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        typename O::T bf[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          bf[nb] = hh ? O::cvt(braw[nb].z, braw[nb].w) : O::cvt(braw[nb].x, braw[nb].y);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint4 af = *reinterpret_cast<const uint4*>(buf + afr + 32 * m * (KS * 2) +
+                                                           16 * ((4 * p + 2 * q + hh) ^ asw));
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) acc[m][nb] = O::mma(af, bf[nb], acc[m][nb]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // each wavefront waits for its own loads (vmcnt 0; the A loads are also
+  // waited for by the LDS writes) before the barrier that ends the stage
+  // before theirs
+  constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0)
+  fetch(lds0, 0);
+  put(lds0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < NS; st += 2) {
+    fetch(lds1, st + 1);
+    compute(lds0, st);
+    put(lds1, st + 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    fetch(lds0, st + 2);
+    compute(lds1, st + 1);
+    put(lds0, st + 2);  // past the end: a repeat, never read
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+  store_y_tile<kMfmaBM, 2, H, true>(
+      acc, unit, herow, yq, 64 * wm, wn, false, valid, n0, orow, wave,
+      [&](int r) { return (r < 64 ? lds0 : lds1) + (r & 63) * 512; },
+      static_cast<uint16_t*>(io.out), io.oexps);
+}
+
 constexpr int kChunkTiles = 512;  // tile lists at least this long are dealt in chunks
 static_assert(kXcds == kXcdCount, "one XCD count");
 
@@ -898,9 +1028,10 @@ void mfma_pass(const uint16_t* __restrict__ act,
                                                         PassIO io) {
   using P = PassShape<GU, H, I>;
   static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
-  // stage buffers: gate/up two separate halves (pass_tile_gu_dma), down one block
-  __shared__ __attribute__((aligned(16))) uint8_t lds[GU ? kLdsBytes / 2 : kLdsBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t ldsb[GU ? kLdsBytes / 2 : 16];
+  // stage buffers and the output tile: two separate LDS halves, so that the
+  // compiler sees that loads into one leave the other alone
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb[kLdsBytes / 2];
   __shared__ int arow[kMfmaBM];
   __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
   constexpr int NKB = P::K / kBK;  // scale blocks along K
@@ -975,8 +1106,8 @@ void mfma_pass(const uint16_t* __restrict__ act,
   else if constexpr (GU)
     pass_tile_gu_dma<H, I>(act, W, ss, arow, valid, r0, n0, lds, ldsb, io);
   else
-    pass_tile<GU, H, I, false>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, ldsb,
-                               io);
+    pass_tile_down_dma<H, I>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, ldsb,
+                             io);
 }
 
 // ---------------------------------------------------------------------------
@@ -1261,8 +1392,10 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
   } else {
     // y as scaled fp16 by slot (acc is y itself: the h exponents ride in the
     // instruction), as in the bf16 down pass
+    static_assert(S::RA * 512 <= kLdsBytes, "output tile exceeds the LDS block");
     store_y_tile<S::RA, MW, H, false>(acc, unit, rowg, yq, S::arow0(wm), wn, idle, valid, n0,
-                                      orow, wave, lds, out.y, out.yexps);
+                                      orow, wave, [&](int r) { return lds + r * 512; }, out.y,
+                                      out.yexps);
   }
 }
 
