@@ -89,17 +89,33 @@ __device__ __forceinline__ int select_token(const float* __restrict__ plog, int 
     for (int i = 1; i < NV; ++i) lm = max(lm, key[i]);
     const uint32_t m = wave_max_u32(lm);
     if (j == 0) first = m;
-    // the lowest expert index holding the maximum: experts 64 i + lane, so
-    // the first row i with a holder, then its lowest lane
+    // the lowest expert index holding the maximum (the lane's experts are
+    // 64 i + lane). Up to two experts per lane: the first row i with a
+    // holder (a ballot per row), then its lowest lane. More: each lane
+    // offers its lowest holder and a second reduction takes the minimum, as
+    // the maximum of the complements (a lane with none offers ~0, which
+    // complements to the maximum's neutral 0); a walk over eight or more
+    // rows costs more in scalar branches than the reduction. Only valid
+    // experts hold m, since every logit's key is above zero.
     int win = -1;
+    if constexpr (NV <= 2) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const unsigned long long b = __ballot(key[i] == m);
-      if (win < 0 && b != 0ull) {
-        const int wl = __ffsll((long long)b) - 1;
-        win = 64 * i + wl;
-        if (lane == wl) key[i] = 0u;
+      for (int i = 0; i < NV; ++i) {
+        const unsigned long long b = __ballot(key[i] == m);
+        if (win < 0 && b != 0ull) {
+          const int wl = __ffsll((long long)b) - 1;
+          win = 64 * i + wl;
+          if (lane == wl) key[i] = 0u;
+        }
       }
+    } else {
+      uint32_t loc = 0xffffffffu;
+#pragma unroll
+      for (int i = NV - 1; i >= 0; --i) loc = key[i] == m ? (uint32_t)(64 * i + lane) : loc;
+      win = (int)~wave_max_u32(~loc);
+      const bool owner = lane == (win & 63);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) key[i] = owner && i == (win >> 6) ? 0u : key[i];
     }
     if (lane == j) {
       mine = m;
