@@ -146,7 +146,10 @@ KERNEL_SOURCES = {
     "mfma": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
     "mfma_fp8": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
 }
-KERNEL_MATCH = {"gemv": "gemv_gate_up<", "gemv_fused": "decode_fused<", "mfma": "mfma_pass<true",
+# the dominant kernel of each path: the gate/up kernel, or the launch that
+# holds it (the decode layer's single launch; the grouped bf16 path's
+# gate/up + down launch)
+KERNEL_MATCH = {"gemv": "gemv_gate_up<", "gemv_fused": "decode_fused<", "mfma": "mfma_layer<",
                 "mfma_fp8": "mfma_pass_f8<true"}
 COPY_MATCH = "MulFunctor"  # the copy kernel of --copy-calibration (dst = src * 1)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -465,8 +468,10 @@ def main():
     f8 = args.path == "mfma_fp8"
     mfma = args.path in ("mfma", "mfma_fp8") or (args.path == "auto" and xdt == torch.bfloat16
                                                  and T > 16)
-    # the single-launch decode layer has a status region; the other paths none
-    fused = moe.workspace_region(cfg, moe.MOE_WS_STATUS)[1] > 0
+    # the single-launch decode layer has a status region (so has the grouped
+    # bf16 path, whose gate/up and down passes share one launch)
+    fused = not mfma and moe.workspace_region(cfg, moe.MOE_WS_STATUS)[1] > 0
+    one_launch = mfma and not f8
     family_key = "mfma_fp8" if f8 else "mfma" if mfma else "gemv_fused" if fused else "gemv"
 
     # routing of each batch: which experts a step touches (outside the timed region)
@@ -556,12 +561,14 @@ def main():
         for j, n in enumerate(phase):
             phase[n].append(hip.elapsed_ms(evs[j], evs[j + 1]) * 1e3)
     phases_us = {n: round(sorted(v)[len(v) // 2], 2) for n, v in phase.items() if v}
+    if one_launch and phases_us:  # the gate/up kernel's events span both passes
+        phases_us["gate_up+down"] = round(phases_us.pop("gate_up") + phases_us.pop("down"), 2)
 
     tokens_per_s = T / (ms / 1e3)
     rows = T * k + T * int(shape.shared)
     flops = rows * 6 * H * I
     gu_flops = rows * 4 * H * I
-    if fused:  # the timed kernel is the whole layer: all expert bytes and products
+    if fused or one_launch:  # the timed kernel runs both contractions: all expert bytes and products
         gu_bytes = gu_bytes / gu_bytes_per_expert * all_bytes_per_expert
         gu_flops = flops
     gu_s = gu_avg_ms / 1e3
@@ -576,6 +583,7 @@ def main():
               "grouped bf16 MFMA" if mfma else "wavefront GEMV")
     what = ("the whole decode layer in one launch (router, selection, permutation, gate/up + "
             "SwiGLU, down, combine; wavefront GEMV)" if fused else
+            f"expert gate/up + SwiGLU and down in one launch ({family})" if one_launch else
             f"expert gate/up + SwiGLU ({family})")
     if gu_flops / gu_bytes > ridge:
         roof = {"bound": "mfma", "kernel": what,

@@ -1001,9 +1001,9 @@ static_assert(kXcds == kXcdCount, "one XCD count");
 // ones it takes tiles x, x + 8, ... The launch gives every XCD
 // mfma_chunk_tiles slots (long lists can occur) or a round-robin share.
 template <int NCB>
-__device__ __forceinline__ int pass_tile_of(const int32_t* __restrict__ meta, int& j) {
-  const int xcd = blockIdx.x % kXcds;
-  j = blockIdx.x / kXcds;
+__device__ __forceinline__ int pass_tile_of(const int32_t* __restrict__ meta, int bid, int& j) {
+  const int xcd = bid % kXcds;
+  j = bid / kXcds;
   // loaded together (clamped indices): no load waits for another
   const int nt = meta[1];
   const int lo = meta[kMetaXcdBounds + (xcd > 0 ? xcd - 1 : 0)];
@@ -1016,34 +1016,102 @@ __device__ __forceinline__ int pass_tile_of(const int32_t* __restrict__ meta, in
   return t < nt ? t : -1;
 }
 
+// LDS of a pass workgroup. lds, ldsb: stage buffers and the output tile, two
+// separate arrays, so that the compiler sees that loads into one leave the
+// other alone; arow: source row of each tile row; orow (down): the y row
+// (slot) of each tile row; ss: the tile's two weight scale rows; hfac, herow
+// (down): the h rows' rescale words per block and their common exponents;
+// yq (down): the two output column blocks' bound exponents; go: the
+// outcome of a one-launch down item's wait.
+struct PassLds {
+  uint8_t* lds;
+  uint8_t* ldsb;
+  int* arow;
+  int* orow;
+  float* ss;
+  uint32_t* hfac;
+  int* herow;
+  int* yq;
+  int* go;
+};
+
+// One-launch hand-over of h (mfma_layer): word 0 is the give-up word, word
+// 1 + t tile t's counter (bits 0-5: gate/up items done; bits 6 (1 + x) ..
+// 6 (1 + x) + 5: those done on XCD x). Null in the two-launch passes.
+struct LayerSync {
+  uint64_t* words;
+  uint32_t* status;
+};
+constexpr uint32_t kLayerSpin = 1u << 21;  // polls before a wait gives up (about a second)
+
+// XCD of the calling wavefront (hardware register XCC_ID, bits 0-3)
+__device__ __forceinline__ int xcc_id() {
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u);
+}
+
+// Down workgroup of mfma_layer: wait until every gate/up item of the tile
+// has published (thread 0 polls at the point of coherence, bounded), and
+// check that they ran on this XCD: h goes between them through the XCD's
+// L2, which another XCD does not see. false: give up the tile (a wait of
+// the call gave up; the status word says so).
+template <int NGU>
+__device__ __forceinline__ bool layer_wait(const LayerSync& ls, int tile, int* flag) {
+  static_assert(NGU < 64, "a tile's gate/up item count fits six bits");
+  if (threadIdx.x == 0) {
+    uint64_t* ctr = ls.words + 1 + tile;
+    uint64_t v = ld_coherent(ctr);
+    bool ok = true;
+    for (uint32_t it = 0; (int)(v & 63u) < NGU; ++it) {
+      if (it >= kLayerSpin || ((it & 255u) == 255u && ld_coherent(ls.words) != 0ull)) {
+        atomicOr(ls.status, kStatusLayerWait);
+        st_coherent(ls.words, (uint64_t)1);
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      v = ld_coherent(ctr);
+    }
+    if (ok && (int)((v >> (6 * (1 + xcc_id()))) & 63u) != NGU) atomicOr(ls.status, kStatusLayerXcd);
+    *flag = ok;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Gate/up workgroup of mfma_layer: this item's h and exponents are in
+// memory (every wavefront's stores complete), then count it on its tile.
+__device__ __forceinline__ void layer_publish(const LayerSync& ls, int tile) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(ls.words + 1 + tile, 1ull + (1ull << (6 * (1 + xcc_id()))),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One work item of a grouped pass: workgroup bid's row tile and column
+// block (pass_tile_of). ls.words non-null: the one-launch layer (a down
+// item first waits for its tile's gate/up items; a gate/up item publishes).
 template <bool GU, int H, int I>
-__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void mfma_pass(const uint16_t* __restrict__ act,
-                                                        MfmaBank bk,
-                                                        const int32_t* __restrict__ meta,
-                                                        const int32_t* __restrict__ tiles,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ rtok,
-                                                        const int32_t* __restrict__ pair, int E,
-                                                        PassIO io) {
+__device__ __forceinline__ void pass_item(int bid, const uint16_t* __restrict__ act, MfmaBank bk,
+                                          const int32_t* __restrict__ meta,
+                                          const int32_t* __restrict__ tiles,
+                                          const int32_t* __restrict__ offsets,
+                                          const int32_t* __restrict__ rtok,
+                                          const int32_t* __restrict__ pair, int E, PassIO io,
+                                          PassLds L, LayerSync ls) {
   using P = PassShape<GU, H, I>;
   static_assert(P::K % kBK == 0 && P::NOUT % P::COLS == 0, "MFMA tiling");
-  // stage buffers and the output tile: two separate LDS halves, so that the
-  // compiler sees that loads into one leave the other alone
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes / 2];
-  __shared__ __attribute__((aligned(16))) uint8_t ldsb[kLdsBytes / 2];
-  __shared__ int arow[kMfmaBM];
-  __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
   constexpr int NKB = P::K / kBK;  // scale blocks along K
-  __shared__ float ss[2 * NKB];    // the tile's two scale rows
-  // down: the tile's h rows' rescale words per block, and their common exponents
-  __shared__ uint32_t hfac[GU ? 1 : kMfmaBM * NKB];
-  __shared__ int herow[GU ? 1 : kMfmaBM];
-  __shared__ int yq[2];  // down: the two output column blocks' bound exponents
   constexpr int NCB = P::NOUT / P::COLS;
+  constexpr int NGU = I / PassShape<true, H, I>::COLS;  // gate/up items per tile
+  uint8_t *lds = L.lds, *ldsb = L.ldsb;
+  int *arow = L.arow, *orow = L.orow, *herow = L.herow, *yq = L.yq;
+  float* ss = L.ss;
+  uint32_t* hfac = L.hfac;
   int j;
-  const int tile = pass_tile_of<NCB>(meta, j);
+  const int tile = pass_tile_of<NCB>(meta, bid, j);
   if (tile < 0) return;
+  if (!GU && ls.words && !layer_wait<NGU>(ls, tile, L.go)) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
   const int tid = threadIdx.x;
@@ -1073,11 +1141,14 @@ void mfma_pass(const uint16_t* __restrict__ act,
       // the h row's common power of two: the largest of its block
       // exponents; its blocks are brought to it by rescale words (exact
       // unless a block lies more than 2^14 below the row's largest block)
+      // (one launch: read past this CU's L1, which may hold a line of them
+      // from a neighbouring tile's rows, fetched before this tile's gate/up
+      // items had written theirs)
       const uint8_t* eb = io.hexps + (size_t)(r0 + rr) * NKB;
       int b[NKB], emax = 0;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        b[kb] = eb[kb];
+        b[kb] = ls.words ? ld_coherent(eb + kb) : eb[kb];
         emax = max(emax, b[kb]);
       }
 #pragma unroll
@@ -1108,6 +1179,61 @@ void mfma_pass(const uint16_t* __restrict__ act,
   else
     pass_tile_down_dma<H, I>(act, W, ss, arow, orow, hfac, herow, yq, valid, r0, n0, lds, ldsb,
                              io);
+  if (GU && ls.words) layer_publish(ls, tile);
+}
+
+// A grouped pass on its own (the FP8-free two-launch form, which a streamed
+// bank takes: its rounds run the passes once per round)
+template <bool GU, int H, int I>
+__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void mfma_pass(const uint16_t* __restrict__ act, MfmaBank bk, const int32_t* __restrict__ meta,
+               const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
+               const int32_t* __restrict__ rtok, const int32_t* __restrict__ pair, int E,
+               PassIO io) {
+  constexpr int NKB = PassShape<GU, H, I>::K / kBK;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb[kLdsBytes / 2];
+  __shared__ int arow[kMfmaBM];
+  __shared__ int orow[GU ? 1 : kMfmaBM];
+  __shared__ float ss[2 * NKB];
+  __shared__ uint32_t hfac[GU ? 1 : kMfmaBM * NKB];
+  __shared__ int herow[GU ? 1 : kMfmaBM];
+  __shared__ int yq[2];
+  pass_item<GU, H, I>(blockIdx.x, act, bk, meta, tiles, offsets, rtok, pair, E, io,
+                      PassLds{lds, ldsb, arow, orow, ss, hfac, herow, yq, nullptr},
+                      LayerSync{nullptr, nullptr});
+}
+
+// Both grouped passes in one launch: workgroups 0 .. n_gu - 1 are gate/up
+// items, the rest down items in the same tile order, so a tile's items of
+// both passes land on one XCD (bid % 8). Workgroups are dispatched in order
+// on each XCD, so a waiting down item never holds back a gate/up item it
+// waits for: every gate/up item of its XCD has been dispatched before it,
+// and a gate/up item never waits. The down items of a tile start while
+// other tiles' gate/up items still run (no drain between the passes).
+template <int H, int I>
+__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void mfma_layer(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, MfmaBank bk,
+                const int32_t* __restrict__ meta, const int32_t* __restrict__ tiles,
+                const int32_t* __restrict__ offsets, const int32_t* __restrict__ rtok,
+                const int32_t* __restrict__ pair, int E, PassIO hio, PassIO yio, int n_gu,
+                LayerSync ls) {
+  constexpr int NKG = H / kBK, NKD = I / kBK;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb[kLdsBytes / 2];
+  __shared__ int arow[kMfmaBM];
+  __shared__ int orow[kMfmaBM];
+  __shared__ float ss[2 * (NKG > NKD ? NKG : NKD)];
+  __shared__ uint32_t hfac[kMfmaBM * NKD];
+  __shared__ int herow[kMfmaBM];
+  __shared__ int yq[2];
+  __shared__ int go;
+  const PassLds L{lds, ldsb, arow, orow, ss, hfac, herow, yq, &go};
+  const int b = blockIdx.x;
+  if (b < n_gu)
+    pass_item<true, H, I>(b, x, bk, meta, tiles, offsets, rtok, pair, E, hio, L, ls);
+  else
+    pass_item<false, H, I>(b - n_gu, h, bk, meta, tiles, offsets, rtok, pair, E, yio, L, ls);
 }
 
 // ---------------------------------------------------------------------------
@@ -1416,7 +1542,7 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   __shared__ int rowg[GU ? 1 : kMfmaBM];  // down: each row's largest h exponent
   __shared__ int yq[2];                   // down: the output column blocks' bound exponents
   int j;  // XCD-aware, as mfma_pass
-  const int tile = pass_tile_of<NCB>(meta, j);
+  const int tile = pass_tile_of<NCB>(meta, blockIdx.x, j);
   if (tile < 0) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
@@ -1506,6 +1632,21 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
   }
   const PassIO hio{w.h, w.hexps, nullptr};
   const PassIO yio{w.y, w.yexps, w.hexps};
+  const uint16_t* hin = reinterpret_cast<const uint16_t*>(w.h);
+  const unsigned n_down = nt8 * (H / PassShape<false, H, I>::COLS);
+  if (!bk.slot) {  // one launch; the permutation cleared its counters and status
+    const LayerSync ls{static_cast<uint64_t*>(w.sync), w.status};
+    const int n_gu = (int)grid.x;
+    const dim3 g2(grid.x + n_down);
+    if (ev.any())
+      hipExtLaunchKernelGGL(mfma_layer<H, I>, g2, dim3(kPassThreads), 0, s, ev.begin, ev.end, 0,
+                            xa, hin, bk, meta, tiles, offsets, rtok, pair, d.E, hio, yio, n_gu,
+                            ls);
+    else
+      mfma_layer<H, I><<<g2, kPassThreads, 0, s>>>(xa, hin, bk, meta, tiles, offsets, rtok, pair,
+                                                   d.E, hio, yio, n_gu, ls);
+    return;
+  }
   if (ev.any()) {  // the events take the kernel's own start and end times
     hipExtLaunchKernelGGL(mfma_pass<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin, ev.end,
                           0, xa, bk, meta, tiles, offsets, rtok, pair, d.E, hio);
@@ -1513,9 +1654,8 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
     mfma_pass<true, H, I><<<grid, kPassThreads, 0, s>>>(xa, bk, meta, tiles, offsets, rtok, pair,
                                                         d.E, hio);
   }
-  mfma_pass<false, H, I><<<nt8 * (H / PassShape<false, H, I>::COLS), kPassThreads, 0, s>>>(
-      reinterpret_cast<const uint16_t*>(w.h), bk, w.meta, w.tiles, w.offsets, w.rtok, w.pair, d.E,
-      yio);
+  mfma_pass<false, H, I><<<n_down, kPassThreads, 0, s>>>(hin, bk, meta, tiles, offsets, rtok,
+                                                        pair, d.E, yio);
 }
 
 #define MOE_MFMA_SHAPES(X) \

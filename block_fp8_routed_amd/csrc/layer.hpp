@@ -122,6 +122,23 @@ struct Work {
 inline int64_t max_mfma_tiles(const Dims& d) {
   return d.P / kMfmaBM + d.E + d.S + 1;
 }
+// The grouped bf16 path runs gate/up and down in one launch (expert_mfma.hip,
+// mfma_layer): the down workgroups wait for their tile's gate/up items
+// through one 64-bit counter per row tile in the workspace, after a give-up
+// word (word 0; tile t's counter is word 1 + t; bits 0-5: items done, bits
+// 6 (1 + x) .. + 5: items done on XCD x). The permutation clears the give-up
+// word, the counters of the call's tiles and the status word. A streamed
+// bank keeps two launches.
+inline bool layer_one_launch(const Dims& d) { return d.mfma && !d.f8; }
+inline size_t layer_sync_bytes(const Dims& d) {
+  return (size_t)(max_mfma_tiles(d) + 1) * 8;
+}
+// status bits of the one-launch grouped path (the single-launch decode
+// layer's are 1, 2 and 4): a down workgroup gave up waiting for its tile's
+// gate/up items; a tile's gate/up items ran on an XCD other than its down
+// workgroup's (h would not be coherent between them)
+constexpr uint32_t kStatusLayerWait = 8u, kStatusLayerXcd = 16u;
+
 // tile slots per XCD that cover the longest cost-balanced chunk of any tile
 // list of this problem (at most max_mfma_tiles tiles, each of cost at most
 // kTileCostFull and at least kTileCostThin)

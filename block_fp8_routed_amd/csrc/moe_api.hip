@@ -37,8 +37,13 @@ static void region_sizes(const Dims& d, size_t* sz) {
   sz[15] = d.mfma ? (size_t)d.P * (d.I / 128) : 0;    // exponents of h
   sz[16] = d.mfma ? (size_t)d.P * (d.H / 128) : 0;    // exponents of y
   sz[17] = (size_t)(d.E + 1) * 4;                     // slot map of a streamed bank
-  sz[18] = d.fused ? fused_sync_bytes(d) : fold_combine_bytes(d);  // flags and counters
-  sz[19] = d.fused ? 16 : 0;  // single-launch decode: status word, then the give-up tag
+  // flags and counters: the single-launch decode layer's, the one-launch
+  // grouped path's per-tile counters, or the decode combine fold's
+  sz[18] = d.fused              ? fused_sync_bytes(d)
+           : layer_one_launch(d) ? layer_sync_bytes(d)
+                                 : fold_combine_bytes(d);
+  // status word (then the decode layer's give-up tag)
+  sz[19] = d.fused || layer_one_launch(d) ? 16 : 0;
 }
 
 size_t workspace_bytes(const Dims& d) {

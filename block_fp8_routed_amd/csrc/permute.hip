@@ -31,10 +31,15 @@ __global__ __launch_bounds__(64 * kGemvMaxTokens) void select_permute_small(
     int E, int S, int32_t* __restrict__ topk, float* __restrict__ gates,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair, int32_t* __restrict__ inv,
     int32_t* __restrict__ rtok, int32_t* __restrict__ meta, int4* __restrict__ gdesc,
-    int32_t* __restrict__ tiles, int tile_rows, int32_t* __restrict__ cmb, int ncmb) {
+    int32_t* __restrict__ tiles, int tile_rows, int32_t* __restrict__ cmb, int ncmb,
+    uint64_t* __restrict__ lsync, int nlsync, uint32_t* __restrict__ status) {
   static_assert(kGemvMaxTokens <= 32, "a token mask is one 32-bit word");
-  // the down kernel's combine counters (when it combines): zero for this call
+  // the down kernel's combine counters (when it combines), or the one-launch
+  // grouped passes' give-up word, per-tile counters and status: zero for
+  // this call
   for (int i = threadIdx.x; i < ncmb; i += blockDim.x) cmb[(size_t)i * kCmbStride] = 0;
+  for (int i = threadIdx.x; i < nlsync; i += blockDim.x) lsync[i] = 0ull;
+  if (nlsync > 0 && threadIdx.x == 0) *status = 0u;
   __shared__ uint32_t tmask[64 * NV];  // bit t: token t chose the expert
   __shared__ int32_t first[64 * NV];   // first row of each expert's group
   __shared__ int32_t routed_rows;
@@ -123,12 +128,16 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
   const unsigned threads = (unsigned)(64 * d.T);
   int32_t* cmb = d.fold_combine ? static_cast<int32_t*>(w.sync) : nullptr;
   const int ncmb = d.fold_combine ? (int)d.T * gemv_down_items(d) : 0;
+  const bool one = tile_rows > 0 && layer_one_launch(d);
+  uint64_t* lsync = one ? static_cast<uint64_t*>(w.sync) : nullptr;
+  const int nlsync = one ? (int)(layer_sync_bytes(d) / 8) : 0;
 #define MOE_SPU(NV, U)                                                                        \
   select_permute_small<NV, U><<<1, threads, 0, s>>>(plog, ns, bias, d.T, d.k, d.E, d.S,       \
                                                     w.topk, w.gates, w.offsets, w.pair, w.inv, \
                                                     w.rtok, w.meta,                            \
                                                     reinterpret_cast<int4*>(w.gdesc), w.tiles, \
-                                                    tile_rows, cmb, ncmb)
+                                                    tile_rows, cmb, ncmb, lsync, nlsync,       \
+                                                    w.status)
 #define MOE_SP(NV)            \
   if (ns == 1)                \
     MOE_SPU(NV, 1);           \
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(1024) void perm_count(
     const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb,
     int32_t* bcnt, int32_t* counter, int32_t* __restrict__ offsets, int32_t* bbase,
     int32_t* __restrict__ meta, int4* __restrict__ gdesc, int32_t* __restrict__ tiles,
-    int tile_rows) {
+    int tile_rows, uint64_t* __restrict__ lsync, uint32_t* __restrict__ status) {
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t tmp[4 * 64];
   __shared__ int last;
@@ -299,6 +308,13 @@ __global__ __launch_bounds__(1024) void perm_count(
     if (S) gdesc[nact] = make_int4(E, total, (int)T, 0);
     meta[0] = nact + S;
     meta[1] = ntile + nshared_tiles;
+  }
+  // the one-launch grouped passes' per-tile counters, give-up word and
+  // status: cleared for this call's tiles
+  if (lsync) {
+    const int ntot = ntile + nshared_tiles;
+    for (int i = tid; i <= ntot; i += 1024) lsync[i] = 0ull;
+    if (tid == 0) *status = 0u;
   }
   for (int y = nact + S + tid; y < E + 2; y += 1024) gdesc[y] = make_int4(-1, 0, 0, 0);
 }
@@ -417,7 +433,11 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int
   const int nb = perm_blocks(TK);
   perm_count<<<nb, 1024, 0, s>>>(topk, d.T, d.k, d.E, d.S, nb, w.pblock, counter, w.offsets,
                                  w.pblock + (size_t)kPermMaxBlocks * d.E, w.meta,
-                                 reinterpret_cast<int4*>(w.gdesc), w.tiles, tile_rows);
+                                 reinterpret_cast<int4*>(w.gdesc), w.tiles, tile_rows,
+                                 tile_rows > 0 && layer_one_launch(d)
+                                     ? static_cast<uint64_t*>(w.sync)
+                                     : nullptr,
+                                 w.status);
   // one counting block leaves the bases of one placing block only: the
   // placing blocks (1024 slots each, one round per wavefront) then count
   // their own prefixes, as long as the extra LDS row keeps the block within

@@ -48,8 +48,10 @@ def test_traffic_report_scales_counters_by_the_copy_kernel(tmp_path, monkeypatch
 
 
 def test_traffic_report_picks_the_mfma_kernel_at_prefill_sizes(tmp_path, monkeypatch):
+    """The grouped bf16 path's gate/up and down passes share one launch
+    (mfma_layer); the two-launch passes (streamed banks) are not it."""
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
-    gu = "void moe::mfma_pass<true, 2048, 768>(unsigned short const*, ...)"
+    gu = "void moe::mfma_layer<2048, 768>(unsigned short const*, ...)"
     dn = "void moe::mfma_pass<false, 2048, 768>(unsigned short const*, ...)"
     fetch = _csv(tmp_path / "f.csv", [(gu, 100.0), (dn, 900.0)])
     write = _csv(tmp_path / "w.csv", [(gu, 1.0), (dn, 9.0)])
@@ -59,7 +61,7 @@ def test_traffic_report_picks_the_mfma_kernel_at_prefill_sizes(tmp_path, monkeyp
                                  tokens=None, path="auto")
     bench.traffic_report(args)
     entry = json.load(open(tmp_path / "traffic.json"))["c2:T512:mfma"]
-    assert entry["kernel"] == "mfma_pass<true"
+    assert entry["kernel"] == "mfma_layer<"
     assert entry["traffic_bytes_per_launch"] == 100 * 1024 + 1 * 1024
 
 

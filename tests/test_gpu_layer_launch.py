@@ -1,0 +1,148 @@
+"""The grouped bf16 path runs its gate/up and down passes as one launch: the
+down workgroups wait on per-tile counters for their tile's gate/up
+workgroups. Its outputs must equal those of the two-launch form bit for bit
+(moe_forward_streamed with every expert resident runs the same per-tile
+arithmetic as two launches), every wait must end normally on the waiting
+workgroup's own XCD (STATUS 0), consecutive calls on one workspace must not
+see each other's counters (each call's permutation clears them), and a
+captured HIP graph must replay correctly (no memset nodes: the clearing is
+part of the permutation kernel). It is held to the oracle by
+test_gpu_parity.py's grouped cases."""
+import pytest
+import torch
+
+import workloads as W
+from parity import DevLayer, host_bank, log
+
+pytestmark = pytest.mark.gpu
+
+C = W.CONFIGS
+
+_PINNED = {}
+
+
+def pinned_bank(shape):
+    key = shape.with_(tokens=0)
+    if key not in _PINNED:
+        import block_fp8_routed_amd as moe
+        bank, _ = host_bank(key)
+        _PINNED.clear()
+        _PINNED[key] = moe.Bank.pinned_from_numpy(bank)
+    return _PINNED[key]
+
+
+def forward(layer, T=None, x=None, ws=None):
+    """moe_forward on the grouped bf16 path; returns (out, status word)."""
+    import block_fp8_routed_amd as moe
+    s = layer.shape
+    xx = layer.x if x is None else x
+    cfg = moe.make_config(len(xx), s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
+                          xx.dtype, torch.float32, "mfma")
+    if ws is None:
+        ws = moe.make_workspace(cfg, "cuda")
+    out = moe.moe_forward(xx, layer.router_w, layer.bank, s.top_k, s.block, shared=layer.shared,
+                          router_bias=layer.bias, path="mfma",
+                          workspace=ws[:moe.workspace_bytes(cfg)], cfg=cfg)
+    torch.cuda.synchronize()
+    st = int(moe.workspace_view(ws, cfg, moe.MOE_WS_STATUS, torch.int32).item())
+    return out, st
+
+
+# (config, tokens, overrides): row tiles dealt round-robin over the XCDs and
+# (8192 tokens: more than 512 tiles) in cost-balanced chunks; decode sizes
+# (selection and permutation in one launch); a ragged tail; the shared
+# expert; uniform routing
+CASES = [
+    ("c2", 512, {}),
+    ("c2", 8192, {}),
+    ("c2", 17, {}),
+    ("c1", 5, {}),
+    ("c2", 300, {"shared": True}),
+    ("c2", 1000, {"bias": None}),
+]
+
+
+def case_id(c):
+    name, T, ov = c
+    return f"{name}-T{T}" + ("-" + "-".join(sorted(ov)) if ov else "")
+
+
+@pytest.mark.parametrize("name,T,ov", CASES, ids=[case_id(c) for c in CASES])
+def test_one_launch_equals_two_launches(name, T, ov):
+    import block_fp8_routed_amd as moe
+    shape = C[name].with_(**ov) if ov else C[name]
+    layer = DevLayer(shape, tokens=T)
+    log(f"one launch vs two {case_id((name, T, ov))}")
+    got, st = forward(layer)
+    assert st == 0, f"status {st:#x}: a wait gave up or ran on another XCD"
+    cache = moe.ExpertCache(shape.experts)
+    slot_bank = moe.Bank.empty_slots(shape.experts, shape.hidden, shape.inter, shape.block)
+    want = moe.moe_forward_streamed(layer.x, layer.router_w, pinned_bank(shape), slot_bank, cache,
+                                    shape.top_k, shape.block, shared=layer.shared,
+                                    router_bias=layer.bias, path="mfma")
+    torch.cuda.synchronize()
+    assert cache.rounds_last == 1
+    assert torch.equal(got, want)
+
+
+def test_back_to_back_calls_share_a_workspace():
+    """Calls of different sizes on one workspace: each equals a call on a
+    fresh workspace, and its status is 0 (a later call with fewer tiles
+    than the one before must not see that call's counters)."""
+    import block_fp8_routed_amd as moe
+    shape = C["c2"]
+    layer = DevLayer(shape, tokens=2048)
+    s = shape
+    big = moe.make_config(2048, s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
+                          layer.x.dtype, torch.float32, "mfma")
+    ws = moe.make_workspace(big, "cuda")
+    for b, T in enumerate([2048, 512, 17, 3, 2048, 900]):
+        x = torch.from_numpy(W.gen_x(shape, 2048, batch=b)[:T]).to(layer.x.dtype).cuda()
+        got, st = forward(layer, x=x, ws=ws)
+        assert st == 0, f"call {b} (T={T}): status {st:#x}"
+        want, st2 = forward(layer, x=x)
+        assert st2 == 0
+        assert torch.equal(got, want), f"call {b} (T={T})"
+
+
+def test_graph_replay():
+    """A HIP graph holding the grouped path (router, selection, permutation,
+    the one-launch passes, combine) replays with new inputs, eager work in
+    between, each replay equal to an eager call and with status 0."""
+    import block_fp8_routed_amd as moe
+    shape = C["c2"]
+    T = 512
+    layer = DevLayer(shape, tokens=T)
+    s = shape
+    cfg = moe.make_config(T, s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
+                          layer.x.dtype, torch.float32, "mfma")
+    ws = moe.make_workspace(cfg, "cuda")
+    x_static = layer.x.clone()
+    out_static = torch.empty((T, s.hidden), dtype=torch.float32, device="cuda")
+
+    def call():
+        moe.moe_forward(x_static, layer.router_w, layer.bank, s.top_k, s.block,
+                        router_bias=layer.bias, path="mfma", out=out_static, workspace=ws,
+                        cfg=cfg)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for b in range(1, 5):
+        x = torch.from_numpy(W.gen_x(shape, T, batch=b)).to(layer.x.dtype).cuda()
+        x_static.copy_(x)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_static.clone()
+        st = int(moe.workspace_view(ws, cfg, moe.MOE_WS_STATUS, torch.int32).item())
+        assert st == 0, f"replay {b}: status {st:#x}"
+        ref, _ = forward(layer, x=x)  # eager work between replays
+        log(f"graph replay {b}: max |diff| {float((got - ref).abs().max()):.3g}")
+        assert torch.equal(got, ref), f"replay {b}"
