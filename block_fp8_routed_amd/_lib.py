@@ -29,7 +29,7 @@ PATHS = {"auto": MOE_PATH_AUTO, "gemv": MOE_PATH_GEMV, "mfma": MOE_PATH_MFMA,
 EXPORTS = ("moe_workspace_bytes", "moe_forward", "moe_forward_static", "moe_forward_streamed", "moe_route",
            "moe_permute",
            "moe_dequant_e4m3", "moe_quantize_act_e4m3", "moe_workspace_region",
-           "moe_status_string", "moe_version")
+           "moe_status_string", "moe_version", "moe_set_wait_limit")
 (MOE_WS_TOPK, MOE_WS_GATES, MOE_WS_OFFSETS, MOE_WS_PAIR, MOE_WS_INV, MOE_WS_H, MOE_WS_H_EXPS,
  MOE_WS_Y, MOE_WS_Y_EXPS, MOE_WS_STATUS, MOE_WS_COUNT) = range(11)
 
@@ -122,6 +122,8 @@ def load() -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_version.argtypes = []
     lib.moe_version.restype = ctypes.c_int32
+    lib.moe_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.moe_set_wait_limit.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -132,6 +134,14 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return int(load().moe_version())
+
+
+def set_wait_limit(polls: int) -> None:
+    """moe_set_wait_limit: the poll bound of the one-launch grouped passes'
+    waits (0: the default); for tests of their give-up path."""
+    st = load().moe_set_wait_limit(int(polls))
+    if st != 0:
+        raise MoeError(st, "moe_set_wait_limit")
 
 
 def make_config(tokens: int, hidden: int, experts: int, inter: int, top_k: int, block: int,

@@ -1041,8 +1041,9 @@ struct PassLds {
 struct LayerSync {
   uint64_t* words;
   uint32_t* status;
+  uint32_t spin;  // polls before a wait gives up
 };
-constexpr uint32_t kLayerSpin = 1u << 21;  // polls before a wait gives up (about a second)
+constexpr uint32_t kLayerSpin = 1u << 21;  // default poll bound (about a second)
 
 // XCD of the calling wavefront (hardware register XCC_ID, bits 0-3)
 __device__ __forceinline__ int xcc_id() {
@@ -1062,7 +1063,7 @@ __device__ __forceinline__ bool layer_wait(const LayerSync& ls, int tile, int* f
     uint64_t v = ld_coherent(ctr);
     bool ok = true;
     for (uint32_t it = 0; (int)(v & 63u) < NGU; ++it) {
-      if (it >= kLayerSpin || ((it & 255u) == 255u && ld_coherent(ls.words) != 0ull)) {
+      if (it >= ls.spin || ((it & 255u) == 255u && ld_coherent(ls.words) != 0ull)) {
         atomicOr(ls.status, kStatusLayerWait);
         st_coherent(ls.words, (uint64_t)1);
         ok = false;
@@ -1201,7 +1202,7 @@ void mfma_pass(const uint16_t* __restrict__ act, MfmaBank bk, const int32_t* __r
   __shared__ int yq[2];
   pass_item<GU, H, I>(blockIdx.x, act, bk, meta, tiles, offsets, rtok, pair, E, io,
                       PassLds{lds, ldsb, arow, orow, ss, hfac, herow, yq, nullptr},
-                      LayerSync{nullptr, nullptr});
+                      LayerSync{nullptr, nullptr, 0u});
 }
 
 // Both grouped passes in one launch: workgroups 0 .. n_gu - 1 are gate/up
@@ -1635,7 +1636,7 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
   const uint16_t* hin = reinterpret_cast<const uint16_t*>(w.h);
   const unsigned n_down = nt8 * (H / PassShape<false, H, I>::COLS);
   if (!bk.slot) {  // one launch; the permutation cleared its counters and status
-    const LayerSync ls{static_cast<uint64_t*>(w.sync), w.status};
+    const LayerSync ls{static_cast<uint64_t*>(w.sync), w.status, layer_wait_limit(kLayerSpin)};
     const int n_gu = (int)grid.x;
     const dim3 g2(grid.x + n_down);
     if (ev.any())

@@ -138,6 +138,8 @@ inline size_t layer_sync_bytes(const Dims& d) {
 // gate/up items; a tile's gate/up items ran on an XCD other than its down
 // workgroup's (h would not be coherent between them)
 constexpr uint32_t kStatusLayerWait = 8u, kStatusLayerXcd = 16u;
+// poll bound of those waits: dflt, unless moe_set_wait_limit set one
+uint32_t layer_wait_limit(uint32_t dflt);
 
 // tile slots per XCD that cover the longest cost-balanced chunk of any tile
 // list of this problem (at most max_mfma_tiles tiles, each of cost at most

@@ -1,17 +1,25 @@
 // moe_api.hip — the C ABI of libmoe_fp8.so (declared in include/moe_fp8.h):
 // argument validation, workspace layout and the launch sequence of one layer.
 //
-// Nothing here allocates, synchronises the host or keeps state between calls.
+// Nothing here allocates or synchronises the host; the only state kept
+// between calls is the poll bound a test may set (moe_set_wait_limit).
 // Every check runs on the host before the first launch, following the colizig
 // page's rule (Status / Contributing) that an unsupported or invalid request
 // returns an error instead of a plausible-looking wrong number.
 #include <algorithm>
+#include <atomic>
 
 #include "layer.hpp"
 
 namespace moe {
 
 static size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+static std::atomic<uint32_t> g_wait_limit{0};  // 0: each wait's default bound
+uint32_t layer_wait_limit(uint32_t dflt) {
+  const uint32_t v = g_wait_limit.load(std::memory_order_relaxed);
+  return v ? v : dflt;
+}
 
 // Region sizes in carve order.
 constexpr int kRegions = 20;
@@ -317,6 +325,11 @@ const char* moe_status_string(moe_status status) {
     case MOE_ERR_TOO_LARGE: return "the call needs more scratch than the static scratch holds";
   }
   return "unknown status";
+}
+
+moe_status moe_set_wait_limit(uint32_t polls) {
+  g_wait_limit.store(polls, std::memory_order_relaxed);
+  return MOE_OK;
 }
 
 int32_t moe_version(void) { return 100; }

@@ -202,7 +202,9 @@ moe_status moe_forward(const void* x, const float* router_w, const float* router
  * one GPU share its array: calls that may overlap on one GPU (several
  * streams or host threads) race and must be serialised by the caller. The
  * first call on a device looks up the array's device address with that
- * device current (MOE_ERR_HIP if that fails). */
+ * device current (MOE_ERR_HIP if that fails). The STATUS word of the paths
+ * with in-kernel waits stays inside that array, where the caller cannot
+ * read it. */
 #define MOE_STATIC_SCRATCH_BYTES (64u << 20)
 moe_status moe_forward_static(const void* x, const float* router_w, const float* router_bias,
                               const moe_expert_bank* experts, const moe_expert_bank* shared,
@@ -362,6 +364,15 @@ const char* moe_status_string(moe_status status);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t moe_version(void);
+
+/* Poll bound of the in-kernel waits of the bf16 MFMA path's one launch (a
+ * down workgroup waiting for its row tile's gate/up workgroups), for tests
+ * of its give-up path: with a small bound, waits that do not see their tile
+ * complete at once give up, set STATUS bit 8 and skip the tile, and every
+ * workgroup still ends (the call's output is then not valid). polls = 0
+ * restores the default bound (about a second). Process-wide; applies to
+ * calls enqueued after it returns. Always MOE_OK. */
+moe_status moe_set_wait_limit(uint32_t polls);
 
 #ifdef __cplusplus
 }

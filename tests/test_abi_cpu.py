@@ -42,6 +42,15 @@ def test_status_strings_and_version():
     assert moe.version() >= 100
 
 
+def test_wait_limit_setter_is_host_only():
+    """moe_set_wait_limit only records the bound (no device call, so it
+    runs without a GPU); 0 restores the default."""
+    lib = moe.load()
+    assert lib.moe_set_wait_limit(7) == _lib.MOE_OK
+    assert lib.moe_set_wait_limit(0) == _lib.MOE_OK
+    moe.set_wait_limit(0)
+
+
 def cfg(**kw):
     base = dict(tokens=4, hidden=64, experts=8, inter=32, top_k=2, block=32, has_shared=False,
                 x_dtype=_lib.torch.float32, out_dtype=_lib.torch.float32, path="auto")

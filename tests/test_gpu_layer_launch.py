@@ -146,3 +146,35 @@ def test_graph_replay():
         ref, _ = forward(layer, x=x)  # eager work between replays
         log(f"graph replay {b}: max |diff| {float((got - ref).abs().max()):.3g}")
         assert torch.equal(got, ref), f"replay {b}"
+
+
+def test_wait_give_up_is_reported_and_cleared():
+    """With a poll bound of 1 (moe_set_wait_limit), down workgroups that do
+    not see their tile complete at once give up, set STATUS bit 8 and skip
+    their tile, and the call still ends. Two tokens on the 128-expert layer
+    make at most 16 row tiles, so every gate/up and down workgroup is
+    resident at once and the down workgroups start polling while their
+    tiles' gate/up workgroups still run (on larger problems the down
+    workgroups are dispatched only as gate/up ones finish, and rarely wait).
+    The next call on the same workspace, with the default bound, waits
+    normally (the selection kernel clears the give-up word and the status)
+    and equals a call on a fresh workspace."""
+    import block_fp8_routed_amd as moe
+    shape = C["c1"]
+    T = 2
+    layer = DevLayer(shape, tokens=T)
+    s = shape
+    cfg = moe.make_config(T, s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
+                          layer.x.dtype, torch.float32, "mfma")
+    ws = moe.make_workspace(cfg, "cuda")
+    try:
+        moe.set_wait_limit(1)
+        _, st = forward(layer, ws=ws)
+    finally:
+        moe.set_wait_limit(0)
+    log(f"poll bound 1: status {st:#x}")
+    assert st & 8, f"status {st:#x}: no wait gave up"
+    got, st2 = forward(layer, ws=ws)
+    assert st2 == 0, f"status {st2:#x} after the default bound was restored"
+    want, _ = forward(layer)
+    assert torch.equal(got, want)
