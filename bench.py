@@ -147,10 +147,10 @@ KERNEL_SOURCES = {
     "mfma_fp8": ["expert_mfma.hip", "device.hpp", "layer.hpp"],
 }
 # the dominant kernel of each path: the gate/up kernel, or the launch that
-# holds it (the decode layer's single launch; the grouped bf16 path's
-# gate/up + down launch)
+# holds it (the decode layer's single launch; the grouped paths' gate/up +
+# down launch)
 KERNEL_MATCH = {"gemv": "gemv_gate_up<", "gemv_fused": "decode_fused<", "mfma": "mfma_layer<",
-                "mfma_fp8": "mfma_pass_f8<true"}
+                "mfma_fp8": "mfma_layer_f8<"}
 COPY_MATCH = "MulFunctor"  # the copy kernel of --copy-calibration (dst = src * 1)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 512
@@ -468,10 +468,10 @@ def main():
     f8 = args.path == "mfma_fp8"
     mfma = args.path in ("mfma", "mfma_fp8") or (args.path == "auto" and xdt == torch.bfloat16
                                                  and T > 16)
-    # the single-launch decode layer has a status region (so has the grouped
-    # bf16 path, whose gate/up and down passes share one launch)
+    # the single-launch decode layer has a status region (so have the grouped
+    # paths, whose gate/up and down passes share one launch)
     fused = not mfma and moe.workspace_region(cfg, moe.MOE_WS_STATUS)[1] > 0
-    one_launch = mfma and not f8
+    one_launch = mfma
     family_key = "mfma_fp8" if f8 else "mfma" if mfma else "gemv_fused" if fused else "gemv"
 
     # routing of each batch: which experts a step touches (outside the timed region)

@@ -1526,25 +1526,45 @@ __device__ __forceinline__ void pass_tile_f8(const uint8_t* __restrict__ act, co
   }
 }
 
+// LDS of an FP8 pass workgroup: lds, the stage buffers and output tile;
+// arow: source row of each tile row; orow (down): the y row (slot) of each
+// tile row; ss: the tile's two weight scale rows; sx: the tile rows' A
+// exponents; rowg (down): each row's largest h exponent; yq (down): the
+// output column blocks' bound exponents; go: a one-launch down item's wait
+// outcome.
+struct PassLdsF8 {
+  uint8_t* lds;
+  int* arow;
+  int* orow;
+  float* ss;
+  uint8_t* sx;
+  int* rowg;
+  int* yq;
+  int* go;
+};
+
+// One work item of an FP8 pass (as pass_item: ls.words non-null in the
+// one-launch layer, mfma_layer_f8).
 template <bool GU, int H, int I>
-__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
-                  MfmaBank bk, const int32_t* __restrict__ meta,
-                  const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
-                  const int32_t* __restrict__ rtok, const int32_t* __restrict__ pair, int E,
-                  F8Out out) {
+__device__ __forceinline__ void pass_item_f8(int bid, const uint8_t* __restrict__ codes,
+                                             const uint8_t* __restrict__ exps, MfmaBank bk,
+                                             const int32_t* __restrict__ meta,
+                                             const int32_t* __restrict__ tiles,
+                                             const int32_t* __restrict__ offsets,
+                                             const int32_t* __restrict__ rtok,
+                                             const int32_t* __restrict__ pair, int E, F8Out out,
+                                             PassLdsF8 L, LayerSync ls) {
   constexpr int K = GU ? H : I, NKB = K / kBK;
   constexpr int COLS = GU ? 128 : 256, NCB = (GU ? I : H) / COLS;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-  __shared__ int arow[kMfmaBM];
-  __shared__ int orow[GU ? 1 : kMfmaBM];  // down: the y row (slot) of each tile row
-  __shared__ float ss[2 * NKB];           // the tile's two weight scale rows
-  __shared__ uint8_t sx[kMfmaBM * NKB];   // the tile rows' A exponents
-  __shared__ int rowg[GU ? 1 : kMfmaBM];  // down: each row's largest h exponent
-  __shared__ int yq[2];                   // down: the output column blocks' bound exponents
+  constexpr int NGU = I / 128;  // gate/up items per tile
+  uint8_t* lds = L.lds;
+  uint8_t* sx = L.sx;
+  int *arow = L.arow, *orow = L.orow, *rowg = L.rowg, *yq = L.yq;
+  float* ss = L.ss;
   int j;  // XCD-aware, as mfma_pass
-  const int tile = pass_tile_of<NCB>(meta, blockIdx.x, j);
+  const int tile = pass_tile_of<NCB>(meta, bid, j);
   if (tile < 0) return;
+  if (!GU && ls.words && !layer_wait<NGU>(ls, tile, L.go)) return;
   const int g = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int valid = min(kMfmaBM, offsets[g + 1] - r0);
   const int tid = threadIdx.x;
@@ -1570,7 +1590,9 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
       orow[tid] = pair[r0 + rr];
       int emax = 0;
       for (int kb = 0; kb < NKB; ++kb) {
-        const int b = exps[(size_t)(r0 + rr) * NKB + kb];
+        // (one launch: past this CU's L1, as the bf16 down items read them)
+        const uint8_t* ep = exps + (size_t)(r0 + rr) * NKB + kb;
+        const int b = ls.words ? ld_coherent(ep) : *ep;
         sx[tid * NKB + kb] = (uint8_t)b;
         emax = max(emax, b);
       }
@@ -1600,6 +1622,58 @@ void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
     pass_tile_f8<GU, H, I, true>(codes, W, ss, sx, arow, orow, rowg, yq, valid, r0, n0, lds, out);
   else
     pass_tile_f8<GU, H, I, false>(codes, W, ss, sx, arow, orow, rowg, yq, valid, r0, n0, lds, out);
+  if (GU && ls.words) layer_publish(ls, tile);
+}
+
+// An FP8 pass on its own (a streamed bank's rounds)
+template <bool GU, int H, int I>
+__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void mfma_pass_f8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
+                  MfmaBank bk, const int32_t* __restrict__ meta,
+                  const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
+                  const int32_t* __restrict__ rtok, const int32_t* __restrict__ pair, int E,
+                  F8Out out) {
+  constexpr int NKB = (GU ? H : I) / kBK;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ int arow[kMfmaBM];
+  __shared__ int orow[GU ? 1 : kMfmaBM];
+  __shared__ float ss[2 * NKB];
+  __shared__ uint8_t sx[kMfmaBM * NKB];
+  __shared__ int rowg[GU ? 1 : kMfmaBM];
+  __shared__ int yq[2];
+  pass_item_f8<GU, H, I>(blockIdx.x, codes, exps, bk, meta, tiles, offsets, rtok, pair, E, out,
+                         PassLdsF8{lds, arow, orow, ss, sx, rowg, yq, nullptr},
+                         LayerSync{nullptr, nullptr, 0u});
+}
+
+// Both FP8 passes in one launch, as mfma_layer: gate/up items (workgroups
+// 0 .. n_gu - 1) publish per tile after their h codes and exponents are
+// stored; down items wait for their tile's.
+template <int H, int I>
+__global__ __launch_bounds__(kPassThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void mfma_layer_f8(const uint8_t* __restrict__ acodes, const uint8_t* __restrict__ aexps,
+                   const uint8_t* __restrict__ hcodes, const uint8_t* __restrict__ hexps,
+                   MfmaBank bk, const int32_t* __restrict__ meta,
+                   const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
+                   const int32_t* __restrict__ rtok, const int32_t* __restrict__ pair, int E,
+                   F8Out hout, F8Out yout, int n_gu, LayerSync ls) {
+  constexpr int NKG = H / kBK, NKD = I / kBK, NKM = NKG > NKD ? NKG : NKD;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ int arow[kMfmaBM];
+  __shared__ int orow[kMfmaBM];
+  __shared__ float ss[2 * NKM];
+  __shared__ uint8_t sx[kMfmaBM * NKM];
+  __shared__ int rowg[kMfmaBM];
+  __shared__ int yq[2];
+  __shared__ int go;
+  const PassLdsF8 L{lds, arow, orow, ss, sx, rowg, yq, &go};
+  const int b = blockIdx.x;
+  if (b < n_gu)
+    pass_item_f8<true, H, I>(b, acodes, aexps, bk, meta, tiles, offsets, rtok, pair, E, hout, L,
+                             ls);
+  else
+    pass_item_f8<false, H, I>(b - n_gu, hcodes, hexps, bk, meta, tiles, offsets, rtok, pair, E,
+                              yout, L, ls);
 }
 
 // ---------------------------------------------------------------------------
@@ -1619,6 +1693,21 @@ static void run_mfma(const Dims& d, const void* x, const MfmaBank& bk, const Wor
   if (d.f8) {  // both contractions on E4M3 operands; h goes between them as E4M3
     const F8Out hout{static_cast<uint8_t*>(w.h), w.hexps, nullptr, nullptr};
     const F8Out yout{nullptr, nullptr, static_cast<uint16_t*>(w.y), w.yexps};
+    if (!bk.slot) {  // one launch, as the bf16 passes
+      const LayerSync ls{static_cast<uint64_t*>(w.sync), w.status, layer_wait_limit(kLayerSpin)};
+      const int n_gu = (int)grid.x;
+      const dim3 g2(grid.x + nt8 * (H / PassShape<false, H, I>::COLS));
+      const uint8_t* hc = static_cast<const uint8_t*>(w.h);
+      if (ev.any())
+        hipExtLaunchKernelGGL(mfma_layer_f8<H, I>, g2, dim3(kPassThreads), 0, s, ev.begin, ev.end,
+                              0, w.acodes, w.aexps, hc, w.hexps, bk, meta, tiles, offsets, rtok,
+                              pair, d.E, hout, yout, n_gu, ls);
+      else
+        mfma_layer_f8<H, I><<<g2, kPassThreads, 0, s>>>(w.acodes, w.aexps, hc, w.hexps, bk, meta,
+                                                        tiles, offsets, rtok, pair, d.E, hout,
+                                                        yout, n_gu, ls);
+      return;
+    }
     if (ev.any())
       hipExtLaunchKernelGGL(mfma_pass_f8<true, H, I>, grid, dim3(kPassThreads), 0, s, ev.begin,
                             ev.end, 0, w.acodes, w.aexps, bk, meta, tiles, offsets, rtok, pair,

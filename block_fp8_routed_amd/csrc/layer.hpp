@@ -122,18 +122,18 @@ struct Work {
 inline int64_t max_mfma_tiles(const Dims& d) {
   return d.P / kMfmaBM + d.E + d.S + 1;
 }
-// The grouped bf16 path runs gate/up and down in one launch (expert_mfma.hip,
-// mfma_layer): the down workgroups wait for their tile's gate/up items
-// through one 64-bit counter per row tile in the workspace, after a give-up
-// word (word 0; tile t's counter is word 1 + t; bits 0-5: items done, bits
-// 6 (1 + x) .. + 5: items done on XCD x). The permutation clears the give-up
-// word, the counters of the call's tiles and the status word. A streamed
-// bank keeps two launches.
-inline bool layer_one_launch(const Dims& d) { return d.mfma && !d.f8; }
+// The grouped paths (bf16 and FP8) run gate/up and down in one launch
+// (expert_mfma.hip, mfma_layer and mfma_layer_f8): the down workgroups wait
+// for their tile's gate/up items through one 64-bit counter per row tile in
+// the workspace, after a give-up word (word 0; tile t's counter is word
+// 1 + t; bits 0-5: items done, bits 6 (1 + x) .. + 5: items done on XCD x).
+// The permutation clears the give-up word, the counters of the call's tiles
+// and the status word. A streamed bank keeps two launches.
+inline bool layer_one_launch(const Dims& d) { return d.mfma; }
 inline size_t layer_sync_bytes(const Dims& d) {
   return (size_t)(max_mfma_tiles(d) + 1) * 8;
 }
-// status bits of the one-launch grouped path (the single-launch decode
+// status bits of the one-launch grouped paths (the single-launch decode
 // layer's are 1, 2 and 4): a down workgroup gave up waiting for its tile's
 // gate/up items; a tile's gate/up items ran on an XCD other than its down
 // workgroup's (h would not be coherent between them)

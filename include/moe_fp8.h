@@ -76,8 +76,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * expert row and 128 columns) before the down contraction. This changes the
  * layer's numerics (about 2^-4 relative per operand value); it requires bf16
  * x and H and I multiples of 128, and is not chosen by AUTO.
- * MFMA (bf16) runs its gate/up and down passes as one kernel launch (not so
- * moe_forward_streamed): a down workgroup waits for its row tile's gate/up
+ * MFMA and MFMA_FP8 run their gate/up and down passes as one kernel launch
+ * (not so moe_forward_streamed): a down workgroup waits for its row tile's gate/up
  * workgroups through a per-tile counter in the workspace, which the
  * permutation clears (no memset). Every wait is bounded; the STATUS region
  * reports one that gave up, or a tile whose two passes ran on different
@@ -152,7 +152,7 @@ typedef enum {
   MOE_EV_PERMUTED = 2,     /* start of the gate/up kernel (after the       */
                            /* token→expert permutation)                     */
   MOE_EV_GATE_UP = 3,      /* end of the gate/up + SwiGLU kernel (routed   */
-                           /* and shared; on the bf16 MFMA path that launch */
+                           /* and shared; on the MFMA paths that launch     */
                            /* also runs the down pass)                      */
   MOE_EV_DOWN = 4,         /* after the down projection                    */
   MOE_EV_END = 5,          /* after the combine                            */
@@ -333,11 +333,11 @@ moe_status moe_quantize_act_e4m3(const void* x, int64_t tokens, int32_t hidden, 
  *   Y        [P][H] expert outputs by slot: fp32 (GEMV family), fp16
  *            scaled by Y_EXPS (MFMA families)
  *   Y_EXPS   uint8 [P][H/128] exponent bytes of Y (MFMA families)
- *   STATUS   uint32 (single-launch decode layer and bf16 MFMA path, else 0
+ *   STATUS   uint32 (single-launch decode layer and MFMA paths, else 0
  *            bytes): error bits of the call's in-kernel waits, 0 when every
  *            wait ended normally (decode layer: 1 router results, 2 the
  *            permutation, 4 gate/up results not seen within the bounded
- *            wait; bf16 MFMA: 8 a down workgroup's wait for its tile's
+ *            wait; MFMA paths: 8 a down workgroup's wait for its tile's
  *            gate/up results gave up, 16 a tile's gate/up and down passes
  *            ran on different XCDs); the output is then not valid
  * Returns MOE_ERR_NULL for a NULL pointer, MOE_ERR_SHAPE for an invalid cfg
@@ -365,7 +365,7 @@ const char* moe_status_string(moe_status status);
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t moe_version(void);
 
-/* Poll bound of the in-kernel waits of the bf16 MFMA path's one launch (a
+/* Poll bound of the in-kernel waits of the MFMA paths' one launch (a
  * down workgroup waiting for its row tile's gate/up workgroups), for tests
  * of its give-up path: with a small bound, waits that do not see their tile
  * complete at once give up, set STATUS bit 8 and skip the tile, and every

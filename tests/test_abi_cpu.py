@@ -181,10 +181,8 @@ def test_fp8_path_validation_and_workspace():
     """The FP8 variant: bf16 activations only; against the bf16 grouped path
     its workspace adds the activation codes (T*H bytes) and their exponents
     (T*H/128 bytes), and holds h as one-byte codes instead of fp16 (P*I bytes
-    fewer); both keep exponent bytes for h and y. It runs its passes as two
-    launches, so it has none of the bf16 path's per-tile counters (a give-up
-    word and one 8-byte counter per possible row tile, P/128 + E + S + 1)
-    and status word (16 bytes)."""
+    fewer); both keep exponent bytes for h and y, and the per-tile counters
+    and status word of their one-launch passes."""
     bf16 = _lib.torch.bfloat16
     shape = dict(tokens=300, hidden=2048, experts=128, inter=768, top_k=8, block=128)
     f32 = cfg(path="mfma_fp8", **shape)
@@ -194,10 +192,8 @@ def test_fp8_path_validation_and_workspace():
     extra = moe.workspace_bytes(f8) - moe.workspace_bytes(plain)
     T, H, I = shape["tokens"], shape["hidden"], shape["inter"]
     P = T * shape["top_k"] + (T if f8.has_shared else 0)
-    S = 1 if f8.has_shared else 0
-    sync = (P // 128 + shape["experts"] + S + 2) * 8
-    want = T * H + T * H // 128 - P * I - sync - 16
-    assert want - 5 * 256 <= extra <= want + 5 * 256  # region alignment
+    want = T * H + T * H // 128 - P * I
+    assert want - 3 * 256 <= extra <= want + 3 * 256  # region alignment
     auto = cfg(path="auto", x_dtype=bf16, **shape)
     assert moe.workspace_bytes(auto) == moe.workspace_bytes(plain)  # AUTO never picks FP8
     assert forward(f8, ws_bytes=moe.workspace_bytes(f8) - 256) == _lib.MOE_ERR_WORKSPACE
@@ -225,8 +221,8 @@ def test_workspace_regions(path, tokens):
             moe.MOE_WS_Y: P * H * (2 if grouped else 4),
             moe.MOE_WS_Y_EXPS: P * H // 128 if grouped else 0,
             # the status word of the single-launch decode layer and of the
-            # grouped bf16 path (its gate/up and down passes share a launch)
-            moe.MOE_WS_STATUS: 4 if path in ("gemv_fused", "mfma") else 0}
+            # grouped paths (their gate/up and down passes share a launch)
+            moe.MOE_WS_STATUS: 4 if path in ("gemv_fused", "mfma", "mfma_fp8") else 0}
     spans = []
     for region, n in want.items():
         off, got = moe.workspace_region(c, region)

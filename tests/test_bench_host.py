@@ -49,12 +49,14 @@ def test_traffic_report_scales_counters_by_the_copy_kernel(tmp_path, monkeypatch
 
 def test_traffic_report_picks_the_mfma_kernel_at_prefill_sizes(tmp_path, monkeypatch):
     """The grouped bf16 path's gate/up and down passes share one launch
-    (mfma_layer); the two-launch passes (streamed banks) are not it."""
+    (mfma_layer); the two-launch passes (streamed banks) and the FP8
+    variant's launch (mfma_layer_f8) are not it."""
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     gu = "void moe::mfma_layer<2048, 768>(unsigned short const*, ...)"
     dn = "void moe::mfma_pass<false, 2048, 768>(unsigned short const*, ...)"
-    fetch = _csv(tmp_path / "f.csv", [(gu, 100.0), (dn, 900.0)])
-    write = _csv(tmp_path / "w.csv", [(gu, 1.0), (dn, 9.0)])
+    f8 = "void moe::mfma_layer_f8<2048, 768>(unsigned char const*, ...)"
+    fetch = _csv(tmp_path / "f.csv", [(gu, 100.0), (dn, 900.0), (f8, 5000.0)])
+    write = _csv(tmp_path / "w.csv", [(gu, 1.0), (dn, 9.0), (f8, 50.0)])
     copy_f = _csv(tmp_path / "cf.csv", [("MulFunctor", bench.COPY_MIB * 1024.0)])
     copy_w = _csv(tmp_path / "cw.csv", [("MulFunctor", bench.COPY_MIB * 1024.0)])
     args = types.SimpleNamespace(traffic_report=[fetch, write, copy_f, copy_w], config="c2",

@@ -1,6 +1,6 @@
-"""The grouped bf16 path runs its gate/up and down passes as one launch: the
-down workgroups wait on per-tile counters for their tile's gate/up
-workgroups. Its outputs must equal those of the two-launch form bit for bit
+"""The grouped paths (bf16, and the FP8 variant) run their gate/up and down
+passes as one launch: the down workgroups wait on per-tile counters for
+their tile's gate/up workgroups. Its outputs must equal those of the two-launch form bit for bit
 (moe_forward_streamed with every expert resident runs the same per-tile
 arithmetic as two launches), every wait must end normally on the waiting
 workgroup's own XCD (STATUS 0), consecutive calls on one workspace must not
@@ -31,17 +31,17 @@ def pinned_bank(shape):
     return _PINNED[key]
 
 
-def forward(layer, T=None, x=None, ws=None):
-    """moe_forward on the grouped bf16 path; returns (out, status word)."""
+def forward(layer, T=None, x=None, ws=None, path="mfma"):
+    """moe_forward on a grouped path; returns (out, status word)."""
     import block_fp8_routed_amd as moe
     s = layer.shape
     xx = layer.x if x is None else x
     cfg = moe.make_config(len(xx), s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
-                          xx.dtype, torch.float32, "mfma")
+                          xx.dtype, torch.float32, path)
     if ws is None:
         ws = moe.make_workspace(cfg, "cuda")
     out = moe.moe_forward(xx, layer.router_w, layer.bank, s.top_k, s.block, shared=layer.shared,
-                          router_bias=layer.bias, path="mfma",
+                          router_bias=layer.bias, path=path,
                           workspace=ws[:moe.workspace_bytes(cfg)], cfg=cfg)
     torch.cuda.synchronize()
     st = int(moe.workspace_view(ws, cfg, moe.MOE_WS_STATUS, torch.int32).item())
@@ -53,33 +53,37 @@ def forward(layer, T=None, x=None, ws=None):
 # (selection and permutation in one launch); a ragged tail; the shared
 # expert; uniform routing
 CASES = [
-    ("c2", 512, {}),
-    ("c2", 8192, {}),
-    ("c2", 17, {}),
-    ("c1", 5, {}),
-    ("c2", 300, {"shared": True}),
-    ("c2", 1000, {"bias": None}),
+    ("c2", 512, {}, "mfma"),
+    ("c2", 8192, {}, "mfma"),
+    ("c2", 17, {}, "mfma"),
+    ("c1", 5, {}, "mfma"),
+    ("c2", 300, {"shared": True}, "mfma"),
+    ("c2", 1000, {"bias": None}, "mfma"),
+    ("c2", 512, {}, "mfma_fp8"),
+    ("c2", 8192, {}, "mfma_fp8"),
+    ("c1", 5, {}, "mfma_fp8"),
+    ("c2", 300, {"shared": True}, "mfma_fp8"),
 ]
 
 
 def case_id(c):
-    name, T, ov = c
-    return f"{name}-T{T}" + ("-" + "-".join(sorted(ov)) if ov else "")
+    name, T, ov, path = c
+    return f"{name}-T{T}-{path}" + ("-" + "-".join(sorted(ov)) if ov else "")
 
 
-@pytest.mark.parametrize("name,T,ov", CASES, ids=[case_id(c) for c in CASES])
-def test_one_launch_equals_two_launches(name, T, ov):
+@pytest.mark.parametrize("name,T,ov,path", CASES, ids=[case_id(c) for c in CASES])
+def test_one_launch_equals_two_launches(name, T, ov, path):
     import block_fp8_routed_amd as moe
     shape = C[name].with_(**ov) if ov else C[name]
     layer = DevLayer(shape, tokens=T)
-    log(f"one launch vs two {case_id((name, T, ov))}")
-    got, st = forward(layer)
+    log(f"one launch vs two {case_id((name, T, ov, path))}")
+    got, st = forward(layer, path=path)
     assert st == 0, f"status {st:#x}: a wait gave up or ran on another XCD"
     cache = moe.ExpertCache(shape.experts)
     slot_bank = moe.Bank.empty_slots(shape.experts, shape.hidden, shape.inter, shape.block)
     want = moe.moe_forward_streamed(layer.x, layer.router_w, pinned_bank(shape), slot_bank, cache,
                                     shape.top_k, shape.block, shared=layer.shared,
-                                    router_bias=layer.bias, path="mfma")
+                                    router_bias=layer.bias, path=path)
     torch.cuda.synchronize()
     assert cache.rounds_last == 1
     assert torch.equal(got, want)
@@ -105,24 +109,26 @@ def test_back_to_back_calls_share_a_workspace():
         assert torch.equal(got, want), f"call {b} (T={T})"
 
 
-def test_graph_replay():
+@pytest.mark.parametrize("path", ["mfma", "mfma_fp8"])
+def test_graph_replay(path):
     """A HIP graph holding the grouped path (router, selection, permutation,
-    the one-launch passes, combine) replays with new inputs, eager work in
-    between, each replay equal to an eager call and with status 0."""
+    the activation quantiser of the FP8 variant, the one-launch passes,
+    combine) replays with new inputs, eager work in between, each replay
+    equal to an eager call and with status 0."""
     import block_fp8_routed_amd as moe
     shape = C["c2"]
     T = 512
     layer = DevLayer(shape, tokens=T)
     s = shape
     cfg = moe.make_config(T, s.hidden, s.experts, s.inter, s.top_k, s.block, s.shared,
-                          layer.x.dtype, torch.float32, "mfma")
+                          layer.x.dtype, torch.float32, path)
     ws = moe.make_workspace(cfg, "cuda")
     x_static = layer.x.clone()
     out_static = torch.empty((T, s.hidden), dtype=torch.float32, device="cuda")
 
     def call():
         moe.moe_forward(x_static, layer.router_w, layer.bank, s.top_k, s.block,
-                        router_bias=layer.bias, path="mfma", out=out_static, workspace=ws,
+                        router_bias=layer.bias, path=path, out=out_static, workspace=ws,
                         cfg=cfg)
 
     side = torch.cuda.Stream()
@@ -143,7 +149,7 @@ def test_graph_replay():
         got = out_static.clone()
         st = int(moe.workspace_view(ws, cfg, moe.MOE_WS_STATUS, torch.int32).item())
         assert st == 0, f"replay {b}: status {st:#x}"
-        ref, _ = forward(layer, x=x)  # eager work between replays
+        ref, _ = forward(layer, x=x, path=path)  # eager work between replays
         log(f"graph replay {b}: max |diff| {float((got - ref).abs().max()):.3g}")
         assert torch.equal(got, ref), f"replay {b}"
 
