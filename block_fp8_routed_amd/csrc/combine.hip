@@ -19,7 +19,11 @@ constexpr int kYBlock = 128;  // columns per exponent byte of a scaled fp16 y ro
 
 // Thread i of a workgroup sums 8 consecutive outputs of one token (16-byte
 // fp16 loads, or two 16-byte fp32 loads, of y; fp32 accumulation). y is read
-// once and out written once, so both go through non-temporal accesses.
+// once and out written once, so both go through non-temporal accesses. The
+// slots are loaded KB at a time, all of a batch's loads issued before the
+// first is added, so that a token's k loads cost ceil(k / KB) load
+// latencies rather than k (at decode sizes the kernel is that latency); the
+// additions keep the slot order.
 template <bool OUT_BF16, bool Y_F32>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yv,
                                                      const uint8_t* __restrict__ yexp,
@@ -31,31 +35,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   float a[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[i] = 0.f;
-  // value v of y row `row`, columns n .. n + 7, times g (g = 1: plain add)
-  auto add = [&](int64_t row, float g, bool gated) {
-    float v[8];
+  // the raw words of y row `row`, columns n .. n + 7 (and its exponent byte)
+  struct Raw {
+    uint4 p, q;
+    uint32_t eb;
+  };
+  auto load = [&](int64_t row) {
+    Raw r;
     if (Y_F32) {
       const float* yr = static_cast<const float*>(yv) + row * H + n;
-      const uint4 p = ld16_nt(yr), q = ld16_nt(yr + 4);
-      const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+      r.p = ld16_nt(yr);
+      r.q = ld16_nt(yr + 4);
+      r.eb = 0;
+    } else {
+      r.p = ld16_nt(static_cast<const uint16_t*>(yv) + row * H + n);
+      r.q = make_uint4(0, 0, 0, 0);
+      r.eb = yexp[row * (H / kYBlock) + n / kYBlock];
+    }
+    return r;
+  };
+  // its values times g added to a (g = 1: plain add)
+  auto add = [&](const Raw& r, float g, bool gated) {
+    float v[8];
+    if (Y_F32) {
+      const uint32_t w[8] = {r.p.x, r.p.y, r.p.z, r.p.w, r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
     } else {
-      const uint4 p = ld16_nt(static_cast<const uint16_t*>(yv) + row * H + n);
-      const uint32_t eb = yexp[row * (H / kYBlock) + n / kYBlock];
-      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+      const uint32_t w[4] = {r.p.x, r.p.y, r.p.z, r.p.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f16x2_t h2 = __builtin_bit_cast(f16x2_t, w[i]);
-        v[2 * i] = f16_scaled_value(h2[0], eb);
-        v[2 * i + 1] = f16_scaled_value(h2[1], eb);
+        v[2 * i] = f16_scaled_value(h2[0], r.eb);
+        v[2 * i + 1] = f16_scaled_value(h2[1], r.eb);
       }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = gated ? fmaf(g, v[i], a[i]) : a[i] + v[i];
   };
-  for (int j = 0; j < k; ++j) add(t * k + j, gates[t * k + j], true);
-  if (S) add(T * k + t, 1.f, false);
+  constexpr int KB = Y_F32 ? 4 : 8;  // slots per batch of loads
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    Raw r[KB];
+    float g[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (j0 + i < k) {
+        r[i] = load(t * k + j0 + i);
+        g[i] = gates[t * k + j0 + i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (j0 + i < k) add(r[i], g[i], true);
+  }
+  if (S) add(load(T * k + t), 1.f, false);
   if (OUT_BF16) {
     uint4 o;
     o.x = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);

@@ -470,10 +470,22 @@ __device__ __forceinline__ void complete_rows(const int4 gd, const int bx,
     const int nrows = H - row0 < ROWS ? H - row0 : ROWS;
     for (int q = tid; q < nm * nrows; q += blockDim.x) {
       const int t = marked[q / nrows], row = row0 + q % nrows;
+      // every slot's value is requested before the first is added (one load
+      // latency, not k), then the sum in slot order
+      float yv[kMaxTopK], gv[kMaxTopK];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          yv[j] = ld_coherent(y + (size_t)(t * k + j) * H + row);
+          gv[j] = gates[t * k + j];
+        }
+      }
+      const float ysh = S ? ld_coherent(y + (size_t)(T * k + t) * H + row) : 0.f;
       float acc = 0.f;
-      for (int j = 0; j < k; ++j)
-        acc = fmaf(gates[t * k + j], ld_coherent(y + (size_t)(t * k + j) * H + row), acc);
-      if (S) acc = acc + ld_coherent(y + (size_t)(T * k + t) * H + row);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) acc = fmaf(gv[j], yv[j], acc);
+      if (S) acc = acc + ysh;
       if (OUT_BF16)
         reinterpret_cast<uint16_t*>(out)[(size_t)t * H + row] = (uint16_t)f32_to_bf16_bits(acc);
       else
