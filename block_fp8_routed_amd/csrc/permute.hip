@@ -171,27 +171,128 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
 //     bbase[b][e] = offsets[e] + (rows of e in blocks before b), group
 //     descriptors and MFMA row tiles. No block waits for another. *counter
 //     must be zero at launch. Up to kPermOneBlock slots run as one block,
-//     which takes the counts straight from LDS (no hand-over).
-//   perm_scatter: block b places its slots: its wavefronts take consecutive
-//     sub-ranges, count per (wavefront, expert), take exclusive prefixes over
-//     wavefronts on top of bbase[b][e], and walk their slots in order with
-//     ballot peer ranks, so rows keep slot order.
+//     which takes the counts straight from LDS (no hand-over); up to
+//     kPermPlaceSlots it then places every slot itself (place_slots), so no
+//     second launch follows.
+//   perm_scatter: block b places its slots (place_slots): its wavefronts
+//     take consecutive sub-ranges, count per (wavefront, expert), take
+//     exclusive prefixes over wavefronts on top of its base (bbase[b][e], or
+//     after a one-block count offsets[e] plus its own count of the earlier
+//     slots), and walk their slots in order with ballot peer ranks, so rows
+//     keep slot order.
 constexpr int kPermBlockSlots = 512;  // slots per block (at most kPermMaxBlocks blocks)
 constexpr int kPermBatch = 4;         // slot loads per thread issued together
 constexpr int kPermMaxBlocks = kPermMaxBlocksHost;
 
 constexpr int kPermOneBlock = 4096;   // up to this many slots: one block, no hand-over
+constexpr int kPermPlaceSlots = 1024; // up to this many: that block also places them
 inline int perm_blocks(int64_t TK) {
   if (TK <= kPermOneBlock) return 1;
   int64_t nb = (TK + kPermBlockSlots - 1) / kPermBlockSlots;
   return (int)(nb < 1 ? 1 : (nb > kPermMaxBlocks ? kPermMaxBlocks : nb));
 }
 
+// Places slots [blo, bhi) of the permutation with the calling block (1024
+// threads): wavefront w takes a consecutive sub-range, counts its experts in
+// wcnt[w][e] (LDS, 16 x E), the exclusive prefixes over wavefronts are taken
+// on top of base(e) (the block's first row of expert e), and each wavefront
+// walks its slots in order with ballot peer ranks, so rows keep slot order.
+template <class Base>
+__device__ __forceinline__ void place_slots(const int32_t* __restrict__ topk, int k, int E,
+                                            int64_t blo, int64_t bhi, Base base, int32_t* wcnt,
+                                            int32_t* __restrict__ pair, int32_t* __restrict__ inv,
+                                            int32_t* __restrict__ rtok) {
+  constexpr int W = 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t wper = (bhi - blo + W - 1) / W;
+  const int64_t lo = blo + w * wper < bhi ? blo + w * wper : bhi;
+  const int64_t hi = lo + wper < bhi ? lo + wper : bhi;
+  for (int i = tid; i < W * E; i += 1024) wcnt[i] = 0;
+  __syncthreads();
+  // the wavefront's slots, kPermBatch rounds of 64 at a time: loaded (clamped,
+  // unconditional) before any is used, kept for the walk below when the
+  // wavefront has at most kPermBatch rounds
+  int ev[kPermBatch];
+#pragma unroll
+  for (int i = 0; i < kPermBatch; ++i) ev[i] = 0;
+  for (int64_t s0 = lo + lane; s0 < hi; s0 += 64 * kPermBatch) {
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i) {
+      const int64_t s = s0 + 64 * i;
+      ev[i] = topk[s < hi ? s : hi - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i)
+      if (s0 + 64 * i < hi && (unsigned)ev[i] < (unsigned)E) atomicAdd(&wcnt[w * E + ev[i]], 1);
+  }
+  __syncthreads();
+  // exclusive prefix over wavefronts on top of the block's base
+  for (int e = tid; e < E; e += 1024) {
+    int run = base(e);
+    for (int ww = 0; ww < W; ++ww) {
+      const int c = wcnt[ww * E + e];
+      wcnt[ww * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const bool held = hi - lo <= 64 * kPermBatch;  // uniform: ev holds every round
+  for (int64_t b0 = lo; b0 < hi; b0 += 64) {
+    const int64_t s = b0 + lane;
+    int e_in = 0;
+    if (held) {
+#pragma unroll
+      for (int i = 0; i < kPermBatch; ++i)
+        if (b0 == lo + 64 * i) e_in = ev[i];
+    } else if (s < hi) {
+      e_in = topk[s];
+    }
+    const bool ok = s < hi && (unsigned)e_in < (unsigned)E;
+    const int e = ok ? e_in : 0;
+    if (s < hi && !ok) inv[s] = -1;
+    unsigned long long peers = __ballot(ok);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long m = __ballot(ok && bit);
+      peers &= bit ? m : ~m;
+    }
+    if (!ok) peers = 0;
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    const int leader = ok ? (__ffsll((long long)peers) - 1) : lane;
+    int old = 0;
+    if (ok && lane == leader) old = atomicAdd(&wcnt[w * E + e], __popcll(peers));
+    old = __shfl(old, leader, 64);
+    if (ok) {
+      const int pos = old + rank;
+      pair[pos] = (int)s;
+      inv[s] = pos;
+      rtok[pos] = (int)(s / k);
+    }
+  }
+}
+
+// The shared group's rows: slot TK + t is token t, at row total + t.
+__device__ __forceinline__ void place_shared(int64_t T, int64_t TK, int total,
+                                             int32_t* __restrict__ pair,
+                                             int32_t* __restrict__ inv,
+                                             int32_t* __restrict__ rtok) {
+  for (int64_t t = threadIdx.x; t < T; t += 1024) {
+    pair[total + t] = (int)(TK + t);
+    inv[TK + t] = (int)(total + t);
+    rtok[total + t] = (int)t;
+  }
+}
+
 __global__ __launch_bounds__(1024) void perm_count(
     const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb,
     int32_t* bcnt, int32_t* counter, int32_t* __restrict__ offsets, int32_t* bbase,
     int32_t* __restrict__ meta, int4* __restrict__ gdesc, int32_t* __restrict__ tiles,
-    int tile_rows, uint64_t* __restrict__ lsync, uint32_t* __restrict__ status) {
+    int tile_rows, uint64_t* __restrict__ lsync, uint32_t* __restrict__ status, int32_t* pair,
+    int32_t* inv, int32_t* rtok, int place_all) {
+  // place_all (uniform, one block only): this block also places every slot
+  // (place_slots), with the dynamic LDS as its 16 x E wavefront counters
+  extern __shared__ int32_t wcnt[];
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t tmp[4 * 64];
   __shared__ int last;
@@ -259,6 +360,7 @@ __global__ __launch_bounds__(1024) void perm_count(
 #pragma unroll
     for (int b = 0; b < kPermMaxBlocks; ++b)
       if (b < nb) bbase[(size_t)b * E + e] = off + pre[b];
+    cnt[e] = off;  // (thread e's own counter, read back by thread e only)
   }
   if (tid == 0) {
     offsets[E] = total;
@@ -317,29 +419,28 @@ __global__ __launch_bounds__(1024) void perm_count(
     if (tid == 0) *status = 0u;
   }
   for (int y = nact + S + tid; y < E + 2; y += 1024) gdesc[y] = make_int4(-1, 0, 0, 0);
+  if (place_all) {
+    place_slots(topk, k, E, 0, TK, [&](int ex) { return cnt[ex]; }, wcnt, pair, inv, rtok);
+    if (S) place_shared(T, TK, total, pair, inv, rtok);
+  }
 }
 
-// lds: (16 + prefix) * E int32 of shared memory. prefix (uniform): the block's base
-// per expert is offsets[e] + its own count of the slots before its range
-// (used when the counting kernel ran as one block and left no per-block
-// bases); otherwise bbase[b][e].
+// lds: (16 + prefix) * E int32. prefix (uniform): the block's base per
+// expert is offsets[e] + its own count of the slots before its range (after
+// a one-block count, which leaves no per-block bases); otherwise bbase[b][e].
 __global__ __launch_bounds__(1024) void perm_scatter(
     const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb, int prefix,
     const int32_t* __restrict__ bbase, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ pair, int32_t* __restrict__ inv, int32_t* __restrict__ rtok) {
   extern __shared__ int32_t wcnt[];  // [16][E], then the prefix counts [E]
-  constexpr int W = 16;
-  int32_t* pcnt = wcnt + W * E;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int32_t* pcnt = wcnt + 16 * E;
+  const int tid = threadIdx.x;
   const int64_t TK = T * k;
   const int64_t per = (TK + nb - 1) / nb;
   const int64_t blo = (int64_t)blockIdx.x * per, bhi = blo + per < TK ? blo + per : TK;
-  const int64_t wper = (bhi - blo + W - 1) / W;
-  const int64_t lo = blo + w * wper < bhi ? blo + w * wper : bhi;
-  const int64_t hi = lo + wper < bhi ? lo + wper : bhi;
-  for (int i = tid; i < (W + prefix) * E; i += 1024) wcnt[i] = 0;
-  __syncthreads();
   if (prefix) {  // count of each expert among slots [0, blo)
+    for (int i = tid; i < E; i += 1024) pcnt[i] = 0;
+    __syncthreads();
     for (int64_t s0 = tid; s0 < blo; s0 += 1024 * kPermBatch) {
       int pv[kPermBatch];
 #pragma unroll
@@ -352,75 +453,13 @@ __global__ __launch_bounds__(1024) void perm_scatter(
         if (s0 + 1024 * i < blo && (unsigned)pv[i] < (unsigned)E) atomicAdd(&pcnt[pv[i]], 1);
     }
   }
-  // the wavefront's slots, kPermBatch rounds of 64 at a time: loaded (clamped,
-  // unconditional) before any is used, kept for the scatter below when the
-  // wavefront has at most kPermBatch rounds
-  int ev[kPermBatch];
-#pragma unroll
-  for (int i = 0; i < kPermBatch; ++i) ev[i] = 0;
-  for (int64_t s0 = lo + lane; s0 < hi; s0 += 64 * kPermBatch) {
-#pragma unroll
-    for (int i = 0; i < kPermBatch; ++i) {
-      const int64_t s = s0 + 64 * i;
-      ev[i] = topk[s < hi ? s : hi - 1];
-    }
-#pragma unroll
-    for (int i = 0; i < kPermBatch; ++i)
-      if (s0 + 64 * i < hi && (unsigned)ev[i] < (unsigned)E) atomicAdd(&wcnt[w * E + ev[i]], 1);
-  }
-  __syncthreads();
-  // exclusive prefix over wavefronts on top of the block's base
-  for (int e = tid; e < E; e += 1024) {
-    int run = prefix ? offsets[e] + pcnt[e] : bbase[(size_t)blockIdx.x * E + e];
-    for (int ww = 0; ww < W; ++ww) {
-      const int c = wcnt[ww * E + e];
-      wcnt[ww * E + e] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const bool held = hi - lo <= 64 * kPermBatch;  // uniform: ev holds every round
-  for (int64_t b0 = lo; b0 < hi; b0 += 64) {
-    const int64_t s = b0 + lane;
-    int e_in = 0;
-    if (held) {
-#pragma unroll
-      for (int i = 0; i < kPermBatch; ++i)
-        if (b0 == lo + 64 * i) e_in = ev[i];
-    } else if (s < hi) {
-      e_in = topk[s];
-    }
-    const bool ok = s < hi && (unsigned)e_in < (unsigned)E;
-    const int e = ok ? e_in : 0;
-    if (s < hi && !ok) inv[s] = -1;
-    unsigned long long peers = __ballot(ok);
-    for (int b = 0; b < ebits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const unsigned long long m = __ballot(ok && bit);
-      peers &= bit ? m : ~m;
-    }
-    if (!ok) peers = 0;
-    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    const int leader = ok ? (__ffsll((long long)peers) - 1) : lane;
-    int old = 0;
-    if (ok && lane == leader) old = atomicAdd(&wcnt[w * E + e], __popcll(peers));
-    old = __shfl(old, leader, 64);
-    if (ok) {
-      const int pos = old + rank;
-      pair[pos] = (int)s;
-      inv[s] = pos;
-      rtok[pos] = (int)(s / k);
-    }
-  }
-  if (S && blockIdx.x == 0) {  // the shared group: slot TK + t is token t
-    const int total = offsets[E];
-    for (int64_t t = tid; t < T; t += 1024) {
-      pair[total + t] = (int)(TK + t);
-      inv[TK + t] = (int)(total + t);
-      rtok[total + t] = (int)t;
-    }
-  }
+  // (place_slots synchronises the block before it reads a base)
+  place_slots(topk, k, E, blo, bhi,
+              [&](int e) {
+                return prefix ? offsets[e] + pcnt[e] : bbase[(size_t)blockIdx.x * E + e];
+              },
+              wcnt, pair, inv, rtok);
+  if (S && blockIdx.x == 0) place_shared(T, TK, offsets[E], pair, inv, rtok);
 }
 
 __global__ void zero_word(int32_t* p) { *p = 0; }
@@ -431,22 +470,27 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int
   if (!counter_zeroed) zero_word<<<1, 1, 0, s>>>(counter);
   const int64_t TK = d.T * d.k;
   const int nb = perm_blocks(TK);
-  perm_count<<<nb, 1024, 0, s>>>(topk, d.T, d.k, d.E, d.S, nb, w.pblock, counter, w.offsets,
-                                 w.pblock + (size_t)kPermMaxBlocks * d.E, w.meta,
-                                 reinterpret_cast<int4*>(w.gdesc), w.tiles, tile_rows,
-                                 tile_rows > 0 && layer_one_launch(d)
-                                     ? static_cast<uint64_t*>(w.sync)
-                                     : nullptr,
-                                 w.status);
-  // one counting block leaves the bases of one placing block only: the
-  // placing blocks (1024 slots each, one round per wavefront) then count
-  // their own prefixes, as long as the extra LDS row keeps the block within
-  // 64 KiB of dynamic LDS (else one placing block takes every slot)
-  const int prefix = (nb == 1 && (size_t)17 * d.E * sizeof(int32_t) <= 65536) ? 1 : 0;
-  const int nbs = prefix ? (int)((TK + 1023) / 1024) : nb;
-  perm_scatter<<<nbs, 1024, (size_t)(16 + prefix) * d.E * sizeof(int32_t), s>>>(
-      topk, d.T, d.k, d.E, d.S, nbs, prefix, w.pblock + (size_t)kPermMaxBlocks * d.E, w.offsets,
-      w.pair, w.inv, w.rtok);
+  // up to kPermPlaceSlots slots (one round of 64 per wavefront) the counting
+  // block also places them, with no second launch; above that, a one-block
+  // count leaves the bases of one placing block only, and the placing
+  // blocks (1024 slots each) count their own prefixes, as long as the extra
+  // LDS row keeps the block within 64 KiB of dynamic LDS (else one placing
+  // block takes every slot)
+  const int place_all = TK <= kPermPlaceSlots ? 1 : 0;
+  const size_t wlds = (size_t)16 * d.E * sizeof(int32_t);  // at most 64 KiB (E <= 1024)
+  perm_count<<<nb, 1024, place_all ? wlds : 0, s>>>(
+      topk, d.T, d.k, d.E, d.S, nb, w.pblock, counter, w.offsets,
+      w.pblock + (size_t)kPermMaxBlocks * d.E, w.meta, reinterpret_cast<int4*>(w.gdesc), w.tiles,
+      tile_rows,
+      tile_rows > 0 && layer_one_launch(d) ? static_cast<uint64_t*>(w.sync) : nullptr, w.status,
+      w.pair, w.inv, w.rtok, place_all);
+  if (!place_all) {
+    const int prefix = (nb == 1 && (size_t)17 * d.E * sizeof(int32_t) <= 65536) ? 1 : 0;
+    const int nbs = prefix ? (int)((TK + 1023) / 1024) : nb;
+    perm_scatter<<<nbs, 1024, (size_t)(16 + prefix) * d.E * sizeof(int32_t), s>>>(
+        topk, d.T, d.k, d.E, d.S, nbs, prefix, w.pblock + (size_t)kPermMaxBlocks * d.E,
+        w.offsets, w.pair, w.inv, w.rtok);
+  }
   return hipGetLastError();
 }
 
