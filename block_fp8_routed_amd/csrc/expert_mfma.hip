@@ -1045,10 +1045,13 @@ struct LayerSync {
 };
 constexpr uint32_t kLayerSpin = 1u << 21;  // default poll bound (about a second)
 
-// XCD of the calling wavefront (hardware register XCC_ID, bits 0-3)
+// XCD of the calling wavefront: hardware register XCC_ID, bits 0-3 (0-7
+// on this 8-XCD chip; masked to 3 bits so that a counter field is never
+// shifted out of its 64-bit word)
 __device__ __forceinline__ int xcc_id() {
-  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u);
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (uint32_t)(kXcds - 1));
 }
+static_assert(6 * (1 + kXcds) <= 64, "one six-bit count per XCD after the total");
 
 // Down workgroup of mfma_layer: wait until every gate/up item of the tile
 // has published (thread 0 polls at the point of coherence, bounded), and
@@ -1079,8 +1082,9 @@ __device__ __forceinline__ bool layer_wait(const LayerSync& ls, int tile, int* f
   return *flag != 0;
 }
 
-// Gate/up workgroup of mfma_layer: this item's h and exponents are in
-// memory (every wavefront's stores complete), then count it on its tile.
+// Gate/up workgroup of mfma_layer: once this item's h and exponents are
+// stored (every wavefront's stores complete, so they are in the XCD's L2),
+// count it on its tile.
 __device__ __forceinline__ void layer_publish(const LayerSync& ls, int tile) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
