@@ -240,14 +240,16 @@ def traffic_report(args):
     import workloads as W
     shape = W.CONFIGS[args.config]
     T = args.tokens if args.tokens is not None else shape.tokens
-    family = args.path if args.path in ("mfma", "mfma_fp8") else (
-        "mfma" if args.path == "auto" and shape.x_dtype == "bf16" and T > 16 else "gemv")
+    import torch
+    import block_fp8_routed_amd as moe
+    xdt = torch.bfloat16 if shape.x_dtype == "bf16" else torch.float32
+    cfg = moe.make_config(T, shape.hidden, shape.experts, shape.inter, shape.top_k,
+                          shape.block, shape.shared, xdt, torch.float32, args.path)
+    # the family the library takes for this call (the grouped ones keep h's
+    # exponent bytes)
+    grouped = moe.workspace_region(cfg, moe.MOE_WS_H_EXPS)[1] > 0
+    family = args.path if args.path in ("mfma", "mfma_fp8") else "mfma" if grouped else "gemv"
     if family == "gemv":  # the single-launch decode layer where the library takes it
-        import torch
-        import block_fp8_routed_amd as moe
-        xdt = torch.bfloat16 if shape.x_dtype == "bf16" else torch.float32
-        cfg = moe.make_config(T, shape.hidden, shape.experts, shape.inter, shape.top_k,
-                              shape.block, shape.shared, xdt, torch.float32, args.path)
         if moe.workspace_region(cfg, moe.MOE_WS_STATUS)[1] > 0:
             family = "gemv_fused"
     f_kib, nf = counter_means(fetch_csv, KERNEL_MATCH[family])
@@ -466,8 +468,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     f8 = args.path == "mfma_fp8"
-    mfma = args.path in ("mfma", "mfma_fp8") or (args.path == "auto" and xdt == torch.bfloat16
-                                                 and T > 16)
+    # the family the library takes (the grouped ones keep h's exponent bytes)
+    mfma = moe.workspace_region(cfg, moe.MOE_WS_H_EXPS)[1] > 0
     # the single-launch decode layer has a status region (so have the grouped
     # paths, whose gate/up and down passes share one launch)
     fused = not mfma and moe.workspace_region(cfg, moe.MOE_WS_STATUS)[1] > 0

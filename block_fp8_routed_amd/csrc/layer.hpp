@@ -12,7 +12,11 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;  // permute keeps per-wave expert counters in LDS
 constexpr int kMaxTopK = 16;       // top-k keeps the selection in registers
-constexpr int kGemvMaxTokens = 16; // AUTO path: wavefront GEMV up to this many tokens
+constexpr int kGemvMaxTokens = 16; // decode sizes: one-workgroup selection + permutation
+// AUTO takes the wavefront GEMV family up to this many tokens (bf16 x; fp32
+// x always): measured faster than the grouped MFMA family through 48 tokens
+// on both the 128- and the 512-expert layer, slower from 56-64 on
+constexpr int kAutoGemvTokens = 48;
 constexpr int kMfmaBM = 128;       // rows (tokens) of one grouped-MFMA tile
 constexpr size_t kAlign = 256;
 

@@ -126,7 +126,7 @@ moe_status basic_dims(const moe_config* c, Dims* d) {
   d->out_bf16 = c->out_dtype == MOE_BF16;
   d->f8 = c->path == MOE_PATH_MFMA_FP8;
   d->mfma = c->path == MOE_PATH_MFMA || d->f8 ||
-            (c->path == MOE_PATH_AUTO && d->x_bf16 && c->tokens > kGemvMaxTokens);
+            (c->path == MOE_PATH_AUTO && d->x_bf16 && c->tokens > kAutoGemvTokens);
   // the single-launch decode layer only when asked for: the five-launch
   // GEMV path measures faster on MI355X at every decode size
   d->fused = c->path == MOE_PATH_GEMV_FUSED && fused_decode_ok(*d);

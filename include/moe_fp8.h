@@ -67,7 +67,7 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Expert-pass kernel family. AUTO picks the wavefront GEMV family when
- * tokens <= 16 or x is fp32, and the bf16-MFMA grouped family otherwise.
+ * tokens <= 48 or x is fp32, and the bf16-MFMA grouped family otherwise.
  * The forced values exist so both families can be exercised at any size;
  * MFMA requires bf16 activations. MFMA_FP8 is the grouped family with both
  * expert contractions in E4M3 on both sides: x is quantised as

@@ -177,12 +177,15 @@ FWD_CASES = [  # (config, tokens, path, overrides)
     ("c0", 20, "gemv", {"experts": 1024, "top_k": 16, "shared": True}),
     ("c0", 3, "gemv", {"experts": 1024, "top_k": 1}),
     # expert counts that leave part of a lane row empty in the one-workgroup
-    # decode selection (two and four experts per lane), and the first token
-    # count the automatic choice sends to the grouped MFMA family with the
-    # multi-kernel selection and permutation
+    # decode selection (two and four experts per lane); the first token count
+    # past it (the GEMV family with the multi-kernel selection and
+    # permutation), the last that AUTO gives the GEMV family, and the first it
+    # sends to the grouped MFMA family
     ("c0", 9, "gemv", {"experts": 100, "top_k": 3, "shared": True}),
     ("c0", 16, "auto", {"experts": 200, "top_k": 5}),
     ("c1", 17, "auto", {}),
+    ("c1", 48, "auto", {}),
+    ("c1", 49, "auto", {}),
     # the single-launch decode layer
     ("c1", 1, "gemv_fused", {}),
     ("c1", 16, "gemv_fused", {}),
