@@ -34,8 +34,9 @@ struct Dims {
 
 // Router kernels and partial logits. The router writes partial logits per
 // slice of H; the top-k kernel sums the slices in slice order.
-//  * decode (T <= 16): wavefront dot products over slices of kRouterSlice
-//    columns (one slice when H < kRouterSlice);
+//  * decode and small batches (T <= kRouterDecodeTokens): wavefront dot
+//    products over slices of kRouterSlice columns (one slice when H <
+//    kRouterSlice), 16 tokens per workgroup;
 //  * prefill with bf16 activations (H a multiple of 64): MFMA tiles of
 //    kRouterTile tokens x kRouterTile experts over the router weights split
 //    exactly into three bf16 planes; H is cut into as many slices (a power of
@@ -46,9 +47,10 @@ struct Dims {
 //    slice.
 constexpr int kRouterSlice = 512;
 constexpr int kRouterTile = 128;
+constexpr int kRouterDecodeTokens = kAutoGemvTokens;
 enum RouterKind { kRouterDecode, kRouterMfma, kRouterGemm, kRouterNone };
 inline RouterKind router_kind(const Dims& d) {
-  if (d.T <= kGemvMaxTokens) {
+  if (d.T <= kRouterDecodeTokens) {
     if (d.H < kRouterSlice || d.H % kRouterSlice == 0) return kRouterDecode;
     return kRouterGemm;
   }

@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void router_slices_kernel(const void* __restri
                                                            const float* __restrict__ wr,
                                                            float* __restrict__ plog, int T,
                                                            int H, int E, int HS) {
-  router_slices_item<NT, XBF16>(x, wr, plog, T, H, E, HS, blockIdx.x, blockIdx.y);
+  router_slices_item<NT, XBF16>(x, wr, plog, T, H, E, HS, blockIdx.x, blockIdx.y,
+                                (int)blockIdx.z * 4 * NT);
 }
 
 template <bool XBF16>
@@ -120,8 +121,11 @@ static void slices_launch(const Dims& d, const void* x, const float* wr, float* 
                           hipStream_t s) {
   const int ns = router_slices(d);
   const int HS = d.H < kRouterSlice ? d.H : kRouterSlice;
-  const dim3 grid((d.E + 3) / 4, ns);
-  const int threads = 64 * (int)((d.T + NT - 1) / NT);
+  // up to four wavefronts (4 NT tokens) per workgroup; more tokens take
+  // more workgroups along z
+  const int64_t per = 4 * NT;
+  const dim3 grid((d.E + 3) / 4, ns, (unsigned)((d.T + per - 1) / per));
+  const int threads = 64 * (int)((std::min<int64_t>(d.T, per) + NT - 1) / NT);
   if (d.x_bf16)
     router_slices_kernel<NT, true><<<grid, threads, 0, s>>>(x, wr, plog, (int)d.T, d.H, d.E, HS);
   else

@@ -14,17 +14,18 @@ namespace moe {
 // partial sums across the wave. Token rows are read straight from global
 // memory; the expert rows are shared by the workgroup's wavefronts through the
 // cache.
-// (bx, by) = (expert quad, slice). Wavefronts whose tokens all lie past T
-// compute on clamped rows and write nothing.
+// (bx, by) = (expert quad, slice); tb: the workgroup's first token (its
+// wavefronts take tokens tb + NT w ..). Wavefronts whose tokens all lie
+// past T compute on clamped rows and write nothing.
 // COHERENT: the partial logits are stored at the point of coherence (for a
 // consumer in the same kernel).
 template <int NT, bool XBF16, bool COHERENT = false>
 __device__ __forceinline__ void router_slices_item(const void* __restrict__ x,
                                                    const float* __restrict__ wr,
                                                    float* __restrict__ plog, int T, int H, int E,
-                                                   int HS, int bx, int by) {
+                                                   int HS, int bx, int by, int tb = 0) {
   const int lane = threadIdx.x & 63;
-  const int t0 = (threadIdx.x >> 6) * NT;
+  const int t0 = tb + (threadIdx.x >> 6) * NT;
   const int h0 = by * HS;
   const int e0 = bx * 4;
   constexpr int J = kRouterSlice / 256;
