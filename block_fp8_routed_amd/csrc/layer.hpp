@@ -34,9 +34,11 @@ struct Dims {
 
 // Router kernels and partial logits. The router writes partial logits per
 // slice of H; the top-k kernel sums the slices in slice order.
-//  * decode and small batches (T <= kRouterDecodeTokens): wavefront dot
-//    products over slices of kRouterSlice columns (one slice when H <
-//    kRouterSlice), 16 tokens per workgroup;
+//  * decode and small batches (T <= 16, or T x E <= kRouterDecodeWork):
+//    wavefront dot products over slices of kRouterSlice columns (one slice
+//    when H < kRouterSlice), 16 tokens per workgroup (measured faster than
+//    the MFMA tiles through 256 tokens of 128 experts and 64 of 512, slower
+//    at 128 of 512);
 //  * prefill with bf16 activations (H a multiple of 64): MFMA tiles of
 //    kRouterTile tokens x kRouterTile experts over the router weights split
 //    exactly into three bf16 planes; H is cut into as many slices (a power of
@@ -47,13 +49,13 @@ struct Dims {
 //    slice.
 constexpr int kRouterSlice = 512;
 constexpr int kRouterTile = 128;
-constexpr int kRouterDecodeTokens = kAutoGemvTokens;
+constexpr int64_t kRouterDecodeWork = 32768;  // tokens x experts
 enum RouterKind { kRouterDecode, kRouterMfma, kRouterGemm, kRouterNone };
 inline RouterKind router_kind(const Dims& d) {
-  if (d.T <= kRouterDecodeTokens) {
-    if (d.H < kRouterSlice || d.H % kRouterSlice == 0) return kRouterDecode;
-    return kRouterGemm;
-  }
+  const bool slices_ok = d.H < kRouterSlice || d.H % kRouterSlice == 0;
+  if (slices_ok && (d.T <= kGemvMaxTokens || d.T * d.E <= kRouterDecodeWork))
+    return kRouterDecode;
+  if (d.T <= kGemvMaxTokens) return kRouterGemm;
   if (d.x_bf16 && d.H % 64 == 0) return kRouterMfma;
   return kRouterGemm;
 }
