@@ -176,10 +176,10 @@ hipError_t launch_select_permute_small(const Dims& d, const float* plog, const f
 //     second launch follows.
 //   perm_scatter: block b places its slots (place_slots): its wavefronts
 //     take consecutive sub-ranges, count per (wavefront, expert), take
-//     exclusive prefixes over wavefronts on top of its base (bbase[b][e], or
-//     after a one-block count offsets[e] plus its own count of the earlier
-//     slots), and walk their slots in order with ballot peer ranks, so rows
-//     keep slot order.
+//     exclusive prefixes over wavefronts on top of bbase[b][e] (after a
+//     one-block count, block b is its 1024-slot chunk b, whose bases the
+//     count took from a histogram per chunk), and walk their slots in order
+//     with ballot peer ranks, so rows keep slot order.
 constexpr int kPermBlockSlots = 512;  // slots per block (at most kPermMaxBlocks blocks)
 constexpr int kPermBatch = 4;         // slot loads per thread issued together
 constexpr int kPermMaxBlocks = kPermMaxBlocksHost;
@@ -294,16 +294,24 @@ __global__ __launch_bounds__(1024) void perm_count(
   // (place_slots), with the dynamic LDS as its 16 x E wavefront counters
   extern __shared__ int32_t wcnt[];
   __shared__ int32_t cnt[kMaxExperts];
+  // one block: a histogram per 1024-slot chunk (the placing blocks' ranges)
+  __shared__ int32_t cntc[kPermBatch][kMaxExperts];
   __shared__ int32_t tmp[4 * 64];
   __shared__ int last;
   const int tid = threadIdx.x;
   const int64_t TK = T * k;
   const int64_t per = (TK + nb - 1) / nb;
   const int64_t lo = (int64_t)blockIdx.x * per, hi = lo + per < TK ? lo + per : TK;
-  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  static_assert(kPermOneBlock == 1024 * kPermBatch, "one block: one load round, chunk i = batch i");
+  for (int e = tid; e < E; e += 1024) {
+    cnt[e] = 0;
+#pragma unroll
+    for (int i = 0; i < kPermBatch; ++i) cntc[i][e] = 0;
+  }
   __syncthreads();
   // kPermBatch slots per thread are loaded before any is counted (indices
-  // clamped, so the loads are unconditional and go out together)
+  // clamped, so the loads are unconditional and go out together); one block
+  // counts slot tid + 1024 i into chunk i's histogram
   for (int64_t s0 = lo + tid; s0 < hi; s0 += 1024 * kPermBatch) {
     int ev[kPermBatch];
 #pragma unroll
@@ -313,16 +321,23 @@ __global__ __launch_bounds__(1024) void perm_count(
     }
 #pragma unroll
     for (int i = 0; i < kPermBatch; ++i)
-      if (s0 + 1024 * i < hi && (unsigned)ev[i] < (unsigned)E) atomicAdd(&cnt[ev[i]], 1);
+      if (s0 + 1024 * i < hi && (unsigned)ev[i] < (unsigned)E)
+        atomicAdd(nb == 1 ? &cntc[i][ev[i]] : &cnt[ev[i]], 1);
   }
   __syncthreads();
   const int e = tid;  // from here on one expert per thread (E <= 1024)
+  // per-block bases for the placing blocks: one per counting block, or
+  // after a one-block count one per 1024-slot chunk
+  const int nbases = nb == 1 ? (int)((TK + 1023) / 1024) : nb;
   int c = 0;
   int32_t pre[kPermMaxBlocks];
-  if (nb == 1) {  // uniform: the one block holds every count
-    c = e < E ? cnt[e] : 0;
+  if (nb == 1) {  // uniform: the one block holds every count, per chunk
 #pragma unroll
-    for (int b = 0; b < kPermMaxBlocks; ++b) pre[b] = 0;
+    for (int b = 0; b < kPermMaxBlocks; ++b) {
+      const int v = (e < E && b < kPermBatch) ? cntc[b < kPermBatch ? b : 0][e < E ? e : 0] : 0;
+      pre[b] = c;
+      c += v;
+    }
   } else {
     for (int i = tid; i < E; i += 1024) bcnt[(size_t)blockIdx.x * E + i] = cnt[i];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(1024) void perm_count(
     offsets[e] = off;
 #pragma unroll
     for (int b = 0; b < kPermMaxBlocks; ++b)
-      if (b < nb) bbase[(size_t)b * E + e] = off + pre[b];
+      if (b < nbases) bbase[(size_t)b * E + e] = off + pre[b];
     cnt[e] = off;  // (thread e's own counter, read back by thread e only)
   }
   if (tid == 0) {
@@ -425,39 +440,16 @@ __global__ __launch_bounds__(1024) void perm_count(
   }
 }
 
-// lds: (16 + prefix) * E int32. prefix (uniform): the block's base per
-// expert is offsets[e] + its own count of the slots before its range (after
-// a one-block count, which leaves no per-block bases); otherwise bbase[b][e].
+// lds: 16 * E int32. Block b places slots [b per, (b + 1) per) on top of
+// its bases bbase[b][e].
 __global__ __launch_bounds__(1024) void perm_scatter(
-    const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int nb, int prefix,
+    const int32_t* __restrict__ topk, int64_t T, int k, int E, int S, int64_t per,
     const int32_t* __restrict__ bbase, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ pair, int32_t* __restrict__ inv, int32_t* __restrict__ rtok) {
-  extern __shared__ int32_t wcnt[];  // [16][E], then the prefix counts [E]
-  int32_t* pcnt = wcnt + 16 * E;
-  const int tid = threadIdx.x;
+  extern __shared__ int32_t wcnt[];  // [16][E]
   const int64_t TK = T * k;
-  const int64_t per = (TK + nb - 1) / nb;
   const int64_t blo = (int64_t)blockIdx.x * per, bhi = blo + per < TK ? blo + per : TK;
-  if (prefix) {  // count of each expert among slots [0, blo)
-    for (int i = tid; i < E; i += 1024) pcnt[i] = 0;
-    __syncthreads();
-    for (int64_t s0 = tid; s0 < blo; s0 += 1024 * kPermBatch) {
-      int pv[kPermBatch];
-#pragma unroll
-      for (int i = 0; i < kPermBatch; ++i) {
-        const int64_t s = s0 + 1024 * i;
-        pv[i] = topk[s < blo ? s : blo - 1];
-      }
-#pragma unroll
-      for (int i = 0; i < kPermBatch; ++i)
-        if (s0 + 1024 * i < blo && (unsigned)pv[i] < (unsigned)E) atomicAdd(&pcnt[pv[i]], 1);
-    }
-  }
-  // (place_slots synchronises the block before it reads a base)
-  place_slots(topk, k, E, blo, bhi,
-              [&](int e) {
-                return prefix ? offsets[e] + pcnt[e] : bbase[(size_t)blockIdx.x * E + e];
-              },
+  place_slots(topk, k, E, blo, bhi, [&](int e) { return bbase[(size_t)blockIdx.x * E + e]; },
               wcnt, pair, inv, rtok);
   if (S && blockIdx.x == 0) place_shared(T, TK, offsets[E], pair, inv, rtok);
 }
@@ -471,11 +463,9 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int
   const int64_t TK = d.T * d.k;
   const int nb = perm_blocks(TK);
   // up to kPermPlaceSlots slots (one round of 64 per wavefront) the counting
-  // block also places them, with no second launch; above that, a one-block
-  // count leaves the bases of one placing block only, and the placing
-  // blocks (1024 slots each) count their own prefixes, as long as the extra
-  // LDS row keeps the block within 64 KiB of dynamic LDS (else one placing
-  // block takes every slot)
+  // block also places them, with no second launch; above that the placing
+  // blocks take the counting blocks' ranges, or after a one-block count its
+  // 1024-slot chunks, with the bases perm_count left for each
   const int place_all = TK <= kPermPlaceSlots ? 1 : 0;
   const size_t wlds = (size_t)16 * d.E * sizeof(int32_t);  // at most 64 KiB (E <= 1024)
   perm_count<<<nb, 1024, place_all ? wlds : 0, s>>>(
@@ -485,11 +475,11 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk, const Work& w, int
       tile_rows > 0 && layer_one_launch(d) ? static_cast<uint64_t*>(w.sync) : nullptr, w.status,
       w.pair, w.inv, w.rtok, place_all);
   if (!place_all) {
-    const int prefix = (nb == 1 && (size_t)17 * d.E * sizeof(int32_t) <= 65536) ? 1 : 0;
-    const int nbs = prefix ? (int)((TK + 1023) / 1024) : nb;
-    perm_scatter<<<nbs, 1024, (size_t)(16 + prefix) * d.E * sizeof(int32_t), s>>>(
-        topk, d.T, d.k, d.E, d.S, nbs, prefix, w.pblock + (size_t)kPermMaxBlocks * d.E,
-        w.offsets, w.pair, w.inv, w.rtok);
+    const int64_t per = nb == 1 ? 1024 : (TK + nb - 1) / nb;
+    const int nbs = (int)((TK + per - 1) / per);
+    perm_scatter<<<nbs, 1024, wlds, s>>>(topk, d.T, d.k, d.E, d.S, per,
+                                         w.pblock + (size_t)kPermMaxBlocks * d.E, w.offsets,
+                                         w.pair, w.inv, w.rtok);
   }
   return hipGetLastError();
 }
