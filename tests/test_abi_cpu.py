@@ -291,3 +291,17 @@ def test_static_scratch_entry_refuses_oversized_calls():
     assert lib.moe_forward_static(FAKE, FAKE, None, ctypes.byref(b), None, 2, FAKE, None, None,
                                   None) == _lib.MOE_ERR_NULL
     assert moe.status_string(moe.MOE_ERR_TOO_LARGE) != "unknown status"
+
+
+@pytest.mark.parametrize("tokens,x_dtype,grouped", [(16, "bf16", False), (48, "bf16", False),
+                                                    (49, "bf16", True), (4096, "bf16", True),
+                                                    (4096, "f32", False)])
+def test_auto_family_choice(tokens, x_dtype, grouped):
+    """AUTO takes the wavefront GEMV family up to 48 tokens (bf16 x) or for
+    fp32 x at any size, and the grouped bf16 MFMA family otherwise; the
+    grouped families keep exponent bytes for h, which the layout shows."""
+    xdt = _lib.torch.bfloat16 if x_dtype == "bf16" else _lib.torch.float32
+    c = cfg(tokens=tokens, hidden=2048, experts=128, inter=768, top_k=8, block=128,
+            x_dtype=xdt, path="auto")
+    _, hexp_bytes = moe.workspace_region(c, moe.MOE_WS_H_EXPS)
+    assert (hexp_bytes > 0) == grouped
