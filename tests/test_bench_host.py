@@ -99,3 +99,24 @@ def test_traffic_report_picks_the_single_launch_layer(tmp_path, monkeypatch):
     entry = json.load(open(tmp_path / "traffic.json"))["c1:T16:gemv_fused"]
     assert entry["kernel"] == "decode_fused<"
     assert entry["traffic_bytes_per_launch"] == 504 * 1024
+
+
+def test_traffic_report_follows_the_library_family_choice(tmp_path, monkeypatch):
+    """Path auto: the dominant kernel is the one of the family the library
+    takes for the call (GEMV up to 48 bf16 tokens, the one-launch grouped
+    kernel above), read from the workspace layout, not from a copy of the
+    rule."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gemv = "void moe::gemv_gate_up<2048, 768, 128, 4, 4, true>(void const*, ...)"
+    layer = "void moe::mfma_layer<2048, 768>(unsigned short const*, ...)"
+    fetch = _csv(tmp_path / "f.csv", [(gemv, 300.0), (layer, 7000.0)])
+    write = _csv(tmp_path / "w.csv", [(gemv, 3.0), (layer, 70.0)])
+    mib = bench.COPY_MIB * 2 ** 20
+    copy_f = _csv(tmp_path / "cf.csv", [("MulFunctor<float>", mib / 1024)])
+    copy_w = _csv(tmp_path / "cw.csv", [("MulFunctor<float>", mib / 1024)])
+    for T, key, kernel in ((48, "c2:T48:gemv", "gemv_gate_up<"), (49, "c2:T49:mfma", "mfma_layer<")):
+        args = types.SimpleNamespace(traffic_report=[fetch, write, copy_f, copy_w], config="c2",
+                                     tokens=T, path="auto")
+        bench.traffic_report(args)
+        entry = json.load(open(tmp_path / "traffic.json"))[key]
+        assert entry["kernel"] == kernel
