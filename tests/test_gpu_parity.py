@@ -93,9 +93,13 @@ def test_activation_quantiser_matches_oracle(T, H):
 
 
 # ---------------------------------------------------------------- router ---
+# (the slices router takes T <= 16 or tokens x experts <= 32768: c1 17, c2
+# 256, c3 64 and c0e1024k16 at 32 tokens are its largest batches; c2 512, c3
+# 65 and c3 300 the MFMA router's)
 ROUTE_CASES = [
-    ("c0", None), ("c1", 1), ("c1", 4), ("c1", 16), ("c1", 17), ("c2", None),
-    ("c3", None), ("c3", 300), ("c4", None), ("c0e1024k16", 16), ("c0e1024k16", 37),
+    ("c0", None), ("c1", 1), ("c1", 4), ("c1", 16), ("c1", 17), ("c2", 256), ("c2", None),
+    ("c3", None), ("c3", 64), ("c3", 65), ("c3", 300), ("c4", None), ("c0e1024k16", 16),
+    ("c0e1024k16", 32), ("c0e1024k16", 37),
 ]
 
 
